@@ -1,0 +1,596 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test fixes one oracle function to a value printed on the pages, a closed
+form, an invariant, a library special case or a brute-force enumeration, so
+that a dropped term, a wrong sign or index, or a transposed operand anywhere in
+the oracle fails at least one of them.  All of these run on the CPU.
+"""
+import cmath
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import kvref as K
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ----------------------------------------------------------------------------
+# bf16 codec: a library special case (torch's float32 -> bfloat16 is RNE)
+# ----------------------------------------------------------------------------
+
+
+def test_bf16_encode_matches_torch_on_float32_inputs():
+    rng = np.random.default_rng(7)
+    bits = rng.integers(0, 2 ** 32, size=1_000_000, dtype=np.uint64).astype(np.uint32)
+    x32 = bits.view(np.float32)
+    x32 = x32[np.isfinite(x32)]
+    specials = np.array([0.0, -0.0, 1.0, 1.00390625, 1.01171875, 3.3895314e38, 3.3961e38,
+                         1e-40, -1e-40, 2.0 ** -133, 2.0 ** -134, 3 * 2.0 ** -135,
+                         np.float32(np.inf), -np.inf], dtype=np.float32)
+    x32 = np.concatenate([x32, specials, rng.standard_normal(100_000).astype(np.float32)])
+    ours = K.f64_to_bf16(x32.astype(np.float64))
+    ref = torch.from_numpy(x32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+def test_bf16_decode_is_exact_and_roundtrips():
+    allbits = np.arange(2 ** 16, dtype=np.uint32).astype(np.uint16)
+    vals = K.bf16_to_f64(allbits)
+    finite = np.isfinite(vals)
+    back = K.f64_to_bf16(vals[finite])
+    assert np.array_equal(back, allbits[finite])
+    ref = torch.from_numpy(allbits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(vals[finite], ref[finite])
+
+
+def test_bf16_rounds_once_from_float64():
+    # 1 + 2^-8 + 2^-30 lies just above the midpoint between two bf16 values:
+    # a single rounding goes up; rounding through float32 first would tie
+    # back down to 1.0.
+    x = 1.0 + 2.0 ** -8 + 2.0 ** -30
+    assert K.bf16_to_f64(K.f64_to_bf16(np.array([x])))[0] == 1.0 + 2.0 ** -7
+
+
+# ----------------------------------------------------------------------------
+# a1: rotary re-alignment
+# ----------------------------------------------------------------------------
+
+
+def test_rope_hand_example():
+    g = golden("rope_hand_example.json")
+    x = np.array(g["input"], dtype=np.float64)
+    out = K.rope_rotate(x, g["delta"], g["theta"], "half")
+    np.testing.assert_allclose(out, g["expected_half_values"], rtol=0, atol=5e-14)
+    np.testing.assert_allclose(K.rope_angles(g["delta"], g["theta"], g["head_dim"]),
+                               g["angles_rad"], rtol=1e-15)
+
+
+def _complex_rotate(x, delta, theta, style):
+    """Textbook form: pair (a, b) is the complex number a + ib times e^(i phi)."""
+    hd = x.shape[-1]
+    out = np.empty_like(x)
+    for i in range(hd // 2):
+        ia, ib = (i, i + hd // 2) if style == "half" else (2 * i, 2 * i + 1)
+        phi = delta * theta ** (-2.0 * i / hd)
+        z = (x[..., ia] + 1j * x[..., ib]) * cmath.exp(1j * phi)
+        out[..., ia], out[..., ib] = z.real, z.imag
+    return out
+
+
+@pytest.mark.parametrize("style", ["half", "interleaved"])
+@pytest.mark.parametrize("hd", [4, 64, 128])
+def test_rope_equals_complex_multiplication(style, hd):
+    rng = np.random.default_rng(hd)
+    x = rng.standard_normal((5, hd))
+    for delta, theta in [(37, 1e4), (8191, 5e5), (-32768, 1e6)]:
+        # angles reach |delta| radians: fp64 keeps them to about |delta| * 1e-16
+        np.testing.assert_allclose(K.rope_rotate(x, delta, theta, style),
+                                   _complex_rotate(x, delta, theta, style), rtol=0,
+                                   atol=1e-14 * max(1, abs(delta)))
+
+
+@pytest.mark.parametrize("style", ["half", "interleaved"])
+def test_rope_composition_inverse_and_norm(style):
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((7, 128))
+    p, d, theta = 1234, 4321, 5e5
+    two_step = K.rope_rotate(K.rope_rotate(x, p, theta, style), d, theta, style)
+    np.testing.assert_allclose(two_step, K.rope_rotate(x, p + d, theta, style), atol=1e-11)
+    back = K.rope_rotate(K.rope_rotate(x, d, theta, style), -d, theta, style)
+    np.testing.assert_allclose(back, x, atol=1e-13)
+    ia, ib = K._pairs(128, style)
+    y = K.rope_rotate(x, d, theta, style)
+    np.testing.assert_allclose(y[:, ia] ** 2 + y[:, ib] ** 2, x[:, ia] ** 2 + x[:, ib] ** 2,
+                               rtol=1e-13)
+
+
+def test_rope_relative_position_property():
+    # <R(p) q, R(p') k> depends only on p' - p.
+    rng = np.random.default_rng(2)
+    q, k = rng.standard_normal(128), rng.standard_normal(128)
+    base = None
+    for p in [0, 17, 5000]:
+        v = K.rope_rotate(q, p, 1e4) @ K.rope_rotate(k, p + 300, 1e4)
+        base = v if base is None else base
+        assert abs(v - base) < 1e-9
+
+
+def test_rope_interleaved_is_half_after_permutation():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((3, 64))
+    perm = np.concatenate([np.arange(0, 64, 2), np.arange(1, 64, 2)])   # interleaved -> half
+    y_int = K.rope_rotate(x, 99, 1e4, "interleaved")
+    y_half = K.rope_rotate(x[:, perm], 99, 1e4, "half")
+    np.testing.assert_allclose(y_int[:, perm], y_half, atol=1e-13)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_rope_shift_zero_delta_is_bitwise_identity(dtype):
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((2, 3, 2, 9, 64))
+    plane = K.store(x, dtype)
+    assert np.array_equal(K.rope_shift(plane, dtype, [0, 0, 0], 1e4), plane)
+
+
+def test_rope_shift_rounds_once_per_segment():
+    rng = np.random.default_rng(5)
+    x = K.store(rng.standard_normal((1, 2, 1, 4, 8)), "bf16")
+    out = K.rope_shift(x, "bf16", [3, -7], 1e4)
+    for s, d in enumerate([3, -7]):
+        exp = K.f64_to_bf16(_complex_rotate(K.bf16_to_f64(x[:, s]), d, 1e4, "half"))
+        assert np.array_equal(out[:, s], exp)
+
+
+# ----------------------------------------------------------------------------
+# a2: L2 score
+# ----------------------------------------------------------------------------
+
+
+def test_score_l2_hand_example():
+    # Two rows, one head, hd = 2, V plane (no rotation):
+    # row 0 differs by (3, 4) -> 5; row 1 by (0, 0) -> 0.
+    fresh = np.array([[[[[3.0, 4.0], [1.0, 1.0]]]]], dtype=np.float32)
+    reuse = np.array([[[[[0.0, 0.0], [1.0, 1.0]]]]], dtype=np.float32)
+    d = K.score_l2(fresh, reuse, "f32", 0)
+    assert d.tolist() == [[5.0, 0.0]]
+
+
+def test_score_l2_spans_heads_and_uses_aligned_keys():
+    rng = np.random.default_rng(6)
+    L, S, H, n, hd, theta = 2, 2, 3, 11, 8, 1e4
+    reuse = K.store(rng.standard_normal((L, S, H, n, hd)), "f32")
+    fresh = K.store(rng.standard_normal((L, S, H, n, hd)), "f32")
+    deltas = [5, 900]
+    d = K.score_l2(fresh, reuse, "f32", 1, deltas, theta)
+    for s in range(S):
+        for j in range(n):
+            al = _complex_rotate(reuse[1, s, :, j].astype(np.float64), deltas[s], theta, "half")
+            ref = np.linalg.norm((fresh[1, s, :, j].astype(np.float64) - al).ravel())
+            assert abs(d[s, j] - ref) <= 1e-6 * ref
+    # fresh equal to the aligned reuse -> all zero
+    fresh_eq = np.stack([K.rope_rotate(reuse[:, s].astype(np.float64), deltas[s], theta)
+                         for s in range(S)], axis=1)
+    d0 = K.score_l2(fresh_eq.astype(np.float64), reuse.astype(np.float64), "f32", 1, deltas, theta)
+    assert np.abs(d0).max() < 1e-5
+
+
+# ----------------------------------------------------------------------------
+# a4: top-b selection (brute force over all subsets)
+# ----------------------------------------------------------------------------
+
+
+def _brute_topb(scores, b):
+    """The unique b-subset S with (s_i > s_j) or (s_i == s_j and i < j) for i in S, j not in S."""
+    n = len(scores)
+    found = []
+    for sub in itertools.combinations(range(n), b):
+        inside = set(sub)
+        ok = all((scores[i] > scores[j]) or (scores[i] == scores[j] and i < j)
+                 for i in inside for j in range(n) if j not in inside)
+        if ok:
+            found.append(list(sub))
+    assert len(found) == 1
+    return found[0]
+
+
+def test_select_topb_brute_force_with_ties():
+    rng = np.random.default_rng(8)
+    for trial in range(60):
+        n = int(rng.integers(1, 9))
+        s = rng.integers(-2, 3, size=n).astype(np.float32)   # many ties
+        for b in range(n + 1):
+            idx, mask = K.select_topb(s[None, :], b)
+            assert idx[0].tolist() == _brute_topb(s.tolist(), b)
+            for j in range(n):
+                assert K.mask_bit(mask[0], j) == (j in idx[0])
+
+
+def test_select_topb_negative_zero_ties_with_zero():
+    idx, _ = K.select_topb(np.array([[-0.0, 0.0, -1.0]], dtype=np.float32), 1)
+    assert idx.tolist() == [[0]]
+
+
+def test_probe_budget_formula():
+    # b = ceil(r n): configuration 1 states b = 26 for r = 0.1, n = 256.
+    assert K.probe_budget(0.1, 256) == 26
+    assert K.probe_budget(0.15, 4096) == 615
+    assert K.probe_budget(0.1, 32768) == 3277
+    assert K.probe_budget(0.1, 4096) == 410
+    assert K.probe_budget(0.3, 10) == 3        # exact product, no float ceil spill
+    assert K.probe_budget(1.0, 77) == 77
+    assert K.probe_budget(0.0, 77) == 0
+
+
+# ----------------------------------------------------------------------------
+# a5 / a6: probe mean and apply
+# ----------------------------------------------------------------------------
+
+
+def _scalar_plane(values, hd=2):
+    """[1][1][1][n][hd] float32 plane with `values` in coordinate 0."""
+    p = np.zeros((1, 1, 1, len(values), hd), dtype=np.float32)
+    p[0, 0, 0, :, 0] = values
+    return p
+
+
+def test_worked_example_printed_on_the_page():
+    g = golden("aks_worked_example.json")
+    # rows 0, 1 are the probes (reused 0, fresh = their residual); rows 2..4 are A, B, C
+    reuse = _scalar_plane([0.0, 0.0] + [r["reused"] for r in g["rows"]])
+    fresh = _scalar_plane(g["probe_residuals"] + [r["fresh"] for r in g["rows"]])
+    idx = np.array([[0, 1]], dtype=np.int32)
+    mask = np.array([[0b11]], dtype=np.uint32)
+    # weights enter as min(d, 1): feed the printed weights as the check-layer scores
+    scores = np.array([[9.0, 9.0] + [r["weight"] for r in g["rows"]]], dtype=np.float32)
+    out, mu = K.correct(fresh, reuse, "f32", idx, mask, scores, w_lo=0.0, w_hi=1.0)
+    assert mu[0, 0, 0, 0] == np.float32(g["mu_hat"])
+    assert mu[0, 0, 0, 1] == 0.0
+    for k, r in enumerate(g["rows"]):
+        assert out[0, 0, 0, 2 + k, 0] == np.float32(r["corrected"])
+        res = abs(r["fresh"] - float(out[0, 0, 0, 2 + k, 0]))
+        assert abs(res - g["residual_after"][r["token"]]) < 1e-5
+    # probes keep their fresh values exactly
+    assert out[0, 0, 0, 0, 0] == fresh[0, 0, 0, 0, 0]
+    assert out[0, 0, 0, 1, 0] == fresh[0, 0, 0, 1, 0]
+
+
+def _random_case(rng, L=2, S=2, H=2, n=40, hd=8):
+    x = rng.standard_normal((L, S, H, n, hd))
+    return x
+
+
+def test_mean_fit_brute_force_loops_with_rank_state():
+    rng = np.random.default_rng(9)
+    L, S, H, n, hd, r, b, theta = 2, 2, 2, 12, 4, 2, 5, 1e4
+    reuse = K.store(rng.standard_normal((L, S, H, n, hd)), "f32")
+    fresh = K.store(rng.standard_normal((L, S, H, n, hd)), "f32")
+    A = rng.standard_normal((L, S, H, n, r)).astype(np.float32)
+    B = rng.standard_normal((L, S, H, r, hd)).astype(np.float32)
+    idx = np.array([sorted(rng.choice(n, b, replace=False)) for _ in range(S)], dtype=np.int32)
+    deltas = [3, -11]
+    mu = K.fit_mean(fresh, reuse, "f32", idx, deltas, theta, "half", A, B)
+    for l in range(L):
+        for s in range(S):
+            for h in range(H):
+                for d in range(hd):
+                    acc = 0.0
+                    for j in idx[s]:
+                        al = _complex_rotate(reuse[l, s, h, j].astype(np.float64), deltas[s],
+                                             theta, "half")[d]
+                        ab = sum(float(A[l, s, h, j, k]) * float(B[l, s, h, k, d]) for k in range(r))
+                        acc += float(fresh[l, s, h, j, d]) - al - ab
+                    assert abs(mu[l, s, h, d] - acc / b) <= 1e-6 * max(1.0, abs(acc / b))
+
+
+def test_full_budget_reproduces_fresh_bitwise():
+    rng = np.random.default_rng(10)
+    for dtype in ["f32", "bf16"]:
+        reuse = K.store(rng.standard_normal((2, 1, 2, 16, 8)), dtype)
+        fresh = K.store(rng.standard_normal((2, 1, 2, 16, 8)), dtype)
+        scores = rng.random((1, 16)).astype(np.float32)
+        idx, mask = K.select_topb(scores, 16)
+        out, _ = K.correct(fresh, reuse, dtype, idx, mask, scores, 0, 2, deltas=[7], theta=1e4)
+        assert np.array_equal(out, fresh)
+
+
+def test_zero_residual_gives_aligned_reuse():
+    rng = np.random.default_rng(11)
+    reuse = K.store(rng.standard_normal((2, 1, 2, 20, 8)), "f32")
+    deltas, theta = [13], 1e4
+    fresh = K.store(K.align_plane_f64(reuse.astype(np.float64), deltas, theta), "f32")
+    scores = K.score_l2(fresh, reuse, "f32", 1, deltas, theta)
+    assert scores.max() < 1e-5
+    idx, mask = K.select_topb(scores, 4)
+    out, mu = K.correct(fresh, reuse, "f32", idx, mask, None, deltas=deltas, theta=theta)
+    assert np.abs(mu).max() < 1e-6
+    np.testing.assert_allclose(out, K.rope_shift(reuse, "f32", deltas, theta), atol=1e-6)
+    # with delta = 0 the whole path is a bitwise identity
+    out0, mu0 = K.correct(reuse.copy(), reuse, "f32", idx, mask, None, deltas=[0], theta=theta)
+    assert np.array_equal(out0, reuse) and not mu0.any()
+
+
+def test_pure_offset_and_rank_state_are_removed_exactly():
+    rng = np.random.default_rng(12)
+    L, S, H, n, hd, r = 2, 1, 2, 64, 8, 3
+    x = rng.standard_normal((L, S, H, n, hd))
+    mu_true = rng.standard_normal((L, S, H, 1, hd))
+    A = rng.standard_normal((L, S, H, n, r)).astype(np.float32)
+    B = rng.standard_normal((L, S, H, r, hd)).astype(np.float32)
+    ab = np.einsum("lshnr,lshrd->lshnd", A.astype(np.float64), B.astype(np.float64))
+    deltas, theta = [321], 1e4
+    reuse = np.stack([K.rope_rotate(x[:, s], -deltas[s], theta) for s in range(S)], axis=1)
+    fresh = x + mu_true + ab                       # float64 "storage" for an exact identity
+    idx = np.array([[3, 9, 20, 41]], dtype=np.int32)
+    mask = np.zeros((1, 2), dtype=np.uint32)
+    for j in idx[0]:
+        mask[0, j // 32] |= np.uint32(1 << (j % 32))
+    mu = K.fit_mean(fresh.astype(np.float32), reuse.astype(np.float32), "f32", idx, deltas,
+                    theta, "half", A, B)
+    np.testing.assert_allclose(mu, mu_true[:, :, :, 0].astype(np.float32), atol=1e-5)
+    out, _ = K.correct(fresh.astype(np.float32), reuse.astype(np.float32), "f32", idx, mask,
+                       None, A=A, B=B, deltas=deltas, theta=theta)
+    np.testing.assert_allclose(out, fresh, atol=2e-5)
+    # without the state the same mean leaves exactly A B behind on non-probe rows
+    out2, _ = K.correct(fresh.astype(np.float32), reuse.astype(np.float32), "f32", idx, mask,
+                        None, deltas=deltas, theta=theta)
+    keep = np.setdiff1d(np.arange(n), idx[0])
+    resid = fresh[:, :, :, keep] - out2[:, :, :, keep]
+    centred = ab[:, :, :, keep] - ab[:, :, :, idx[0]].mean(axis=3, keepdims=True)
+    np.testing.assert_allclose(resid, centred, atol=5e-5)
+
+
+def test_error_identity_for_unweighted_mean():
+    # AgentKVShift: with w = 1, e = mu_hat - mu and the corrected residual of
+    # a non-probe row is xi_j - e.
+    rng = np.random.default_rng(13)
+    n, hd = 50, 6
+    reuse = rng.standard_normal((1, 1, 1, n, hd))
+    mu = rng.standard_normal(hd)
+    xi = 0.1 * rng.standard_normal((n, hd))
+    fresh = reuse.copy()
+    fresh[0, 0, 0] += mu + xi
+    idx = np.array([[1, 7, 30]], dtype=np.int32)
+    mask = np.zeros((1, 2), dtype=np.uint32)
+    for j in idx[0]:
+        mask[0, j // 32] |= np.uint32(1 << (j % 32))
+    out, mu_hat = K.correct(fresh.astype(np.float32), reuse.astype(np.float32), "f32", idx, mask)
+    e = mu_hat[0, 0, 0].astype(np.float64) - mu
+    keep = np.setdiff1d(np.arange(n), idx[0])
+    r_corr = fresh[0, 0, 0, keep] - out[0, 0, 0, keep]
+    np.testing.assert_allclose(r_corr, xi[keep] - e, atol=2e-6)
+
+
+def test_weights_clip_and_scope():
+    # w multiplies only the mean; the rank term is added unweighted; no
+    # scores means w = 1.
+    w = K.weights(np.array([-1.0, 0.5, 3.0], dtype=np.float32), 0.0, 2.0, 3)
+    assert w.tolist() == [0.0, 0.5, 2.0]
+    assert K.weights(None, 0.0, 2.0, 4).tolist() == [1.0] * 4
+    reuse = np.zeros((1, 1, 1, 3, 2), dtype=np.float32)
+    mu = np.full((1, 1, 1, 2), 1.0, dtype=np.float32)
+    A = np.ones((1, 1, 1, 3, 1), dtype=np.float32)
+    B = np.full((1, 1, 1, 1, 2), 10.0, dtype=np.float32)
+    out = K.apply(reuse, "f32", None, mu, np.array([[0.0, 0.5, 5.0]], dtype=np.float32),
+                  0.0, 2.0, A, B)
+    assert out[0, 0, 0, :, 0].tolist() == [10.0, 10.5, 12.0]
+
+
+def test_empty_budget_is_pure_realignment():
+    rng = np.random.default_rng(14)
+    reuse = K.store(rng.standard_normal((1, 1, 2, 10, 8)), "bf16")
+    fresh = K.store(rng.standard_normal((1, 1, 2, 10, 8)), "bf16")
+    idx = np.zeros((1, 0), dtype=np.int32)
+    mask = np.zeros((1, 1), dtype=np.uint32)
+    out, mu = K.correct(fresh, reuse, "bf16", idx, mask, deltas=[5], theta=1e4)
+    assert not mu.any()
+    assert np.array_equal(out, K.rope_shift(reuse, "bf16", [5], 1e4))
+
+
+def test_fresh_by_slot_matches_dense_fresh():
+    rng = np.random.default_rng(15)
+    reuse = K.store(rng.standard_normal((2, 2, 2, 30, 8)), "bf16")
+    fresh = K.store(rng.standard_normal((2, 2, 2, 30, 8)), "bf16")
+    idx = np.array([[0, 4, 29], [2, 3, 17]], dtype=np.int32)
+    compact = np.stack([fresh[:, s][:, :, idx[s]] for s in range(2)], axis=1)
+    a = K.fit_mean(fresh, reuse, "bf16", idx, [1, 2], 1e4)
+    b = K.fit_mean(compact, reuse, "bf16", idx, [1, 2], 1e4, fresh_by_slot=True)
+    assert np.array_equal(a, b)
+
+
+# ----------------------------------------------------------------------------
+# a3: draft attention mass
+# ----------------------------------------------------------------------------
+
+
+def test_softmax_counterexample_printed_on_the_page():
+    g = golden("aks_softmax_l1.json")
+    d = np.abs(K.softmax(np.array(g["z_prime"])) - K.softmax(np.array(g["z"]))).sum()
+    assert round(float(d), g["printed_decimals"]) == g["l1_printed"]
+    # closed form: 2 (sigma(0.2) - 1/2)
+    assert abs(d - 2 * (1 / (1 + math.exp(-0.2)) - 0.5)) < 1e-15
+
+
+def _draft_case(rng, L=3, H=2, Hq=4, T=2, n=13, hd=8):
+    q = K.f64_to_bf16(rng.standard_normal((L, Hq, T, hd)))
+    k = K.f64_to_bf16(rng.standard_normal((L, 1, H, n, hd)))
+    return q, k
+
+
+def test_draft_mass_sums_to_rows_times_layers():
+    rng = np.random.default_rng(16)
+    q, k = _draft_case(rng)
+    a = K.score_draft(q, k, [17], 1e4, first_layer=1)
+    assert abs(float(a.astype(np.float64).sum()) - (3 - 1) * 4 * 2) < 1e-5
+    assert (a > 0).all()
+
+
+def test_draft_brute_force_scalar_loops():
+    rng = np.random.default_rng(17)
+    L, H, Hq, T, n, hd, theta, delta = 3, 2, 4, 2, 7, 4, 1e4, 9
+    q, k = _draft_case(rng, L, H, Hq, T, n, hd)
+    a = K.score_draft(q, k, [delta], theta, first_layer=1)
+    qf, kf = K.bf16_to_f64(q), K.bf16_to_f64(k)
+    ref = [0.0] * n
+    for l in range(1, L):
+        for h in range(Hq):
+            g = h // (Hq // H)
+            keys = [_complex_rotate(kf[l, 0, g, j], delta, theta, "half") for j in range(n)]
+            for t in range(T):
+                z = [sum(qf[l, h, t, d] * keys[j][d] for d in range(hd)) / math.sqrt(hd)
+                     for j in range(n)]
+                m = max(z)
+                e = [math.exp(v - m) for v in z]
+                tot = sum(e)
+                for j in range(n):
+                    ref[j] += e[j] / tot
+    np.testing.assert_allclose(a[0], np.array(ref, dtype=np.float32), rtol=2e-7)
+
+
+def test_draft_common_key_shift_invariance():
+    # AgentKVShift, "Limitations": adding one vector to every visible key
+    # leaves the softmax unchanged.  A common shift c of the stored keys of a
+    # segment is a common shift R(delta) c of its aligned keys.  Small integer
+    # keys and shifts keep k + c exact in bf16.
+    rng = np.random.default_rng(18)
+    L, H, Hq, T, n, hd = 3, 2, 4, 2, 11, 8
+    q = K.f64_to_bf16(rng.standard_normal((L, Hq, T, hd)))
+    k = rng.integers(-4, 5, size=(L, 1, H, n, hd)).astype(np.float64)
+    c = rng.integers(-2, 3, size=(L, 1, H, 1, hd)).astype(np.float64)
+    a0 = K.score_draft(q, K.f64_to_bf16(k), [5], 1e4)
+    a1 = K.score_draft(q, K.f64_to_bf16(k + c), [5], 1e4)
+    np.testing.assert_allclose(a1, a0, rtol=2e-6)
+    assert not np.allclose(K.score_draft(q, K.f64_to_bf16(k + rng.integers(-2, 3, size=k.shape)),
+                                         [5], 1e4), a0, rtol=1e-3)
+
+
+def test_draft_gqa_group_one_is_plain_multihead():
+    rng = np.random.default_rng(19)
+    q, k = _draft_case(rng, H=4, Hq=4, n=9)
+    a = K.score_draft(q, k, [3], 1e4)
+    # With 8 query heads over 4 key heads, query heads 2h and 2h+1 read key
+    # head h.  Make both copies of the old query head h: the mass doubles.
+    q2 = np.repeat(q, 2, axis=1)
+    a2 = K.score_draft(q2, k, [3], 1e4)
+    np.testing.assert_allclose(a2, 2 * a, rtol=1e-6)
+
+
+def test_query_rotation_identity():
+    # q . R(d) k = R(-d) q . k  (the kernel scores without rotating keys)
+    rng = np.random.default_rng(20)
+    q, k = rng.standard_normal(128), rng.standard_normal(128)
+    lhs = q @ K.rope_rotate(k, 777, 1e6)
+    rhs = K.rope_rotate(q, -777, 1e6) @ k
+    assert abs(lhs - rhs) < 1e-11
+
+
+# ----------------------------------------------------------------------------
+# a7: paged addressing
+# ----------------------------------------------------------------------------
+
+
+def test_paged_offsets_hand_computed():
+    # 2 segments x 4 tokens, page size 2, 2 heads, hd 3, 4 pages, 1 layer.
+    pt = np.array([[2, 0], [3, 1]], dtype=np.int32)
+    # s_token = H*hd = 6, s_page = 2*6 = 12, s_layer = 4*12 = 48
+    cases = {  # (l, s, h, j) -> offset worked by hand
+        (0, 0, 0, 0): 2 * 12,
+        (0, 0, 1, 1): 2 * 12 + 6 + 3,
+        (0, 0, 0, 2): 0,
+        (0, 1, 1, 3): 1 * 12 + 6 + 3,
+        (1, 1, 0, 0): 48 + 3 * 12,
+    }
+    for (l, s, h, j), off in cases.items():
+        assert K.paged_offset(pt, 2, 48, 12, 6, 3, l, s, h, j) == off
+
+
+def test_paged_tagging_roundtrip():
+    rng = np.random.default_rng(21)
+    L, S, H, n, hd, ps = 2, 3, 2, 8, 4, 2
+    n_pages = 14
+    pt = rng.permutation(n_pages)[: S * n // ps].reshape(S, n // ps).astype(np.int32)
+    tag = np.zeros((L, S, H, n, hd), dtype=np.float32)
+    for l, s, h, j in itertools.product(range(L), range(S), range(H), range(n)):
+        tag[l, s, h, j] = [l, s, h, j]
+    pool = np.full(L * n_pages * ps * H * hd, -1.0, dtype=np.float32)
+    K.paged_scatter(pool, tag, pt, ps)
+    assert np.array_equal(K.paged_gather(pool, pt, ps, L, H, n, hd), tag)
+    # every untouched page stays untouched
+    used = np.zeros(n_pages, dtype=bool)
+    used[pt.ravel()] = True
+    pv = pool.reshape(L, n_pages, -1)
+    assert (pv[:, ~used] == -1).all() and (pv[:, used] != -1).any()
+
+
+# ----------------------------------------------------------------------------
+# a8 / a9: block-sparse diff
+# ----------------------------------------------------------------------------
+
+
+def test_diff_roundtrip_lossless_with_zero_shift_and_zero_eps():
+    rng = np.random.default_rng(22)
+    L, A, H, n, hd, bt = 2, 3, 2, 37, 8, 16      # ragged last block
+    master_k = K.store(rng.standard_normal((L, 1, H, n, hd)), "bf16")
+    master_v = K.store(rng.standard_normal((L, 1, H, n, hd)), "bf16")
+    sib_k = np.repeat(master_k, A, axis=1)
+    sib_v = np.repeat(master_v, A, axis=1)
+    sib_k[1, 0, 1, 5, 3] ^= 1                      # one bit flipped -> block 0 listed
+    sib_v[0, 2, 0, 36, 0] ^= 4                     # the ragged tail block
+    d = K.diff_encode(master_k, master_v, sib_k, sib_v, [0] * A, 1e4, 0.0, bt)
+    assert d["total"] == 2
+    assert d["offsets"].tolist() == [0, 0, 1, 1, 1, 2, 2]
+    assert d["block_idx"].tolist() == [0, 2]
+    ok, ov = K.diff_decode(master_k, master_v, d, [0] * A, 1e4, A, bt)
+    assert np.array_equal(ok, sib_k) and np.array_equal(ov, sib_v)
+
+
+def test_diff_recovers_planted_blocks_and_empty_diff_is_rotated_master():
+    from synthetic import CONFIGS, draw_collective
+    cfg = CONFIGS["c3"].replace(n_layers=2, n_kv_heads=2, n_tokens=160, n_segs=3)
+    raw = draw_collective(cfg, "cpu")
+    theta, bt = cfg.theta, cfg.block_tokens
+    offs = raw["offsets"].tolist()
+    yk = raw["y_k"].view(torch.int16).numpy().view(np.uint16)
+    yv = raw["y_v"].view(torch.int16).numpy().view(np.uint16)
+    mk = raw["master_k"].view(torch.int16).numpy().view(np.uint16)
+    mv = raw["master_v"].view(torch.int16).numpy().view(np.uint16)
+    sib_k = K.rope_shift(yk, "bf16", offs, theta)
+    d = K.diff_encode(mk, mv, sib_k, yv, [-o for o in offs], theta, cfg.eps, bt)
+    nb = 10
+    for a in range(3):
+        for l in range(2):
+            flagged = [K.mask_bit(d["mask"][a, l], beta) for beta in range(nb)]
+            assert flagged == raw["planted"][a].tolist()
+    ok, ov = K.diff_decode(mk, mv, d, offs, theta, 3, bt)
+    assert np.array_equal(ov, yv)
+    err = np.abs(K.bf16_to_f64(ok) - K.bf16_to_f64(sib_k))
+    assert err.max() < 0.1                           # two roundings of a rotation
+    empty = {"mask": np.zeros_like(d["mask"]), "offsets": np.zeros(7, dtype=np.int64),
+             "vals_k": d["vals_k"][:0], "vals_v": d["vals_v"][:0], "block_idx": d["block_idx"][:0]}
+    ek, ev = K.diff_decode(mk, mv, empty, offs, theta, 3, bt)
+    for a in range(3):
+        assert np.array_equal(ek[:, a:a + 1], K.rope_shift(mk, "bf16", [offs[a]], theta))
+        assert np.array_equal(ev[:, a], mv[:, 0])
+
+
+def test_storage_formulas_printed_on_the_page():
+    g = golden("td_storage.json")
+    for c in g["cases"]:
+        full = 1.0
+        diff = full / c["R"]
+        assert abs(K.mirror_ratio(full, diff) - c["R"]) < 1e-12
+        if "mirror_percent" in c:
+            assert round(100 * diff) == c["mirror_percent"]
+        cost = K.group_cost(c["N"], c["R"])
+        assert round(cost, 1) == c["cost_printed"]
+        assert round(c["N"] / round(cost, 1), 1) == c["reduction_printed"]
