@@ -1,0 +1,227 @@
+// Shared device helpers for the kvfix HIP kernels (gfx950, wave64).
+//
+// Lane-to-row map.  A row is head_dim contiguous elements of one (layer,
+// segment, head, token).  G = HD / (2 V) lanes serve one row, V being the
+// elements in 16 bytes (8 bf16 or 4 fp32).  Each lane moves two 16-byte parts
+// of its row and owns V rotary pairs entirely, so a rotation never needs a
+// cross-lane exchange:
+//   rotate-half : part 0 = dims [gV, gV+V), part 1 = dims [HD/2+gV, HD/2+gV+V);
+//                 pair m = (part0[m], part1[m])
+//   interleaved : parts 0,1 = dims [2gV, 2gV+2V); pair m = (dim 2gV+2m, 2gV+2m+1)
+// In both cases pair m of lane g has frequency index gV + m.
+// A wave covers RPW = 64 / G rows per step.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kvfix.h"
+
+namespace kvfix {
+
+constexpr int kWave = 64;
+constexpr int kStyleNone = -1;   // value plane: no rotation
+constexpr int kStyleHalf = KVFIX_ROPE_HALF;
+constexpr int kStyleInter = KVFIX_ROPE_INTERLEAVED;
+constexpr int kMaxHeadDim = 256;
+
+typedef uint16_t bf16_t;          // bfloat16 storage (bit pattern)
+typedef uint32_t vu4 __attribute__((ext_vector_type(4)));   // one 16-byte vector
+
+// Device view of a plane (element strides; byte base pointer).
+struct DPlane {
+  char* data;
+  int64_t s_layer, s_seg, s_head, s_token, s_page;
+  const int32_t* page_table;
+  int32_t page_size, pages_per_seg;
+  int64_t n_pool_pages;
+};
+
+inline DPlane make_dplane(const kvfix_plane& p) {
+  DPlane d;
+  d.data = static_cast<char*>(p.data);
+  d.s_layer = p.s_layer; d.s_seg = p.s_seg; d.s_head = p.s_head; d.s_token = p.s_token;
+  d.s_page = p.s_page; d.page_table = p.page_table; d.page_size = p.page_size;
+  d.pages_per_seg = p.pages_per_seg; d.n_pool_pages = p.n_pool_pages;
+  return d;
+}
+
+// Element offset of row (l, s, h, j), or -1 if its page id is out of range.
+__device__ __forceinline__ int64_t row_offset(const DPlane& p, int l, int s, int h, int j) {
+  if (p.page_table == nullptr)
+    return (int64_t)l * p.s_layer + (int64_t)s * p.s_seg + (int64_t)h * p.s_head +
+           (int64_t)j * p.s_token;
+  const int page = p.page_table[(int64_t)s * p.pages_per_seg + j / p.page_size];
+  if (page < 0 || (int64_t)page >= p.n_pool_pages) return -1;
+  return (int64_t)l * p.s_layer + (int64_t)page * p.s_page +
+         (int64_t)(j % p.page_size) * p.s_token + (int64_t)h * p.s_head;
+}
+
+template <typename T> struct Vec;
+template <> struct Vec<float> { static constexpr int N = 4; };
+template <> struct Vec<bf16_t> { static constexpr int N = 8; };
+
+template <typename T, int HD, int STYLE>
+struct RowMap {
+  static constexpr int V = Vec<T>::N;
+  static constexpr int G = HD / (2 * V);
+  static constexpr int RPW = kWave / G;
+  static_assert(G >= 1 && G <= kWave && (kWave % G) == 0, "unsupported head_dim");
+  __device__ static constexpr int off0(int g) { return STYLE == kStyleInter ? 2 * g * V : g * V; }
+  __device__ static constexpr int off1(int g) {
+    return STYLE == kStyleInter ? 2 * g * V + V : HD / 2 + g * V;
+  }
+  __device__ static constexpr int dim_a(int g, int m) {
+    return STYLE == kStyleInter ? 2 * g * V + 2 * m : g * V + m;
+  }
+  __device__ static constexpr int dim_b(int g, int m) {
+    return STYLE == kStyleInter ? 2 * g * V + 2 * m + 1 : HD / 2 + g * V + m;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// 16-byte vector codecs
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ vu4 ld16(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const vu4*>(p));
+}
+__device__ __forceinline__ vu4 ld16_cached(const void* p) {
+  return *reinterpret_cast<const vu4*>(p);
+}
+__device__ __forceinline__ void st16(void* p, vu4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<vu4*>(p));
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float -> bf16 bits, round to nearest even (gfx950 v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const __bf16 a = static_cast<__bf16>(lo);
+  const __bf16 b = static_cast<__bf16>(hi);
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// double -> float rounded to odd: exact results pass through; inexact ones
+// are truncated and get their last bit set.  Rounding that float to bf16
+// (nearest even) then equals a single rounding of the double to bf16.
+__device__ __forceinline__ float f64_to_f32_odd(double d) {
+  float f = __double2float_rz(d);
+  if ((double)f != d && d == d) f = __uint_as_float(__float_as_uint(f) | 1u);
+  return f;
+}
+
+template <typename C> __device__ __forceinline__ float to_bf16_input(C x);
+template <> __device__ __forceinline__ float to_bf16_input<float>(float x) { return x; }
+template <> __device__ __forceinline__ float to_bf16_input<double>(double x) {
+  return f64_to_f32_odd(x);
+}
+
+// Unpack 16 bytes of T into V compute values.
+template <typename T, typename C> struct Codec;
+
+template <typename C> struct Codec<bf16_t, C> {
+  static constexpr int V = 8;
+  __device__ static __forceinline__ void unpack(vu4 v, C* x) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = (C)bf16_lo(w[i]);
+      x[2 * i + 1] = (C)bf16_hi(w[i]);
+    }
+  }
+  __device__ static __forceinline__ vu4 pack(const C* x) {
+    vu4 v;
+    v.x = pack_bf16x2(to_bf16_input<C>(x[0]), to_bf16_input<C>(x[1]));
+    v.y = pack_bf16x2(to_bf16_input<C>(x[2]), to_bf16_input<C>(x[3]));
+    v.z = pack_bf16x2(to_bf16_input<C>(x[4]), to_bf16_input<C>(x[5]));
+    v.w = pack_bf16x2(to_bf16_input<C>(x[6]), to_bf16_input<C>(x[7]));
+    return v;
+  }
+};
+
+template <typename C> struct Codec<float, C> {
+  static constexpr int V = 4;
+  __device__ static __forceinline__ void unpack(vu4 v, C* x) {
+    x[0] = (C)__uint_as_float(v.x);
+    x[1] = (C)__uint_as_float(v.y);
+    x[2] = (C)__uint_as_float(v.z);
+    x[3] = (C)__uint_as_float(v.w);
+  }
+  __device__ static __forceinline__ vu4 pack(const C* x) {
+    vu4 v;
+    v.x = __float_as_uint((float)x[0]);
+    v.y = __float_as_uint((float)x[1]);
+    v.z = __float_as_uint((float)x[2]);
+    v.w = __float_as_uint((float)x[3]);
+    return v;
+  }
+};
+
+// Split the two 16-byte parts of a lane into its V pairs (a[m], b[m]).
+template <int STYLE, int V, typename C>
+__device__ __forceinline__ void parts_to_pairs(const C* p0, const C* p1, C* a, C* b) {
+  if constexpr (STYLE == kStyleInter) {
+#pragma unroll
+    for (int m = 0; m < V; ++m) {
+      const int e0 = 2 * m, e1 = 2 * m + 1;
+      a[m] = e0 < V ? p0[e0] : p1[e0 - V];
+      b[m] = e1 < V ? p0[e1] : p1[e1 - V];
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < V; ++m) { a[m] = p0[m]; b[m] = p1[m]; }
+  }
+}
+
+template <int STYLE, int V, typename C>
+__device__ __forceinline__ void pairs_to_parts(const C* a, const C* b, C* p0, C* p1) {
+  if constexpr (STYLE == kStyleInter) {
+#pragma unroll
+    for (int m = 0; m < V; ++m) {
+      const int e0 = 2 * m, e1 = 2 * m + 1;
+      if (e0 < V) p0[e0] = a[m]; else p1[e0 - V] = a[m];
+      if (e1 < V) p0[e1] = b[m]; else p1[e1 - V] = b[m];
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < V; ++m) { p0[m] = a[m]; p1[m] = b[m]; }
+  }
+}
+
+// Rotate the pairs forward by the angles whose cos/sin are given.
+template <int V, typename C>
+__device__ __forceinline__ void rotate_pairs(C* a, C* b, const C* c, const C* s) {
+#pragma unroll
+  for (int m = 0; m < V; ++m) {
+    const C x = a[m], y = b[m];
+    a[m] = x * c[m] - y * s[m];
+    b[m] = y * c[m] + x * s[m];
+  }
+}
+
+// Host-side argument block carrying the rotary inverse frequencies
+// theta^(-2i/hd), computed on the host in fp64 (same formula as the angles'
+// definition) so that every kernel uses identical frequencies.
+struct RopeArgs {
+  const int64_t* delta;
+  double inv_freq[kMaxHeadDim / 2];
+};
+
+// Fill cos/sin of the HD/2 pair angles for a shift of delta positions into
+// LDS (fp64 angle and sincos, stored in C).  Called by the whole block;
+// followed by __syncthreads() at the call site.
+template <int HD, typename C>
+__device__ __forceinline__ void rope_table(const RopeArgs& r, int64_t delta, C* tc, C* ts) {
+  for (int t = threadIdx.x; t < HD / 2; t += blockDim.x) {
+    const double phi = (double)delta * r.inv_freq[t];
+    double sv, cv;
+    sincos(phi, &sv, &cv);
+    tc[t] = (C)cv;
+    ts[t] = (C)sv;
+  }
+}
+
+}  // namespace kvfix

@@ -1,0 +1,281 @@
+// L2 divergence score (a2) and top-b selection (a4).
+//
+// score: one 256-thread block per (segment, RPW tokens).  The four waves
+// split the KV heads; each lane accumulates (fresh - align(reuse))^2 of its
+// pairs in fp64, lanes of a row reduce by a fixed butterfly, the waves add in
+// index order, and sqrt is rounded once to fp32.
+//
+// select: one 1024-thread block per row.  Scores become order-preserving
+// 32-bit keys (NaN lowest, -0 = +0).  Four 8-bit radix passes (LDS integer
+// histograms) find the key T of the b-th largest element and how many
+// elements equal to T are still needed; then a block scan over contiguous
+// per-thread index ranges keeps every key > T and the lowest-index keys == T,
+// writing indices in ascending order and the bitmask word by word.
+#include <type_traits>
+
+#include "common.h"
+#include "host_util.h"
+
+namespace kvfix {
+
+constexpr int kScoreBlock = 256;
+
+struct ScoreParams {
+  DPlane fresh, reuse;
+  int32_t fl, rl;                 // layer read in each plane
+  RopeArgs rope;
+  float* scores;
+  int32_t S, H, n, tok_blocks;
+};
+
+template <typename T, int HD, int STYLE>
+__global__ __launch_bounds__(kScoreBlock) void score_l2_kernel(ScoreParams P) {
+  constexpr int MS = STYLE == kStyleNone ? kStyleHalf : STYLE;
+  using M = RowMap<T, HD, MS>;
+  using Cd = Codec<T, double>;
+  constexpr int V = M::V, G = M::G, RPW = M::RPW;
+  constexpr int W = kScoreBlock / kWave;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int g = lane % G, rw = lane / G;
+  const int tb = blockIdx.x % P.tok_blocks;
+  const int s = blockIdx.x / P.tok_blocks;
+  const int j = tb * RPW + rw;
+
+  __shared__ double tc[HD / 2], ts[HD / 2];
+  __shared__ double part[W][RPW];
+  if constexpr (STYLE != kStyleNone) rope_table<HD, double>(P.rope, P.rope.delta[s], tc, ts);
+  __syncthreads();
+  double cs[V], sn[V];
+  if constexpr (STYLE != kStyleNone) {
+#pragma unroll
+    for (int m = 0; m < V; ++m) { cs[m] = tc[g * V + m]; sn[m] = ts[g * V + m]; }
+  }
+
+  double acc = 0.0;
+  if (j < P.n) {
+    for (int h = wave; h < P.H; h += W) {
+      const int64_t fo = row_offset(P.fresh, P.fl, s, h, j);
+      const int64_t ro = row_offset(P.reuse, P.rl, s, h, j);
+      if (fo < 0 || ro < 0) continue;
+      const T* fr = reinterpret_cast<const T*>(P.fresh.data) + fo;
+      const T* rr = reinterpret_cast<const T*>(P.reuse.data) + ro;
+      const vu4 f0 = ld16(fr + M::off0(g)), f1 = ld16(fr + M::off1(g));
+      const vu4 q0 = ld16(rr + M::off0(g)), q1 = ld16(rr + M::off1(g));
+      double p0[V], p1[V], fa[V], fb[V], ra[V], rb[V];
+      Cd::unpack(f0, p0);
+      Cd::unpack(f1, p1);
+      parts_to_pairs<MS, V>(p0, p1, fa, fb);
+      Cd::unpack(q0, p0);
+      Cd::unpack(q1, p1);
+      parts_to_pairs<MS, V>(p0, p1, ra, rb);
+      if constexpr (STYLE != kStyleNone) rotate_pairs<V>(ra, rb, cs, sn);
+#pragma unroll
+      for (int m = 0; m < V; ++m) {
+        const double da = fa[m] - ra[m], db = fb[m] - rb[m];
+        acc = fma(da, da, acc);
+        acc = fma(db, db, acc);
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 1; off < G; off <<= 1) acc += __shfl_xor(acc, off);
+  if (g == 0) part[wave][rw] = acc;
+  __syncthreads();
+  if (threadIdx.x < RPW) {
+    const int jj = tb * RPW + threadIdx.x;
+    if (jj < P.n) {
+      double t = 0.0;
+#pragma unroll
+      for (int w = 0; w < W; ++w) t += part[w][threadIdx.x];
+      P.scores[(int64_t)s * P.n + jj] = (float)sqrt(t);
+    }
+  }
+}
+
+template <typename T, int HD, int STYLE>
+struct ScoreLaunch {
+  static kvfix_status run(const ScoreParams& P, hipStream_t st) {
+    constexpr int MS = STYLE == kStyleNone ? kStyleHalf : STYLE;
+    constexpr int RPW = RowMap<T, HD, MS>::RPW;
+    ScoreParams Q = P;
+    Q.tok_blocks = (P.n + RPW - 1) / RPW;
+    const int64_t grid = (int64_t)Q.tok_blocks * P.S;
+    if (grid > kMaxGrid) return KVFIX_ERR_ARG;
+    score_l2_kernel<T, HD, STYLE><<<dim3((unsigned)grid), dim3(kScoreBlock), 0, st>>>(Q);
+    return launch_status();
+  }
+};
+
+// ---------------------------------------------------------------------------
+// top-b selection
+// ---------------------------------------------------------------------------
+
+constexpr int kSelBlock = 1024;
+
+__device__ __forceinline__ uint32_t order_key(float f) {
+  if (f != f) return 0u;                                   // NaN ranks lowest
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) == 0u) u = 0u;                     // -0 == +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Exclusive block-wide scan of one value per thread (fixed order).
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* lds,
+                                                        uint32_t* total) {
+  const int t = threadIdx.x;
+  lds[t] = v;
+  __syncthreads();
+  for (int off = 1; off < kSelBlock; off <<= 1) {
+    const uint32_t add = t >= off ? lds[t - off] : 0u;
+    __syncthreads();
+    lds[t] += add;
+    __syncthreads();
+  }
+  const uint32_t incl = lds[t];
+  *total = lds[kSelBlock - 1];
+  __syncthreads();
+  return incl - v;
+}
+
+__global__ __launch_bounds__(kSelBlock) void select_topb_kernel(const float* __restrict__ scores,
+                                                                int n, int b,
+                                                                int32_t* __restrict__ idx,
+                                                                uint32_t* __restrict__ mask,
+                                                                int words) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t scan[kSelBlock];
+  __shared__ uint32_t sh_prefix, sh_remaining;
+  const int row = blockIdx.x;
+  const int t = threadIdx.x;
+  const float* sc = scores + (int64_t)row * n;
+  int32_t* out_idx = idx + (int64_t)row * b;
+  uint32_t* out_mask = mask + (int64_t)row * words;
+
+  // Threshold search: after four passes T = sh_prefix is the b-th largest
+  // key and sh_remaining elements equal to T must still be taken.
+  uint32_t prefix = 0, pmask = 0;
+  if (t == 0) { sh_prefix = 0; sh_remaining = (uint32_t)b; }
+  __syncthreads();
+  if (b > 0) {
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      for (int i = t; i < 256; i += kSelBlock) hist[i] = 0;
+      __syncthreads();
+      for (int j = t; j < n; j += kSelBlock) {
+        const uint32_t k = order_key(sc[j]);
+        if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (t == 0) {
+        uint32_t need = sh_remaining, above = 0;
+        int d = 255;
+        for (; d > 0; --d) {
+          if (above + hist[d] >= need) break;
+          above += hist[d];
+        }
+        sh_remaining = need - above;
+        sh_prefix = prefix | ((uint32_t)d << shift);
+      }
+      __syncthreads();
+      prefix = sh_prefix;
+      pmask |= 255u << shift;
+    }
+  }
+  const uint32_t T = sh_prefix;
+  const uint32_t need_eq = b > 0 ? sh_remaining : 0u;
+
+  // Each thread owns a contiguous, 32-aligned range of indices.
+  const int per = ((n + kSelBlock - 1) / kSelBlock + 31) & ~31;
+  const int lo = min(n, t * per), hi = min(n, lo + per);
+  uint32_t n_eq = 0;
+  if (b > 0)
+    for (int j = lo; j < hi; ++j) n_eq += order_key(sc[j]) == T;
+  uint32_t tot;
+  const uint32_t eq_before = block_exclusive_scan(n_eq, scan, &tot);
+  uint32_t n_sel = 0;
+  if (b > 0) {
+    uint32_t eq_seen = eq_before;
+    for (int j = lo; j < hi; ++j) {
+      const uint32_t k = order_key(sc[j]);
+      const bool sel = k > T || (k == T && eq_seen < need_eq);
+      eq_seen += k == T;
+      n_sel += sel;
+    }
+  }
+  const uint32_t sel_before = block_exclusive_scan(n_sel, scan, &tot);
+  // Write indices (ascending) and the mask words of this range.
+  uint32_t pos = sel_before, eq_seen = eq_before, word = 0;
+  for (int j = lo; j < hi; ++j) {
+    bool sel = false;
+    if (b > 0) {
+      const uint32_t k = order_key(sc[j]);
+      sel = k > T || (k == T && eq_seen < need_eq);
+      eq_seen += k == T;
+    }
+    if (sel) {
+      if (pos < (uint32_t)b) out_idx[pos] = j;   // exactly b are selected; never write past b
+      ++pos;
+      word |= 1u << (j & 31);
+    }
+    if ((j & 31) == 31 || j == hi - 1) {
+      out_mask[j >> 5] = word;
+      word = 0;
+    }
+  }
+  // Mask words past the last index (none when n is a multiple of 32, else
+  // already written by the owner of the tail).
+  for (int wi = t; wi < words; wi += kSelBlock)
+    if (wi * 32 >= n) out_mask[wi] = 0u;
+}
+
+}  // namespace kvfix
+
+using namespace kvfix;
+
+extern "C" kvfix_status kvfix_score(const kvfix_plane* fresh, int32_t fresh_layer,
+                                    const kvfix_plane* reuse, int32_t reuse_layer,
+                                    const kvfix_rope* rope, float* scores, void* stream) {
+  KVFIX_TRY(check_plane(fresh));
+  KVFIX_TRY(check_plane(reuse));
+  KVFIX_TRY(same_rows(fresh, reuse));
+  if (scores == nullptr) return KVFIX_ERR_ARG;
+  if (fresh_layer < 0 || fresh_layer >= fresh->n_layers || reuse_layer < 0 ||
+      reuse_layer >= reuse->n_layers)
+    return KVFIX_ERR_ARG;
+  KVFIX_TRY(check_rope(rope, reuse->head_dim));
+  if (reuse->n_segs == 0 || reuse->n_tokens == 0) return KVFIX_OK;
+  ScoreParams P;
+  P.fresh = make_dplane(*fresh);
+  P.reuse = make_dplane(*reuse);
+  P.fl = fresh_layer;
+  P.rl = reuse_layer;
+  P.rope = make_rope_args(rope, reuse->head_dim);
+  P.scores = scores;
+  P.S = reuse->n_segs; P.H = reuse->n_heads; P.n = reuse->n_tokens;
+  P.tok_blocks = 0;
+  const int style = rope ? rope->style : kStyleNone;
+  // The dispatcher lives with the correction kernels; replicate it here.
+#define KVFIX_SCASE(T_, HD_, ST_)                                              \
+  if (reuse->dtype == (std::is_same<T_, float>::value ? KVFIX_F32 : KVFIX_BF16) && \
+      reuse->head_dim == HD_ && style == ST_)                                  \
+    return ScoreLaunch<T_, HD_, ST_>::run(P, (hipStream_t)stream);
+#define KVFIX_SSTYLES(T_, HD_) \
+  KVFIX_SCASE(T_, HD_, kStyleNone) KVFIX_SCASE(T_, HD_, kStyleHalf) KVFIX_SCASE(T_, HD_, kStyleInter)
+  KVFIX_SSTYLES(float, 64) KVFIX_SSTYLES(float, 128) KVFIX_SSTYLES(float, 256)
+  KVFIX_SSTYLES(bf16_t, 64) KVFIX_SSTYLES(bf16_t, 128) KVFIX_SSTYLES(bf16_t, 256)
+#undef KVFIX_SSTYLES
+#undef KVFIX_SCASE
+  return KVFIX_ERR_UNSUPPORTED;
+}
+
+extern "C" kvfix_status kvfix_select_topb(const float* scores, int32_t n_rows, int32_t n,
+                                          int32_t b, int32_t* idx, uint32_t* mask,
+                                          void* stream) {
+  if (n_rows < 0 || n < 0 || b < 0 || b > n) return KVFIX_ERR_ARG;
+  if (n_rows == 0 || n == 0) return KVFIX_OK;
+  if (scores == nullptr || mask == nullptr || (b > 0 && idx == nullptr)) return KVFIX_ERR_ARG;
+  if (n_rows > kMaxGrid) return KVFIX_ERR_ARG;
+  const int words = (n + 31) / 32;
+  select_topb_kernel<<<dim3((unsigned)n_rows), dim3(kSelBlock), 0, (hipStream_t)stream>>>(
+      scores, n, b, idx, mask, words);
+  return launch_status();
+}

@@ -1,0 +1,274 @@
+/*
+ * kvfix.h — C ABI of the cross-context KV-cache correction library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The library corrects a reused KV cache of a shared segment so that it can
+ * stand in for a fresh prefill under a new prefix.  Its calls are the steps of
+ * that correction and of the block-sparse storage of sibling caches:
+ *
+ *   kvfix_rope_shift   rotary re-alignment of cached keys to new positions
+ *   kvfix_score        fresh-vs-reused L2 divergence per token at a check layer
+ *   kvfix_score_draft  attention mass that draft query rows pay each token
+ *   kvfix_select_topb  exactly b tokens with the largest score (probe set)
+ *   kvfix_fit_mean     per-layer mean residual over the probe set (+ fresh scatter)
+ *   kvfix_apply        fused re-align + weighted mean + rank-r correction
+ *   kvfix_diff_encode  block-sparse diff of N sibling caches against a master
+ *   kvfix_diff_decode  fused restore: master + diff blocks + rotation, per sibling
+ *
+ * Sources (page titles; sections named, not quoted):
+ *   [KVCMAS] "KVCMAS: Efficient KV cache Correction for Shared Context in
+ *            Multi-Agent Systems" (arXiv 2609.34060)
+ *   [AKS]    "AgentKVShift: Correcting Reused KV" (review page)
+ *   [TD]     "TokenDance: Scaling Multi-Agent LLM Serving via Collective KV
+ *            Cache Sharing" (summary page)
+ *   [BCR]    "Budgeted Cache Repair for Cross-Context KV-Cache Reuse"
+ *            (arXiv 2610.02233)
+ *
+ * Conventions shared by every call
+ *   - Every tensor pointer is a CALLER-OWNED DEVICE pointer (memory from
+ *     hipMalloc or a framework allocator on the current device).  The library
+ *     never allocates device memory; temporary space comes from a caller
+ *     workspace whose size a *_workspace_size() call returns.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream).  No call synchronises.  Host-side argument checks run before
+ *     any launch; on failure nothing is launched and a status is returned.
+ *   - Results are bitwise identical from run to run (no floating-point
+ *     atomics; every reduction has a fixed order).
+ *   - Layout: a plane is one K or V cache, [layer][segment][kv_head][token]
+ *     [head_dim] with free element strides (head_dim contiguous), or a paged
+ *     pool [layer][page][page_size][kv_head][head_dim] addressed through a
+ *     per-segment page table.
+ *   - Alignment: data pointers and every row must be 16-byte aligned (the
+ *     kernels move 128-bit vectors); otherwise KVFIX_ERR_ALIGN.
+ *   - Arithmetic: fp32 storage is computed in fp64; bf16 storage is computed
+ *     in fp32 (apply, fit_mean) or fp64 (rotation-only, scores, diff paths);
+ *     each output element is rounded once (round to nearest even).
+ */
+#ifndef KVFIX_H
+#define KVFIX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVFIX_OK = 0,
+  KVFIX_ERR_ARG = 1,          /* null pointer, size or index out of range, shape mismatch */
+  KVFIX_ERR_ALIGN = 2,        /* pointer or row stride not 16-byte aligned */
+  KVFIX_ERR_CAPACITY = 3,     /* diff encode listed more blocks than the diff can hold */
+  KVFIX_ERR_HIP = 4,          /* a HIP runtime or launch error */
+  KVFIX_ERR_UNSUPPORTED = 5   /* dtype / head_dim / rank outside the compiled set */
+} kvfix_status;
+
+typedef enum { KVFIX_F32 = 0, KVFIX_BF16 = 1 } kvfix_dtype;
+
+/* Rotary pairing.  HALF pairs dims (i, i + hd/2) (Llama / Qwen checkpoints);
+ * INTERLEAVED pairs (2i, 2i + 1).  Pair i has frequency theta^(-2i/hd). */
+typedef enum { KVFIX_ROPE_HALF = 0, KVFIX_ROPE_INTERLEAVED = 1 } kvfix_rope_style;
+
+/* One K or V plane.
+ *   contiguous (page_table == NULL):
+ *     row (l, s, h, j) starts at  data + l*s_layer + s*s_seg + h*s_head + j*s_token
+ *   paged (page_table != NULL):
+ *     row (l, s, h, j) starts at  data + l*s_layer + page*s_page + (j % page_size)*s_token
+ *                                      + h*s_head,  page = page_table[s*pages_per_seg + j/page_size]
+ *   Strides count elements of `dtype`.  A row holds head_dim contiguous elements.
+ *   Rows whose page id is outside [0, n_pool_pages) are skipped (neither read
+ *   nor written): a bad id cannot make a kernel touch memory outside the pool.
+ *   s_seg may be 0 (every segment reads the same data: a broadcast source). */
+typedef struct {
+  void*          data;
+  int32_t        dtype;          /* kvfix_dtype */
+  int32_t        n_layers;
+  int32_t        n_segs;
+  int32_t        n_heads;        /* KV heads */
+  int32_t        n_tokens;       /* tokens per segment */
+  int32_t        head_dim;       /* 64, 128 or 256 */
+  int64_t        s_layer, s_seg, s_head, s_token;
+  const int32_t* page_table;     /* device int32 [n_segs][pages_per_seg], or NULL */
+  int32_t        page_size;
+  int32_t        pages_per_seg;
+  int64_t        s_page;
+  int64_t        n_pool_pages;
+} kvfix_plane;
+
+/* Rotary shift: segment s is rotated forward by delta[s] positions, i.e. pair
+ * i turns by delta[s] * theta^(-2i/hd) radians.  Angles are formed and their
+ * sine/cosine taken in fp64 on the device.  [KVCMAS §2.2, App. A.3 "Correction
+ * Weighting and Positional Alignment"; TD Algorithm 1, RoPERecover] */
+typedef struct {
+  double         theta;
+  int32_t        style;          /* kvfix_rope_style */
+  const int64_t* delta;          /* device int64 [n_segs] */
+} kvfix_rope;
+
+/* Rank-r residual state Z = A B per (layer, segment, head).  [KVCMAS eq. 7-8]
+ *   A: fp32, element (l, s, h, j, k) at  A + l*sA_layer + s*sA_seg + h*sA_head + j*rank + k
+ *   B: fp32, element (l, s, h, k, d) at  B + l*sB_layer + s*sB_seg + h*sB_head + k*head_dim + d
+ *   j is the token index within the segment; sA_head (or any A stride) may be
+ *   0 to share A.  rank 0 means no state. */
+typedef struct {
+  const float* A;
+  const float* B;
+  int32_t      rank;             /* 0..8 */
+  int64_t      sA_layer, sA_seg, sA_head;
+  int64_t      sB_layer, sB_seg, sB_head;
+} kvfix_lowrank;
+
+/* ---------------------------------------------------------------------------
+ * a1. Rotary re-alignment.  dst(l, s, h, j) = R(delta[s]) src(l, s, h, j).
+ * [KVCMAS §2.2: every method re-aligns cached keys to their target positions
+ * before reuse; TD §4.2: one batched rotary call for the whole group]
+ * src and dst have the same shape and dtype; dst may alias src exactly
+ * (in place).  Only keys are rotated; values need no call.
+ * Arithmetic: fp64, one rounding per element.
+ * ------------------------------------------------------------------------- */
+kvfix_status kvfix_rope_shift(const kvfix_plane* src, const kvfix_plane* dst,
+                              const kvfix_rope* rope, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * a2. L2 divergence score at a check layer.
+ *   scores[s][j] = || fresh(fresh_layer, s, :, j, :) - align(reuse(reuse_layer, s, :, j, :)) ||_2
+ * taken over all heads and dims of token j.  rope == NULL scores a value plane
+ * (no rotation).  [AKS "Core idea and method", step 1 and the equation for d;
+ * TD §4.2, one batched difference pass at the check layer]
+ * fresh and reuse must agree in n_segs, n_heads, n_tokens, head_dim and dtype.
+ * scores: device fp32 [n_segs][n_tokens], written in full.
+ * Arithmetic: fp64 accumulation, rounded once to fp32.
+ * ------------------------------------------------------------------------- */
+kvfix_status kvfix_score(const kvfix_plane* fresh, int32_t fresh_layer,
+                         const kvfix_plane* reuse, int32_t reuse_layer,
+                         const kvfix_rope* rope, float* scores, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * a3. Draft attention-mass score.
+ *   scores[s][j] = sum_{l >= first_layer} sum_t sum_h softmax_j( q'(s,l,h,t) . k(l,s,g(h),j) )
+ *   q' = R(-delta[s]) q / sqrt(head_dim),   g(h) = h / (n_q_heads / n_heads)
+ * i.e. the attention the draft query rows pay each re-aligned key
+ * (q . R(delta) k = R(-delta) q . k, so keys are scored without rotating them).
+ * [BCR §3 "The repair" (the score a_j), App. B Algorithm 2 and "The policy",
+ * step 2 (grouped-query keys expanded to the query heads)]
+ * q: device bf16 [n_segs][n_layers][n_q_heads][n_draft][head_dim], contiguous.
+ * k: bf16 plane; n_q_heads must be a multiple of k->n_heads; n_q_heads/n_heads
+ *    * n_draft <= 16.  head_dim 128 only.
+ * scores: device fp32 [n_segs][n_tokens].
+ * ws: device workspace of kvfix_score_draft_workspace(...) bytes, 256-byte aligned.
+ * Arithmetic: bf16 MFMA on a 3-term bf16 split of q' (fp32-accurate logits),
+ * fp32 exp, fp64 mass accumulation, rounded once to fp32.
+ * ------------------------------------------------------------------------- */
+size_t kvfix_score_draft_workspace(int32_t n_segs, int32_t n_layers, int32_t first_layer,
+                                   int32_t n_q_heads, int32_t n_draft, int32_t n_tokens);
+kvfix_status kvfix_score_draft(const void* q, int32_t n_q_heads, int32_t n_draft,
+                               const kvfix_plane* k, int32_t first_layer, const kvfix_rope* rope,
+                               float* scores, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * a4. Top-b selection.  For each of n_rows rows of n scores, exactly b indices
+ * with the largest score; equal scores go to the lower index; -0 equals +0;
+ * NaN ranks below every number.  [AKS step 2, b = ceil(r n); BCR-single]
+ * scores: device fp32 [n_rows][n].  idx: device int32 [n_rows][b], ascending.
+ * mask: device uint32 [n_rows][ceil(n/32)], bit j%32 of word j/32 set iff j
+ * is selected (all words written).  0 <= b <= n.
+ * ------------------------------------------------------------------------- */
+kvfix_status kvfix_select_topb(const float* scores, int32_t n_rows, int32_t n, int32_t b,
+                               int32_t* idx, uint32_t* mask, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * a5. Probe mean residual, re-estimated per layer, and fresh scatter.
+ *   mu[l][s][h][:] = (1/b) sum_{k<b} ( fresh_k - align(reuse_j) - A_j B ),  j = idx[s][k]
+ * fresh_k is fresh row j (fresh_by_slot == 0) or fresh row k (fresh_by_slot
+ * == 1: fresh holds only the probe rows, in idx order).  If out != NULL the
+ * fresh rows are also copied into out at the probe positions (exact copy).
+ * b == 0 gives mu = 0.  [AKS step 3 and the equation for mu-hat; KVCMAS eq. 7]
+ * mu: device fp32 [n_layers][n_segs][n_heads][head_dim], contiguous.
+ * idx: device int32 [n_segs][b], each in [0, n_tokens) (not checked on the host).
+ * out may alias reuse (in-place correction).
+ * Arithmetic: fp64 accumulation in a fixed order, rounded once to fp32.
+ * ------------------------------------------------------------------------- */
+kvfix_status kvfix_fit_mean(const kvfix_plane* fresh, int32_t fresh_by_slot,
+                            const kvfix_plane* reuse, const kvfix_plane* out,
+                            const int32_t* idx, int32_t b, const kvfix_rope* rope,
+                            const kvfix_lowrank* lowrank, float* mu, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * a6. Fused apply.  For every token j whose mask bit is clear:
+ *   out_j = round( align(reuse_j) + w_j mu + A_j B ),   w_j = clamp(scores[s][j], w_lo, w_hi)
+ * (w = 1 when scores == NULL).  Rows whose mask bit is set are not touched.
+ * [AKS equation for the corrected key: probes keep their fresh rows, others
+ * get reuse + w mu-hat; KVCMAS eq. 3 (selective recompute) and eq. 4 / eq. 8
+ * (add the estimated deviation to the aligned source cache)]
+ * mask: device uint32 [n_segs][ceil(n_tokens/32)] or NULL (no probes).
+ * mu: device fp32 [n_layers][n_segs][n_heads][head_dim].
+ * out may alias reuse exactly (in place; each row is read and written by the
+ * same lanes).  rope == NULL for value planes.
+ * Arithmetic: fp32 for bf16 planes, fp64 for fp32 planes; one rounding.
+ * ------------------------------------------------------------------------- */
+kvfix_status kvfix_apply(const kvfix_plane* reuse, const kvfix_plane* out,
+                         const uint32_t* mask, const float* scores, float w_lo, float w_hi,
+                         const float* mu, const kvfix_lowrank* lowrank,
+                         const kvfix_rope* rope, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * a8 / a9. Master-mirror block-sparse diff.  [TD §4.3 master-mirror layout and
+ * block-sparse diff representation; §5, one index list shared by K and V;
+ * §4.4 and Algorithm 1, fused diff restore]
+ *
+ * A block is (agent a, layer l, token block beta) = tokens
+ * [beta*block_tokens, min(n, (beta+1)*block_tokens)) of every head.
+ *   mask      device uint32 [n_agents][n_layers][ceil(n_blocks/32)]
+ *   offsets   device int64  [n_agents*n_layers + 1]: exclusive prefix count of
+ *             listed blocks in (agent, layer) order; offsets[last] = total
+ *   block_idx device int32  [capacity_blocks]: beta of each packed slot
+ *   vals_k/v  device, plane dtype, [capacity_blocks][n_heads][block_tokens][head_dim]
+ *             (rows past a ragged last block are left unwritten)
+ * Packed slots are in (agent, layer, beta)-ascending order.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  uint32_t* mask;
+  int64_t*  offsets;
+  int32_t*  block_idx;
+  void*     vals_k;
+  void*     vals_v;
+  int64_t   capacity_blocks;
+  int32_t   block_tokens;        /* 1..64 */
+} kvfix_diff;
+
+/* Encode: sibling a's keys are re-aligned into the master frame by
+ * to_master->delta[a] positions (fp64); a block is listed when any element of
+ * K or V differs from the master by more than eps (|x - m| > eps).  The listed
+ * blocks' re-aligned K (rounded once) and raw V are packed.
+ * master_k/v: planes with n_segs == 1; sib_k/v: planes with n_segs = n_agents.
+ * dev_status: device int32, set to KVFIX_OK or KVFIX_ERR_CAPACITY (more listed
+ * blocks than capacity_blocks: no slot past the capacity is written; the
+ * packed values are then incomplete, mask and offsets are still exact).
+ * ws: device workspace of kvfix_diff_encode_workspace(...) bytes. */
+size_t kvfix_diff_encode_workspace(int32_t n_agents, int32_t n_layers, int32_t n_tokens,
+                                   int32_t block_tokens);
+kvfix_status kvfix_diff_encode(const kvfix_plane* master_k, const kvfix_plane* master_v,
+                               const kvfix_plane* sib_k, const kvfix_plane* sib_v,
+                               const kvfix_rope* to_master, float eps, const kvfix_diff* out,
+                               int32_t* dev_status, void* ws, size_t ws_bytes, void* stream);
+
+/* Decode: for every agent a, out(l, a) = master(l) with the listed blocks of
+ * (a, l) overwritten by their packed values, keys then rotated forward by
+ * from_master->delta[a] positions (fp64, one rounding); values copied.  No
+ * dense mirror is materialised: each master block is read once and written to
+ * every agent.  out_k/out_v: planes with n_segs = n_agents. */
+kvfix_status kvfix_diff_decode(const kvfix_plane* master_k, const kvfix_plane* master_v,
+                               const kvfix_diff* diff, const kvfix_rope* from_master,
+                               const kvfix_plane* out_k, const kvfix_plane* out_v, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* kvfix_status_string(kvfix_status status);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int32_t kvfix_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVFIX_H */

@@ -1,0 +1,378 @@
+"""GPU parity of the correction path (a1 a2 a4 a5 a6 a7) against the CPU oracle.
+
+Every test calls the library through its C ABI (the ctypes binding) on
+seeded synthetic inputs and compares with the oracle element by element:
+indices and masks bit-exact, values within max |g - o| / (|o| + 1e-3) <=
+8e-3 (bf16) or 1e-5 (fp32).  Chained steps are also re-checked against the
+oracle run on the GPU's own previous-step outputs, so one ulp at step k
+cannot compound.
+"""
+import numpy as np
+import pytest
+import torch
+
+from helpers import TOL, assert_values, correction_case, from_np, log, mask_from_idx, rel_err, to_np
+from oracle import kvref as K
+from synthetic import CONFIGS
+
+import cross_context_kv_amd.kvfix as kv
+from cross_context_kv_amd.kvfix import Plane
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def small_c2(**kw):
+    base = dict(n_layers=3, n_kv_heads=2, n_tokens=300)
+    base.update(kw)
+    return CONFIGS["c2"].replace(**base)
+
+
+def gpu_chain(cfg, case, style=kv.ROPE_HALF, in_place=False, fresh_by_slot=False):
+    """Run score -> select -> fit_mean -> apply for K and V on the GPU."""
+    L, S, H, n, hd, b = cfg.n_layers, cfg.n_segs, cfg.n_kv_heads, cfg.n_tokens, cfg.head_dim, cfg.b
+    words = (n + 31) // 32
+    t = {k: from_np(case[k], DEV) for k in ("reuse_k", "reuse_v", "fresh_k", "fresh_v")}
+    delta = torch.tensor(case["deltas"], dtype=torch.int64, device=DEV)
+    AB = {}
+    for p in ("k", "v"):
+        AB[p] = (None, None) if case["A_" + p] is None else (
+            torch.from_numpy(case["A_" + p]).to(DEV), torch.from_numpy(case["B_" + p]).to(DEV))
+    scores = torch.full((2, S, n), float("nan"), dtype=torch.float32, device=DEV)
+    c = cfg.check_layer
+    log("score", cfg.name, (L, S, H, n, hd))
+    kv.kvfix_score(Plane.dense(t["fresh_k"]), c, Plane.dense(t["reuse_k"]), c, scores[0], delta,
+                   cfg.theta, style)
+    kv.kvfix_score(Plane.dense(t["fresh_v"]), c, Plane.dense(t["reuse_v"]), c, scores[1])
+    idx = torch.full((2, S, b), -1, dtype=torch.int32, device=DEV)
+    mask = torch.full((2, S, words), -1, dtype=torch.int32, device=DEV)
+    log("select", n, b)
+    kv.kvfix_select_topb(scores.view(2 * S, n), b, idx.view(2 * S, max(b, 0)),
+                         mask.view(2 * S, words))
+    mu = torch.full((2, L, S, H, hd), float("nan"), dtype=torch.float32, device=DEV)
+    outs = {}
+    for pi, p in enumerate(("k", "v")):
+        reuse = t["reuse_" + p]
+        out = reuse if in_place else torch.full_like(reuse, float("nan"))
+        fresh = t["fresh_" + p]
+        if fresh_by_slot:
+            fresh = torch.stack([fresh[:, s][:, :, idx[pi, s].long()] for s in range(S)], dim=1)
+        rope = (delta, cfg.theta, style) if p == "k" else (None, 0.0, style)
+        A, B = AB[p]
+        log("fit_mean", p)
+        kv.kvfix_fit_mean(Plane.dense(fresh), Plane.dense(reuse), Plane.dense(out), idx[pi], b,
+                          mu[pi], rope[0], rope[1], rope[2], A, B, fresh_by_slot=fresh_by_slot)
+        sc = scores[pi] if cfg.weight == "clip" else None
+        log("apply", p)
+        kv.kvfix_apply(Plane.dense(reuse), Plane.dense(out), mask[pi], mu[pi], sc, cfg.w_lo,
+                       cfg.w_hi, rope[0], rope[1], rope[2], A, B)
+        outs[p] = out
+    torch.cuda.synchronize()
+    return {
+        "scores": scores.cpu().numpy(),
+        "idx": idx.cpu().numpy(),
+        "mask": mask.cpu().numpy().view(np.uint32),
+        "mu": mu.cpu().numpy(),
+        "out_k": to_np(outs["k"]),
+        "out_v": to_np(outs["v"]),
+    }
+
+
+def check_chain(cfg, case, g, style="half", fresh_by_slot=False):
+    """Compare every step with the oracle; chained steps use the GPU's inputs."""
+    dt, c, b, n = cfg.dtype, cfg.check_layer, cfg.b, cfg.n_tokens
+    deltas = case["deltas"]
+    o_sk = K.score_l2(case["fresh_k"], case["reuse_k"], dt, c, deltas, cfg.theta, style)
+    o_sv = K.score_l2(case["fresh_v"], case["reuse_v"], dt, c)
+    for pi, o_s in enumerate((o_sk, o_sv)):
+        err = np.abs(g["scores"][pi].astype(np.float64) - o_s) / np.maximum(np.abs(o_s), 1e-30)
+        assert err.max() <= 2.0 ** -23, f"score plane {pi}: rel err {err.max():.3g}"
+    report = {"scores_bitexact": float(np.mean(g["scores"][0] == o_sk))}
+    for pi, o_s in enumerate((o_sk, o_sv)):
+        # tier 1: selection on the GPU's own scores is bit-exact
+        i1, m1 = K.select_topb(g["scores"][pi], b)
+        assert np.array_equal(g["idx"][pi], i1), f"plane {pi}: select differs on GPU scores"
+        assert np.array_equal(g["mask"][pi], m1)
+        # tier 2: end to end, the oracle's own scores give the same set
+        i2, _ = K.select_topb(o_s, b)
+        assert np.array_equal(g["idx"][pi], i2), f"plane {pi}: end-to-end selection differs"
+    for pi, p in enumerate(("k", "v")):
+        rope = (deltas, cfg.theta, style) if p == "k" else (None, 0.0, style)
+        idx = g["idx"][pi]
+        fresh = case["fresh_" + p]
+        if fresh_by_slot:
+            fresh = np.stack([fresh[:, s][:, :, idx[s]] for s in range(cfg.n_segs)], axis=1)
+        o_mu = K.fit_mean(fresh, case["reuse_" + p], dt, idx, rope[0], rope[1], rope[2],
+                          case["A_" + p], case["B_" + p], fresh_by_slot)
+        e = rel_err(g["mu"][pi], o_mu, "f32")
+        assert e <= 1e-5, f"mu {p}: {e:.3g}"
+        sc = g["scores"][pi] if cfg.weight == "clip" else None
+        # chain: oracle apply on the GPU's mean, scores and mask
+        o_out = case["reuse_" + p].copy()
+        K.scatter_fresh(o_out, fresh, idx, fresh_by_slot)
+        K.apply(case["reuse_" + p], dt, g["mask"][pi], g["mu"][pi], sc, cfg.w_lo, cfg.w_hi,
+                case["A_" + p], case["B_" + p], rope[0], rope[1], rope[2], out=o_out)
+        report["out_" + p] = assert_values(g["out_" + p], o_out, dt, "out " + p)
+        # probe rows are exact copies of the fresh rows
+        for s in range(cfg.n_segs):
+            assert np.array_equal(g["out_" + p][:, s][:, :, idx[s]], fresh[:, s][:, :, idx[s]]
+                                  if not fresh_by_slot else fresh[:, s])
+        # end to end against the oracle's own chain
+        o_full, _ = K.correct(fresh, case["reuse_" + p], dt, idx, g["mask"][pi],
+                              o_sk if p == "k" and cfg.weight == "clip" else
+                              (o_sv if cfg.weight == "clip" else None),
+                              cfg.w_lo, cfg.w_hi, case["A_" + p], case["B_" + p], rope[0],
+                              rope[1], rope[2], fresh_by_slot)
+        report["e2e_" + p] = assert_values(g["out_" + p], o_full, dt, "e2e " + p)
+    log("report", report)
+    return report
+
+
+def test_c1_tiny_fp32_full_config():
+    cfg = CONFIGS["c1"]
+    case = correction_case(cfg)
+    g = gpu_chain(cfg, case)
+    check_chain(cfg, case, g)
+    # the eight outlier rows of each plane are among the probes
+    from synthetic import make_gen
+    for pi, p in enumerate(("k", "v")):
+        gen = make_gen("cpu", cfg.seed, p, 0, 0, "outlier_rows")
+        rows = set(torch.randperm(cfg.n_tokens, generator=gen)[: cfg.n_outliers].tolist())
+        assert rows <= set(g["idx"][pi, 0].tolist())
+
+
+@pytest.mark.parametrize("style", [kv.ROPE_HALF, kv.ROPE_INTERLEAVED])
+def test_c2_shape_small_with_rank_state_and_clip(style):
+    cfg = small_c2()
+    case = correction_case(cfg)
+    g = gpu_chain(cfg, case, style=style)
+    check_chain(cfg, case, g, style="half" if style == kv.ROPE_HALF else "interleaved")
+
+
+@pytest.mark.parametrize("hd,dtype", [(64, "bf16"), (256, "bf16"), (128, "f32"), (256, "f32")])
+def test_head_dims_and_dtypes(hd, dtype):
+    cfg = small_c2(head_dim=hd, dtype=dtype, n_tokens=77, n_segs=2, b=9, rank=3,
+                   per_segment_delta=True)
+    case = correction_case(cfg)
+    g = gpu_chain(cfg, case)
+    check_chain(cfg, case, g)
+
+
+def test_in_place_and_fresh_by_slot():
+    cfg = small_c2(n_tokens=257, n_segs=3, b=40, rank=2, per_segment_delta=True)
+    case = correction_case(cfg)
+    g1 = gpu_chain(cfg, case, in_place=True, fresh_by_slot=True)
+    check_chain(cfg, case, g1, fresh_by_slot=True)
+    g2 = gpu_chain(cfg, case)
+    for k in ("out_k", "out_v", "mu", "idx", "mask"):
+        assert np.array_equal(g1[k], g2[k]), k
+
+
+def test_budget_edges_zero_and_full():
+    cfg0 = small_c2(b=0)
+    case = correction_case(cfg0)
+    g0 = gpu_chain(cfg0, case)
+    check_chain(cfg0, case, g0)
+    assert not g0["mu"].any()
+    cfgn = small_c2(b=300)
+    gn = gpu_chain(cfgn, case)
+    assert np.array_equal(gn["out_k"], case["fresh_k"])
+    assert np.array_equal(gn["out_v"], case["fresh_v"])
+
+
+def test_zero_shift_zero_residual_is_bitwise_identity():
+    cfg = small_c2(rank=0, weight="one")
+    case = correction_case(cfg)
+    case["deltas"] = [0] * cfg.n_segs
+    case["fresh_k"], case["fresh_v"] = case["reuse_k"].copy(), case["reuse_v"].copy()
+    case["A_k"] = case["B_k"] = case["A_v"] = case["B_v"] = None
+    g = gpu_chain(cfg, case)
+    assert not g["scores"].any() and not g["mu"].any()
+    assert np.array_equal(g["out_k"], case["reuse_k"])
+    assert np.array_equal(g["out_v"], case["reuse_v"])
+
+
+def test_deterministic_run_to_run():
+    cfg = small_c2(n_tokens=1000, b=150)
+    case = correction_case(cfg)
+    g1 = gpu_chain(cfg, case)
+    g2 = gpu_chain(cfg, case)
+    for k in g1:
+        assert np.array_equal(g1[k], g2[k]), k
+
+
+# ----------------------------------------------------------------------------
+# rotary shift on its own (a1), batched over segments, with a broadcast source
+# ----------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("dtype,hd,style", [("bf16", 128, "half"), ("bf16", 128, "interleaved"),
+                                            ("bf16", 64, "half"), ("f32", 64, "half"),
+                                            ("f32", 256, "interleaved")])
+def test_rope_shift_batched(dtype, hd, style):
+    rng = np.random.default_rng(31)
+    L, S, H, n = 2, 5, 3, 133
+    x = K.store(rng.standard_normal((L, S, H, n, hd)) * 2, dtype)
+    deltas = [0, 1, 37, 16384, -8191]
+    st = kv.ROPE_HALF if style == "half" else kv.ROPE_INTERLEAVED
+    src = from_np(x, DEV)
+    dst = torch.empty_like(src)
+    d = torch.tensor(deltas, dtype=torch.int64, device=DEV)
+    log("rope_shift", dtype, hd, style)
+    kv.kvfix_rope_shift(Plane.dense(src), Plane.dense(dst), d, 5e5, st)
+    torch.cuda.synchronize()
+    o = K.rope_shift(x, dtype, deltas, 5e5, style)
+    g = to_np(dst)
+    assert_values(g, o, dtype, "rope_shift")
+    assert np.mean(g == o) > 0.999               # fp64 on both sides: nearly all bit-exact
+    assert np.array_equal(g[:, 0], x[:, 0])      # delta 0 is the identity
+    # in place
+    kv.kvfix_rope_shift(Plane.dense(src), Plane.dense(src), d, 5e5, st)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(src), g)
+    # broadcast source: segment stride 0 rotates one master into every segment
+    master = from_np(x[:, :1].copy(), DEV).expand(L, S, H, n, hd)
+    out = torch.empty(L, S, H, n, hd, dtype=src.dtype, device=DEV)
+    kv.kvfix_rope_shift(Plane.dense(master), Plane.dense(out), d, 5e5, st)
+    torch.cuda.synchronize()
+    ob = K.rope_shift(np.repeat(x[:, :1], S, axis=1), dtype, deltas, 5e5, style)
+    assert_values(to_np(out), ob, dtype, "broadcast")
+
+
+# ----------------------------------------------------------------------------
+# top-b selection (a4) on the oracle's own scores: bit-exact, with ties
+# ----------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("n", [1, 31, 32, 33, 300, 4096, 32768, 40000])
+def test_select_topb_matches_oracle(n):
+    rng = np.random.default_rng(n)
+    rows = 3
+    s = rng.standard_normal((rows, n)).astype(np.float32)
+    s[1] = np.round(s[1] * 2) / 2                   # heavy ties
+    s[2, : n // 2] = 0.0
+    s[2, n // 2:] = -0.0                            # -0 and +0 tie
+    for b in sorted({0, 1, n // 3, n // 2, max(n - 1, 0), n}):
+        st = torch.from_numpy(s).to(DEV)
+        idx = torch.full((rows, b), -7, dtype=torch.int32, device=DEV)
+        mask = torch.full((rows, (n + 31) // 32), -1, dtype=torch.int32, device=DEV)
+        log("select", n, b)
+        kv.kvfix_select_topb(st, b, idx, mask)
+        torch.cuda.synchronize()
+        oi, om = K.select_topb(s, b)
+        assert np.array_equal(idx.cpu().numpy(), oi), (n, b)
+        assert np.array_equal(mask.cpu().numpy().view(np.uint32), om), (n, b)
+
+
+def test_select_nan_ranks_lowest():
+    s = np.array([[np.nan, 1.0, -np.inf, np.nan, 0.5, -1.0]], dtype=np.float32)
+    st = torch.from_numpy(s).to(DEV)
+    idx = torch.empty((1, 4), dtype=torch.int32, device=DEV)
+    mask = torch.empty((1, 1), dtype=torch.int32, device=DEV)
+    kv.kvfix_select_topb(st, 4, idx, mask)
+    torch.cuda.synchronize()
+    assert idx.cpu().tolist() == [[1, 2, 4, 5]]
+
+
+# ----------------------------------------------------------------------------
+# paged addressing (a7): a tagging test and paged == dense after gather
+# ----------------------------------------------------------------------------
+
+
+def paged_case(L=3, S=4, H=2, n=70, hd=128, ps=16, n_pages=29, seed=41):
+    rng = np.random.default_rng(seed)
+    pps = -(-n // ps)
+    pt = rng.permutation(n_pages)[: S * pps].reshape(S, pps).astype(np.int32)
+    return pt, pps
+
+
+def test_paged_tagging_maps_every_row_exactly():
+    L, S, H, n, hd, ps, n_pages = 3, 4, 2, 70, 128, 16, 29
+    pt, pps = paged_case(L, S, H, n, hd, ps, n_pages)
+    # every row holds a bf16-exact code of (layer, segment, head, token)
+    tag = np.zeros((L, S, H, n, hd), dtype=np.float64)
+    for l in range(L):
+        for s in range(S):
+            for h in range(H):
+                tag[l, s, h, :, 0] = l
+                tag[l, s, h, :, 1] = s
+                tag[l, s, h, :, 2] = h
+                tag[l, s, h, :, 3] = np.arange(n) % 256
+                tag[l, s, h, :, 4] = np.arange(n) // 256
+    tag_b = K.store(tag, "bf16")
+    pool = np.full(L * n_pages * ps * H * hd, K.f64_to_bf16(np.array([-1.0]))[0], dtype=np.uint16)
+    K.paged_scatter(pool, tag_b, pt, ps)
+    pool_t = from_np(pool.reshape(L, n_pages, ps, H, hd), DEV)
+    pt_t = torch.from_numpy(pt).to(DEV)
+    zeros_mu = torch.zeros(L, S, H, hd, dtype=torch.float32, device=DEV)
+    delta0 = torch.zeros(S, dtype=torch.int64, device=DEV)
+    out = torch.full((L, S, H, n, hd), float("nan"), dtype=torch.bfloat16, device=DEV)
+    log("paged tag: paged -> dense through apply")
+    kv.kvfix_apply(Plane.paged(pool_t, pt_t, ps, n), Plane.dense(out), None, zeros_mu,
+                   delta=delta0, theta=1e4)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(out), tag_b)
+    # and dense -> paged into a fresh pool
+    pool2 = torch.full_like(pool_t, -1.0)
+    kv.kvfix_apply(Plane.dense(out), Plane.paged(pool2, pt_t, ps, n), None, zeros_mu)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(pool2).ravel(), pool)
+
+
+def test_paged_in_place_correction_equals_dense():
+    cfg = CONFIGS["c5"].replace(n_layers=3, n_segs=4, n_kv_heads=2, n_tokens=70, b=7,
+                                n_pages=29, check_layer=1)
+    case = correction_case(cfg)
+    L, S, H, n, hd, ps = 3, 4, 2, 70, 128, 16
+    pt, pps = paged_case(L, S, H, n, hd, ps, cfg.n_pages)
+    # dense reference chain
+    g = gpu_chain(cfg, case)
+    check_chain(cfg, case, g)
+    # paged in-place chain on the same rows
+    pools = {}
+    for p in ("k", "v"):
+        pool = np.zeros(L * cfg.n_pages * ps * H * hd, dtype=np.uint16)
+        K.paged_scatter(pool, case["reuse_" + p], pt, ps)
+        pools[p] = from_np(pool.reshape(L, cfg.n_pages, ps, H, hd), DEV)
+    pt_t = torch.from_numpy(pt).to(DEV)
+    delta = torch.tensor(case["deltas"], dtype=torch.int64, device=DEV)
+    scores = torch.empty(2, S, n, dtype=torch.float32, device=DEV)
+    fk, fv = from_np(case["fresh_k"], DEV), from_np(case["fresh_v"], DEV)
+    kv.kvfix_score(Plane.dense(fk), 1, Plane.paged(pools["k"], pt_t, ps, n), 1, scores[0], delta,
+                   cfg.theta)
+    kv.kvfix_score(Plane.dense(fv), 1, Plane.paged(pools["v"], pt_t, ps, n), 1, scores[1])
+    idx = torch.empty(2, S, cfg.b, dtype=torch.int32, device=DEV)
+    mask = torch.empty(2, S, (n + 31) // 32, dtype=torch.int32, device=DEV)
+    kv.kvfix_select_topb(scores.view(2 * S, n), cfg.b, idx.view(2 * S, cfg.b), mask.view(2 * S, -1))
+    mu = torch.empty(2, L, S, H, hd, dtype=torch.float32, device=DEV)
+    for pi, p in enumerate(("k", "v")):
+        A = torch.from_numpy(case["A_" + p]).to(DEV)
+        B = torch.from_numpy(case["B_" + p]).to(DEV)
+        plane = Plane.paged(pools[p], pt_t, ps, n)
+        fresh = fk if p == "k" else fv
+        d = delta if p == "k" else None
+        kv.kvfix_fit_mean(Plane.dense(fresh), plane, plane, idx[pi], cfg.b, mu[pi], d, cfg.theta,
+                          A=A, B=B)
+        kv.kvfix_apply(plane, plane, mask[pi], mu[pi], None, 0.0, 1.0, d, cfg.theta, A=A, B=B)
+    torch.cuda.synchronize()
+    assert np.array_equal(scores.cpu().numpy(), g["scores"])
+    assert np.array_equal(idx.cpu().numpy(), g["idx"])
+    assert np.array_equal(mu.cpu().numpy(), g["mu"])
+    for p in ("k", "v"):
+        pool = to_np(pools[p]).ravel()
+        dense = K.paged_gather(pool, pt, ps, L, H, n, hd)
+        assert np.array_equal(dense, g["out_" + p]), p
+
+
+def test_bad_page_ids_are_skipped_not_followed():
+    L, S, H, n, hd, ps, n_pages = 1, 2, 1, 32, 128, 16, 4
+    pt = np.array([[0, 99], [-5, 3]], dtype=np.int32)
+    pool = torch.ones(L, n_pages, ps, H, hd, dtype=torch.bfloat16, device=DEV)
+    out = torch.zeros(L, S, H, n, hd, dtype=torch.bfloat16, device=DEV)
+    mu = torch.zeros(L, S, H, hd, dtype=torch.float32, device=DEV)
+    kv.kvfix_apply(Plane.paged(pool, torch.from_numpy(pt).to(DEV), ps, n), Plane.dense(out), None,
+                   mu)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy()
+    assert (o[0, 0, 0, :16] == 1).all() and (o[0, 0, 0, 16:] == 0).all()
+    assert (o[0, 1, 0, :16] == 0).all() and (o[0, 1, 0, 16:] == 1).all()

@@ -1,0 +1,126 @@
+"""CPU checks of the C ABI: the library loads, exports every declared entry
+point, and rejects bad arguments with a status before touching a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import cross_context_kv_amd.kvfix as kv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvfix.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(kv._LIB_PATH),
+                                reason="libkvfix.so not built (run the build first)")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvfix_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_expected_calls():
+    names = declared_functions()
+    assert set(names) == set(kv.EXPORTS), names
+
+
+def test_library_exports_every_declared_symbol():
+    L = kv.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert L.kvfix_version() == 100
+
+
+def test_status_strings():
+    L = kv.lib()
+    for code, name in kv.STATUS.items():
+        assert L.kvfix_status_string(code).decode().startswith(name)
+
+
+def plane(**kw):
+    base = dict(data=256, dtype=kv.BF16, n_layers=2, n_segs=1, n_heads=2, n_tokens=64,
+                head_dim=128, s_layer=2 * 64 * 128, s_seg=2 * 64 * 128, s_head=64 * 128,
+                s_token=128, page_table=None, page_size=0, pages_per_seg=0, s_page=0,
+                n_pool_pages=0)
+    base.update(kw)
+    return kv.c_plane(**base)
+
+
+def rope(**kw):
+    base = dict(theta=1e4, style=kv.ROPE_HALF, delta=4096)
+    base.update(kw)
+    return kv.c_rope(**base)
+
+
+R = ctypes.byref
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(data=None), 1),
+    (dict(dtype=7), 5),
+    (dict(head_dim=96), 5),
+    (dict(head_dim=100), 5),
+    (dict(n_tokens=-1), 1),
+    (dict(s_token=-128), 1),
+    (dict(data=258), 2),
+    (dict(s_token=129), 2),
+    (dict(page_table=4096, page_size=16, pages_per_seg=3, s_page=4096, n_pool_pages=8), 1),
+    (dict(page_table=4096, page_size=0, pages_per_seg=4, s_page=4096, n_pool_pages=8), 1),
+    (dict(page_table=4096, page_size=16, pages_per_seg=4, s_page=4097, n_pool_pages=8), 2),
+])
+def test_plane_validation(bad, status):
+    L = kv.lib()
+    p, good = plane(**bad), plane()
+    mu = ctypes.c_void_p(512)
+    assert L.kvfix_apply(R(p), R(good), None, None, 0.0, 1.0, mu, None, None, None) == status
+    assert L.kvfix_rope_shift(R(p), R(good), R(rope()), None) == status
+
+
+def test_call_level_validation():
+    L = kv.lib()
+    p, mu = plane(), ctypes.c_void_p(512)
+    # shapes must agree
+    assert L.kvfix_apply(R(p), R(plane(n_heads=3)), None, None, 0.0, 1.0, mu, None, None, None) == 1
+    assert L.kvfix_apply(R(p), R(p), None, None, 0.0, 1.0, None, None, None, None) == 1
+    # weights need lo <= hi
+    assert L.kvfix_apply(R(p), R(p), None, ctypes.c_void_p(512), 2.0, 1.0, mu, None, None, None) == 1
+    # rotary arguments
+    assert L.kvfix_rope_shift(R(p), R(p), None, None) == 1
+    assert L.kvfix_rope_shift(R(p), R(p), R(rope(delta=None)), None) == 1
+    assert L.kvfix_rope_shift(R(p), R(p), R(rope(style=3)), None) == 1
+    assert L.kvfix_rope_shift(R(p), R(p), R(rope(theta=0.0)), None) == 1
+    assert L.kvfix_rope_shift(R(p), R(plane(n_layers=3)), R(rope()), None) == 1
+    # rank state
+    lr = kv.c_lowrank(A=512, B=512, rank=9)
+    assert L.kvfix_apply(R(p), R(p), None, None, 0.0, 1.0, mu, R(lr), None, None) == 5
+    lr = kv.c_lowrank(A=None, B=512, rank=2)
+    assert L.kvfix_apply(R(p), R(p), None, None, 0.0, 1.0, mu, R(lr), None, None) == 1
+    # score layers in range
+    sc = ctypes.c_void_p(512)
+    assert L.kvfix_score(R(p), 2, R(p), 0, None, sc, None) == 1
+    assert L.kvfix_score(R(p), 0, R(p), -1, None, sc, None) == 1
+    assert L.kvfix_score(R(p), 0, R(p), 0, None, None, None) == 1
+    # select: 0 <= b <= n
+    assert L.kvfix_select_topb(sc, 1, 10, 11, ctypes.c_void_p(512), ctypes.c_void_p(512), None) == 1
+    assert L.kvfix_select_topb(sc, 1, 10, -1, ctypes.c_void_p(512), ctypes.c_void_p(512), None) == 1
+    assert L.kvfix_select_topb(None, 1, 10, 3, ctypes.c_void_p(512), ctypes.c_void_p(512), None) == 1
+    # fit_mean: b within n, idx needed when b > 0, fresh rows by slot need >= b rows
+    assert L.kvfix_fit_mean(R(p), 0, R(p), None, None, 3, None, None, mu, None) == 1
+    assert L.kvfix_fit_mean(R(p), 0, R(p), None, ctypes.c_void_p(512), 65, None, None, mu, None) == 1
+    assert L.kvfix_fit_mean(R(plane(n_tokens=2)), 1, R(p), None, ctypes.c_void_p(512), 3, None,
+                            None, mu, None) == 1
+    assert L.kvfix_fit_mean(R(plane(n_tokens=3)), 0, R(p), None, ctypes.c_void_p(512), 3, None,
+                            None, mu, None) == 1
+
+
+def test_empty_shapes_are_noops_without_launch():
+    L = kv.lib()
+    mu = ctypes.c_void_p(512)
+    for kw in (dict(n_tokens=0), dict(n_layers=0), dict(n_segs=0), dict(n_heads=0)):
+        p = plane(**kw)
+        assert L.kvfix_apply(R(p), R(p), None, None, 0.0, 1.0, mu, None, None, None) == 0
+        assert L.kvfix_rope_shift(R(p), R(p), R(rope()), None) == 0
+    assert L.kvfix_select_topb(None, 0, 10, 3, None, None, None) == 0
+    assert L.kvfix_select_topb(None, 4, 0, 0, None, None, None) == 0
