@@ -63,7 +63,7 @@ def mask_from_idx(idx: np.ndarray, n: int) -> np.ndarray:
     return m
 
 
-def correction_case(cfg, device="cpu"):
+def correction_case(cfg, device="cpu", style="half"):
     """Assemble one correction workload (small sizes: drawn on the CPU).
 
     Returns numpy arrays in oracle format (reuse_k/v, fresh_k/v, A/B per
@@ -77,7 +77,7 @@ def correction_case(cfg, device="cpu"):
     xv = raw["x_v"].double().cpu().numpy()
     case = {
         "deltas": deltas,
-        "reuse_k": K.store(K.align_plane_f64(xk, [-d for d in deltas], cfg.theta), cfg.dtype),
+        "reuse_k": K.store(K.align_plane_f64(xk, [-d for d in deltas], cfg.theta, style), cfg.dtype),
         "reuse_v": K.store(xv, cfg.dtype),
         "fresh_k": to_np(raw["fresh_k"]),
         "fresh_v": to_np(raw["fresh_v"]),

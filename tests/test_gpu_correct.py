@@ -23,8 +23,11 @@ DEV = "cuda"
 
 
 def small_c2(**kw):
+    """The 8B-shaped workload shrunk to 3 layers, 2 heads, 300 tokens."""
     base = dict(n_layers=3, n_kv_heads=2, n_tokens=300)
     base.update(kw)
+    if "b" not in kw:
+        base["b"] = K.probe_budget(CONFIGS["c2"].ratio, base["n_tokens"])
     return CONFIGS["c2"].replace(**base)
 
 
@@ -144,9 +147,10 @@ def test_c1_tiny_fp32_full_config():
 @pytest.mark.parametrize("style", [kv.ROPE_HALF, kv.ROPE_INTERLEAVED])
 def test_c2_shape_small_with_rank_state_and_clip(style):
     cfg = small_c2()
-    case = correction_case(cfg)
+    name = "half" if style == kv.ROPE_HALF else "interleaved"
+    case = correction_case(cfg, style=name)
     g = gpu_chain(cfg, case, style=style)
-    check_chain(cfg, case, g, style="half" if style == kv.ROPE_HALF else "interleaved")
+    check_chain(cfg, case, g, style=name)
 
 
 @pytest.mark.parametrize("hd,dtype", [(64, "bf16"), (256, "bf16"), (128, "f32"), (256, "f32")])
