@@ -122,15 +122,19 @@ def kv_event_pair_end(pair):
     pair[1].record()
 
 
-def cpu_baseline(cfg, t, torch, n_layers_sample=4):
-    """The oracle (as it stands) on the first layers of the same input bytes."""
+def cpu_baseline(cfg, t, torch, n_layers_sample=None, repeats=3):
+    """The oracle (as it stands, one thread) on the same input bytes.
+
+    Sample: the whole step (scores, selection, mean fit and apply of K and V)
+    over the first n_layers_sample layers (default: all), repeated `repeats`
+    times; the rate uses the median time."""
     import numpy as np
     try:
         from threadpoolctl import threadpool_limits
     except ImportError:  # pragma: no cover
         threadpool_limits = None
     from oracle import kvref as K
-    Ls = max(n_layers_sample, cfg.check_layer + 1)
+    Ls = cfg.n_layers if not n_layers_sample else max(n_layers_sample, cfg.check_layer + 1)
 
     def host(x):
         x = x[:Ls].detach().cpu()
@@ -153,19 +157,21 @@ def cpu_baseline(cfg, t, torch, n_layers_sample=4):
                       cfg.w_hi, data["A_" + p], data["B_" + p],
                       deltas if p == "k" else None, cfg.theta)
 
-    ctx = threadpool_limits(limits=1) if threadpool_limits else None
-    t0 = time.perf_counter()
-    if ctx:
-        with ctx:
+    times = []
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        if threadpool_limits:
+            with threadpool_limits(limits=1):
+                run()
+        else:
             run()
-    else:
-        run()
-    dt = time.perf_counter() - t0
+        times.append(time.perf_counter() - t0)
+    dt = sorted(times)[len(times) // 2]
     nbytes = alg_bytes(sub)["total"]
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"the full step on layers 0..{Ls - 1} of the same input bytes "
+            "sample": f"the whole step on layers 0..{Ls - 1} of the same input bytes "
                       f"({Ls} of {cfg.n_layers} layers, {nbytes / 1e6:.1f} MB algorithmic), "
-                      f"numpy fp64, one thread, {dt:.1f} s"}
+                      f"median of {repeats} runs of {dt:.1f} s, numpy fp64, one thread"}
 
 
 def read_traffic(per_launch_units: int):
@@ -186,7 +192,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-layers", type=int, default=4)
+    ap.add_argument("--cpu-layers", type=int, default=0, help="oracle sample layers (0 = all)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
