@@ -12,6 +12,7 @@ from .kvfix import (  # noqa: F401
     Plane,
     kvfix_apply,
     kvfix_diff_decode,
+    kvfix_diff_decode_workspace,
     kvfix_diff_encode,
     kvfix_diff_encode_workspace,
     kvfix_fit_mean,

@@ -30,14 +30,16 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 // Validate one plane description.  Shapes may be empty (a zero extent makes
 // every call on it a no-op).
 inline kvfix_status check_plane(const kvfix_plane* p) {
-  if (p == nullptr || p->data == nullptr) return KVFIX_ERR_ARG;
+  if (p == nullptr) return KVFIX_ERR_ARG;
+  const bool empty = p->n_layers == 0 || p->n_segs == 0 || p->n_heads == 0 || p->n_tokens == 0;
+  if (p->data == nullptr && !empty) return KVFIX_ERR_ARG;   // an empty plane needs no memory
   if (p->dtype != KVFIX_F32 && p->dtype != KVFIX_BF16) return KVFIX_ERR_UNSUPPORTED;
   if (!hd_supported(p->head_dim)) return KVFIX_ERR_UNSUPPORTED;
   if (p->n_layers < 0 || p->n_segs < 0 || p->n_heads < 0 || p->n_tokens < 0)
     return KVFIX_ERR_ARG;
   if (p->s_layer < 0 || p->s_seg < 0 || p->s_head < 0 || p->s_token < 0) return KVFIX_ERR_ARG;
   const int64_t es = elem_size(p->dtype);
-  if (!aligned16(p->data)) return KVFIX_ERR_ALIGN;
+  if (p->data != nullptr && !aligned16(p->data)) return KVFIX_ERR_ALIGN;
   if ((p->s_layer * es) % 16 || (p->s_seg * es) % 16 || (p->s_head * es) % 16 ||
       (p->s_token * es) % 16)
     return KVFIX_ERR_ALIGN;

@@ -22,7 +22,8 @@ STATUS = {0: "KVFIX_OK", 1: "KVFIX_ERR_ARG", 2: "KVFIX_ERR_ALIGN", 3: "KVFIX_ERR
 
 EXPORTS = ("kvfix_rope_shift", "kvfix_score", "kvfix_score_draft_workspace", "kvfix_score_draft",
            "kvfix_select_topb", "kvfix_fit_mean", "kvfix_apply", "kvfix_diff_encode_workspace",
-           "kvfix_diff_encode", "kvfix_diff_decode", "kvfix_status_string", "kvfix_version")
+           "kvfix_diff_encode", "kvfix_diff_decode_workspace", "kvfix_diff_decode",
+           "kvfix_status_string", "kvfix_version")
 
 
 class KvfixError(RuntimeError):
@@ -84,7 +85,8 @@ def lib() -> ctypes.CDLL:
             "kvfix_apply": [P, P, P, P, F, F, P, P, P, P],
             "kvfix_diff_encode_workspace": [I32, I32, I32, I32],
             "kvfix_diff_encode": [P, P, P, P, P, F, P, P, P, ctypes.c_size_t, P],
-            "kvfix_diff_decode": [P, P, P, P, P, P, P],
+            "kvfix_diff_decode_workspace": [I32, I32],
+            "kvfix_diff_decode": [P, P, P, P, P, P, P, ctypes.c_size_t, P],
             "kvfix_status_string": [I32],
             "kvfix_version": [],
         }
@@ -94,6 +96,7 @@ def lib() -> ctypes.CDLL:
             fn.restype = ctypes.c_int32
         L.kvfix_score_draft_workspace.restype = ctypes.c_size_t
         L.kvfix_diff_encode_workspace.restype = ctypes.c_size_t
+        L.kvfix_diff_decode_workspace.restype = ctypes.c_size_t
         L.kvfix_status_string.restype = ctypes.c_char_p
         _lib = L
     return _lib
@@ -296,10 +299,15 @@ def kvfix_diff_encode(master_k: Plane, master_v: Plane, sib_k: Plane, sib_v: Pla
         ctypes.byref(d), _ptr(dev_status), _ptr(ws), ws.numel() * ws.element_size(), _stream()))
 
 
+def kvfix_diff_decode_workspace(n_agents: int, head_dim: int) -> int:
+    return int(lib().kvfix_diff_decode_workspace(n_agents, head_dim))
+
+
 def kvfix_diff_decode(master_k: Plane, master_v: Plane, diff: Diff, from_master: torch.Tensor,
-                      theta: float, out_k: Plane, out_v: Plane, style: int = ROPE_HALF) -> None:
+                      theta: float, out_k: Plane, out_v: Plane, ws: torch.Tensor,
+                      style: int = ROPE_HALF) -> None:
     r, _ = make_rope(from_master, theta, style)
     d = diff.c()
     _check("kvfix_diff_decode", lib().kvfix_diff_decode(
         master_k.ref(), master_v.ref(), ctypes.byref(d), ctypes.byref(r), out_k.ref(),
-        out_v.ref(), _stream()))
+        out_v.ref(), _ptr(ws), ws.numel() * ws.element_size(), _stream()))

@@ -255,11 +255,17 @@ kvfix_status kvfix_diff_encode(const kvfix_plane* master_k, const kvfix_plane* m
 /* Decode: for every agent a, out(l, a) = master(l) with the listed blocks of
  * (a, l) overwritten by their packed values, keys then rotated forward by
  * from_master->delta[a] positions (fp64, one rounding); values copied.  No
- * dense mirror is materialised: each master block is read once and written to
- * every agent.  out_k/out_v: planes with n_segs = n_agents. */
+ * dense mirror is materialised: each master block is read once from HBM and
+ * written to every agent.  out_k/out_v: planes with n_segs = n_agents.
+ * A listed block whose slot lies at or past capacity_blocks (an encode that
+ * reported KVFIX_ERR_CAPACITY) is restored from the master instead.
+ * ws: device workspace of kvfix_diff_decode_workspace(...) bytes (the
+ * per-agent rotary table), 256-byte aligned. */
+size_t kvfix_diff_decode_workspace(int32_t n_agents, int32_t head_dim);
 kvfix_status kvfix_diff_decode(const kvfix_plane* master_k, const kvfix_plane* master_v,
                                const kvfix_diff* diff, const kvfix_rope* from_master,
-                               const kvfix_plane* out_k, const kvfix_plane* out_v, void* stream);
+                               const kvfix_plane* out_k, const kvfix_plane* out_v,
+                               void* ws, size_t ws_bytes, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* kvfix_status_string(kvfix_status status);
