@@ -141,7 +141,7 @@ class Plane:
             raise ValueError("dense plane must be [L, S, H, n, hd]")
         L, S, H, n, hd = t.shape
         sl, ss, sh, sn, sd = t.stride()
-        if sd != 1 and hd > 1:
+        if sd != 1 and hd > 1 and t.numel() > 0:
             raise ValueError("head_dim must be contiguous")
         c = c_plane(t.data_ptr(), _dtype(t), L, S, H, n, hd, sl, ss, sh, sn,
                     None, 0, 0, 0, 0)

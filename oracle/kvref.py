@@ -445,8 +445,8 @@ def paged_scatter(pool: np.ndarray, plane: np.ndarray, page_table: np.ndarray,
 
 def diff_encode(master_k: np.ndarray, master_v: np.ndarray, sib_k: np.ndarray,
                 sib_v: np.ndarray, to_master: Sequence[int], theta: float, eps: float,
-                block_tokens: int, style: str = "half") -> dict:
-    """Block-sparse diff of every sibling against the master (all bf16 bits).
+                block_tokens: int, style: str = "half", dtype: str = "bf16") -> dict:
+    """Block-sparse diff of every sibling against the master (storage `dtype`).
 
     master_*: [L][1][H][n][hd]; sib_*: [L][A][H][n][hd].  Sibling a's keys are
     first re-aligned into the master's frame by to_master[a] positions.  Block
@@ -456,8 +456,8 @@ def diff_encode(master_k: np.ndarray, master_v: np.ndarray, sib_k: np.ndarray,
 
     Returns dict: mask uint32 [A][L][ceil(nb/32)], offsets int64 [A*L+1]
     (exclusive prefix count per (agent, layer)), block_idx int32 [total],
-    vals_k / vals_v bf16 bits [total][H][bt][hd] (rows past a ragged tail = 0),
-    total int.
+    vals_k / vals_v [total][H][bt][hd] in the storage dtype (rows past a
+    ragged tail = 0), total int.
     """
     L, A, H, n, hd = sib_k.shape
     bt = block_tokens
@@ -465,12 +465,12 @@ def diff_encode(master_k: np.ndarray, master_v: np.ndarray, sib_k: np.ndarray,
     mask = np.zeros((A, L, (nb + 31) // 32), dtype=np.uint32)
     listed = []                                          # (a, l, beta) in ascending order
     packed_k, packed_v = [], []
-    mk_all = bf16_to_f64(master_k[:, 0])                 # [L][H][n][hd]
-    mv_all = bf16_to_f64(master_v[:, 0])
+    mk_all = to_f64(master_k[:, 0], dtype)               # [L][H][n][hd]
+    mv_all = to_f64(master_v[:, 0], dtype)
     for a in range(A):
         for l in range(L):
-            xk = rope_rotate(bf16_to_f64(sib_k[l, a]), to_master[a], theta, style)
-            xv = bf16_to_f64(sib_v[l, a])
+            xk = rope_rotate(to_f64(sib_k[l, a], dtype), to_master[a], theta, style)
+            xv = to_f64(sib_v[l, a], dtype)
             for beta in range(nb):
                 t0, t1 = beta * bt, min(n, beta * bt + bt)
                 dk = np.abs(xk[:, t0:t1] - mk_all[l][:, t0:t1]).max()
@@ -478,9 +478,9 @@ def diff_encode(master_k: np.ndarray, master_v: np.ndarray, sib_k: np.ndarray,
                 if dk > eps or dv > eps:
                     mask[a, l, beta // 32] |= np.uint32(1) << np.uint32(beta % 32)
                     listed.append((a, l, beta))
-                    pk = np.zeros((H, bt, hd), dtype=np.uint16)
-                    pv = np.zeros((H, bt, hd), dtype=np.uint16)
-                    pk[:, : t1 - t0] = f64_to_bf16(xk[:, t0:t1])
+                    pk = np.zeros((H, bt, hd), dtype=sib_k.dtype)
+                    pv = np.zeros((H, bt, hd), dtype=sib_v.dtype)
+                    pk[:, : t1 - t0] = store(xk[:, t0:t1], dtype)
                     pv[:, : t1 - t0] = sib_v[l, a][:, t0:t1]
                     packed_k.append(pk)
                     packed_v.append(pv)
@@ -489,7 +489,7 @@ def diff_encode(master_k: np.ndarray, master_v: np.ndarray, sib_k: np.ndarray,
         counts[a * L + l] += 1
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
     total = len(listed)
-    empty = np.zeros((0, H, bt, hd), dtype=np.uint16)
+    empty = np.zeros((0, H, bt, hd), dtype=sib_k.dtype)
     return {
         "mask": mask,
         "offsets": offsets,
@@ -502,16 +502,16 @@ def diff_encode(master_k: np.ndarray, master_v: np.ndarray, sib_k: np.ndarray,
 
 def diff_decode(master_k: np.ndarray, master_v: np.ndarray, diff: dict,
                 from_master: Sequence[int], theta: float, n_agents: int, block_tokens: int,
-                style: str = "half"):
+                style: str = "half", dtype: str = "bf16"):
     """Restore every sibling: master, overwritten by its listed blocks, keys rotated.
 
-    Returns (out_k, out_v) bf16 bits [L][A][H][n][hd].
+    Returns (out_k, out_v) [L][A][H][n][hd] in the storage dtype.
     """
     L, _, H, n, hd = master_k.shape
     A, bt = n_agents, block_tokens
     nb = (n + bt - 1) // bt
-    out_k = np.empty((L, A, H, n, hd), dtype=np.uint16)
-    out_v = np.empty((L, A, H, n, hd), dtype=np.uint16)
+    out_k = np.empty((L, A, H, n, hd), dtype=master_k.dtype)
+    out_v = np.empty((L, A, H, n, hd), dtype=master_v.dtype)
     offsets, mask = diff["offsets"], diff["mask"]
     for a in range(A):
         for l in range(L):
@@ -524,7 +524,7 @@ def diff_decode(master_k: np.ndarray, master_v: np.ndarray, diff: dict,
                     k[:, t0:t1] = diff["vals_k"][slot][:, : t1 - t0]
                     v[:, t0:t1] = diff["vals_v"][slot][:, : t1 - t0]
                     slot += 1
-            out_k[l, a] = f64_to_bf16(rope_rotate(bf16_to_f64(k), from_master[a], theta, style))
+            out_k[l, a] = store(rope_rotate(to_f64(k, dtype), from_master[a], theta, style), dtype)
             out_v[l, a] = v
     return out_k, out_v
 

@@ -190,7 +190,7 @@ def test_diff_encode_decode_small_collective(style, dtype, hd_note):
     cfg, raw, offs, mk, mv, sk, sv = collective_case(style=style, dtype=dtype)
     A, L, bt, n = cfg.n_segs, cfg.n_layers, cfg.block_tokens, cfg.n_tokens
     st = kv.ROPE_HALF if style == "half" else kv.ROPE_INTERLEAVED
-    o = K.diff_encode(mk, mv, sk, sv, [-x for x in offs], cfg.theta, cfg.eps, bt, style)
+    o = K.diff_encode(mk, mv, sk, sv, [-x for x in offs], cfg.theta, cfg.eps, bt, style, dtype)
     diff, status, t = gpu_encode(mk, mv, sk, sv, [-x for x in offs], cfg.theta, cfg.eps, bt,
                                  o["total"] + 5, st)
     assert status == 0
@@ -213,7 +213,7 @@ def test_diff_encode_decode_small_collective(style, dtype, hd_note):
     # decode against the oracle's decode of the same (GPU) diff
     ok, ov = gpu_decode(t, diff, offs, cfg.theta, A, st)
     gd = dict(g)
-    ook, oov = K.diff_decode(mk, mv, gd, offs, cfg.theta, A, bt, style)
+    ook, oov = K.diff_decode(mk, mv, gd, offs, cfg.theta, A, bt, style, dtype)
     assert_values(ok, ook, dtype, "decode K")
     assert np.array_equal(ov, oov)
     assert np.mean(ok == ook) > 0.999

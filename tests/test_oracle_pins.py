@@ -594,3 +594,17 @@ def test_storage_formulas_printed_on_the_page():
         cost = K.group_cost(c["N"], c["R"])
         assert round(cost, 1) == c["cost_printed"]
         assert round(c["N"] / round(cost, 1), 1) == c["reduction_printed"]
+
+
+def test_diff_roundtrip_lossless_fp32_storage():
+    rng = np.random.default_rng(23)
+    L, A, H, n, hd, bt = 2, 2, 2, 21, 8, 16
+    mk = rng.standard_normal((L, 1, H, n, hd)).astype(np.float32)
+    mv = rng.standard_normal((L, 1, H, n, hd)).astype(np.float32)
+    sk, sv = np.repeat(mk, A, axis=1), np.repeat(mv, A, axis=1)
+    sk[0, 1, 0, 17, 2] += np.float32(1e-3)         # tail block of agent 1, layer 0
+    d = K.diff_encode(mk, mv, sk, sv, [0] * A, 1e4, 0.0, bt, dtype="f32")
+    assert d["total"] == 1 and d["offsets"].tolist() == [0, 0, 0, 1, 1]
+    assert d["vals_k"].dtype == np.float32
+    ok, ov = K.diff_decode(mk, mv, d, [0] * A, 1e4, A, bt, dtype="f32")
+    assert np.array_equal(ok, sk) and np.array_equal(ov, sv)
