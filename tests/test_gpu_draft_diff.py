@@ -218,10 +218,11 @@ def test_diff_encode_decode_small_collective(style, dtype, hd_note):
     assert np.array_equal(ov, oov)
     assert np.mean(ok == ook) > 0.999
     # the restored caches are the siblings: values exactly, keys within the
-    # two roundings of a rotation there and back (fp32 storage)
+    # two roundings of a rotation there and back (fp32 storage: a few float
+    # ulps of the largest element, an absolute bound)
     assert np.array_equal(ov, sv)
     if dtype == "f32":
-        assert_values(ok, sk, dtype, "restored vs sibling")
+        assert np.abs(ok.astype(np.float64) - sk).max() <= 8 * 2.0 ** -24 * np.abs(sk).max()
 
 
 def test_diff_lossless_roundtrip_zero_shift_zero_eps():
