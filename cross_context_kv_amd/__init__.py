@@ -16,6 +16,7 @@ from .kvfix import (  # noqa: F401
     kvfix_diff_encode,
     kvfix_diff_encode_workspace,
     kvfix_fit_mean,
+    kvfix_fit_mean_workspace,
     kvfix_rope_shift,
     kvfix_score,
     kvfix_score_draft,

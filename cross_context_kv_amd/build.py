@@ -5,7 +5,9 @@ Usage:  python -m cross_context_kv_amd.build   (or build() from Python)
 Every source under csrc/ is compiled to an object with hipcc (in parallel),
 then linked into cross_context_kv_amd/libkvfix.so.  Packed-fp32 instructions
 are disabled on the device (-packed-fp32-ops); hipcc's host pass warns that
-it does not know that feature, which is harmless.
+it does not know that feature, which is harmless.  Contraction is off: the
+kernels spell out every fused multiply-add, so that every kernel instance
+rounds the same way.
 """
 from __future__ import annotations
 
@@ -24,7 +26,7 @@ ARCH = os.environ.get("KVFIX_ARCH", "gfx950")
 SOURCES = ["correct.hip", "score_select.hip", "draft.hip", "diff.hip", "api.hip"]
 
 CFLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]

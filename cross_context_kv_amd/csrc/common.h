@@ -57,6 +57,47 @@ __device__ __forceinline__ int64_t row_offset(const DPlane& p, int l, int s, int
          (int64_t)(j % p.page_size) * p.s_token + (int64_t)h * p.s_head;
 }
 
+// Page ids of tokens [j0, j1) of segment s, staged in LDS by the whole block,
+// so that a row address never waits on a dependent global load.  `first` is
+// the first page index covered; the block calls __syncthreads() afterwards.
+__device__ __forceinline__ int stage_pages(const DPlane& p, int s, int j0, int j1, int32_t* lds) {
+  if (p.page_table == nullptr || j1 <= j0) return 0;
+  const int first = j0 / p.page_size, last = (j1 - 1) / p.page_size;
+  const int32_t* pt = p.page_table + (int64_t)s * p.pages_per_seg;
+  for (int i = threadIdx.x; i <= last - first; i += blockDim.x) lds[i] = pt[first + i];
+  return first;
+}
+
+// Element offset of row (l, s, h, j) using staged page ids (or the dense
+// formula); -1 for an out-of-range page id.
+__device__ __forceinline__ int64_t row_offset_staged(const DPlane& p, int l, int s, int h, int j,
+                                                    const int32_t* lds, int first) {
+  if (p.page_table == nullptr)
+    return (int64_t)l * p.s_layer + (int64_t)s * p.s_seg + (int64_t)h * p.s_head +
+           (int64_t)j * p.s_token;
+  const int page = lds[j / p.page_size - first];
+  if (page < 0 || (int64_t)page >= p.n_pool_pages) return -1;
+  return (int64_t)l * p.s_layer + (int64_t)page * p.s_page +
+         (int64_t)(j % p.page_size) * p.s_token + (int64_t)h * p.s_head;
+}
+
+// Page id of token j of segment s (read directly; for staging loops).
+__device__ __forceinline__ int32_t page_of(const DPlane& p, int s, int j) {
+  return p.page_table ? p.page_table[(int64_t)s * p.pages_per_seg + j / p.page_size] : 0;
+}
+
+// Element offset of row (l, s, h, j) given its page id (ignored for dense
+// planes); -1 for an out-of-range page id.
+__device__ __forceinline__ int64_t row_offset_page(const DPlane& p, int l, int s, int h, int j,
+                                                  int32_t page) {
+  if (p.page_table == nullptr)
+    return (int64_t)l * p.s_layer + (int64_t)s * p.s_seg + (int64_t)h * p.s_head +
+           (int64_t)j * p.s_token;
+  if (page < 0 || (int64_t)page >= p.n_pool_pages) return -1;
+  return (int64_t)l * p.s_layer + (int64_t)page * p.s_page +
+         (int64_t)(j % p.page_size) * p.s_token + (int64_t)h * p.s_head;
+}
+
 template <typename T> struct Vec;
 template <> struct Vec<float> { static constexpr int N = 4; };
 template <> struct Vec<bf16_t> { static constexpr int N = 8; };
@@ -79,6 +120,66 @@ struct RowMap {
   }
 };
 
+// One-part lane map: G1 = HD / V lanes serve a row, lane g owning dims
+// [gV, gV + V) (one 16-byte part).  For rotate-half, lanes g < X hold the
+// first components of pairs (g mod X)V .. +V and lanes g >= X the second
+// ones, X = HD / (2V); a lane's rotation partner is lane g ^ X.  For
+// interleaved pairs, element m pairs with m ^ 1 inside the lane.  Halving
+// the dims per lane halves the per-lane constants (mean, rank-state right
+// factor, cos/sin), which keeps the streaming kernels at high occupancy.
+template <typename T, int HD, int STYLE>
+struct PartMap {
+  static constexpr int V = Vec<T>::N;
+  static constexpr int G = HD / V;
+  static constexpr int RPW = kWave / G;
+  static constexpr int X = HD / (2 * V);
+  static_assert(G >= 2 && G <= kWave && (kWave % G) == 0, "unsupported head_dim");
+  __device__ static constexpr int dim(int g, int m) { return g * V + m; }
+  // rotary pair index of element m of lane g
+  __device__ static constexpr int pair(int g, int m) {
+    return STYLE == kStyleInter ? (g * V + m) / 2 : (g % X) * V + m;
+  }
+};
+
+// Exchange a 16-byte value with lane ^ X (rotation partner).  X = 8 stays
+// inside a 16-lane DPP row (row_ror:8); other distances use a lane shuffle.
+template <int X>
+__device__ __forceinline__ vu4 partner16(vu4 v) {
+  vu4 r;
+  if constexpr (X == 8) {
+    r.x = __builtin_amdgcn_mov_dpp((int)v.x, 0x128, 0xf, 0xf, false);
+    r.y = __builtin_amdgcn_mov_dpp((int)v.y, 0x128, 0xf, 0xf, false);
+    r.z = __builtin_amdgcn_mov_dpp((int)v.z, 0x128, 0xf, 0xf, false);
+    r.w = __builtin_amdgcn_mov_dpp((int)v.w, 0x128, 0xf, 0xf, false);
+  } else {
+    r.x = __shfl_xor((int)v.x, X);
+    r.y = __shfl_xor((int)v.y, X);
+    r.z = __shfl_xor((int)v.z, X);
+    r.w = __shfl_xor((int)v.w, X);
+  }
+  return r;
+}
+
+// Rotate one lane's V elements (x) by the cos/sin of their pairs.
+// Rotate-half: p holds the partner lane's elements; ss is -sin on lanes that
+// hold first components and +sin on the others, so every element becomes
+// x*cos + p*ss (the same operations, in the same order, as rotate_pairs).
+// Interleaved: pairs are (x[2i], x[2i+1]) inside the lane; c, s indexed by m.
+template <int STYLE, int V, typename C>
+__device__ __forceinline__ void rotate_part(C* x, const C* p, const C* c, const C* ss) {
+  if constexpr (STYLE == kStyleInter) {
+#pragma unroll
+    for (int m = 0; m < V; m += 2) {
+      const C a = x[m], b = x[m + 1];
+      x[m] = fma(a, c[m], -(b * ss[m]));
+      x[m + 1] = fma(b, c[m], a * ss[m]);
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < V; ++m) x[m] = fma(x[m], c[m], p[m] * ss[m]);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // 16-byte vector codecs
 // ---------------------------------------------------------------------------
@@ -96,12 +197,14 @@ __device__ __forceinline__ void st16(void* p, vu4 v) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// float -> bf16 bits, round to nearest even (gfx950 v_cvt_pk_bf16_f32).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed bf16 bits, round to nearest even (one gfx950
+// v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const __bf16 a = static_cast<__bf16>(lo);
-  const __bf16 b = static_cast<__bf16>(hi);
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // double -> float rounded to odd: exact results pass through; inexact ones
@@ -191,14 +294,16 @@ __device__ __forceinline__ void pairs_to_parts(const C* a, const C* b, C* p0, C*
   }
 }
 
-// Rotate the pairs forward by the angles whose cos/sin are given.
+// Rotate the pairs forward by the angles whose cos/sin are given.  The
+// operation order is spelled out (explicit fma, contraction off in the
+// build), so every kernel that rotates rounds identically.
 template <int V, typename C>
 __device__ __forceinline__ void rotate_pairs(C* a, C* b, const C* c, const C* s) {
 #pragma unroll
   for (int m = 0; m < V; ++m) {
     const C x = a[m], y = b[m];
-    a[m] = x * c[m] - y * s[m];
-    b[m] = y * c[m] + x * s[m];
+    a[m] = fma(x, c[m], -(y * s[m]));
+    b[m] = fma(y, c[m], x * s[m]);
   }
 }
 

@@ -10,6 +10,7 @@
 // so the block's rotary table (fp64 sincos, one per segment) and its mu / B
 // constants live in LDS and registers for the whole chunk.  fit_mean gives
 // each block one whole unit and reduces in a fixed order (deterministic).
+#include <stdlib.h>
 #include <type_traits>
 
 #include "common.h"
@@ -19,6 +20,16 @@ namespace kvfix {
 
 constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / kWave;
+// Rows per block of the streaming kernels (the block stages per-row data
+// for that many rows in LDS).
+constexpr int kRowsPerBlock = 2048;
+
+// Wait until every vector-memory load this wave issued has returned.  Placed
+// after a batch of row loads, it lets the following stores issue back to back
+// (across per-row branches the compiler cannot count outstanding loads and
+// would otherwise wait for every earlier store before each store).
+__device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+constexpr int kMaxRowsPerBlock = kRowsPerBlock;
 
 // ---------------------------------------------------------------------------
 // rope_shift
@@ -46,7 +57,10 @@ __global__ __launch_bounds__(kBlock) void rope_shift_kernel(RopeShiftParams P) {
   const int j_end = min(P.n, j_begin + P.rows_per_block);
 
   __shared__ double tc[HD / 2], ts[HD / 2];
+  __shared__ int32_t spin[kMaxRowsPerBlock + 1], spout[kMaxRowsPerBlock + 1];
   rope_table<HD, double>(P.rope, P.rope.delta[s], tc, ts);
+  const int pin0 = stage_pages(P.src, s, j_begin, j_end, spin);
+  const int pout0 = stage_pages(P.dst, s, j_begin, j_end, spout);
   __syncthreads();
   double cs[V], sn[V];
 #pragma unroll
@@ -64,8 +78,8 @@ __global__ __launch_bounds__(kBlock) void rope_shift_kernel(RopeShiftParams P) {
       int64_t io = -1;
       oo[u] = -1;
       if (live[u]) {
-        io = row_offset(P.src, l, s, h, j);
-        oo[u] = row_offset(P.dst, l, s, h, j);
+        io = row_offset_staged(P.src, l, s, h, j, spin, pin0);
+        oo[u] = row_offset_staged(P.dst, l, s, h, j, spout, pout0);
         live[u] = io >= 0 && oo[u] >= 0;
       }
       if (live[u]) {
@@ -91,160 +105,185 @@ __global__ __launch_bounds__(kBlock) void rope_shift_kernel(RopeShiftParams P) {
 }
 
 // ---------------------------------------------------------------------------
-// fit_mean
+// fit_mean: two stages.  Stage 1 gives each block a slice of <= kFitRows
+// probe rows of one (layer, segment, head); the block scatters the fresh rows
+// and writes, in fp64, the sum of fresh - align(reuse) over its slice and the
+// sum of the slice's rank-state rows A_j.  Stage 2 adds a unit's slices in
+// slice order and forms mu = (sum(fresh - align(reuse)) - (sum A_j) B) / b,
+// which is the mean of fresh - align(reuse) - A_j B by linearity.
+// Fixed order throughout.
 // ---------------------------------------------------------------------------
+
+constexpr int kFitRows = 256;
+constexpr int kFitMaxRank = 8;
 
 struct FitParams {
   DPlane fresh, reuse, out;
-  int32_t has_out, fresh_by_slot, rotate;
+  int32_t has_out, fresh_by_slot;
   const int32_t* idx;
-  int32_t b;
+  int32_t b, parts;
   DLowRank lr;
   RopeArgs rope;
-  float* mu;
+  double* partial;          // [units][parts][HD + kFitMaxRank]
   int32_t S, H, n;
 };
 
-template <typename T, int HD, int STYLE, int MAXR>
-__global__ __launch_bounds__(kBlock) void fit_mean_kernel(FitParams P) {
-  constexpr int MS = STYLE == kStyleNone ? kStyleHalf : STYLE;
-  using M = RowMap<T, HD, MS>;
+template <typename T, int HD, int STYLE>
+__global__ __launch_bounds__(kBlock) void fit_partial_kernel(FitParams P) {
+  using M = PartMap<T, HD, STYLE>;
   using Cd = Codec<T, double>;
-  constexpr int V = M::V, G = M::G, RPW = M::RPW, U = 2;
+  constexpr int V = M::V, G = M::G, RPW = M::RPW, U = 4;
+  constexpr int PW = HD + kFitMaxRank;         // partial row width
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int g = lane % G, rw = lane / G;
-  int unit = blockIdx.x;
+  const int part = blockIdx.x % P.parts;
+  int unit = blockIdx.x / P.parts;
   const int h = unit % P.H; unit /= P.H;
   const int s = unit % P.S;
   const int l = unit / P.S;
+  const int k_begin = part * kFitRows;
+  const int k_end = min(P.b, k_begin + kFitRows);
+  const int nk = k_end - k_begin;
 
   __shared__ double tc[HD / 2], ts[HD / 2];
-  __shared__ double part[kWavesPerBlock][HD];
+  __shared__ double red[kWavesPerBlock][HD];
+  __shared__ int32_t sj[kFitRows], spf[kFitRows], spr[kFitRows], spo[kFitRows];
   if constexpr (STYLE != kStyleNone) rope_table<HD, double>(P.rope, P.rope.delta[s], tc, ts);
-
-  // Rank-state right factor B (zero past the rank).
-  double Ba[MAXR > 0 ? MAXR : 1][V], Bb[MAXR > 0 ? MAXR : 1][V];
-  const float* Arow_base = nullptr;
-  if constexpr (MAXR > 0) {
-    const float* Bp = P.lr.B + l * P.lr.sB_layer + s * P.lr.sB_seg + h * P.lr.sB_head;
-    Arow_base = P.lr.A + l * P.lr.sA_layer + s * P.lr.sA_seg + h * P.lr.sA_head;
-#pragma unroll
-    for (int k = 0; k < MAXR; ++k)
-#pragma unroll
-      for (int m = 0; m < V; ++m) {
-        const bool on = k < P.lr.rank;
-        Ba[k][m] = on ? (double)Bp[k * HD + M::dim_a(g, m)] : 0.0;
-        Bb[k][m] = on ? (double)Bp[k * HD + M::dim_b(g, m)] : 0.0;
-      }
+  // Stage the slice's probe indices and their page ids.
+  const int32_t* idx = P.idx + (int64_t)s * P.b;
+  for (int i = threadIdx.x; i < nk; i += kBlock) {
+    const int k = k_begin + i;
+    const int j = idx[k];
+    const bool ok = j >= 0 && j < P.n;            // an index out of range is dropped
+    sj[i] = ok ? j : -1;
+    spf[i] = ok ? page_of(P.fresh, s, P.fresh_by_slot ? k : j) : -1;
+    spr[i] = ok ? page_of(P.reuse, s, j) : -1;
+    spo[i] = ok && P.has_out ? page_of(P.out, s, j) : 0;
   }
   __syncthreads();
-  double cs[V], sn[V];
-  if constexpr (STYLE != kStyleNone) {
+  // Sum of the slice's rank-state rows: one row per thread, then a fixed-order
+  // butterfly over the wave and the waves in index order.
+  __shared__ double redA[kWavesPerBlock][kFitMaxRank];
+  double* outp = P.partial + (int64_t)blockIdx.x * PW;
+  const int rank = P.lr.rank;
+  if (rank > 0) {
+    const float* Ab = P.lr.A + l * P.lr.sA_layer + s * P.lr.sA_seg + h * P.lr.sA_head;
+    const int j = threadIdx.x < nk ? sj[threadIdx.x] : -1;
+    for (int k = 0; k < rank; ++k) {
+      double a = j >= 0 ? (double)Ab[(int64_t)j * rank + k] : 0.0;
 #pragma unroll
-    for (int m = 0; m < V; ++m) { cs[m] = tc[g * V + m]; sn[m] = ts[g * V + m]; }
+      for (int off = 1; off < kWave; off <<= 1) a += __shfl_xor(a, off);
+      if (lane == 0) redA[wave][k] = a;
+    }
   }
-
-  double acc_a[V], acc_b[V];
+  static_assert(kFitRows == kBlock, "one probe row per thread in the rank-state sum");
+  double cs[V], ss[V];
+  if constexpr (STYLE != kStyleNone) {
+    const bool first_half = STYLE == kStyleHalf && g < M::X;
 #pragma unroll
-  for (int m = 0; m < V; ++m) { acc_a[m] = 0.0; acc_b[m] = 0.0; }
+    for (int m = 0; m < V; ++m) {
+      cs[m] = tc[M::pair(g, m)];
+      ss[m] = first_half ? -ts[M::pair(g, m)] : ts[M::pair(g, m)];
+    }
+  }
+  double acc[V];
+#pragma unroll
+  for (int m = 0; m < V; ++m) acc[m] = 0.0;
 
-  const int32_t* idx = P.idx + (int64_t)s * P.b;
   constexpr int kStep = kWavesPerBlock * RPW;
-  for (int k0 = wave * RPW + rw; k0 < P.b; k0 += kStep * U) {
-    vu4 f0[U], f1[U], q0[U], q1[U];
-    int jj[U];
+  for (int i0 = wave * RPW + rw; i0 < nk; i0 += kStep * U) {
+    vu4 f[U], q[U];
     int64_t oo[U];
     bool live[U];
+    // unconditional loads (a dead slot reads the plane's first vector)
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int k = k0 + u * kStep;
-      live[u] = k < P.b;
-      jj[u] = 0;
+      const int i = i0 + u * kStep;
+      const int j = i < nk ? sj[i] : -1;
+      int64_t fo = -1, ro = -1;
       oo[u] = -1;
-      if (live[u]) {
-        const int j = idx[k];
-        jj[u] = j;
-        live[u] = j >= 0 && j < P.n;   // an index out of range is dropped, never followed
+      if (j >= 0) {
+        fo = row_offset_page(P.fresh, l, s, h, P.fresh_by_slot ? k_begin + i : j, spf[i]);
+        ro = row_offset_page(P.reuse, l, s, h, j, spr[i]);
+        if (P.has_out) oo[u] = row_offset_page(P.out, l, s, h, j, spo[i]);
       }
-      if (live[u]) {
-        const int j = jj[u];
-        const int64_t fo = row_offset(P.fresh, l, s, h, P.fresh_by_slot ? k : j);
-        const int64_t ro = row_offset(P.reuse, l, s, h, j);
-        if (P.has_out) oo[u] = row_offset(P.out, l, s, h, j);
-        live[u] = fo >= 0 && ro >= 0 && (!P.has_out || oo[u] >= 0);
-        if (live[u]) {
-          const T* fr = reinterpret_cast<const T*>(P.fresh.data) + fo;
-          const T* rr = reinterpret_cast<const T*>(P.reuse.data) + ro;
-          f0[u] = ld16(fr + M::off0(g));
-          f1[u] = ld16(fr + M::off1(g));
-          q0[u] = ld16(rr + M::off0(g));
-          q1[u] = ld16(rr + M::off1(g));
-        }
-      }
+      live[u] = j >= 0 && fo >= 0 && ro >= 0 && (!P.has_out || oo[u] >= 0);
+      const T* fp = reinterpret_cast<const T*>(P.fresh.data) + (live[u] ? fo + M::dim(g, 0) : 0);
+      const T* rp = reinterpret_cast<const T*>(P.reuse.data) + (live[u] ? ro + M::dim(g, 0) : 0);
+      f[u] = ld16(fp);
+      q[u] = ld16(rp);
     }
+    wait_loads();
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      vu4 pr = q[u];
+      if constexpr (STYLE == kStyleHalf) pr = partner16<M::X>(q[u]);
       if (!live[u]) continue;
-      double p0[V], p1[V], fa[V], fb[V], ra[V], rb[V];
-      Cd::unpack(f0[u], p0);
-      Cd::unpack(f1[u], p1);
-      parts_to_pairs<MS, V>(p0, p1, fa, fb);
-      Cd::unpack(q0[u], p0);
-      Cd::unpack(q1[u], p1);
-      parts_to_pairs<MS, V>(p0, p1, ra, rb);
-      if constexpr (STYLE != kStyleNone) rotate_pairs<V>(ra, rb, cs, sn);
-      double ab_a[V], ab_b[V];
+      double x[V], pv[V], fr[V];
+      Cd::unpack(q[u], x);
+      if constexpr (STYLE == kStyleHalf) Cd::unpack(pr, pv);
+      if constexpr (STYLE != kStyleNone) rotate_part<STYLE, V>(x, pv, cs, ss);
+      Cd::unpack(f[u], fr);
 #pragma unroll
-      for (int m = 0; m < V; ++m) { ab_a[m] = 0.0; ab_b[m] = 0.0; }
-      if constexpr (MAXR > 0) {
-        const float* Ar = Arow_base + (int64_t)jj[u] * P.lr.rank;
-#pragma unroll
-        for (int kk = 0; kk < MAXR; ++kk) {
-          const double a = kk < P.lr.rank ? (double)Ar[kk] : 0.0;
-#pragma unroll
-          for (int m = 0; m < V; ++m) {
-            ab_a[m] = fma(a, Ba[kk][m], ab_a[m]);
-            ab_b[m] = fma(a, Bb[kk][m], ab_b[m]);
-          }
-        }
-      }
-#pragma unroll
-      for (int m = 0; m < V; ++m) {
-        acc_a[m] += (fa[m] - ra[m]) - ab_a[m];
-        acc_b[m] += (fb[m] - rb[m]) - ab_b[m];
-      }
-      if (P.has_out) {
-        T* orow = reinterpret_cast<T*>(P.out.data) + oo[u];
-        st16(orow + M::off0(g), f0[u]);
-        st16(orow + M::off1(g), f1[u]);
-      }
+      for (int m = 0; m < V; ++m) acc[m] += fr[m] - x[m];
+      if (P.has_out) st16(reinterpret_cast<T*>(P.out.data) + oo[u] + M::dim(g, 0), f[u]);
     }
   }
-
   // Fixed-order reduction: butterfly over the rows of a wave, then the waves
   // in index order.
 #pragma unroll
-  for (int off = G; off < kWave; off <<= 1) {
+  for (int off = G; off < kWave; off <<= 1)
 #pragma unroll
-    for (int m = 0; m < V; ++m) {
-      acc_a[m] += __shfl_xor(acc_a[m], off);
-      acc_b[m] += __shfl_xor(acc_b[m], off);
-    }
-  }
+    for (int m = 0; m < V; ++m) acc[m] += __shfl_xor(acc[m], off);
   if (rw == 0) {
 #pragma unroll
-    for (int m = 0; m < V; ++m) {
-      part[wave][M::dim_a(g, m)] = acc_a[m];
-      part[wave][M::dim_b(g, m)] = acc_b[m];
-    }
+    for (int m = 0; m < V; ++m) red[wave][M::dim(g, m)] = acc[m];
   }
   __syncthreads();
   for (int d = threadIdx.x; d < HD; d += kBlock) {
     double t = 0.0;
 #pragma unroll
-    for (int w = 0; w < kWavesPerBlock; ++w) t += part[w][d];
-    const double mean = P.b > 0 ? t / (double)P.b : 0.0;
-    P.mu[(((int64_t)l * P.S + s) * P.H + h) * HD + d] = (float)mean;
+    for (int w = 0; w < kWavesPerBlock; ++w) t += red[w][d];
+    outp[d] = t;
+  }
+  if (threadIdx.x < kFitMaxRank) {
+    double a = 0.0;
+    if ((int)threadIdx.x < rank) {
+#pragma unroll
+      for (int w = 0; w < kWavesPerBlock; ++w) a += redA[w][threadIdx.x];
+    }
+    outp[HD + threadIdx.x] = a;
+  }
+}
+
+// mu[unit][d] = (sum_p partial[p][d] - sum_k (sum_p partial[p][HD + k]) B[k][d]) / b
+struct FitFinishParams {
+  const double* partial;
+  DLowRank lr;
+  float* mu;
+  int32_t parts, hd, b, S, H;
+};
+
+__global__ void fit_finish_kernel(FitFinishParams F) {
+  __shared__ double sA[kFitMaxRank];
+  const int unit = blockIdx.x;
+  const int pw = F.hd + kFitMaxRank;
+  const double* pp = F.partial + (int64_t)unit * F.parts * pw;
+  if (threadIdx.x < kFitMaxRank) {
+    double a = 0.0;
+    for (int p = 0; p < F.parts; ++p) a += pp[(int64_t)p * pw + F.hd + threadIdx.x];
+    sA[threadIdx.x] = a;
+  }
+  __syncthreads();
+  const int h = unit % F.H, s = (unit / F.H) % F.S, l = unit / (F.H * F.S);
+  const float* Bp = F.lr.rank > 0 ? F.lr.B + l * F.lr.sB_layer + s * F.lr.sB_seg + h * F.lr.sB_head
+                                  : nullptr;
+  for (int d = threadIdx.x; d < F.hd; d += blockDim.x) {
+    double t = 0.0;
+    for (int p = 0; p < F.parts; ++p) t += pp[(int64_t)p * pw + d];
+    double ab = 0.0;
+    for (int k = 0; k < F.lr.rank; ++k) ab = fma(sA[k], (double)Bp[k * F.hd + d], ab);
+    F.mu[(int64_t)unit * F.hd + d] = F.b > 0 ? (float)((t - ab) / (double)F.b) : 0.0f;
   }
 }
 
@@ -261,12 +300,29 @@ struct ApplyParams {
   DLowRank lr;
   RopeArgs rope;
   int32_t S, H, n, chunks, rows_per_block, mask_words;
+  int32_t a_vec;               // A rows may be read as whole 16-byte vectors
 };
 
-template <typename T, typename C, int HD, int STYLE, int MAXR>
+// Rank-state left factor of one row: MAXR values (zero past the rank).
+template <int MAXR, typename C>
+__device__ __forceinline__ void load_a_row(const float* Ar, int rank, bool vec, C* out) {
+  if constexpr (MAXR >= 4) {
+    if (vec) {
+#pragma unroll
+      for (int q = 0; q < MAXR / 4; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(Ar + 4 * q);
+        out[4 * q] = (C)v.x; out[4 * q + 1] = (C)v.y; out[4 * q + 2] = (C)v.z; out[4 * q + 3] = (C)v.w;
+      }
+      return;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < MAXR; ++k) out[k] = k < rank ? (C)Ar[k] : (C)0;
+}
+
+template <typename T, typename C, int HD, int STYLE, int MAXR, bool PAGED>
 __global__ __launch_bounds__(kBlock) void apply_kernel(ApplyParams P) {
-  constexpr int MS = STYLE == kStyleNone ? kStyleHalf : STYLE;
-  using M = RowMap<T, HD, MS>;
+  using M = PartMap<T, HD, STYLE>;
   using Cc = Codec<T, C>;
   constexpr int V = M::V, G = M::G, RPW = M::RPW, U = 4;
   constexpr int R = MAXR > 0 ? MAXR : 1;
@@ -279,99 +335,131 @@ __global__ __launch_bounds__(kBlock) void apply_kernel(ApplyParams P) {
   const int l = unit / P.S;
   const int j_begin = chunk * P.rows_per_block;
   const int j_end = min(P.n, j_begin + P.rows_per_block);
+  const int nrows = j_end - j_begin;
 
   __shared__ C tc[HD / 2], ts[HD / 2];
+  __shared__ uint32_t smask[kRowsPerBlock / 32 + 1];
+  __shared__ float sw[kRowsPerBlock];                         // per-row weights
+  __shared__ __attribute__((aligned(16))) float sa[MAXR > 0 ? kRowsPerBlock * MAXR : 1];
+  __shared__ int32_t spin[PAGED ? kRowsPerBlock + 1 : 1], spout[PAGED ? kRowsPerBlock + 1 : 1];
   if constexpr (STYLE != kStyleNone) rope_table<HD, C>(P.rope, P.rope.delta[s], tc, ts);
-
-  // Per-unit constants: mean residual and rank-state right factor.
-  const int64_t ubase = (((int64_t)l * P.S + s) * P.H + h) * HD;
-  C mua[V], mub[V];
-#pragma unroll
-  for (int m = 0; m < V; ++m) {
-    mua[m] = (C)P.mu[ubase + M::dim_a(g, m)];
-    mub[m] = (C)P.mu[ubase + M::dim_b(g, m)];
+  // Stage this block's per-row data: probe bits, weights, rank-state rows,
+  // page ids.  Each is one contiguous range, read with coalesced loads.
+  const int w0 = j_begin >> 5;
+  if (P.mask) {
+    const uint32_t* mrow = P.mask + (int64_t)s * P.mask_words;
+    for (int i = threadIdx.x; i <= ((j_end - 1) >> 5) - w0; i += kBlock) smask[i] = mrow[w0 + i];
   }
-  C Ba[R][V], Bb[R][V];
-  const float* Arow_base = nullptr;
+  const float* srow = P.scores ? P.scores + (int64_t)s * P.n + j_begin : nullptr;
+  for (int i = threadIdx.x; i < nrows; i += kBlock)
+    sw[i] = srow ? fminf(fmaxf(srow[i], P.w_lo), P.w_hi) : 1.0f;
+  const int rank = P.lr.rank;
+  if constexpr (MAXR > 0) {
+    const float* Ab = P.lr.A + l * P.lr.sA_layer + s * P.lr.sA_seg + h * P.lr.sA_head +
+                      (int64_t)j_begin * rank;
+    const int na = nrows * rank;
+    if (P.a_vec) {
+      for (int i = threadIdx.x; i < na / 4; i += kBlock)
+        *reinterpret_cast<float4*>(&sa[4 * i]) = *reinterpret_cast<const float4*>(Ab + 4 * i);
+    } else {
+      for (int i = threadIdx.x; i < na; i += kBlock) sa[i] = Ab[i];
+    }
+  }
+  int pin0 = 0, pout0 = 0;
+  if constexpr (PAGED) {
+    pin0 = stage_pages(P.in, s, j_begin, j_end, spin);
+    pout0 = stage_pages(P.out, s, j_begin, j_end, spout);
+  }
+
+  // Per-unit constants of this lane's dims: mean residual, rank-state B.
+  const int64_t ubase = (((int64_t)l * P.S + s) * P.H + h) * HD;
+  C mu[V];
+#pragma unroll
+  for (int m = 0; m < V; ++m) mu[m] = (C)P.mu[ubase + M::dim(g, m)];
+  C Bv[R][V];
   if constexpr (MAXR > 0) {
     const float* Bp = P.lr.B + l * P.lr.sB_layer + s * P.lr.sB_seg + h * P.lr.sB_head;
-    Arow_base = P.lr.A + l * P.lr.sA_layer + s * P.lr.sA_seg + h * P.lr.sA_head;
 #pragma unroll
     for (int k = 0; k < MAXR; ++k)
 #pragma unroll
-      for (int m = 0; m < V; ++m) {
-        const bool on = k < P.lr.rank;
-        Ba[k][m] = on ? (C)Bp[k * HD + M::dim_a(g, m)] : (C)0;
-        Bb[k][m] = on ? (C)Bp[k * HD + M::dim_b(g, m)] : (C)0;
-      }
+      for (int m = 0; m < V; ++m) Bv[k][m] = k < rank ? (C)Bp[k * HD + M::dim(g, m)] : (C)0;
   }
   __syncthreads();
-  C cs[V], sn[V];
+  C cs[V], ss[V];
   if constexpr (STYLE != kStyleNone) {
+    const bool first_half = STYLE == kStyleHalf && g < M::X;
 #pragma unroll
-    for (int m = 0; m < V; ++m) { cs[m] = tc[g * V + m]; sn[m] = ts[g * V + m]; }
+    for (int m = 0; m < V; ++m) {
+      cs[m] = tc[M::pair(g, m)];
+      ss[m] = first_half ? -ts[M::pair(g, m)] : ts[M::pair(g, m)];
+    }
   }
 
-  const uint32_t* mrow = P.mask ? P.mask + (int64_t)s * P.mask_words : nullptr;
-  const float* srow = P.scores ? P.scores + (int64_t)s * P.n : nullptr;
+  // Dense planes: the unit's base addresses are loop invariant.
+  const T* in_unit = reinterpret_cast<const T*>(P.in.data) + (int64_t)l * P.in.s_layer +
+                     (int64_t)s * P.in.s_seg + (int64_t)h * P.in.s_head;
+  T* out_unit = reinterpret_cast<T*>(P.out.data) + (int64_t)l * P.out.s_layer +
+                (int64_t)s * P.out.s_seg + (int64_t)h * P.out.s_head;
   constexpr int kStep = kWavesPerBlock * RPW;
-  for (int j0 = j_begin + wave * RPW + rw; j0 < j_end; j0 += kStep * U) {
-    vu4 r0[U], r1[U];
-    int64_t oo[U];
+  for (int i0 = wave * RPW + rw; i0 < nrows; i0 += kStep * U) {
+    vu4 r0[U];
+    T* op[U];
     bool live[U];
-    C w[U];
-    C Av[U][R];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int j = j0 + u * kStep;
-      live[u] = j < j_end;
-      oo[u] = -1;
-      w[u] = (C)1;
-      if (live[u] && mrow) live[u] = ((mrow[j >> 5] >> (j & 31)) & 1u) == 0;
-      int64_t io = -1;
-      if (live[u]) {
-        io = row_offset(P.in, l, s, h, j);
-        oo[u] = row_offset(P.out, l, s, h, j);
-        live[u] = io >= 0 && oo[u] >= 0;
-      }
-      if (live[u]) {
-        const T* row = reinterpret_cast<const T*>(P.in.data) + io;
-        r0[u] = ld16(row + M::off0(g));
-        r1[u] = ld16(row + M::off1(g));
-        if (srow) w[u] = (C)fminf(fmaxf(srow[j], P.w_lo), P.w_hi);
-        if constexpr (MAXR > 0) {
-          const float* Ar = Arow_base + (int64_t)j * P.lr.rank;
-#pragma unroll
-          for (int k = 0; k < MAXR; ++k) Av[u][k] = k < P.lr.rank ? (C)Ar[k] : (C)0;
-        }
-      }
+      const int i = i0 + u * kStep, j = j_begin + i;
+      live[u] = i < nrows;
+      if (P.mask && live[u]) live[u] = ((smask[(j >> 5) - w0] >> (j & 31)) & 1u) == 0;
     }
+    // Loads are unconditional (no branch between them, so they all stay in
+    // flight together): a dead row reads the plane's first vector instead, an
+    // address that always exists and stays in cache.
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      const int j = j_begin + i0 + u * kStep;
+      const T* ip;
+      if constexpr (PAGED) {
+        const int64_t io = live[u] ? row_offset_staged(P.in, l, s, h, j, spin, pin0) : -1;
+        const int64_t oo = live[u] ? row_offset_staged(P.out, l, s, h, j, spout, pout0) : -1;
+        live[u] = live[u] && io >= 0 && oo >= 0;
+        ip = reinterpret_cast<const T*>(P.in.data) + (live[u] ? io + M::dim(g, 0) : 0);
+        op[u] = reinterpret_cast<T*>(P.out.data) + oo;
+      } else {
+        ip = live[u] ? in_unit + (int64_t)j * P.in.s_token + M::dim(g, 0)
+                     : reinterpret_cast<const T*>(P.in.data);
+        op[u] = out_unit + (int64_t)j * P.out.s_token;
+      }
+      r0[u] = ld16(ip);
+    }
+    wait_loads();
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      // the partner exchange runs on every lane of the wave (both halves of a
+      // row are live or dead together)
+      vu4 pr = r0[u];
+      if constexpr (STYLE == kStyleHalf) pr = partner16<M::X>(r0[u]);
       if (!live[u]) continue;
-      C p0[V], p1[V], a[V], b[V];
-      Cc::unpack(r0[u], p0);
-      Cc::unpack(r1[u], p1);
-      parts_to_pairs<MS, V>(p0, p1, a, b);
-      if constexpr (STYLE != kStyleNone) rotate_pairs<V>(a, b, cs, sn);
+      const int i = i0 + u * kStep;
+      C x[V], pv[V];
+      Cc::unpack(r0[u], x);
+      if constexpr (STYLE == kStyleHalf) Cc::unpack(pr, pv);
+      if constexpr (STYLE != kStyleNone) rotate_part<STYLE, V>(x, pv, cs, ss);
+      const C w = (C)sw[i];
+      C Av[R];
+      if constexpr (MAXR > 0) {
+#pragma unroll
+        for (int k = 0; k < MAXR; ++k) Av[k] = k < rank ? (C)sa[i * rank + k] : (C)0;
+      }
 #pragma unroll
       for (int m = 0; m < V; ++m) {
-        C xa = a[m] + w[u] * mua[m];
-        C xb = b[m] + w[u] * mub[m];
+        C y = fma(w, mu[m], x[m]);
         if constexpr (MAXR > 0) {
 #pragma unroll
-          for (int k = 0; k < MAXR; ++k) {
-            xa += Av[u][k] * Ba[k][m];
-            xb += Av[u][k] * Bb[k][m];
-          }
+          for (int k = 0; k < MAXR; ++k) y = fma(Av[k], Bv[k][m], y);
         }
-        a[m] = xa;
-        b[m] = xb;
+        x[m] = y;
       }
-      pairs_to_parts<MS, V>(a, b, p0, p1);
-      T* row = reinterpret_cast<T*>(P.out.data) + oo[u];
-      st16(row + M::off0(g), Cc::pack(p0));
-      st16(row + M::off1(g), Cc::pack(p1));
+      st16(op[u] + M::dim(g, 0), Cc::pack(x));
     }
   }
 }
@@ -411,13 +499,8 @@ struct RopeShiftLaunch {
 
 template <typename T, int HD, int STYLE>
 struct FitLaunch {
-  static kvfix_status run(const FitParams& P, int rank_var, int64_t grid, hipStream_t st) {
-    switch (rank_var) {
-      case 0: fit_mean_kernel<T, HD, STYLE, 0><<<dim3((unsigned)grid), dim3(kBlock), 0, st>>>(P); break;
-      case 2: fit_mean_kernel<T, HD, STYLE, 2><<<dim3((unsigned)grid), dim3(kBlock), 0, st>>>(P); break;
-      case 4: fit_mean_kernel<T, HD, STYLE, 4><<<dim3((unsigned)grid), dim3(kBlock), 0, st>>>(P); break;
-      default: fit_mean_kernel<T, HD, STYLE, 8><<<dim3((unsigned)grid), dim3(kBlock), 0, st>>>(P); break;
-    }
+  static kvfix_status run(const FitParams& P, int64_t grid, hipStream_t st) {
+    fit_partial_kernel<T, HD, STYLE><<<dim3((unsigned)grid), dim3(kBlock), 0, st>>>(P);
     return launch_status();
   }
 };
@@ -425,19 +508,21 @@ struct FitLaunch {
 template <typename T, int HD, int STYLE>
 struct ApplyLaunch {
   using C = typename std::conditional<std::is_same<T, float>::value, double, float>::type;
-  static kvfix_status run(const ApplyParams& P, int rank_var, int64_t grid, hipStream_t st) {
+  template <bool PG>
+  static void go(const ApplyParams& P, int rank_var, int64_t grid, hipStream_t st) {
     switch (rank_var) {
-      case 0: apply_kernel<T, C, HD, STYLE, 0><<<dim3((unsigned)grid), dim3(kBlock), 0, st>>>(P); break;
-      case 2: apply_kernel<T, C, HD, STYLE, 2><<<dim3((unsigned)grid), dim3(kBlock), 0, st>>>(P); break;
-      case 4: apply_kernel<T, C, HD, STYLE, 4><<<dim3((unsigned)grid), dim3(kBlock), 0, st>>>(P); break;
-      default: apply_kernel<T, C, HD, STYLE, 8><<<dim3((unsigned)grid), dim3(kBlock), 0, st>>>(P); break;
+      case 0: apply_kernel<T, C, HD, STYLE, 0, PG><<<dim3((unsigned)grid), dim3(kBlock), 0, st>>>(P); break;
+      case 2: apply_kernel<T, C, HD, STYLE, 2, PG><<<dim3((unsigned)grid), dim3(kBlock), 0, st>>>(P); break;
+      case 4: apply_kernel<T, C, HD, STYLE, 4, PG><<<dim3((unsigned)grid), dim3(kBlock), 0, st>>>(P); break;
+      default: apply_kernel<T, C, HD, STYLE, 8, PG><<<dim3((unsigned)grid), dim3(kBlock), 0, st>>>(P); break;
     }
+  }
+  static kvfix_status run(const ApplyParams& P, int rank_var, int64_t grid, hipStream_t st) {
+    if (P.in.page_table || P.out.page_table) go<true>(P, rank_var, grid, st);
+    else go<false>(P, rank_var, grid, st);
     return launch_status();
   }
 };
-
-// Rows per block: 256 for streaming kernels (64 KB of bf16 hd-128 rows).
-constexpr int kRowsPerBlock = 256;
 
 }  // namespace kvfix
 
@@ -465,10 +550,20 @@ extern "C" kvfix_status kvfix_rope_shift(const kvfix_plane* src, const kvfix_pla
                                               (hipStream_t)stream);
 }
 
+static int fit_parts(int32_t b) { return b > 0 ? (b + kFitRows - 1) / kFitRows : 1; }
+
+extern "C" size_t kvfix_fit_mean_workspace(int32_t n_layers, int32_t n_segs, int32_t n_heads,
+                                           int32_t head_dim, int32_t b) {
+  if (n_layers < 0 || n_segs < 0 || n_heads < 0 || head_dim < 0 || b < 0) return 0;
+  return (size_t)n_layers * n_segs * n_heads * fit_parts(b) * (head_dim + kFitMaxRank) *
+         sizeof(double);
+}
+
 extern "C" kvfix_status kvfix_fit_mean(const kvfix_plane* fresh, int32_t fresh_by_slot,
                                        const kvfix_plane* reuse, const kvfix_plane* out,
                                        const int32_t* idx, int32_t b, const kvfix_rope* rope,
-                                       const kvfix_lowrank* lowrank, float* mu, void* stream) {
+                                       const kvfix_lowrank* lowrank, float* mu, void* ws,
+                                       size_t ws_bytes, void* stream) {
   KVFIX_TRY(check_plane(fresh));
   KVFIX_TRY(check_plane(reuse));
   if (out) {
@@ -489,23 +584,35 @@ extern "C" kvfix_status kvfix_fit_mean(const kvfix_plane* fresh, int32_t fresh_b
   KVFIX_TRY(check_lowrank(lowrank));
   const int64_t units = (int64_t)reuse->n_layers * reuse->n_segs * reuse->n_heads;
   if (units == 0) return KVFIX_OK;
-  if (units > kMaxGrid) return KVFIX_ERR_ARG;
+  const size_t need = kvfix_fit_mean_workspace(reuse->n_layers, reuse->n_segs, reuse->n_heads,
+                                               reuse->head_dim, b);
+  if (ws == nullptr || ws_bytes < need || !aligned16(ws)) return KVFIX_ERR_ARG;
+  const int parts = fit_parts(b);
+  const int64_t grid = units * parts;
+  if (grid > kMaxGrid) return KVFIX_ERR_ARG;
   FitParams P;
   P.fresh = make_dplane(*fresh);
   P.reuse = make_dplane(*reuse);
   P.out = out ? make_dplane(*out) : make_dplane(*reuse);
   P.has_out = out != nullptr;
   P.fresh_by_slot = fresh_by_slot != 0;
-  P.rotate = rope != nullptr;
   P.idx = idx;
   P.b = b;
+  P.parts = parts;
   P.lr = make_dlowrank(lowrank);
   P.rope = make_rope_args(rope, reuse->head_dim);
-  P.mu = mu;
+  P.partial = static_cast<double*>(ws);
   P.S = reuse->n_segs; P.H = reuse->n_heads; P.n = reuse->n_tokens;
+  hipStream_t st = (hipStream_t)stream;
   const int style = rope ? rope->style : kStyleNone;
-  return dispatch_t_hd_style<FitLaunch>(reuse->dtype, reuse->head_dim, style, P,
-                                        rank_variant(P.lr.rank), units, (hipStream_t)stream);
+  KVFIX_TRY(dispatch_t_hd_style<FitLaunch>(reuse->dtype, reuse->head_dim, style, P, grid, st));
+  FitFinishParams F;
+  F.partial = P.partial;
+  F.lr = P.lr;
+  F.mu = mu;
+  F.parts = parts; F.hd = reuse->head_dim; F.b = b; F.S = P.S; F.H = P.H;
+  fit_finish_kernel<<<dim3((unsigned)units), dim3(128), 0, st>>>(F);
+  return launch_status();
 }
 
 extern "C" kvfix_status kvfix_apply(const kvfix_plane* reuse, const kvfix_plane* out,
@@ -530,11 +637,14 @@ extern "C" kvfix_status kvfix_apply(const kvfix_plane* reuse, const kvfix_plane*
   P.w_hi = w_hi;
   P.mu = mu;
   P.lr = make_dlowrank(lowrank);
+  P.a_vec = P.lr.rank > 0 && aligned16(P.lr.A) && (P.lr.sA_layer * 4) % 16 == 0 &&
+            (P.lr.sA_seg * 4) % 16 == 0 && (P.lr.sA_head * 4) % 16 == 0 && (P.lr.rank * 4) % 16 == 0;
   P.rope = make_rope_args(rope, reuse->head_dim);
   P.S = reuse->n_segs; P.H = reuse->n_heads; P.n = reuse->n_tokens;
   P.mask_words = (reuse->n_tokens + 31) / 32;
-  P.rows_per_block = kRowsPerBlock;
-  P.chunks = (reuse->n_tokens + kRowsPerBlock - 1) / kRowsPerBlock;
+  int rpb = kRowsPerBlock;
+  P.rows_per_block = rpb;
+  P.chunks = (reuse->n_tokens + rpb - 1) / rpb;
   const int64_t grid = units * P.chunks;
   if (grid > kMaxGrid) return KVFIX_ERR_ARG;
   const int style = rope ? rope->style : kStyleNone;

@@ -111,6 +111,8 @@ struct ScoreLaunch {
 // ---------------------------------------------------------------------------
 
 constexpr int kSelBlock = 1024;
+constexpr int kSelWaves = kSelBlock / 64;
+constexpr int kSelRegKeys = 32;        // keys held in registers per thread (n <= 32768)
 
 __device__ __forceinline__ uint32_t order_key(float f) {
   if (f != f) return 0u;                                   // NaN ranks lowest
@@ -119,61 +121,117 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive block-wide scan of one value per thread (fixed order).
+// Exclusive prefix of a per-thread count over the block (integer, so order
+// does not matter): wave prefix by shuffles, then the wave totals.
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* lds,
                                                         uint32_t* total) {
-  const int t = threadIdx.x;
-  lds[t] = v;
-  __syncthreads();
-  for (int off = 1; off < kSelBlock; off <<= 1) {
-    const uint32_t add = t >= off ? lds[t - off] : 0u;
-    __syncthreads();
-    lds[t] += add;
-    __syncthreads();
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  uint32_t incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
   }
-  const uint32_t incl = lds[t];
-  *total = lds[kSelBlock - 1];
+  if (lane == 63) lds[wave] = incl;
   __syncthreads();
-  return incl - v;
+  if (wave == 0) {
+    const uint32_t wt = lane < kSelWaves ? lds[lane] : 0u;
+    uint32_t wi = wt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t y = __shfl_up(wi, off);
+      if (lane >= off) wi += y;
+    }
+    if (lane < kSelWaves) lds[64 + lane] = wi - wt;        // exclusive prefix of wave totals
+    if (lane == kSelWaves - 1) lds[128] = wi;
+  }
+  __syncthreads();
+  const uint32_t r = lds[64 + wave] + incl - v;
+  *total = lds[128];
+  __syncthreads();
+  return r;
 }
 
+// One block per row.  Keys j = t + 1024 q live in registers (read once).
+// Four 8-bit radix passes over per-wave LDS histograms find the b-th largest
+// key T and how many keys equal to T are still needed; the compaction then
+// walks the row in index order, 1024 keys at a time, so indices come out
+// ascending and the lowest-index keys equal to T are the ones taken.
 __global__ __launch_bounds__(kSelBlock) void select_topb_kernel(const float* __restrict__ scores,
                                                                 int n, int b,
                                                                 int32_t* __restrict__ idx,
                                                                 uint32_t* __restrict__ mask,
                                                                 int words) {
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t scan[kSelBlock];
+  __shared__ uint32_t hist[kSelWaves][256];
+  __shared__ uint32_t scan[160];
   __shared__ uint32_t sh_prefix, sh_remaining;
   const int row = blockIdx.x;
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const float* sc = scores + (int64_t)row * n;
   int32_t* out_idx = idx + (int64_t)row * b;
   uint32_t* out_mask = mask + (int64_t)row * words;
+  const bool in_regs = n <= kSelBlock * kSelRegKeys;
 
-  // Threshold search: after four passes T = sh_prefix is the b-th largest
-  // key and sh_remaining elements equal to T must still be taken.
-  uint32_t prefix = 0, pmask = 0;
+  uint32_t key[kSelRegKeys];
+  if (in_regs) {
+#pragma unroll
+    for (int q = 0; q < kSelRegKeys; ++q) {
+      const int j = t + q * kSelBlock;
+      key[q] = j < n ? order_key(sc[j]) : 0u;
+    }
+  }
   if (t == 0) { sh_prefix = 0; sh_remaining = (uint32_t)b; }
   __syncthreads();
+  uint32_t prefix = 0, pmask = 0;
   if (b > 0) {
     for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int i = t; i < 256; i += kSelBlock) hist[i] = 0;
+      for (int i = lane; i < 256; i += 64) hist[wave][i] = 0;
       __syncthreads();
-      for (int j = t; j < n; j += kSelBlock) {
-        const uint32_t k = order_key(sc[j]);
-        if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+      if (in_regs) {
+#pragma unroll
+        for (int q = 0; q < kSelRegKeys; ++q) {
+          const int j = t + q * kSelBlock;
+          if (j < n && (key[q] & pmask) == prefix) atomicAdd(&hist[wave][(key[q] >> shift) & 255u], 1u);
+        }
+      } else {
+        for (int j = t; j < n; j += kSelBlock) {
+          const uint32_t k = order_key(sc[j]);
+          if ((k & pmask) == prefix) atomicAdd(&hist[wave][(k >> shift) & 255u], 1u);
+        }
       }
       __syncthreads();
-      if (t == 0) {
-        uint32_t need = sh_remaining, above = 0;
-        int d = 255;
-        for (; d > 0; --d) {
-          if (above + hist[d] >= need) break;
-          above += hist[d];
+      if (t < 256) {                                       // fold the wave histograms
+        uint32_t c = 0;
+#pragma unroll
+        for (int w = 0; w < kSelWaves; ++w) c += hist[w][t];
+        hist[0][t] = c;
+      }
+      __syncthreads();
+      if (t < 64) {
+        // lane L owns bins 255-4L .. 252-4L (descending); find the bin that
+        // holds the need-th largest key by a prefix over the lanes
+        const uint32_t need = sh_remaining;
+        uint32_t c[4], sum = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { c[i] = hist[0][255 - 4 * t - i]; sum += c[i]; }
+        uint32_t incl = sum;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const uint32_t y = __shfl_up(incl, off);
+          if (t >= off) incl += y;
         }
-        sh_remaining = need - above;
-        sh_prefix = prefix | ((uint32_t)d << shift);
+        const uint32_t excl = incl - sum;
+        if (excl < need && need <= incl) {
+          uint32_t above = excl;
+          int d = 255 - 4 * t - 3;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (above + c[i] >= need) { d = 255 - 4 * t - i; break; }
+            above += c[i];
+          }
+          sh_remaining = need - above;
+          sh_prefix = prefix | ((uint32_t)d << shift);
+        }
       }
       __syncthreads();
       prefix = sh_prefix;
@@ -183,48 +241,36 @@ __global__ __launch_bounds__(kSelBlock) void select_topb_kernel(const float* __r
   const uint32_t T = sh_prefix;
   const uint32_t need_eq = b > 0 ? sh_remaining : 0u;
 
-  // Each thread owns a contiguous, 32-aligned range of indices.
-  const int per = ((n + kSelBlock - 1) / kSelBlock + 31) & ~31;
-  const int lo = min(n, t * per), hi = min(n, lo + per);
-  uint32_t n_eq = 0;
-  if (b > 0)
-    for (int j = lo; j < hi; ++j) n_eq += order_key(sc[j]) == T;
-  uint32_t tot;
-  const uint32_t eq_before = block_exclusive_scan(n_eq, scan, &tot);
-  uint32_t n_sel = 0;
-  if (b > 0) {
-    uint32_t eq_seen = eq_before;
-    for (int j = lo; j < hi; ++j) {
-      const uint32_t k = order_key(sc[j]);
-      const bool sel = k > T || (k == T && eq_seen < need_eq);
-      eq_seen += k == T;
-      n_sel += sel;
+  // Compaction in index order: chunk c covers keys [1024 c, 1024 c + 1024),
+  // thread t holds key 1024 c + t (register q = c when in_regs).
+  uint32_t eq_base = 0, sel_base = 0;
+  const int n_chunks = (n + kSelBlock - 1) / kSelBlock;
+  for (int c = 0; c < n_chunks; ++c) {
+    const int j = c * kSelBlock + t;
+    uint32_t k = 0;
+    if (j < n) {
+      if (in_regs) {
+#pragma unroll
+        for (int q = 0; q < kSelRegKeys; ++q)
+          if (q == c) k = key[q];
+      } else {
+        k = order_key(sc[j]);
+      }
     }
+    const bool valid = j < n && b > 0;
+    const uint32_t is_eq = valid && k == T;
+    uint32_t tot;
+    const uint32_t eq_rank = eq_base + block_exclusive_scan(is_eq, scan, &tot);
+    eq_base += tot;
+    const uint32_t sel = valid && (k > T || (is_eq && eq_rank < need_eq));
+    const uint32_t pos = sel_base + block_exclusive_scan(sel, scan, &tot);
+    sel_base += tot;
+    if (sel && pos < (uint32_t)b) out_idx[pos] = j;        // exactly b are selected
+    const uint64_t bal = __ballot(sel);
+    const int wbase = (c * kSelBlock + wave * 64) >> 5;    // first mask word of this wave
+    if (lane == 0 && wbase < words) out_mask[wbase] = (uint32_t)bal;
+    if (lane == 32 && wbase + 1 < words) out_mask[wbase + 1] = (uint32_t)(bal >> 32);
   }
-  const uint32_t sel_before = block_exclusive_scan(n_sel, scan, &tot);
-  // Write indices (ascending) and the mask words of this range.
-  uint32_t pos = sel_before, eq_seen = eq_before, word = 0;
-  for (int j = lo; j < hi; ++j) {
-    bool sel = false;
-    if (b > 0) {
-      const uint32_t k = order_key(sc[j]);
-      sel = k > T || (k == T && eq_seen < need_eq);
-      eq_seen += k == T;
-    }
-    if (sel) {
-      if (pos < (uint32_t)b) out_idx[pos] = j;   // exactly b are selected; never write past b
-      ++pos;
-      word |= 1u << (j & 31);
-    }
-    if ((j & 31) == 31 || j == hi - 1) {
-      out_mask[j >> 5] = word;
-      word = 0;
-    }
-  }
-  // Mask words past the last index (none when n is a multiple of 32, else
-  // already written by the owner of the tail).
-  for (int wi = t; wi < words; wi += kSelBlock)
-    if (wi * 32 >= n) out_mask[wi] = 0u;
 }
 
 }  // namespace kvfix

@@ -21,7 +21,7 @@ STATUS = {0: "KVFIX_OK", 1: "KVFIX_ERR_ARG", 2: "KVFIX_ERR_ALIGN", 3: "KVFIX_ERR
           4: "KVFIX_ERR_HIP", 5: "KVFIX_ERR_UNSUPPORTED"}
 
 EXPORTS = ("kvfix_rope_shift", "kvfix_score", "kvfix_score_draft_workspace", "kvfix_score_draft",
-           "kvfix_select_topb", "kvfix_fit_mean", "kvfix_apply", "kvfix_diff_encode_workspace",
+           "kvfix_select_topb", "kvfix_fit_mean_workspace", "kvfix_fit_mean", "kvfix_apply", "kvfix_diff_encode_workspace",
            "kvfix_diff_encode", "kvfix_diff_decode_workspace", "kvfix_diff_decode",
            "kvfix_status_string", "kvfix_version")
 
@@ -81,7 +81,8 @@ def lib() -> ctypes.CDLL:
             "kvfix_score_draft_workspace": [I32, I32, I32, I32, I32, I32],
             "kvfix_score_draft": [P, I32, I32, P, I32, P, P, P, ctypes.c_size_t, P],
             "kvfix_select_topb": [P, I32, I32, I32, P, P, P],
-            "kvfix_fit_mean": [P, I32, P, P, P, I32, P, P, P, P],
+            "kvfix_fit_mean_workspace": [I32, I32, I32, I32, I32],
+            "kvfix_fit_mean": [P, I32, P, P, P, I32, P, P, P, P, ctypes.c_size_t, P],
             "kvfix_apply": [P, P, P, P, F, F, P, P, P, P],
             "kvfix_diff_encode_workspace": [I32, I32, I32, I32],
             "kvfix_diff_encode": [P, P, P, P, P, F, P, P, P, ctypes.c_size_t, P],
@@ -95,6 +96,7 @@ def lib() -> ctypes.CDLL:
             fn.argtypes = args
             fn.restype = ctypes.c_int32
         L.kvfix_score_draft_workspace.restype = ctypes.c_size_t
+        L.kvfix_fit_mean_workspace.restype = ctypes.c_size_t
         L.kvfix_diff_encode_workspace.restype = ctypes.c_size_t
         L.kvfix_diff_decode_workspace.restype = ctypes.c_size_t
         L.kvfix_status_string.restype = ctypes.c_char_p
@@ -215,18 +217,30 @@ def kvfix_select_topb(scores: torch.Tensor, b: int, idx: torch.Tensor,
                                                         _ptr(mask), _stream()))
 
 
+def kvfix_fit_mean_workspace(n_layers: int, n_segs: int, n_heads: int, head_dim: int,
+                             b: int) -> int:
+    return int(lib().kvfix_fit_mean_workspace(n_layers, n_segs, n_heads, head_dim, b))
+
+
 def kvfix_fit_mean(fresh: Plane, reuse: Plane, out: Optional[Plane], idx: torch.Tensor, b: int,
                    mu: torch.Tensor, delta: Optional[torch.Tensor] = None, theta: float = 0.0,
-                   style: int = ROPE_HALF, A=None, B=None, fresh_by_slot: bool = False) -> None:
+                   style: int = ROPE_HALF, A=None, B=None, fresh_by_slot: bool = False,
+                   ws: Optional[torch.Tensor] = None) -> None:
+    """ws: device workspace (any dtype) of at least kvfix_fit_mean_workspace bytes; a
+    fresh one is allocated through torch when omitted."""
     rr = None
     if delta is not None:
         r, _ = make_rope(delta, theta, style)
         rr = ctypes.byref(r)
     lr = make_lowrank(A, B)
     lrp = ctypes.byref(lr[0]) if lr else None
+    c = reuse.c
+    need = kvfix_fit_mean_workspace(c.n_layers, c.n_segs, c.n_heads, c.head_dim, b)
+    if ws is None:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=mu.device)
     _check("kvfix_fit_mean", lib().kvfix_fit_mean(
         fresh.ref(), int(fresh_by_slot), reuse.ref(), out.ref() if out else None, _ptr(idx), b,
-        rr, lrp, _ptr(mu), _stream()))
+        rr, lrp, _ptr(mu), _ptr(ws), ws.numel() * ws.element_size(), _stream()))
 
 
 def kvfix_apply(reuse: Plane, out: Plane, mask: Optional[torch.Tensor], mu: torch.Tensor,

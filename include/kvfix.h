@@ -184,14 +184,20 @@ kvfix_status kvfix_select_topb(const float* scores, int32_t n_rows, int32_t n, i
  * fresh rows are also copied into out at the probe positions (exact copy).
  * b == 0 gives mu = 0.  [AKS step 3 and the equation for mu-hat; KVCMAS eq. 7]
  * mu: device fp32 [n_layers][n_segs][n_heads][head_dim], contiguous.
- * idx: device int32 [n_segs][b], each in [0, n_tokens) (not checked on the host).
+ * idx: device int32 [n_segs][b]; an index outside [0, n_tokens) is skipped
+ * (device data is not checked on the host).
  * out may alias reuse (in-place correction).
- * Arithmetic: fp64 accumulation in a fixed order, rounded once to fp32.
+ * ws: device workspace of kvfix_fit_mean_workspace(...) bytes, 16-byte
+ * aligned (partial sums of 128-probe slices).
+ * Arithmetic: fp64 residuals and sums in a fixed order, rounded once to fp32.
  * ------------------------------------------------------------------------- */
+size_t kvfix_fit_mean_workspace(int32_t n_layers, int32_t n_segs, int32_t n_heads,
+                                int32_t head_dim, int32_t b);
 kvfix_status kvfix_fit_mean(const kvfix_plane* fresh, int32_t fresh_by_slot,
                             const kvfix_plane* reuse, const kvfix_plane* out,
                             const int32_t* idx, int32_t b, const kvfix_rope* rope,
-                            const kvfix_lowrank* lowrank, float* mu, void* stream);
+                            const kvfix_lowrank* lowrank, float* mu, void* ws, size_t ws_bytes,
+                            void* stream);
 
 /* ---------------------------------------------------------------------------
  * a6. Fused apply.  For every token j whose mask bit is clear:
