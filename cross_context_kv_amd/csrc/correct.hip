@@ -290,6 +290,34 @@ __global__ void fit_finish_kernel(FitFinishParams F) {
 // ---------------------------------------------------------------------------
 // apply
 // ---------------------------------------------------------------------------
+//
+// Persistent blocks sweep the plane: the rows are cut into chunks of CH rows
+// (one batch of U rows per lane), and block b takes chunks b, b + grid,
+// b + 2 grid, ...  At any moment the whole chip therefore streams one compact
+// window of HBM instead of one separate stream per block, which keeps the
+// memory system close to its copy rate.  Chunks are numbered segment-major,
+// so a block recomputes its rotary table only when the segment changes.
+//
+// Per chunk, a block issues its row loads first, then the chunk's set-up
+// loads (probe bits, weights, rank-state rows; the lane's mean and B
+// values), so both share one memory round trip; the per-row data goes
+// through LDS (double-buffered: one barrier per chunk).
+//
+// bf16 planes with head_dim 128 take the rank-r term on the matrix cores: a
+// wave's U x RPW = 16 rows form one 16 x 16 x 4 fp32 MFMA tile per 16-dim
+// slice, with the tile's columns permuted so that each lane receives exactly
+// the 8 contiguous dims it holds (see apply_kernel), and the rotated row plus
+// the weighted mean as the accumulator input.
+
+constexpr int kApplyBlock = 256;
+constexpr int kApplyWaves = kApplyBlock / kWave;
+constexpr int kApplyU = 4;
+constexpr int64_t kApplyGrid = 768;
+
+// Rows per chunk for storage type T and head_dim HD (host and device).
+__host__ __device__ constexpr int apply_chunk_rows(int vec, int hd) {
+  return kApplyWaves * (kWave / (hd / vec)) * kApplyU;
+}
 
 struct ApplyParams {
   DPlane in, out;
@@ -299,8 +327,10 @@ struct ApplyParams {
   const float* mu;
   DLowRank lr;
   RopeArgs rope;
-  int32_t S, H, n, chunks, rows_per_block, mask_words;
+  int32_t S, L, H, n, cpu, mask_words;
+  int64_t n_chunks;
   int32_t a_vec;               // A rows may be read as whole 16-byte vectors
+  int32_t b_vec;               // B rows may be read as whole 16-byte vectors
 };
 
 // Rank-state left factor of one row: MAXR values (zero past the rank).
@@ -320,147 +350,270 @@ __device__ __forceinline__ void load_a_row(const float* Ar, int rank, bool vec, 
   for (int k = 0; k < MAXR; ++k) out[k] = k < rank ? (C)Ar[k] : (C)0;
 }
 
+// N consecutive floats (N a multiple of 4 when vec) from global memory.
+template <int N, typename C>
+__device__ __forceinline__ void load_floats(const float* p, bool vec, C* out) {
+  if constexpr (N % 4 == 0) {
+    if (vec) {
+#pragma unroll
+      for (int q = 0; q < N / 4; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(p + 4 * q);
+        out[4 * q] = (C)v.x; out[4 * q + 1] = (C)v.y; out[4 * q + 2] = (C)v.z; out[4 * q + 3] = (C)v.w;
+      }
+      return;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < N; ++k) out[k] = (C)p[k];
+}
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 template <typename T, typename C, int HD, int STYLE, int MAXR, bool PAGED>
-__global__ __launch_bounds__(kBlock) void apply_kernel(ApplyParams P) {
+__global__ __launch_bounds__(kApplyBlock) __attribute__((amdgpu_waves_per_eu(3))) void apply_kernel(ApplyParams P) {
   using M = PartMap<T, HD, STYLE>;
   using Cc = Codec<T, C>;
-  constexpr int V = M::V, G = M::G, RPW = M::RPW, U = 4;
+  constexpr int V = M::V, G = M::G, RPW = M::RPW, U = kApplyU;
+  constexpr int kStep = kApplyWaves * RPW;          // rows per block per batch step
+  constexpr int CH = kStep * U;                     // rows per chunk
+  static_assert(CH == apply_chunk_rows(V, HD), "chunk size");
+  static_assert(CH <= kApplyBlock, "one thread per chunk row in the set-up");
   constexpr int R = MAXR > 0 ? MAXR : 1;
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  constexpr int RS = MAXR > 0 ? (MAXR + 3) / 4 * 4 : 1;   // LDS row stride of A
+  constexpr int KB = (MAXR + 3) / 4;                      // MFMA k-blocks
+  constexpr bool kMfma = std::is_same<T, bf16_t>::value && std::is_same<C, float>::value &&
+                         HD == 128 && MAXR > 0;
+  static_assert(!kMfma || (V == 8 && G == 16 && RPW == 4 && U == 4), "MFMA tile shape");
+  constexpr int NW = CH >= 32 ? CH / 32 : 1;        // probe-bit words per chunk
+  static_assert(CH % 32 == 0 || 32 % CH == 0, "chunks start on a word or inside one");
+  constexpr int kPages = CH + 2;
+
+  __shared__ C tab_c[2][HD / 2], tab_s[2][HD / 2];
+  __shared__ __attribute__((aligned(16))) float sa[2][MAXR > 0 ? CH * RS : 1];
+  __shared__ float sw[2][CH];
+  __shared__ int32_t spin[2][PAGED ? kPages : 1], spout[2][PAGED ? kPages : 1];
+
+  const int t = threadIdx.x;
+  const int lane = t & (kWave - 1), wave = t / kWave;
   const int g = lane % G, rw = lane / G;
-  const int chunk = blockIdx.x % P.chunks;
-  int unit = blockIdx.x / P.chunks;
-  const int h = unit % P.H; unit /= P.H;
-  const int s = unit % P.S;
-  const int l = unit / P.S;
-  const int j_begin = chunk * P.rows_per_block;
-  const int j_end = min(P.n, j_begin + P.rows_per_block);
-  const int nrows = j_end - j_begin;
-
-  __shared__ C tc[HD / 2], ts[HD / 2];
-  __shared__ uint32_t smask[kRowsPerBlock / 32 + 1];
-  __shared__ float sw[kRowsPerBlock];                         // per-row weights
-  __shared__ __attribute__((aligned(16))) float sa[MAXR > 0 ? kRowsPerBlock * MAXR : 1];
-  __shared__ int32_t spin[PAGED ? kRowsPerBlock + 1 : 1], spout[PAGED ? kRowsPerBlock + 1 : 1];
-  if constexpr (STYLE != kStyleNone) rope_table<HD, C>(P.rope, P.rope.delta[s], tc, ts);
-  // Stage this block's per-row data: probe bits, weights, rank-state rows,
-  // page ids.  Each is one contiguous range, read with coalesced loads.
-  const int w0 = j_begin >> 5;
-  if (P.mask) {
-    const uint32_t* mrow = P.mask + (int64_t)s * P.mask_words;
-    for (int i = threadIdx.x; i <= ((j_end - 1) >> 5) - w0; i += kBlock) smask[i] = mrow[w0 + i];
-  }
-  const float* srow = P.scores ? P.scores + (int64_t)s * P.n + j_begin : nullptr;
-  for (int i = threadIdx.x; i < nrows; i += kBlock)
-    sw[i] = srow ? fminf(fmaxf(srow[i], P.w_lo), P.w_hi) : 1.0f;
+  const int i_first = wave * RPW + rw;
   const int rank = P.lr.rank;
-  if constexpr (MAXR > 0) {
-    const float* Ab = P.lr.A + l * P.lr.sA_layer + s * P.lr.sA_seg + h * P.lr.sA_head +
-                      (int64_t)j_begin * rank;
-    const int na = nrows * rank;
-    if (P.a_vec) {
-      for (int i = threadIdx.x; i < na / 4; i += kBlock)
-        *reinterpret_cast<float4*>(&sa[4 * i]) = *reinterpret_cast<const float4*>(Ab + 4 * i);
-    } else {
-      for (int i = threadIdx.x; i < na; i += kBlock) sa[i] = Ab[i];
-    }
-  }
-  int pin0 = 0, pout0 = 0;
-  if constexpr (PAGED) {
-    pin0 = stage_pages(P.in, s, j_begin, j_end, spin);
-    pout0 = stage_pages(P.out, s, j_begin, j_end, spout);
-  }
-
-  // Per-unit constants of this lane's dims: mean residual, rank-state B.
-  const int64_t ubase = (((int64_t)l * P.S + s) * P.H + h) * HD;
-  C mu[V];
-#pragma unroll
-  for (int m = 0; m < V; ++m) mu[m] = (C)P.mu[ubase + M::dim(g, m)];
-  C Bv[R][V];
-  if constexpr (MAXR > 0) {
-    const float* Bp = P.lr.B + l * P.lr.sB_layer + s * P.lr.sB_seg + h * P.lr.sB_head;
-#pragma unroll
-    for (int k = 0; k < MAXR; ++k)
-#pragma unroll
-      for (int m = 0; m < V; ++m) Bv[k][m] = k < rank ? (C)Bp[k * HD + M::dim(g, m)] : (C)0;
-  }
-  __syncthreads();
+  int cur_s = -1, gen = 0;
   C cs[V], ss[V];
-  if constexpr (STYLE != kStyleNone) {
-    const bool first_half = STYLE == kStyleHalf && g < M::X;
 #pragma unroll
-    for (int m = 0; m < V; ++m) {
-      cs[m] = tc[M::pair(g, m)];
-      ss[m] = first_half ? -ts[M::pair(g, m)] : ts[M::pair(g, m)];
-    }
-  }
+  for (int m = 0; m < V; ++m) { cs[m] = (C)1; ss[m] = (C)0; }
 
-  // Dense planes: the unit's base addresses are loop invariant.
-  const T* in_unit = reinterpret_cast<const T*>(P.in.data) + (int64_t)l * P.in.s_layer +
-                     (int64_t)s * P.in.s_seg + (int64_t)h * P.in.s_head;
-  T* out_unit = reinterpret_cast<T*>(P.out.data) + (int64_t)l * P.out.s_layer +
-                (int64_t)s * P.out.s_seg + (int64_t)h * P.out.s_head;
-  constexpr int kStep = kWavesPerBlock * RPW;
-  for (int i0 = wave * RPW + rw; i0 < nrows; i0 += kStep * U) {
-    vu4 r0[U];
-    T* op[U];
+  // Probe bits of a chunk: NW words, uniform over the block (scalar loads),
+  // fetched one chunk ahead so that the row loads can skip probe rows.
+  auto chunk_words = [&](int64_t cc, uint32_t* w) {
+#pragma unroll
+    for (int qq = 0; qq < NW; ++qq) w[qq] = 0u;
+    if (P.mask == nullptr || cc >= P.n_chunks) return;
+    const int kk = (int)(cc % P.cpu);
+    const int ss_ = (int)(cc / ((int64_t)P.cpu * P.H * P.L));
+    const int wb = (kk * CH) >> 5;
+#pragma unroll
+    for (int qq = 0; qq < NW; ++qq)
+      if (wb + qq < P.mask_words) w[qq] = P.mask[(int64_t)ss_ * P.mask_words + wb + qq];
+  };
+  uint32_t mw[NW];
+  chunk_words(blockIdx.x, mw);
+
+  int it = 0;
+  for (int64_t c = blockIdx.x; c < P.n_chunks; c += gridDim.x, ++it) {
+    const int buf = it & 1;
+    int64_t q = c;
+    const int k = (int)(q % P.cpu); q /= P.cpu;
+    const int h = (int)(q % P.H); q /= P.H;
+    const int l = (int)(q % P.L);
+    const int s = (int)(q / P.L);
+    const int j_begin = k * CH;
+    const int j_end = min(P.n, j_begin + CH);
+    const int nrows = j_end - j_begin;
+    uint32_t mw_next[NW];
+    chunk_words(c + gridDim.x, mw_next);
+    // live rows of this lane: in range and not a probe
     bool live[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int i = i0 + u * kStep, j = j_begin + i;
-      live[u] = i < nrows;
-      if (P.mask && live[u]) live[u] = ((smask[(j >> 5) - w0] >> (j & 31)) & 1u) == 0;
+      const int i = i_first + u * kStep;
+      const int bit = (CH >= 32 ? i : (j_begin & 31) + i);
+      live[u] = i < nrows && ((mw[bit >> 5 < NW ? bit >> 5 : 0] >> (bit & 31)) & 1u) == 0;
     }
-    // Loads are unconditional (no branch between them, so they all stay in
-    // flight together): a dead row reads the plane's first vector instead, an
-    // address that always exists and stays in cache.
+
+    // Row loads are unconditional (no branch between them, so they all stay
+    // in flight together): a row past the chunk reads the plane's first
+    // vector instead, an address that always exists and stays in cache.
+    // Probe rows are loaded too and simply not stored.
+    vu4 r0[U];
+    const T* in_unit = reinterpret_cast<const T*>(P.in.data) + (int64_t)l * P.in.s_layer +
+                       (int64_t)s * P.in.s_seg + (int64_t)h * P.in.s_head;
+    T* out_unit = reinterpret_cast<T*>(P.out.data) + (int64_t)l * P.out.s_layer +
+                  (int64_t)s * P.out.s_seg + (int64_t)h * P.out.s_head;
+    if constexpr (!PAGED) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = j_begin + i0 + u * kStep;
-      const T* ip;
-      if constexpr (PAGED) {
-        const int64_t io = live[u] ? row_offset_staged(P.in, l, s, h, j, spin, pin0) : -1;
-        const int64_t oo = live[u] ? row_offset_staged(P.out, l, s, h, j, spout, pout0) : -1;
-        live[u] = live[u] && io >= 0 && oo >= 0;
-        ip = reinterpret_cast<const T*>(P.in.data) + (live[u] ? io + M::dim(g, 0) : 0);
-        op[u] = reinterpret_cast<T*>(P.out.data) + oo;
-      } else {
-        ip = live[u] ? in_unit + (int64_t)j * P.in.s_token + M::dim(g, 0)
-                     : reinterpret_cast<const T*>(P.in.data);
-        op[u] = out_unit + (int64_t)j * P.out.s_token;
+      for (int u = 0; u < U; ++u) {
+        const int i = i_first + u * kStep;
+        const T* ip = live[u] ? in_unit + (int64_t)(j_begin + i) * P.in.s_token + M::dim(g, 0)
+                              : reinterpret_cast<const T*>(P.in.data);
+        r0[u] = ld16(ip);
       }
-      r0[u] = ld16(ip);
     }
-    wait_loads();
+
+    // Set-up loads: this thread's chunk row (weight, rank-state row) and the
+    // lane's per-unit mean and B values.
+    float wt = 1.0f;
+    if (P.scores && t < nrows) wt = P.scores[(int64_t)s * P.n + j_begin + t];
+    float arow[R];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      // the partner exchange runs on every lane of the wave (both halves of a
-      // row are live or dead together)
-      vu4 pr = r0[u];
-      if constexpr (STYLE == kStyleHalf) pr = partner16<M::X>(r0[u]);
-      if (!live[u]) continue;
-      const int i = i0 + u * kStep;
-      C x[V], pv[V];
-      Cc::unpack(r0[u], x);
-      if constexpr (STYLE == kStyleHalf) Cc::unpack(pr, pv);
-      if constexpr (STYLE != kStyleNone) rotate_part<STYLE, V>(x, pv, cs, ss);
-      const C w = (C)sw[i];
-      C Av[R];
+    for (int kk = 0; kk < R; ++kk) arow[kk] = 0.0f;
+    if constexpr (MAXR > 0) {
+      if (t < nrows) {
+        const float* Ar = P.lr.A + l * P.lr.sA_layer + s * P.lr.sA_seg + h * P.lr.sA_head +
+                          (int64_t)(j_begin + t) * rank;
+        load_a_row<MAXR>(Ar, rank, P.a_vec, arow);
+      }
+    }
+    const int64_t ubase = (((int64_t)l * P.S + s) * P.H + h) * HD;
+    C mu[V];
+    load_floats<V>(P.mu + ubase + M::dim(g, 0), true, mu);
+    const float* Bp = MAXR > 0 ? P.lr.B + l * P.lr.sB_layer + s * P.lr.sB_seg + h * P.lr.sB_head
+                               : nullptr;
+    // MFMA operand: lane supplies B[4 kb + lane / 16][8 (lane % 16) + n], n < 8.
+    float Bm[kMfma ? KB : 1][kMfma ? 8 : 1];
+    // VALU operand: B[k][dims of this lane].
+    C Bv[kMfma ? 1 : R][kMfma ? 1 : V];
+    if constexpr (kMfma) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int kr = 4 * kb + lane / 16;
+        if (kr < rank) load_floats<8>(Bp + kr * HD + 8 * (lane % 16), P.b_vec, Bm[kb]);
+        else
+#pragma unroll
+          for (int n = 0; n < 8; ++n) Bm[kb][n] = 0.0f;
+      }
+    } else if constexpr (MAXR > 0) {
+#pragma unroll
+      for (int kk = 0; kk < MAXR; ++kk) {
+        if (kk < rank) load_floats<V>(Bp + kk * HD + M::dim(g, 0), P.b_vec, Bv[kk]);
+        else
+#pragma unroll
+          for (int m = 0; m < V; ++m) Bv[kk][m] = (C)0;
+      }
+    }
+    const bool new_seg = STYLE != kStyleNone && s != cur_s;      // uniform over the block
+    if (new_seg) {
+      ++gen;
+      rope_table<HD, C>(P.rope, P.rope.delta[s], tab_c[gen & 1], tab_s[gen & 1]);
+    }
+    if (t < nrows) {
+      sw[buf][t] = fminf(fmaxf(wt, P.w_lo), P.w_hi);
       if constexpr (MAXR > 0) {
 #pragma unroll
-        for (int k = 0; k < MAXR; ++k) Av[k] = k < rank ? (C)sa[i * rank + k] : (C)0;
+        for (int kk = 0; kk < RS; ++kk) sa[buf][t * RS + kk] = kk < MAXR ? arow[kk] : 0.0f;
       }
+    }
+    int pin0 = 0, pout0 = 0;
+    if constexpr (PAGED) {
+      pin0 = stage_pages(P.in, s, j_begin, j_end, spin[buf]);
+      pout0 = stage_pages(P.out, s, j_begin, j_end, spout[buf]);
+    }
+    __syncthreads();
+    if (new_seg) {
+      const bool first_half = STYLE == kStyleHalf && g < M::X;
 #pragma unroll
       for (int m = 0; m < V; ++m) {
-        C y = fma(w, mu[m], x[m]);
+        cs[m] = tab_c[gen & 1][M::pair(g, m)];
+        const C sv = tab_s[gen & 1][M::pair(g, m)];
+        ss[m] = first_half ? -sv : sv;
+      }
+      cur_s = s;
+    }
+
+    T* op[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i_first + u * kStep, j = j_begin + i;
+      if constexpr (PAGED) {
+        const int64_t io = live[u] ? row_offset_staged(P.in, l, s, h, j, spin[buf], pin0) : -1;
+        const int64_t oo = live[u] ? row_offset_staged(P.out, l, s, h, j, spout[buf], pout0) : -1;
+        live[u] = live[u] && io >= 0 && oo >= 0;
+        r0[u] = ld16(reinterpret_cast<const T*>(P.in.data) + (live[u] ? io + M::dim(g, 0) : 0));
+        op[u] = reinterpret_cast<T*>(P.out.data) + oo;
+      } else {
+        op[u] = out_unit + (int64_t)j * P.out.s_token;
+      }
+    }
+    wait_loads();
+
+    if constexpr (kMfma) {
+      // Accumulator input: rotated row plus weighted mean; lane holds
+      // acc[m][u] = element m of its 8 dims for batch row u.
+      f32x4 acc[V];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        vu4 pr = r0[u];
+        if constexpr (STYLE == kStyleHalf) pr = partner16<M::X>(r0[u]);
+        C x[V], pv[V];
+        Cc::unpack(r0[u], x);
+        if constexpr (STYLE == kStyleHalf) Cc::unpack(pr, pv);
+        if constexpr (STYLE != kStyleNone) rotate_part<STYLE, V>(x, pv, cs, ss);
+        const C w = (C)sw[buf][i_first + u * kStep];
+#pragma unroll
+        for (int m = 0; m < V; ++m) acc[m][u] = fma(w, mu[m], x[m]);
+      }
+      // Tile row r = 4 (lane / 16) + u holds chunk row i_first + u kStep of
+      // the lane group lane / 16; as an A operand, lane supplies tile row
+      // lane % 16, i.e. chunk row wave RPW + (lane % 16) / 4 + ((lane % 16) % 4) kStep.
+      const int arow_i = wave * RPW + (lane % 16) / 4 + ((lane % 16) % 4) * kStep;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const float a = sa[buf][arow_i * RS + 4 * kb + lane / 16];
+#pragma unroll
+        for (int m = 0; m < V; ++m)
+          acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, Bm[kb][m], acc[m], 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (!live[u]) continue;
+        C y[V];
+#pragma unroll
+        for (int m = 0; m < V; ++m) y[m] = acc[m][u];
+        st16(op[u] + M::dim(g, 0), Cc::pack(y));
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        // the partner exchange runs on every lane of the wave (both halves of
+        // a row are live or dead together)
+        vu4 pr = r0[u];
+        if constexpr (STYLE == kStyleHalf) pr = partner16<M::X>(r0[u]);
+        if (!live[u]) continue;
+        const int i = i_first + u * kStep;
+        C x[V], pv[V];
+        Cc::unpack(r0[u], x);
+        if constexpr (STYLE == kStyleHalf) Cc::unpack(pr, pv);
+        if constexpr (STYLE != kStyleNone) rotate_part<STYLE, V>(x, pv, cs, ss);
+        const C w = (C)sw[buf][i];
+        C Av[R];
         if constexpr (MAXR > 0) {
 #pragma unroll
-          for (int k = 0; k < MAXR; ++k) y = fma(Av[k], Bv[k][m], y);
+          for (int kk = 0; kk < MAXR; ++kk) Av[kk] = (C)sa[buf][i * RS + kk];
         }
-        x[m] = y;
+#pragma unroll
+        for (int m = 0; m < V; ++m) {
+          C y = fma(w, mu[m], x[m]);
+          if constexpr (MAXR > 0) {
+#pragma unroll
+            for (int kk = 0; kk < MAXR; ++kk) y = fma(Av[kk], Bv[kk][m], y);
+          }
+          x[m] = y;
+        }
+        st16(op[u] + M::dim(g, 0), Cc::pack(x));
       }
-      st16(op[u] + M::dim(g, 0), Cc::pack(x));
     }
+#pragma unroll
+    for (int qq = 0; qq < NW; ++qq) mw[qq] = mw_next[qq];
   }
 }
 
@@ -510,11 +663,12 @@ struct ApplyLaunch {
   using C = typename std::conditional<std::is_same<T, float>::value, double, float>::type;
   template <bool PG>
   static void go(const ApplyParams& P, int rank_var, int64_t grid, hipStream_t st) {
+    const dim3 g((unsigned)grid), b(kApplyBlock);
     switch (rank_var) {
-      case 0: apply_kernel<T, C, HD, STYLE, 0, PG><<<dim3((unsigned)grid), dim3(kBlock), 0, st>>>(P); break;
-      case 2: apply_kernel<T, C, HD, STYLE, 2, PG><<<dim3((unsigned)grid), dim3(kBlock), 0, st>>>(P); break;
-      case 4: apply_kernel<T, C, HD, STYLE, 4, PG><<<dim3((unsigned)grid), dim3(kBlock), 0, st>>>(P); break;
-      default: apply_kernel<T, C, HD, STYLE, 8, PG><<<dim3((unsigned)grid), dim3(kBlock), 0, st>>>(P); break;
+      case 0: apply_kernel<T, C, HD, STYLE, 0, PG><<<g, b, 0, st>>>(P); break;
+      case 2: apply_kernel<T, C, HD, STYLE, 2, PG><<<g, b, 0, st>>>(P); break;
+      case 4: apply_kernel<T, C, HD, STYLE, 4, PG><<<g, b, 0, st>>>(P); break;
+      default: apply_kernel<T, C, HD, STYLE, 8, PG><<<g, b, 0, st>>>(P); break;
     }
   }
   static kvfix_status run(const ApplyParams& P, int rank_var, int64_t grid, hipStream_t st) {
@@ -628,6 +782,7 @@ extern "C" kvfix_status kvfix_apply(const kvfix_plane* reuse, const kvfix_plane*
   KVFIX_TRY(check_lowrank(lowrank));
   const int64_t units = (int64_t)reuse->n_layers * reuse->n_segs * reuse->n_heads;
   if (units == 0 || reuse->n_tokens == 0) return KVFIX_OK;
+  if (!aligned16(mu)) return KVFIX_ERR_ALIGN;
   ApplyParams P;
   P.in = make_dplane(*reuse);
   P.out = make_dplane(*out);
@@ -639,14 +794,15 @@ extern "C" kvfix_status kvfix_apply(const kvfix_plane* reuse, const kvfix_plane*
   P.lr = make_dlowrank(lowrank);
   P.a_vec = P.lr.rank > 0 && aligned16(P.lr.A) && (P.lr.sA_layer * 4) % 16 == 0 &&
             (P.lr.sA_seg * 4) % 16 == 0 && (P.lr.sA_head * 4) % 16 == 0 && (P.lr.rank * 4) % 16 == 0;
+  P.b_vec = P.lr.rank > 0 && aligned16(P.lr.B) && (P.lr.sB_layer * 4) % 16 == 0 &&
+            (P.lr.sB_seg * 4) % 16 == 0 && (P.lr.sB_head * 4) % 16 == 0;
   P.rope = make_rope_args(rope, reuse->head_dim);
-  P.S = reuse->n_segs; P.H = reuse->n_heads; P.n = reuse->n_tokens;
+  P.S = reuse->n_segs; P.L = reuse->n_layers; P.H = reuse->n_heads; P.n = reuse->n_tokens;
   P.mask_words = (reuse->n_tokens + 31) / 32;
-  int rpb = kRowsPerBlock;
-  P.rows_per_block = rpb;
-  P.chunks = (reuse->n_tokens + rpb - 1) / rpb;
-  const int64_t grid = units * P.chunks;
-  if (grid > kMaxGrid) return KVFIX_ERR_ARG;
+  const int ch = apply_chunk_rows(reuse->dtype == KVFIX_F32 ? 4 : 8, reuse->head_dim);
+  P.cpu = (reuse->n_tokens + ch - 1) / ch;
+  P.n_chunks = units * P.cpu;
+  const int64_t grid = P.n_chunks < kApplyGrid ? P.n_chunks : kApplyGrid;
   const int style = rope ? rope->style : kStyleNone;
   return dispatch_t_hd_style<ApplyLaunch>(reuse->dtype, reuse->head_dim, style, P,
                                           rank_variant(P.lr.rank), grid, (hipStream_t)stream);
