@@ -315,6 +315,46 @@ struct RopeArgs {
   double inv_freq[kMaxHeadDim / 2];
 };
 
+// sin and cos of a rotary angle x in fp64, small enough in code and
+// registers to sit inside streaming loops.  Cody-Waite reduction: k =
+// nearest integer to x 2/pi, r = x - k pi/2 with pi/2 split into two 30-bit
+// parts and a remainder, so k P1 and k P2 are exact for |k| < 2^23 (|x| up to
+// about 1.3e7 rad, i.e. shifts up to 2^23 positions); then the Taylor series
+// of sin and cos on |r| <= pi/4, through r^19 and r^20 (truncation below
+// 1e-22), and the quadrant k mod 4.  Within about one unit of 2^-53 of the
+// exact values.
+__device__ __forceinline__ void rope_sincos(double x, double* sp, double* cp) {
+  constexpr double kTwoOverPi = 0x1.45f306dc9c883p-1;
+  constexpr double kP1 = 0x1.921fb54000000p+0;     // pi/2, first 30 bits
+  constexpr double kP2 = 0x1.10b4611800000p-30;    // next 30 bits
+  constexpr double kP3 = 0x1.313198a2e0370p-61;    // remainder
+  const double k = rint(x * kTwoOverPi);
+  double r = fma(-k, kP1, x);
+  r = fma(-k, kP2, r);
+  r = fma(-k, kP3, r);
+  const double r2 = r * r;
+  // (-1)^i / (2i+1)!, i = 1..9 and (-1)^i / (2i)!, i = 1..10
+  constexpr double s3 = -1.0 / 6, s5 = 1.0 / 120, s7 = -1.0 / 5040, s9 = 1.0 / 362880,
+                   s11 = -1.0 / 39916800, s13 = 1.0 / 6227020800.0,
+                   s15 = -1.0 / 1307674368000.0, s17 = 1.0 / 355687428096000.0,
+                   s19 = -1.0 / 121645100408832000.0;
+  constexpr double c2 = -1.0 / 2, c4 = 1.0 / 24, c6 = -1.0 / 720, c8 = 1.0 / 40320,
+                   c10 = -1.0 / 3628800, c12 = 1.0 / 479001600.0,
+                   c14 = -1.0 / 87178291200.0, c16 = 1.0 / 20922789888000.0,
+                   c18 = -1.0 / 6402373705728000.0, c20 = 1.0 / 2432902008176640000.0;
+  double ps = fma(s19, r2, s17);
+  ps = fma(ps, r2, s15); ps = fma(ps, r2, s13); ps = fma(ps, r2, s11); ps = fma(ps, r2, s9);
+  ps = fma(ps, r2, s7); ps = fma(ps, r2, s5); ps = fma(ps, r2, s3);
+  const double sr = fma(r * r2, ps, r);
+  double pc = fma(c20, r2, c18);
+  pc = fma(pc, r2, c16); pc = fma(pc, r2, c14); pc = fma(pc, r2, c12); pc = fma(pc, r2, c10);
+  pc = fma(pc, r2, c8); pc = fma(pc, r2, c6); pc = fma(pc, r2, c4); pc = fma(pc, r2, c2);
+  const double cr = fma(r2, pc, 1.0);
+  const int q = (int)((int64_t)k & 3);
+  *sp = q == 0 ? sr : q == 1 ? cr : q == 2 ? -sr : -cr;
+  *cp = q == 0 ? cr : q == 1 ? -sr : q == 2 ? -cr : sr;
+}
+
 // Fill cos/sin of the HD/2 pair angles for a shift of delta positions into
 // LDS (fp64 angle and sincos, stored in C).  Called by the whole block;
 // followed by __syncthreads() at the call site.
@@ -323,7 +363,7 @@ __device__ __forceinline__ void rope_table(const RopeArgs& r, int64_t delta, C* 
   for (int t = threadIdx.x; t < HD / 2; t += blockDim.x) {
     const double phi = (double)delta * r.inv_freq[t];
     double sv, cv;
-    sincos(phi, &sv, &cv);
+    rope_sincos(phi, &sv, &cv);
     tc[t] = (C)cv;
     ts[t] = (C)sv;
   }

@@ -149,34 +149,35 @@ __global__ __launch_bounds__(kBlock) void fit_partial_kernel(FitParams P) {
   __shared__ double red[kWavesPerBlock][HD];
   __shared__ int32_t sj[kFitRows], spf[kFitRows], spr[kFitRows], spo[kFitRows];
   if constexpr (STYLE != kStyleNone) rope_table<HD, double>(P.rope, P.rope.delta[s], tc, ts);
-  // Stage the slice's probe indices and their page ids.
+  // Stage the slice's probe indices and their page ids.  Thread t < nk also
+  // loads the rank-state row of slot t now (summed after the main loop), so
+  // that load shares a memory round trip with the staging.
   const int32_t* idx = P.idx + (int64_t)s * P.b;
-  for (int i = threadIdx.x; i < nk; i += kBlock) {
-    const int k = k_begin + i;
-    const int j = idx[k];
-    const bool ok = j >= 0 && j < P.n;            // an index out of range is dropped
-    sj[i] = ok ? j : -1;
-    spf[i] = ok ? page_of(P.fresh, s, P.fresh_by_slot ? k : j) : -1;
-    spr[i] = ok ? page_of(P.reuse, s, j) : -1;
-    spo[i] = ok && P.has_out ? page_of(P.out, s, j) : 0;
-  }
-  __syncthreads();
-  // Sum of the slice's rank-state rows: one row per thread, then a fixed-order
-  // butterfly over the wave and the waves in index order.
-  __shared__ double redA[kWavesPerBlock][kFitMaxRank];
-  double* outp = P.partial + (int64_t)blockIdx.x * PW;
   const int rank = P.lr.rank;
-  if (rank > 0) {
-    const float* Ab = P.lr.A + l * P.lr.sA_layer + s * P.lr.sA_seg + h * P.lr.sA_head;
-    const int j = threadIdx.x < nk ? sj[threadIdx.x] : -1;
-    for (int k = 0; k < rank; ++k) {
-      double a = j >= 0 ? (double)Ab[(int64_t)j * rank + k] : 0.0;
+  double* outp = P.partial + (int64_t)blockIdx.x * PW;
+  float arow[kFitMaxRank];
 #pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) a += __shfl_xor(a, off);
-      if (lane == 0) redA[wave][k] = a;
+  for (int k = 0; k < kFitMaxRank; ++k) arow[k] = 0.0f;
+  {
+    const int i = threadIdx.x;
+    if (i < nk) {
+      const int k = k_begin + i;
+      const int j = idx[k];
+      const bool ok = j >= 0 && j < P.n;            // an index out of range is dropped
+      sj[i] = ok ? j : -1;
+      spf[i] = ok ? page_of(P.fresh, s, P.fresh_by_slot ? k : j) : -1;
+      spr[i] = ok ? page_of(P.reuse, s, j) : -1;
+      spo[i] = ok && P.has_out ? page_of(P.out, s, j) : 0;
+      if (ok && rank > 0) {
+        const float* Ar = P.lr.A + l * P.lr.sA_layer + s * P.lr.sA_seg + h * P.lr.sA_head +
+                          (int64_t)j * rank;
+#pragma unroll
+        for (int kk = 0; kk < kFitMaxRank; ++kk) arow[kk] = kk < rank ? Ar[kk] : 0.0f;
+      }
     }
   }
-  static_assert(kFitRows == kBlock, "one probe row per thread in the rank-state sum");
+  __syncthreads();
+  static_assert(kFitRows <= kBlock, "one probe row per thread in the rank-state sum");
   double cs[V], ss[V];
   if constexpr (STYLE != kStyleNone) {
     const bool first_half = STYLE == kStyleHalf && g < M::X;
@@ -227,6 +228,17 @@ __global__ __launch_bounds__(kBlock) void fit_partial_kernel(FitParams P) {
 #pragma unroll
       for (int m = 0; m < V; ++m) acc[m] += fr[m] - x[m];
       if (P.has_out) st16(reinterpret_cast<T*>(P.out.data) + oo[u] + M::dim(g, 0), f[u]);
+    }
+  }
+  // Sum of the slice's rank-state rows (one row per thread): fixed-order
+  // butterfly over the wave, then the waves in index order.
+  __shared__ double redA[kWavesPerBlock][kFitMaxRank];
+  if (rank > 0) {
+    for (int k = 0; k < rank; ++k) {
+      double a = (double)arow[k];
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) a += __shfl_xor(a, off);
+      if (lane == 0) redA[wave][k] = a;
     }
   }
   // Fixed-order reduction: butterfly over the rows of a wave, then the waves
@@ -328,7 +340,8 @@ struct ApplyParams {
   DLowRank lr;
   RopeArgs rope;
   int32_t S, L, H, n, cpu, mask_words;
-  int64_t n_chunks;
+  // chunk c = ((s L + l) H + h) cpu + k; the grid stride in the same digits
+  int32_t gk, gh, gl, gs;
   int32_t a_vec;               // A rows may be read as whole 16-byte vectors
   int32_t b_vec;               // B rows may be read as whole 16-byte vectors
 };
@@ -370,7 +383,7 @@ __device__ __forceinline__ void load_floats(const float* p, bool vec, C* out) {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <typename T, typename C, int HD, int STYLE, int MAXR, bool PAGED>
-__global__ __launch_bounds__(kApplyBlock) __attribute__((amdgpu_waves_per_eu(3))) void apply_kernel(ApplyParams P) {
+__device__ __forceinline__ void apply_body(const ApplyParams& P) {
   using M = PartMap<T, HD, STYLE>;
   using Cc = Codec<T, C>;
   constexpr int V = M::V, G = M::G, RPW = M::RPW, U = kApplyU;
@@ -398,40 +411,75 @@ __global__ __launch_bounds__(kApplyBlock) __attribute__((amdgpu_waves_per_eu(3))
   const int g = lane % G, rw = lane / G;
   const int i_first = wave * RPW + rw;
   const int rank = P.lr.rank;
+  const int64_t in_step = (int64_t)kStep * P.in.s_token;
+  const int64_t out_step = (int64_t)kStep * P.out.s_token;
   int cur_s = -1, gen = 0;
-  C cs[V], ss[V];
-#pragma unroll
-  for (int m = 0; m < V; ++m) { cs[m] = (C)1; ss[m] = (C)0; }
-
+  const bool first_half = STYLE == kStyleHalf && g < M::X;
+  // Chunk coordinates (block-uniform).  The block advances by the grid
+  // stride, added digit by digit with carries: no division in the loop.
+  struct Pos { int k, h, l, s; };
+  auto advance = [&](Pos p) {
+    p.k += P.gk;
+    int cy = p.k >= P.cpu; if (cy) p.k -= P.cpu;
+    p.h += P.gh + cy;
+    cy = p.h >= P.H; if (cy) p.h -= P.H;
+    p.l += P.gl + cy;
+    cy = p.l >= P.L; if (cy) p.l -= P.L;
+    p.s += P.gs + cy;
+    return p;
+  };
   // Probe bits of a chunk: NW words, uniform over the block (scalar loads),
   // fetched one chunk ahead so that the row loads can skip probe rows.
-  auto chunk_words = [&](int64_t cc, uint32_t* w) {
+  auto chunk_words = [&](Pos p, uint32_t* w) {
 #pragma unroll
     for (int qq = 0; qq < NW; ++qq) w[qq] = 0u;
-    if (P.mask == nullptr || cc >= P.n_chunks) return;
-    const int kk = (int)(cc % P.cpu);
-    const int ss_ = (int)(cc / ((int64_t)P.cpu * P.H * P.L));
-    const int wb = (kk * CH) >> 5;
+    if (P.mask == nullptr || p.s >= P.S) return;
+    const int wb = (p.k * CH) >> 5;
 #pragma unroll
     for (int qq = 0; qq < NW; ++qq)
-      if (wb + qq < P.mask_words) w[qq] = P.mask[(int64_t)ss_ * P.mask_words + wb + qq];
+      if (wb + qq < P.mask_words) w[qq] = P.mask[(int64_t)p.s * P.mask_words + wb + qq];
   };
+  Pos pos;
+  {
+    unsigned q = blockIdx.x;
+    pos.k = (int)(q % (unsigned)P.cpu); q /= (unsigned)P.cpu;
+    pos.h = (int)(q % (unsigned)P.H); q /= (unsigned)P.H;
+    pos.l = (int)(q % (unsigned)P.L);
+    pos.s = (int)(q / (unsigned)P.L);
+  }
   uint32_t mw[NW];
-  chunk_words(blockIdx.x, mw);
+  chunk_words(pos, mw);
+  // rotary frequency of table entry t (parked in LDS: written and read by
+  // thread t only), and the current segment's shift
+  __shared__ double sfreq[STYLE != kStyleNone ? HD / 2 : 1];
+  if (STYLE != kStyleNone && t < HD / 2) sfreq[t] = P.rope.inv_freq[t];
+  int64_t delta_cur = STYLE != kStyleNone && pos.s < P.S ? P.rope.delta[pos.s] : 0;
 
   int it = 0;
-  for (int64_t c = blockIdx.x; c < P.n_chunks; c += gridDim.x, ++it) {
+  for (; pos.s < P.S; ++it) {
     const int buf = it & 1;
-    int64_t q = c;
-    const int k = (int)(q % P.cpu); q /= P.cpu;
-    const int h = (int)(q % P.H); q /= P.H;
-    const int l = (int)(q % P.L);
-    const int s = (int)(q / P.L);
+    const int k = pos.k, h = pos.h, l = pos.l, s = pos.s;
     const int j_begin = k * CH;
     const int j_end = min(P.n, j_begin + CH);
     const int nrows = j_end - j_begin;
+    // A new segment needs its rotary table; it is computed first, while
+    // nothing else of the chunk is live (chunks are segment-major, so this
+    // is rare).  Its shift was fetched one chunk ahead.
+    const bool new_seg = STYLE != kStyleNone && s != cur_s;      // uniform over the block
+    if (new_seg) {
+      ++gen;
+      if (t < HD / 2) {
+        double sv, cv;
+        rope_sincos((double)delta_cur * sfreq[t], &sv, &cv);
+        tab_c[gen & 1][t] = (C)cv;
+        tab_s[gen & 1][t] = (C)sv;
+      }
+    }
+    const Pos next = advance(pos);
     uint32_t mw_next[NW];
-    chunk_words(c + gridDim.x, mw_next);
+    chunk_words(next, mw_next);
+    int64_t delta_next = 0;
+    if (STYLE != kStyleNone && next.s < P.S && next.s != s) delta_next = P.rope.delta[next.s];
     // live rows of this lane: in range and not a probe
     bool live[U];
 #pragma unroll
@@ -446,18 +494,19 @@ __global__ __launch_bounds__(kApplyBlock) __attribute__((amdgpu_waves_per_eu(3))
     // vector instead, an address that always exists and stays in cache.
     // Probe rows are loaded too and simply not stored.
     vu4 r0[U];
-    const T* in_unit = reinterpret_cast<const T*>(P.in.data) + (int64_t)l * P.in.s_layer +
-                       (int64_t)s * P.in.s_seg + (int64_t)h * P.in.s_head;
-    T* out_unit = reinterpret_cast<T*>(P.out.data) + (int64_t)l * P.out.s_layer +
-                  (int64_t)s * P.out.s_seg + (int64_t)h * P.out.s_head;
+    // Dense planes: this lane's first row of the chunk; its further rows
+    // are kStep rows apart.
+    const int64_t jf = j_begin + i_first;
+    const T* ip0 = reinterpret_cast<const T*>(P.in.data) + (int64_t)l * P.in.s_layer +
+                   (int64_t)s * P.in.s_seg + (int64_t)h * P.in.s_head + jf * P.in.s_token +
+                   M::dim(g, 0);
+    T* op0 = reinterpret_cast<T*>(P.out.data) + (int64_t)l * P.out.s_layer +
+             (int64_t)s * P.out.s_seg + (int64_t)h * P.out.s_head + jf * P.out.s_token +
+             M::dim(g, 0);
     if constexpr (!PAGED) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int i = i_first + u * kStep;
-        const T* ip = live[u] ? in_unit + (int64_t)(j_begin + i) * P.in.s_token + M::dim(g, 0)
-                              : reinterpret_cast<const T*>(P.in.data);
-        r0[u] = ld16(ip);
-      }
+      for (int u = 0; u < U; ++u)
+        r0[u] = ld16(live[u] ? ip0 + u * in_step : reinterpret_cast<const T*>(P.in.data));
     }
 
     // Set-up loads: this thread's chunk row (weight, rank-state row) and the
@@ -501,11 +550,6 @@ __global__ __launch_bounds__(kApplyBlock) __attribute__((amdgpu_waves_per_eu(3))
           for (int m = 0; m < V; ++m) Bv[kk][m] = (C)0;
       }
     }
-    const bool new_seg = STYLE != kStyleNone && s != cur_s;      // uniform over the block
-    if (new_seg) {
-      ++gen;
-      rope_table<HD, C>(P.rope, P.rope.delta[s], tab_c[gen & 1], tab_s[gen & 1]);
-    }
     if (t < nrows) {
       sw[buf][t] = fminf(fmaxf(wt, P.w_lo), P.w_hi);
       if constexpr (MAXR > 0) {
@@ -519,31 +563,36 @@ __global__ __launch_bounds__(kApplyBlock) __attribute__((amdgpu_waves_per_eu(3))
       pout0 = stage_pages(P.out, s, j_begin, j_end, spout[buf]);
     }
     __syncthreads();
-    if (new_seg) {
-      const bool first_half = STYLE == kStyleHalf && g < M::X;
+    if (new_seg) cur_s = s;
+    // This lane's cos / signed sin (read from the block's table for the
+    // segment each chunk, so they hold no registers across the loads).
+    C cs[V], ss[V];
+    if constexpr (STYLE != kStyleNone) {
 #pragma unroll
       for (int m = 0; m < V; ++m) {
         cs[m] = tab_c[gen & 1][M::pair(g, m)];
         const C sv = tab_s[gen & 1][M::pair(g, m)];
         ss[m] = first_half ? -sv : sv;
       }
-      cur_s = s;
     }
 
-    T* op[U];
+    // Output row of batch row u (dense: op0 + u out_step; paged: looked up).
+    int64_t po[PAGED ? U : 1];
+    if constexpr (PAGED) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = i_first + u * kStep, j = j_begin + i;
-      if constexpr (PAGED) {
+      for (int u = 0; u < U; ++u) {
+        const int j = j_begin + i_first + u * kStep;
         const int64_t io = live[u] ? row_offset_staged(P.in, l, s, h, j, spin[buf], pin0) : -1;
         const int64_t oo = live[u] ? row_offset_staged(P.out, l, s, h, j, spout[buf], pout0) : -1;
         live[u] = live[u] && io >= 0 && oo >= 0;
         r0[u] = ld16(reinterpret_cast<const T*>(P.in.data) + (live[u] ? io + M::dim(g, 0) : 0));
-        op[u] = reinterpret_cast<T*>(P.out.data) + oo;
-      } else {
-        op[u] = out_unit + (int64_t)j * P.out.s_token;
+        po[u] = oo + M::dim(g, 0);
       }
     }
+    auto out_row = [&](int u) -> T* {
+      if constexpr (PAGED) return reinterpret_cast<T*>(P.out.data) + po[u];
+      else return op0 + u * out_step;
+    };
     wait_loads();
 
     if constexpr (kMfma) {
@@ -561,6 +610,8 @@ __global__ __launch_bounds__(kApplyBlock) __attribute__((amdgpu_waves_per_eu(3))
         const C w = (C)sw[buf][i_first + u * kStep];
 #pragma unroll
         for (int m = 0; m < V; ++m) acc[m][u] = fma(w, mu[m], x[m]);
+        // one row at a time: keeps the unpacked rows out of registers together
+        __builtin_amdgcn_sched_barrier(0);
       }
       // Tile row r = 4 (lane / 16) + u holds chunk row i_first + u kStep of
       // the lane group lane / 16; as an A operand, lane supplies tile row
@@ -579,7 +630,7 @@ __global__ __launch_bounds__(kApplyBlock) __attribute__((amdgpu_waves_per_eu(3))
         C y[V];
 #pragma unroll
         for (int m = 0; m < V; ++m) y[m] = acc[m][u];
-        st16(op[u] + M::dim(g, 0), Cc::pack(y));
+        st16(out_row(u), Cc::pack(y));
       }
     } else {
 #pragma unroll
@@ -609,12 +660,33 @@ __global__ __launch_bounds__(kApplyBlock) __attribute__((amdgpu_waves_per_eu(3))
           }
           x[m] = y;
         }
-        st16(op[u] + M::dim(g, 0), Cc::pack(x));
+        st16(out_row(u), Cc::pack(x));
       }
     }
 #pragma unroll
     for (int qq = 0; qq < NW; ++qq) mw[qq] = mw_next[qq];
+    if (next.s != s) delta_cur = delta_next;
+    pos = next;
   }
+}
+
+// Register budget: the dense bf16 / hd 128 / rank <= 4 instances fit in 168
+// VGPRs without spilling (3 waves per SIMD, so 3 resident blocks per CU); the
+// other instances keep the compiler's own choice.
+template <typename T, int HD, int MAXR, bool PAGED>
+constexpr bool apply_occ3() {
+  return std::is_same<T, bf16_t>::value && HD == 128 && MAXR <= 4 && !PAGED;
+}
+
+template <typename T, typename C, int HD, int STYLE, int MAXR, bool PAGED>
+__global__ __launch_bounds__(kApplyBlock) __attribute__((amdgpu_waves_per_eu(3)))
+void apply_kernel(ApplyParams P) {
+  apply_body<T, C, HD, STYLE, MAXR, PAGED>(P);
+}
+
+template <typename T, typename C, int HD, int STYLE, int MAXR, bool PAGED>
+__global__ __launch_bounds__(kApplyBlock) void apply_kernel_wide(ApplyParams P) {
+  apply_body<T, C, HD, STYLE, MAXR, PAGED>(P);
 }
 
 // ---------------------------------------------------------------------------
@@ -661,14 +733,21 @@ struct FitLaunch {
 template <typename T, int HD, int STYLE>
 struct ApplyLaunch {
   using C = typename std::conditional<std::is_same<T, float>::value, double, float>::type;
+  template <int R, bool PG>
+  static void launch(const ApplyParams& P, int64_t grid, hipStream_t st) {
+    const dim3 g((unsigned)grid), b(kApplyBlock);
+    if constexpr (apply_occ3<T, HD, R, PG>())
+      apply_kernel<T, C, HD, STYLE, R, PG><<<g, b, 0, st>>>(P);
+    else
+      apply_kernel_wide<T, C, HD, STYLE, R, PG><<<g, b, 0, st>>>(P);
+  }
   template <bool PG>
   static void go(const ApplyParams& P, int rank_var, int64_t grid, hipStream_t st) {
-    const dim3 g((unsigned)grid), b(kApplyBlock);
     switch (rank_var) {
-      case 0: apply_kernel<T, C, HD, STYLE, 0, PG><<<g, b, 0, st>>>(P); break;
-      case 2: apply_kernel<T, C, HD, STYLE, 2, PG><<<g, b, 0, st>>>(P); break;
-      case 4: apply_kernel<T, C, HD, STYLE, 4, PG><<<g, b, 0, st>>>(P); break;
-      default: apply_kernel<T, C, HD, STYLE, 8, PG><<<g, b, 0, st>>>(P); break;
+      case 0: launch<0, PG>(P, grid, st); break;
+      case 2: launch<2, PG>(P, grid, st); break;
+      case 4: launch<4, PG>(P, grid, st); break;
+      default: launch<8, PG>(P, grid, st); break;
     }
   }
   static kvfix_status run(const ApplyParams& P, int rank_var, int64_t grid, hipStream_t st) {
@@ -801,8 +880,12 @@ extern "C" kvfix_status kvfix_apply(const kvfix_plane* reuse, const kvfix_plane*
   P.mask_words = (reuse->n_tokens + 31) / 32;
   const int ch = apply_chunk_rows(reuse->dtype == KVFIX_F32 ? 4 : 8, reuse->head_dim);
   P.cpu = (reuse->n_tokens + ch - 1) / ch;
-  P.n_chunks = units * P.cpu;
-  const int64_t grid = P.n_chunks < kApplyGrid ? P.n_chunks : kApplyGrid;
+  const int64_t n_chunks = units * P.cpu;
+  const int64_t grid = n_chunks < kApplyGrid ? n_chunks : kApplyGrid;
+  P.gk = (int32_t)(grid % P.cpu);
+  P.gh = (int32_t)(grid / P.cpu % P.H);
+  P.gl = (int32_t)(grid / P.cpu / P.H % P.L);
+  P.gs = (int32_t)(grid / P.cpu / P.H / P.L);
   const int style = rope ? rope->style : kStyleNone;
   return dispatch_t_hd_style<ApplyLaunch>(reuse->dtype, reuse->head_dim, style, P,
                                           rank_variant(P.lr.rank), grid, (hipStream_t)stream);

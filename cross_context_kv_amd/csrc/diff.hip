@@ -35,7 +35,7 @@ __global__ void rope_table_kernel(RopeArgs r, int half, int n_segs, double2* tab
   const double d = (double)r.delta[s];
   for (int t = threadIdx.x; t < half; t += blockDim.x) {
     double sv, cv;
-    sincos(d * r.inv_freq[t], &sv, &cv);
+    rope_sincos(d * r.inv_freq[t], &sv, &cv);
     tab[(int64_t)s * half + t] = make_double2(cv, sv);
   }
 }

@@ -61,7 +61,7 @@ __global__ __launch_bounds__(kDraftBlock) void draft_logits_kernel(DraftParams P
   // rotary table for a shift of -delta: cos stays, sin flips sign
   if (tid < HD / 2) {
     double sv, cv;
-    sincos((double)P.rope.delta[s] * P.rope.inv_freq[tid], &sv, &cv);
+    rope_sincos((double)P.rope.delta[s] * P.rope.inv_freq[tid], &sv, &cv);
     tc[tid] = cv;
     ts[tid] = -sv;
   }
