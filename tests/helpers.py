@@ -87,3 +87,53 @@ def correction_case(cfg, device="cpu", style="half"):
         "B_v": None if raw["b_v"] is None else raw["b_v"].cpu().numpy(),
     }
     return case
+
+
+def torch_rotate(x: torch.Tensor, deltas, theta: float, style: str = "half") -> torch.Tensor:
+    """Rotary rotation by deltas[s] positions in fp64 with plain torch ops (test
+    infrastructure for building stored caches on the GPU; the library under
+    test is not involved).  x: [..., S, H, n, hd]; returns float64."""
+    hd = x.shape[-1]
+    dev = x.device
+    i = torch.arange(hd // 2, dtype=torch.float64, device=dev)
+    inv_freq = torch.pow(torch.tensor(theta, dtype=torch.float64, device=dev), -2.0 * i / hd)
+    d = torch.as_tensor(list(deltas), dtype=torch.float64, device=dev)
+    phi = d[:, None] * inv_freq[None, :]                       # [S][hd/2]
+    c = torch.cos(phi)[:, None, None, :]
+    s = torch.sin(phi)[:, None, None, :]
+    x = x.double()
+    if style == "half":
+        a, b = x[..., : hd // 2], x[..., hd // 2:]
+        return torch.cat([a * c - b * s, b * c + a * s], dim=-1)
+    a, b = x[..., 0::2], x[..., 1::2]
+    out = torch.empty_like(x)
+    out[..., 0::2] = a * c - b * s
+    out[..., 1::2] = b * c + a * s
+    return out
+
+
+def correction_case_gpu(cfg, style: str = "half"):
+    """The full-size correction workload drawn on the GPU (same recipe as
+    correction_case, different random numbers); numpy arrays in oracle format.
+    Stored keys are rotated back by -delta with torch_rotate, layer by layer."""
+    from synthetic import draw_correction
+    raw = draw_correction(cfg, "cuda")
+    deltas = [int(d) for d in raw["delta"].tolist()]
+    neg = [-d for d in deltas]
+    xk = raw["x_k"]
+    reuse_k = torch.empty(xk.shape, dtype=cfg.torch_dtype, device=xk.device)
+    for l in range(xk.shape[0]):
+        reuse_k[l] = torch_rotate(xk[l], neg, cfg.theta, style).to(cfg.torch_dtype)
+    case = {
+        "deltas": deltas,
+        "reuse_k": to_np(reuse_k),
+        "reuse_v": to_np(raw["x_v"].to(cfg.torch_dtype)),
+        "fresh_k": to_np(raw["fresh_k"]),
+        "fresh_v": to_np(raw["fresh_v"]),
+    }
+    for p in ("k", "v"):
+        case["A_" + p] = None if raw["a_" + p] is None else raw["a_" + p].cpu().numpy()
+        case["B_" + p] = None if raw["b_" + p] is None else raw["b_" + p].cpu().numpy()
+    del raw, xk, reuse_k
+    torch.cuda.empty_cache()
+    return case
