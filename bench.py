@@ -1,20 +1,30 @@
 #!/usr/bin/env python3
 """Benchmark of the KV-correction hot path on one MI355X.
 
-One step = the whole correction of one Llama-3-8B-shaped segment cache
-(32 layers x 8 KV heads x 4096 tokens x head_dim 128, bf16): L2 scores of K
-and V at check layer 1, top-b selection (b = 615 = ceil(0.15 * 4096)), the
-per-layer probe mean with fresh scatter, and the fused apply (rotary
-re-alignment + clipped-weight mean + rank-4 state) of both planes.  Inputs
-are synthetic, seeded, and resident in HBM before timing starts.
+Default workload (c2): the whole correction of one Llama-3-8B-shaped segment
+cache (32 layers x 8 KV heads x 4096 tokens x head_dim 128, bf16): L2 scores
+of K and V at check layer 1, top-b selection (b = 615 = ceil(0.15 * 4096)),
+the per-layer probe mean with fresh scatter, and the fused apply (rotary
+re-alignment + clipped-weight mean + rank-4 state) of both planes.
 
+Other workloads (--workload), one step each:
+  c3  collective round: 16 agents x 32 layers x 8192 tokens, block-sparse diff
+      encode against the master, then the fused restore of all 16 caches;
+  c4  Qwen2.5-14B-shaped draft repair: 48 layers, 40/8 heads, 32768 tokens,
+      draft attention mass -> top 10 % -> mean fit and apply of K and V;
+  c5  Llama-3-70B-shaped paged batch: 80 layers x 32 segments x 4096 tokens,
+      scores at check layer 1 -> top 10 % -> mean + rank-2 fit and apply, in
+      place through the page tables.
+
+Inputs are synthetic, seeded, and resident in HBM before timing starts.
 Prints one JSON line: corrected-KV GB/s of algorithmic bytes (each reused
 byte read once, each output byte written once, fresh bytes only for probe
-rows, plus states, scores and indices), the apply kernel's roofline from
+rows, plus states, scores and indices), the dominant kernel's roofline from
 events recorded around its launches, and the CPU oracle timed on a bounded
 sample of the same workload.
 
-  python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+  python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload c2]
+                  [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -30,8 +40,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
-COUNTERS = os.path.join(ROOT, "profiles", "apply_c2_counters.json")
-KERNEL_SOURCES = ["cross_context_kv_amd/csrc/correct.hip", "cross_context_kv_amd/csrc/common.h"]
+METRIC = "corrected-KV GB/s (read+write) and % of HBM peak; segment-layers/s at 8B shape"
+KERNEL_SOURCES = ["cross_context_kv_amd/csrc/correct.hip", "cross_context_kv_amd/csrc/common.h",
+                  "cross_context_kv_amd/csrc/diff.hip", "cross_context_kv_amd/csrc/draft.hip",
+                  "cross_context_kv_amd/csrc/score_select.hip"]
 
 
 def kernel_hash() -> str:
@@ -42,148 +54,523 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def alg_bytes(cfg):
-    """Algorithmic bytes of one step, split by kernel."""
-    L, S, H, n, hd, b, r = (cfg.n_layers, cfg.n_segs, cfg.n_kv_heads, cfg.n_tokens,
-                            cfg.head_dim, cfg.b, cfg.rank)
-    row = hd * 2
-    words = (n + 31) // 32
-    score = 2 * (2 * S * H * n * row + S * n * 4)                  # fresh + reuse at the check layer
-    select = 2 * (S * n * 4 + S * b * 4 + S * words * 4)
-    fit = 2 * (L * S * H * b * (3 * row + r * 4) + L * S * H * (r * hd * 4 + hd * 4) + S * b * 4)
-    apply_one = (L * S * H * (n - b) * (2 * row + r * 4) + L * S * H * (r * hd * 4 + hd * 4)
-                 + S * n * 4 + S * words * 4)
-    return {"score": score, "select": select, "fit_mean": fit, "apply": 2 * apply_one,
-            "apply_per_launch": apply_one, "apply_units_per_launch": L * S * H * (n - b),
-            "total": score + select + fit + 2 * apply_one}
+def counters_path(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"{Workload.ALL[workload].kernel_tag}_{workload}_counters.json")
 
 
-def build_inputs(cfg, torch, kv):
-    """Seeded synthetic C2 inputs, generated on the GPU."""
-    from synthetic import draw_correction
-    raw = draw_correction(cfg, "cuda")
-    delta = raw["delta"].to("cuda")
-    t = {"delta": delta}
-    # stored keys: the aligned content rotated back to the old position
-    xk = raw["x_k"].to(torch.bfloat16)
-    reuse_k = torch.empty_like(xk)
-    kv.kvfix_rope_shift(kv.Plane.dense(xk), kv.Plane.dense(reuse_k), -delta, cfg.theta)
-    t["reuse_k"], t["reuse_v"] = reuse_k, raw["x_v"].to(torch.bfloat16)
-    t["fresh_k"], t["fresh_v"] = raw["fresh_k"].contiguous(), raw["fresh_v"].contiguous()
-    t["A_k"], t["B_k"], t["A_v"], t["B_v"] = raw["a_k"], raw["b_k"], raw["a_v"], raw["b_v"]
-    S, n, b, L, H, hd = cfg.n_segs, cfg.n_tokens, cfg.b, cfg.n_layers, cfg.n_kv_heads, cfg.head_dim
-    t["scores"] = torch.empty(2, S, n, dtype=torch.float32, device="cuda")
-    t["idx"] = torch.empty(2, S, b, dtype=torch.int32, device="cuda")
-    t["mask"] = torch.empty(2, S, (n + 31) // 32, dtype=torch.int32, device="cuda")
-    t["mu"] = torch.empty(2, L, S, H, hd, dtype=torch.float32, device="cuda")
-    t["out_k"] = torch.empty_like(reuse_k)
-    t["out_v"] = torch.empty_like(t["reuse_v"])
-    del raw, xk
-    torch.cuda.synchronize()
-    return t
+def read_traffic(workload: str):
+    """HBM bytes per launch of the roofline kernel from the committed counter
+    summary, or None when the kernel sources changed since it was taken."""
+    p = counters_path(workload)
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        c = json.load(f)
+    if c.get("kernel_hash") != kernel_hash():
+        return None
+    return c.get("traffic_bytes_per_launch")
 
 
-def make_step(cfg, t, kv, events=None):
-    P = kv.Plane.dense
-    planes = {p: (P(t["fresh_" + p]), P(t["reuse_" + p]), P(t["out_" + p])) for p in ("k", "v")}
-    S, n, b = cfg.n_segs, cfg.n_tokens, cfg.b
-    c = cfg.check_layer
-    sc2, idx2, mask2 = t["scores"].view(2 * S, n), t["idx"].view(2 * S, b), t["mask"].view(2 * S, -1)
-
-    def step():
-        kv.kvfix_score(planes["k"][0], c, planes["k"][1], c, t["scores"][0], t["delta"], cfg.theta)
-        kv.kvfix_score(planes["v"][0], c, planes["v"][1], c, t["scores"][1])
-        kv.kvfix_select_topb(sc2, b, idx2, mask2)
-        for i, p in enumerate(("k", "v")):
-            fresh, reuse, out = planes[p]
-            d = t["delta"] if p == "k" else None
-            kv.kvfix_fit_mean(fresh, reuse, out, t["idx"][i], b, t["mu"][i], d, cfg.theta,
-                              A=t["A_" + p], B=t["B_" + p])
-        for i, p in enumerate(("k", "v")):
-            fresh, reuse, out = planes[p]
-            d = t["delta"] if p == "k" else None
-            if events is not None:
-                events.append(kv_event_pair_start())
-            kv.kvfix_apply(reuse, out, t["mask"][i], t["mu"][i], t["scores"][i], cfg.w_lo,
-                           cfg.w_hi, d, cfg.theta, A=t["A_" + p], B=t["B_" + p])
-            if events is not None:
-                kv_event_pair_end(events[-1])
-    return step
+def _events(torch):
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
 
-def kv_event_pair_start():
-    import torch
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record()          # torch's current stream: the stream every kvfix call here uses
-    return (s, e)
+class Timed:
+    """Events around the roofline kernel's launches (torch's current stream,
+    the stream every kvfix call here is issued on)."""
+
+    def __init__(self, torch):
+        self.torch, self.pairs, self.on = torch, [], False
+
+    def __enter__(self):
+        if self.on:
+            s, e = _events(self.torch)
+            s.record()
+            self.pairs.append((s, e))
+        return self
+
+    def __exit__(self, *a):
+        if self.on:
+            self.pairs[-1][1].record()
+
+    def avg_ms(self):
+        return sum(s.elapsed_time(e) for s, e in self.pairs) / len(self.pairs)
 
 
-def kv_event_pair_end(pair):
-    pair[1].record()
+def host(t, torch, np):
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+    return t.contiguous().numpy()
 
 
-def cpu_baseline(cfg, t, torch, n_layers_sample=None, repeats=3):
-    """The oracle (as it stands, one thread) on the same input bytes.
-
-    Sample: the whole step (scores, selection, mean fit and apply of K and V)
-    over the first n_layers_sample layers (default: all), repeated `repeats`
-    times; the rate uses the median time."""
-    import numpy as np
+def timed_oracle(fn, repeats):
+    """Median wall time of the oracle on one thread (BLAS pinned to one thread)."""
     try:
         from threadpoolctl import threadpool_limits
     except ImportError:  # pragma: no cover
         threadpool_limits = None
-    from oracle import kvref as K
-    Ls = cfg.n_layers if not n_layers_sample else max(n_layers_sample, cfg.check_layer + 1)
-
-    def host(x):
-        x = x[:Ls].detach().cpu()
-        if x.dtype == torch.bfloat16:
-            return x.contiguous().view(torch.int16).numpy().view(np.uint16)
-        return x.contiguous().numpy()
-
-    data = {k: host(t[k]) for k in ("reuse_k", "reuse_v", "fresh_k", "fresh_v", "A_k", "B_k",
-                                     "A_v", "B_v")}
-    deltas = [int(v) for v in t["delta"].tolist()]
-    sub = cfg.replace(n_layers=Ls)
-
-    def run():
-        c = cfg.check_layer
-        sk = K.score_l2(data["fresh_k"], data["reuse_k"], "bf16", c, deltas, cfg.theta)
-        sv = K.score_l2(data["fresh_v"], data["reuse_v"], "bf16", c)
-        for p, s in (("k", sk), ("v", sv)):
-            idx, mask = K.select_topb(s, cfg.b)
-            K.correct(data["fresh_" + p], data["reuse_" + p], "bf16", idx, mask, s, cfg.w_lo,
-                      cfg.w_hi, data["A_" + p], data["B_" + p],
-                      deltas if p == "k" else None, cfg.theta)
-
     times = []
     for _ in range(repeats):
         t0 = time.perf_counter()
         if threadpool_limits:
             with threadpool_limits(limits=1):
-                run()
+                fn()
         else:
-            run()
+            fn()
         times.append(time.perf_counter() - t0)
-    dt = sorted(times)[len(times) // 2]
-    nbytes = alg_bytes(sub)["total"]
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"the whole step on layers 0..{Ls - 1} of the same input bytes "
-                      f"({Ls} of {cfg.n_layers} layers, {nbytes / 1e6:.1f} MB algorithmic), "
-                      f"median of {repeats} runs of {dt:.1f} s, numpy fp64, one thread"}
+    return sorted(times)[len(times) // 2]
 
 
-def read_traffic(per_launch_units: int):
-    """HBM traffic of the apply kernel from the committed counter summary, or None
-    when the kernel source has changed since the counters were taken."""
-    if not os.path.exists(COUNTERS):
-        return None
-    with open(COUNTERS) as f:
-        c = json.load(f)
-    if c.get("kernel_hash") != kernel_hash():
-        return None
-    return c.get("traffic_bytes_per_launch")
+class Workload:
+    ALL = {}
+    kernel_tag = "apply"
+
+    def __init__(self, cfg, torch, kv):
+        self.cfg, self.torch, self.kv = cfg, torch, kv
+        self.timed = Timed(torch)
+
+
+# ----------------------------------------------------------------------------
+# correction chains: c2 (dense, L2 at a check layer), c5 (paged, in place)
+# ----------------------------------------------------------------------------
+
+
+class Correction(Workload):
+    kernel_tag = "apply"
+    paged = False
+
+    def alg_bytes(self):
+        """Algorithmic bytes of one step, split by kernel."""
+        c = self.cfg
+        L, S, H, n, hd, b, r = (c.n_layers, c.n_segs, c.n_kv_heads, c.n_tokens, c.head_dim,
+                                c.b, c.rank)
+        row = hd * 2
+        words = (n + 31) // 32
+        wbytes = S * n * 4 if c.weight == "clip" else 0
+        score = 2 * (2 * S * H * n * row + S * n * 4)        # fresh + reuse at the check layer
+        select = 2 * (S * n * 4 + S * b * 4 + S * words * 4)
+        state = L * S * H * (r * hd * 4) if r else 0
+        fit = 2 * (L * S * H * b * (3 * row + r * 4) + state + L * S * H * hd * 4 + S * b * 4)
+        apply_one = (L * S * H * (n - b) * (2 * row + r * 4) + state + L * S * H * hd * 4
+                     + wbytes + S * words * 4)
+        return {"score": score, "select": select, "fit_mean": fit, "apply": 2 * apply_one,
+                "roofline_per_launch": apply_one, "roofline_units": L * S * H * (n - b),
+                "total": score + select + fit + 2 * apply_one}
+
+    def step(self):
+        kv, t, c = self.kv, self.t, self.cfg
+        S, n, b, ck = c.n_segs, c.n_tokens, c.b, c.check_layer
+        F, R = self.fresh_check_planes, self.reuse_planes
+        fl = self.fresh_check_layer
+        kv.kvfix_score(F["k"], fl, R["k"], ck, t["scores"][0], t["delta"], c.theta)
+        kv.kvfix_score(F["v"], fl, R["v"], ck, t["scores"][1])
+        kv.kvfix_select_topb(t["scores"].view(2 * S, n), b, t["idx"].view(2 * S, b),
+                             t["mask"].view(2 * S, -1))
+        for i, p in enumerate("kv"):
+            d = t["delta"] if p == "k" else None
+            kv.kvfix_fit_mean(self.fit_fresh_planes[p], R[p], self.out_planes[p], t["idx"][i], b,
+                              t["mu"][i], d, c.theta, A=t["A_" + p], B=t["B_" + p],
+                              fresh_by_slot=self.paged, ws=t["ws_fit"])
+        for i, p in enumerate("kv"):
+            d = t["delta"] if p == "k" else None
+            sc = t["scores"][i] if c.weight == "clip" else None
+            with self.timed:
+                kv.kvfix_apply(R[p], self.out_planes[p], t["mask"][i], t["mu"][i], sc, c.w_lo,
+                               c.w_hi, d, c.theta, A=t["A_" + p], B=t["B_" + p])
+
+
+class C2(Correction):
+    name = "c2"
+
+    def workload_text(self):
+        return ("c2_llama3_8b: one segment, 32 layers x 8 KV heads x 4096 tokens x hd 128 "
+                "bf16; L2 probes at check layer 1, b=615 (r=0.15), w=clip(d,0,2), "
+                "rank-4 state, theta 5e5")
+
+    def build(self):
+        torch, kv, c = self.torch, self.kv, self.cfg
+        from synthetic import draw_correction
+        raw = draw_correction(c, "cuda")
+        delta = raw["delta"].to("cuda")
+        t = {"delta": delta}
+        # stored keys: the aligned content rotated back to the old position
+        xk = raw["x_k"].to(torch.bfloat16)
+        reuse_k = torch.empty_like(xk)
+        kv.kvfix_rope_shift(kv.Plane.dense(xk), kv.Plane.dense(reuse_k), -delta, c.theta)
+        t["reuse_k"], t["reuse_v"] = reuse_k, raw["x_v"].to(torch.bfloat16)
+        t["fresh_k"], t["fresh_v"] = raw["fresh_k"].contiguous(), raw["fresh_v"].contiguous()
+        for p in "kv":
+            t["A_" + p], t["B_" + p] = raw["a_" + p], raw["b_" + p]
+        self._alloc_step_buffers(t)
+        t["out_k"] = torch.empty_like(reuse_k)
+        t["out_v"] = torch.empty_like(t["reuse_v"])
+        del raw, xk
+        P = kv.Plane.dense
+        self.reuse_planes = {p: P(t["reuse_" + p]) for p in "kv"}
+        self.out_planes = {p: P(t["out_" + p]) for p in "kv"}
+        self.fit_fresh_planes = {p: P(t["fresh_" + p]) for p in "kv"}
+        self.fresh_check_planes = self.fit_fresh_planes
+        self.fresh_check_layer = c.check_layer
+        self.t = t
+        torch.cuda.synchronize()
+
+    def _alloc_step_buffers(self, t):
+        torch, kv, c = self.torch, self.kv, self.cfg
+        S, n, b, L, H, hd = c.n_segs, c.n_tokens, c.b, c.n_layers, c.n_kv_heads, c.head_dim
+        t["scores"] = torch.empty(2, S, n, dtype=torch.float32, device="cuda")
+        t["idx"] = torch.empty(2, S, b, dtype=torch.int32, device="cuda")
+        t["mask"] = torch.empty(2, S, (n + 31) // 32, dtype=torch.int32, device="cuda")
+        t["mu"] = torch.empty(2, L, S, H, hd, dtype=torch.float32, device="cuda")
+        ws = kv.kvfix_fit_mean_workspace(L, S, H, hd, b)
+        t["ws_fit"] = torch.empty(max(ws, 16), dtype=torch.uint8, device="cuda")
+
+    def cpu_baseline(self, np):
+        """The oracle (as it stands, one thread) on the same input bytes: the
+        whole step over all 32 layers, median of 3 runs."""
+        torch, c, t = self.torch, self.cfg, self.t
+        from oracle import kvref as K
+        data = {k: host(t[k], torch, np) for k in ("reuse_k", "reuse_v", "fresh_k", "fresh_v",
+                                                   "A_k", "B_k", "A_v", "B_v")}
+        deltas = [int(v) for v in t["delta"].tolist()]
+
+        def run():
+            ck = c.check_layer
+            sk = K.score_l2(data["fresh_k"], data["reuse_k"], "bf16", ck, deltas, c.theta)
+            sv = K.score_l2(data["fresh_v"], data["reuse_v"], "bf16", ck)
+            for p, s in (("k", sk), ("v", sv)):
+                idx, mask = K.select_topb(s, c.b)
+                K.correct(data["fresh_" + p], data["reuse_" + p], "bf16", idx, mask, s, c.w_lo,
+                          c.w_hi, data["A_" + p], data["B_" + p],
+                          deltas if p == "k" else None, c.theta)
+
+        dt = timed_oracle(run, 3)
+        nbytes = self.alg_bytes()["total"]
+        return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "sample": f"the whole step on all {c.n_layers} layers of the same input bytes "
+                          f"({nbytes / 1e6:.1f} MB algorithmic), median of 3 runs of {dt:.1f} s, "
+                          f"numpy fp64, one thread"}
+
+
+class C5(Correction):
+    name = "c5"
+    paged = True
+
+    def workload_text(self):
+        return ("c5_llama3_70b_paged: 32 segments x 80 layers x 8 KV heads x 4096 tokens x hd 128 "
+                "bf16 in a paged pool (page 16, seeded permutation of 8192 pages); L2 probes at "
+                "check layer 1, b=410 (r=0.1), w=1, rank-2 state, in place, theta 5e5")
+
+    def build(self):
+        torch, kv, c = self.torch, self.kv, self.cfg
+        from synthetic import draw_correction, draw_deltas, draw_page_table
+        L, S, H, n, hd, ps, NP, b = (c.n_layers, c.n_segs, c.n_kv_heads, c.n_tokens, c.head_dim,
+                                     c.page_size, c.n_pages, c.b)
+        t = {"delta": draw_deltas(c).to("cuda")}
+        pt = draw_page_table(c, "cuda")
+        t["pt"] = pt
+        neg = -t["delta"]
+        for p in "kv":
+            t["pool_" + p] = torch.empty(L, NP, ps, H, hd, dtype=torch.bfloat16, device="cuda")
+            t["A_" + p] = torch.empty(L, S, H, n, c.rank, dtype=torch.float32, device="cuda")
+            t["B_" + p] = torch.empty(L, S, H, c.rank, hd, dtype=torch.float32, device="cuda")
+            # fresh rows by probe slot, for every layer; filled with each layer's
+            # fresh rows of a fixed seeded slot set (the probe set itself is only
+            # known inside the step; the bytes moved are the same)
+            t["fslot_" + p] = torch.empty(L, S, H, b, hd, dtype=torch.bfloat16, device="cuda")
+        g = torch.Generator(device="cpu")
+        g.manual_seed(c.seed)
+        slots = torch.sort(torch.randperm(n, generator=g)[:b]).values.to("cuda")
+        tmp = torch.empty(1, S, H, n, hd, dtype=torch.bfloat16, device="cuda")
+        for l in range(L):
+            raw = draw_correction(c, "cuda", layers=[l])
+            for p in "kv":
+                x = raw["x_" + p].to(torch.bfloat16)
+                if p == "k":
+                    kv.kvfix_rope_shift(kv.Plane.dense(x), kv.Plane.dense(tmp), neg, c.theta)
+                    x = tmp
+                pool_l = t["pool_" + p][l]
+                pool_l[pt.long()] = x[0].permute(0, 2, 1, 3).reshape(S, pt.shape[1], ps, H, hd)
+                t["A_" + p][l] = raw["a_" + p][0]
+                t["B_" + p][l] = raw["b_" + p][0]
+                t["fslot_" + p][l] = raw["fresh_" + p][0][:, :, slots]
+                if l == c.check_layer:
+                    t["fcheck_" + p] = raw["fresh_" + p].contiguous()
+            del raw
+        del tmp
+        self._alloc_step_buffers(t)
+        P = kv.Plane
+        self.reuse_planes = {p: P.paged(t["pool_" + p], pt, ps, n) for p in "kv"}
+        self.out_planes = self.reuse_planes                       # in place
+        self.fit_fresh_planes = {p: P.dense(t["fslot_" + p]) for p in "kv"}
+        self.fresh_check_planes = {p: P.dense(t["fcheck_" + p]) for p in "kv"}
+        self.fresh_check_layer = 0
+        self.t = t
+        torch.cuda.synchronize()
+
+    _alloc_step_buffers = C2._alloc_step_buffers
+
+    def cpu_baseline(self, np):
+        """The oracle on a bounded sample: scores at the check layer for all 32
+        segments, selection, and fit + apply of K and V on layers 0 and 1."""
+        torch, c, t = self.torch, self.cfg, self.t
+        from oracle import kvref as K
+        L2 = 2
+        S, H, n, hd, ps = c.n_segs, c.n_kv_heads, c.n_tokens, c.head_dim, c.page_size
+        pt = t["pt"].long()
+
+        def logical(pool):
+            return torch.stack([pool[l][pt].reshape(S, n, H, hd).permute(0, 2, 1, 3)
+                                for l in range(L2)])
+
+        data = {}
+        for p in "kv":
+            data["reuse_" + p] = host(logical(t["pool_" + p]), torch, np)
+            data["fslot_" + p] = host(t["fslot_" + p][:L2], torch, np)
+            data["fcheck_" + p] = host(t["fcheck_" + p], torch, np)
+            data["A_" + p] = host(t["A_" + p][:L2], torch, np)
+            data["B_" + p] = host(t["B_" + p][:L2], torch, np)
+        deltas = [int(v) for v in t["delta"].tolist()]
+        ck = c.check_layer
+
+        def run():
+            for p in "kv":
+                d = deltas if p == "k" else None
+                s = K.score_l2(data["fcheck_" + p], data["reuse_" + p][ck:ck + 1], "bf16", 0, d,
+                               c.theta)
+                idx, mask = K.select_topb(s, c.b)
+                K.correct(data["fslot_" + p], data["reuse_" + p], "bf16", idx, mask, None, 0.0,
+                          1.0, data["A_" + p], data["B_" + p], d, c.theta, "half", True)
+
+        dt = timed_oracle(run, 1)
+        sub = c.replace(n_layers=L2)
+        ab = Correction.alg_bytes(type("X", (), {"cfg": sub})())
+        nbytes = ab["total"]
+        return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "sample": f"scores at the check layer, selection, and fit + apply of K and V on "
+                          f"layers 0-1 (2 of {c.n_layers}) for all {S} segments "
+                          f"({nbytes / 1e6:.1f} MB algorithmic), one run of {dt:.1f} s, numpy "
+                          f"fp64, one thread"}
+
+
+# ----------------------------------------------------------------------------
+# c4: draft-selected repair
+# ----------------------------------------------------------------------------
+
+
+class C4(Workload):
+    name = "c4"
+    kernel_tag = "apply"
+
+    def workload_text(self):
+        return ("c4_qwen25_14b_draft: 48 layers x 8 KV heads (40 query heads) x 32768 tokens x "
+                "hd 128 bf16; draft mass of 2 query tokens over layers 1-47, b=3277 (r=0.1) for "
+                "both planes, w=1, no rank state, theta 1e6")
+
+    def alg_bytes(self):
+        c = self.cfg
+        L, S, H, Hq, T, n, hd, b = (c.n_layers, c.n_segs, c.n_kv_heads, c.n_q_heads, c.n_draft,
+                                    c.n_tokens, c.head_dim, c.b)
+        row = hd * 2
+        words = (n + 31) // 32
+        draft = (L - c.first_layer) * S * H * n * row + L * Hq * T * row * S + S * n * 4
+        select = S * n * 4 + S * b * 4 + S * words * 4
+        fit = 2 * (L * S * H * b * 3 * row + L * S * H * hd * 4 + S * b * 4)
+        apply_one = L * S * H * (n - b) * 2 * row + L * S * H * hd * 4 + S * words * 4
+        return {"draft": draft, "select": select, "fit_mean": fit, "apply": 2 * apply_one,
+                "roofline_per_launch": apply_one, "roofline_units": L * S * H * (n - b),
+                "total": draft + select + fit + 2 * apply_one}
+
+    def build(self):
+        torch, kv, c = self.torch, self.kv, self.cfg
+        from synthetic import draw_correction, draw_deltas, draw_draft_queries
+        L, S, H, Hq, T, n, hd, b = (c.n_layers, c.n_segs, c.n_kv_heads, c.n_q_heads, c.n_draft,
+                                    c.n_tokens, c.head_dim, c.b)
+        t = {"delta": draw_deltas(c).to("cuda")}
+        for p in "kv":
+            t["reuse_" + p] = torch.empty(L, S, H, n, hd, dtype=torch.bfloat16, device="cuda")
+            t["fresh_" + p] = torch.empty(L, S, H, n, hd, dtype=torch.bfloat16, device="cuda")
+            t["out_" + p] = torch.empty(L, S, H, n, hd, dtype=torch.bfloat16, device="cuda")
+        for l in range(L):
+            raw = draw_correction(c, "cuda", layers=[l])
+            xk = raw["x_k"].to(torch.bfloat16)
+            kv.kvfix_rope_shift(kv.Plane.dense(xk), kv.Plane.dense(t["reuse_k"][l:l + 1]),
+                                -t["delta"], c.theta)
+            t["reuse_v"][l] = raw["x_v"][0].to(torch.bfloat16)
+            t["fresh_k"][l], t["fresh_v"][l] = raw["fresh_k"][0], raw["fresh_v"][0]
+            del raw, xk
+        t["q"] = draw_draft_queries(c, "cuda")[None].contiguous()
+        t["ws_draft"] = torch.empty(kv.kvfix_score_draft_workspace(S, L, c.first_layer, Hq, T, n)
+                                    // 4 + 64, dtype=torch.float32, device="cuda")
+        t["scores"] = torch.empty(S, n, dtype=torch.float32, device="cuda")
+        t["idx"] = torch.empty(S, b, dtype=torch.int32, device="cuda")
+        t["mask"] = torch.empty(S, (n + 31) // 32, dtype=torch.int32, device="cuda")
+        t["mu"] = torch.empty(2, L, S, H, hd, dtype=torch.float32, device="cuda")
+        t["ws_fit"] = torch.empty(kv.kvfix_fit_mean_workspace(L, S, H, hd, b), dtype=torch.uint8,
+                                  device="cuda")
+        P = kv.Plane.dense
+        self.planes = {k: P(t[k]) for k in ("reuse_k", "reuse_v", "fresh_k", "fresh_v", "out_k",
+                                            "out_v")}
+        self.t = t
+        torch.cuda.synchronize()
+
+    def step(self):
+        kv, t, c, P = self.kv, self.t, self.cfg, self.planes
+        kv.kvfix_score_draft(t["q"], P["reuse_k"], c.first_layer, t["delta"], c.theta,
+                             t["scores"], t["ws_draft"])
+        kv.kvfix_select_topb(t["scores"], c.b, t["idx"], t["mask"])
+        for i, p in enumerate("kv"):
+            d = t["delta"] if p == "k" else None
+            kv.kvfix_fit_mean(P["fresh_" + p], P["reuse_" + p], P["out_" + p], t["idx"], c.b,
+                              t["mu"][i], d, c.theta, ws=t["ws_fit"])
+        for i, p in enumerate("kv"):
+            d = t["delta"] if p == "k" else None
+            with self.timed:
+                kv.kvfix_apply(P["reuse_" + p], P["out_" + p], t["mask"], t["mu"][i], None, 0.0,
+                               1.0, d, c.theta)
+
+    def cpu_baseline(self, np):
+        """The oracle on a bounded sample: the draft mass over layers 1-3,
+        selection, and fit + apply of K and V on layers 0-3."""
+        torch, c, t = self.torch, self.cfg, self.t
+        from oracle import kvref as K
+        L4 = 4
+        data = {k: host(t[k][:L4], torch, np) for k in ("reuse_k", "reuse_v", "fresh_k",
+                                                       "fresh_v")}
+        q = host(t["q"][0, :L4], torch, np)
+        deltas = [int(v) for v in t["delta"].tolist()]
+
+        def run():
+            s = K.score_draft(q, data["reuse_k"], deltas, c.theta, c.first_layer)
+            idx, mask = K.select_topb(s, c.b)
+            for p in "kv":
+                K.correct(data["fresh_" + p], data["reuse_" + p], "bf16", idx, mask, None, 0.0,
+                          1.0, None, None, deltas if p == "k" else None, c.theta)
+
+        dt = timed_oracle(run, 1)
+        nbytes = C4.alg_bytes(type("X", (), {"cfg": c.replace(n_layers=L4)})())["total"]
+        return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "sample": f"the whole step on layers 0-3 (4 of {c.n_layers}; draft mass over "
+                          f"layers 1-3) of the same input bytes ({nbytes / 1e6:.1f} MB "
+                          f"algorithmic), one run of {dt:.1f} s, numpy fp64, one thread"}
+
+
+# ----------------------------------------------------------------------------
+# c3: collective round (diff encode + fused restore)
+# ----------------------------------------------------------------------------
+
+
+class C3(Workload):
+    name = "c3"
+    kernel_tag = "diff_decode"
+
+    def workload_text(self):
+        return ("c3_collective: 16 agents x 32 layers x 8 KV heads x 8192 tokens x hd 128 bf16 at "
+                "distinct offsets in [0,16384]; 16-token blocks, 3-9 % planted, eps 0.0625; "
+                "diff encode against the master, then restore of all 16 caches, theta 5e5")
+
+    def alg_bytes(self, total_blocks=None):
+        c = self.cfg
+        L, A, H, n, hd, bt = (c.n_layers, c.n_segs, c.n_kv_heads, c.n_tokens, c.head_dim,
+                              c.block_tokens)
+        nb = -(-n // bt)
+        plane = L * H * n * hd * 2
+        blk = H * bt * hd * 2
+        tot = self.total if total_blocks is None else total_blocks
+        meta = A * L * (-(-nb // 32)) * 4 + (A * L + 1) * 8 + tot * 4
+        encode = 2 * A * plane + 2 * plane + 2 * tot * blk + meta
+        decode = 2 * plane + 2 * tot * blk + meta + 2 * A * plane
+        return {"encode": encode, "decode": decode, "roofline_per_launch": decode,
+                "roofline_units": A * L * H * n, "total": encode + decode}
+
+    def build(self):
+        torch, kv, c = self.torch, self.kv, self.cfg
+        from synthetic import draw_collective
+        L, A, H, n, hd, bt = (c.n_layers, c.n_segs, c.n_kv_heads, c.n_tokens, c.head_dim,
+                              c.block_tokens)
+        t = {}
+        for p in "kv":
+            t["m_" + p] = torch.empty(L, 1, H, n, hd, dtype=torch.bfloat16, device="cuda")
+            t["s_" + p] = torch.empty(L, A, H, n, hd, dtype=torch.bfloat16, device="cuda")
+            t["o_" + p] = torch.empty(L, A, H, n, hd, dtype=torch.bfloat16, device="cuda")
+        planted = offs = None
+        for l in range(L):
+            raw = draw_collective(c, "cuda", layers=[l])
+            planted, offs = raw["planted"], raw["offsets"].to("cuda")
+            t["m_k"][l], t["m_v"][l] = raw["master_k"][0], raw["master_v"][0]
+            kv.kvfix_rope_shift(kv.Plane.dense(raw["y_k"]), kv.Plane.dense(t["s_k"][l:l + 1]),
+                                offs, c.theta)
+            t["s_v"][l] = raw["y_v"][0]
+            del raw
+        t["to_m"], t["from_m"] = -offs, offs
+        self.total = int(planted.sum()) * L
+        self.diff = kv.Diff(A, L, n, H, hd, bt, self.total + 64, dtype=torch.bfloat16)
+        t["status"] = torch.zeros(1, dtype=torch.int32, device="cuda")
+        t["ws_e"] = torch.empty(kv.kvfix_diff_encode_workspace(A, L, n, bt) + 256,
+                                dtype=torch.uint8, device="cuda")
+        t["ws_d"] = torch.empty(kv.kvfix_diff_decode_workspace(A, hd) + 256, dtype=torch.uint8,
+                                device="cuda")
+        P = kv.Plane.dense
+        self.planes = {k: P(t[k]) for k in ("m_k", "m_v", "s_k", "s_v", "o_k", "o_v")}
+        self.t = t
+        torch.cuda.synchronize()
+
+    def step(self):
+        kv, t, c, P = self.kv, self.t, self.cfg, self.planes
+        kv.kvfix_diff_encode(P["m_k"], P["m_v"], P["s_k"], P["s_v"], t["to_m"], c.theta, c.eps,
+                             self.diff, t["status"], t["ws_e"])
+        with self.timed:
+            kv.kvfix_diff_decode(P["m_k"], P["m_v"], self.diff, t["from_m"], c.theta, P["o_k"],
+                                 P["o_v"], t["ws_d"])
+
+    def cpu_baseline(self, np):
+        """The oracle on a bounded sample: encode and restore of layer 0 for all
+        16 agents."""
+        torch, c, t = self.torch, self.cfg, self.t
+        from oracle import kvref as K
+        d = {k: host(t[k][:1], torch, np) for k in ("m_k", "m_v", "s_k", "s_v")}
+        offs = [int(v) for v in t["from_m"].tolist()]
+        box = {}
+
+        def run():
+            o = K.diff_encode(d["m_k"], d["m_v"], d["s_k"], d["s_v"], [-x for x in offs],
+                              c.theta, c.eps, c.block_tokens)
+            K.diff_decode(d["m_k"], d["m_v"], o, offs, c.theta, c.n_segs, c.block_tokens)
+            box["total"] = o["total"]
+
+        dt = timed_oracle(run, 1)
+        sub = C3.alg_bytes(type("X", (), {"cfg": c.replace(n_layers=1), "total": box["total"]})())
+        nbytes = sub["total"]
+        return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "sample": f"encode + restore of layer 0 (1 of {c.n_layers}) for all {c.n_segs} "
+                          f"agents ({nbytes / 1e6:.1f} MB algorithmic), one run of {dt:.1f} s, "
+                          f"numpy fp64, one thread"}
+
+
+Workload.ALL = {"c2": C2, "c3": C3, "c4": C4, "c5": C5}
+
+ROOFLINE_KERNEL = {
+    "c2": "kvfix apply_kernel<bf16, fp32, hd128, rotate-half, rank 4>",
+    "c3": "kvfix diff_decode_kernel<bf16, hd128, rotate-half> (with its rotary-table pre-kernel)",
+    "c4": "kvfix apply_kernel<bf16, fp32, hd128, rotate-half, rank 0>",
+    "c5": "kvfix apply_kernel_wide<bf16, fp32, hd128, rotate-half, rank 2, paged>",
+}
+
+
+def copy_ceiling(torch):
+    """Measured copy ceiling: a plain device-to-device bf16 copy of 512 MiB."""
+    n_copy = 256 << 20
+    src = torch.empty(n_copy, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    c0, c1 = _events(torch)
+    torch.cuda.synchronize()
+    c0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    c1.record()
+    torch.cuda.synchronize()
+    return 2 * src.numel() * 2 / (c0.elapsed_time(c1) / 5 * 1e-3) / 1e9
 
 
 def main():
@@ -191,8 +578,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c2", choices=sorted(Workload.ALL))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-layers", type=int, default=0, help="oracle sample layers (0 = all)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
@@ -200,51 +587,35 @@ def main():
               "see DESIGN.md for the multi-GPU design)", file=sys.stderr)
         sys.exit(2)
 
+    import numpy as np
     import torch
     import cross_context_kv_amd.kvfix as kv
     from synthetic import CONFIGS
     kv.lib()                          # fails loudly without the built library
-    cfg = CONFIGS["c2"]
-    t = build_inputs(cfg, torch, kv)
-    step = make_step(cfg, t, kv)
+    w = Workload.ALL[args.workload](CONFIGS[args.workload], torch, kv)
+    w.build()
     for _ in range(args.warmup):
-        step()
+        w.step()
     torch.cuda.synchronize()
 
-    events = []
-    timed = make_step(cfg, t, kv, events)
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w.timed.on = True
+    start, end = _events(torch)
     torch.cuda.synchronize()
     start.record()
     for _ in range(args.steps):
-        timed()
+        w.step()
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
-    apply_ms = sum(s.elapsed_time(e) for s, e in events) / len(events)
+    roof_ms = w.timed.avg_ms()
+    copy_gbs = copy_ceiling(torch)
 
-    # Measured copy ceiling: a plain device-to-device copy of a known size
-    # (also the calibration kernel for the HBM byte counters).
-    n_copy = 256 << 20
-    src_c = torch.empty(n_copy, dtype=torch.bfloat16, device="cuda").fill_(1.0)
-    dst_c = torch.empty_like(src_c)
-    dst_c.copy_(src_c)
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    c0.record()
-    for _ in range(5):
-        dst_c.copy_(src_c)
-    c1.record()
-    torch.cuda.synchronize()
-    copy_gbs = 2 * src_c.numel() * 2 / (c0.elapsed_time(c1) / 5 * 1e-3) / 1e9
-    del src_c, dst_c
-
-    ab = alg_bytes(cfg)
+    ab = w.alg_bytes()
     gbs = ab["total"] / (ms * 1e-3) / 1e9
-    apply_gbs = ab["apply_per_launch"] / (apply_ms * 1e-3) / 1e9
-    traffic = read_traffic(ab["apply_units_per_launch"])
+    roof_gbs = ab["roofline_per_launch"] / (roof_ms * 1e-3) / 1e9
+    c = w.cfg
     line = {
-        "metric": "corrected-KV GB/s (read+write) and % of HBM peak; segment-layers/s at 8B shape",
+        "metric": METRIC,
         "value": round(gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -257,30 +628,28 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "c2_llama3_8b: one segment, 32 layers x 8 KV heads x 4096 tokens x hd 128 "
-                        "bf16; L2 probes at check layer 1, b=615 (r=0.15), w=clip(d,0,2), "
-                        "rank-4 state, theta 5e5",
+            "workload": w.workload_text(),
             "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-            "segment_layers_per_s": round(cfg.n_segs * cfg.n_layers / (ms * 1e-3), 1),
+            "segment_layers_per_s": round(c.n_segs * c.n_layers / (ms * 1e-3), 1),
             "alg_bytes_per_step": ab["total"],
             "copy_ceiling_GBs": round(copy_gbs, 1),
             "pct_copy_ceiling": round(100 * gbs / copy_gbs, 2),
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "kvfix apply_kernel<bf16, fp32, hd128, rotate-half, rank 4>",
-            "achieved": round(apply_gbs, 2),
+            "kernel": ROOFLINE_KERNEL[args.workload],
+            "achieved": round(roof_gbs, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(apply_gbs / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
-            "alg_bytes_per_launch": ab["apply_per_launch"],
-            "avg_launch_ms": round(apply_ms, 5),
+            "frac": round(roof_gbs / HBM_PEAK_GBS, 4),
+            "traffic": read_traffic(args.workload),
+            "alg_bytes_per_launch": ab["roofline_per_launch"],
+            "avg_launch_ms": round(roof_ms, 5),
         },
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(cfg, t, torch, args.cpu_layers)
+        line["cpu_baseline"] = w.cpu_baseline(np)
     print(json.dumps(line), flush=True)
 
 
