@@ -324,7 +324,6 @@ __global__ void fit_finish_kernel(FitFinishParams F) {
 constexpr int kApplyBlock = 256;
 constexpr int kApplyWaves = kApplyBlock / kWave;
 constexpr int kApplyU = 4;
-constexpr int64_t kApplyGrid = 768;
 
 // Rows per chunk for storage type T and head_dim HD (host and device).
 __host__ __device__ constexpr int apply_chunk_rows(int vec, int hd) {
@@ -340,8 +339,13 @@ struct ApplyParams {
   DLowRank lr;
   RopeArgs rope;
   int32_t S, L, H, n, cpu, mask_words;
-  // chunk c = ((s L + l) H + h) cpu + k; the grid stride in the same digits
-  int32_t gk, gh, gl, gs;
+  // Chunk order: c = ((s L + l) X + x) Y + y, where (x, y) = (head, chunk
+  // of tokens) or, when a head's rows are farther apart than a token's
+  // (paged pools, token-major layouts), (chunk of tokens, head), so that the
+  // chunks in flight together cover neighbouring bytes.  g0..g3: the grid
+  // stride in the same digits (innermost first).
+  int32_t h_inner;
+  int32_t g0, g1, g2, g3;
   int32_t a_vec;               // A rows may be read as whole 16-byte vectors
   int32_t b_vec;               // B rows may be read as whole 16-byte vectors
 };
@@ -399,12 +403,10 @@ __device__ __forceinline__ void apply_body(const ApplyParams& P) {
   static_assert(!kMfma || (V == 8 && G == 16 && RPW == 4 && U == 4), "MFMA tile shape");
   constexpr int NW = CH >= 32 ? CH / 32 : 1;        // probe-bit words per chunk
   static_assert(CH % 32 == 0 || 32 % CH == 0, "chunks start on a word or inside one");
-  constexpr int kPages = CH + 2;
 
   __shared__ C tab_c[2][HD / 2], tab_s[2][HD / 2];
   __shared__ __attribute__((aligned(16))) float sa[2][MAXR > 0 ? CH * RS : 1];
   __shared__ float sw[2][CH];
-  __shared__ int32_t spin[2][PAGED ? kPages : 1], spout[2][PAGED ? kPages : 1];
 
   const int t = threadIdx.x;
   const int lane = t & (kWave - 1), wave = t / kWave;
@@ -418,14 +420,18 @@ __device__ __forceinline__ void apply_body(const ApplyParams& P) {
   // Chunk coordinates (block-uniform).  The block advances by the grid
   // stride, added digit by digit with carries: no division in the loop.
   struct Pos { int k, h, l, s; };
+  const int r0 = P.h_inner ? P.H : P.cpu, r1 = P.h_inner ? P.cpu : P.H;
   auto advance = [&](Pos p) {
-    p.k += P.gk;
-    int cy = p.k >= P.cpu; if (cy) p.k -= P.cpu;
-    p.h += P.gh + cy;
-    cy = p.h >= P.H; if (cy) p.h -= P.H;
-    p.l += P.gl + cy;
+    int d0 = P.h_inner ? p.h : p.k, d1 = P.h_inner ? p.k : p.h;
+    d0 += P.g0;
+    int cy = d0 >= r0; if (cy) d0 -= r0;
+    d1 += P.g1 + cy;
+    cy = d1 >= r1; if (cy) d1 -= r1;
+    p.l += P.g2 + cy;
     cy = p.l >= P.L; if (cy) p.l -= P.L;
-    p.s += P.gs + cy;
+    p.s += P.g3 + cy;
+    p.h = P.h_inner ? d0 : d1;
+    p.k = P.h_inner ? d1 : d0;
     return p;
   };
   // Probe bits of a chunk: NW words, uniform over the block (scalar loads),
@@ -442,13 +448,28 @@ __device__ __forceinline__ void apply_body(const ApplyParams& P) {
   Pos pos;
   {
     unsigned q = blockIdx.x;
-    pos.k = (int)(q % (unsigned)P.cpu); q /= (unsigned)P.cpu;
-    pos.h = (int)(q % (unsigned)P.H); q /= (unsigned)P.H;
+    const int d0 = (int)(q % (unsigned)r0); q /= (unsigned)r0;
+    const int d1 = (int)(q % (unsigned)r1); q /= (unsigned)r1;
     pos.l = (int)(q % (unsigned)P.L);
     pos.s = (int)(q / (unsigned)P.L);
+    pos.h = P.h_inner ? d0 : d1;
+    pos.k = P.h_inner ? d1 : d0;
   }
   uint32_t mw[NW];
   chunk_words(pos, mw);
+  // Page ids of this lane's rows of a chunk (paged planes), also fetched one
+  // chunk ahead, so a paged chunk issues its row loads as early as a dense one.
+  auto chunk_pages = [&](Pos p, int32_t* pi, int32_t* po) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = p.k * CH + i_first + u * kStep;
+      const bool ok = p.s < P.S && j < P.n;
+      pi[u] = ok ? page_of(P.in, p.s, j) : 0;
+      po[u] = ok ? page_of(P.out, p.s, j) : 0;
+    }
+  };
+  int32_t pgi[PAGED ? U : 1], pgo[PAGED ? U : 1];
+  if constexpr (PAGED) chunk_pages(pos, pgi, pgo);
   // rotary frequency of table entry t (parked in LDS: written and read by
   // thread t only), and the current segment's shift
   __shared__ double sfreq[STYLE != kStyleNone ? HD / 2 : 1];
@@ -503,11 +524,24 @@ __device__ __forceinline__ void apply_body(const ApplyParams& P) {
     T* op0 = reinterpret_cast<T*>(P.out.data) + (int64_t)l * P.out.s_layer +
              (int64_t)s * P.out.s_seg + (int64_t)h * P.out.s_head + jf * P.out.s_token +
              M::dim(g, 0);
+    int64_t po[PAGED ? U : 1];            // paged: output row offsets
     if constexpr (!PAGED) {
 #pragma unroll
       for (int u = 0; u < U; ++u)
         r0[u] = ld16(live[u] ? ip0 + u * in_step : reinterpret_cast<const T*>(P.in.data));
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = j_begin + i_first + u * kStep;
+        const int64_t io = live[u] ? row_offset_page(P.in, l, s, h, j, pgi[u]) : -1;
+        const int64_t oo = live[u] ? row_offset_page(P.out, l, s, h, j, pgo[u]) : -1;
+        live[u] = live[u] && io >= 0 && oo >= 0;          // a bad page id skips the row
+        r0[u] = ld16(reinterpret_cast<const T*>(P.in.data) + (live[u] ? io + M::dim(g, 0) : 0));
+        po[u] = oo + M::dim(g, 0);
+      }
     }
+    int32_t pgi_next[PAGED ? U : 1], pgo_next[PAGED ? U : 1];
+    if constexpr (PAGED) chunk_pages(next, pgi_next, pgo_next);
 
     // Set-up loads: this thread's chunk row (weight, rank-state row) and the
     // lane's per-unit mean and B values.
@@ -557,11 +591,6 @@ __device__ __forceinline__ void apply_body(const ApplyParams& P) {
         for (int kk = 0; kk < RS; ++kk) sa[buf][t * RS + kk] = kk < MAXR ? arow[kk] : 0.0f;
       }
     }
-    int pin0 = 0, pout0 = 0;
-    if constexpr (PAGED) {
-      pin0 = stage_pages(P.in, s, j_begin, j_end, spin[buf]);
-      pout0 = stage_pages(P.out, s, j_begin, j_end, spout[buf]);
-    }
     __syncthreads();
     if (new_seg) cur_s = s;
     // This lane's cos / signed sin (read from the block's table for the
@@ -577,18 +606,6 @@ __device__ __forceinline__ void apply_body(const ApplyParams& P) {
     }
 
     // Output row of batch row u (dense: op0 + u out_step; paged: looked up).
-    int64_t po[PAGED ? U : 1];
-    if constexpr (PAGED) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int j = j_begin + i_first + u * kStep;
-        const int64_t io = live[u] ? row_offset_staged(P.in, l, s, h, j, spin[buf], pin0) : -1;
-        const int64_t oo = live[u] ? row_offset_staged(P.out, l, s, h, j, spout[buf], pout0) : -1;
-        live[u] = live[u] && io >= 0 && oo >= 0;
-        r0[u] = ld16(reinterpret_cast<const T*>(P.in.data) + (live[u] ? io + M::dim(g, 0) : 0));
-        po[u] = oo + M::dim(g, 0);
-      }
-    }
     auto out_row = [&](int u) -> T* {
       if constexpr (PAGED) return reinterpret_cast<T*>(P.out.data) + po[u];
       else return op0 + u * out_step;
@@ -665,17 +682,21 @@ __device__ __forceinline__ void apply_body(const ApplyParams& P) {
     }
 #pragma unroll
     for (int qq = 0; qq < NW; ++qq) mw[qq] = mw_next[qq];
+    if constexpr (PAGED) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) { pgi[u] = pgi_next[u]; pgo[u] = pgo_next[u]; }
+    }
     if (next.s != s) delta_cur = delta_next;
     pos = next;
   }
 }
 
-// Register budget: the dense bf16 / hd 128 / rank <= 4 instances fit in 168
-// VGPRs without spilling (3 waves per SIMD, so 3 resident blocks per CU); the
-// other instances keep the compiler's own choice.
+// Register budget: the bf16 / hd 128 / rank <= 4 instances fit in 168 VGPRs
+// without spilling (3 waves per SIMD, so 3 resident blocks per CU); the other
+// instances keep the compiler's own choice.
 template <typename T, int HD, int MAXR, bool PAGED>
 constexpr bool apply_occ3() {
-  return std::is_same<T, bf16_t>::value && HD == 128 && MAXR <= 4 && !PAGED;
+  return std::is_same<T, bf16_t>::value && HD == 128 && MAXR <= 4;
 }
 
 template <typename T, typename C, int HD, int STYLE, int MAXR, bool PAGED>
@@ -733,13 +754,28 @@ struct FitLaunch {
 template <typename T, int HD, int STYLE>
 struct ApplyLaunch {
   using C = typename std::conditional<std::is_same<T, float>::value, double, float>::type;
+  // The blocks are persistent: the grid is what the chip holds at once
+  // (resident blocks per CU of this instance x CUs), or fewer when there
+  // are fewer chunks, so no block waits for another to finish.
   template <int R, bool PG>
-  static void launch(const ApplyParams& P, int64_t grid, hipStream_t st) {
-    const dim3 g((unsigned)grid), b(kApplyBlock);
-    if constexpr (apply_occ3<T, HD, R, PG>())
-      apply_kernel<T, C, HD, STYLE, R, PG><<<g, b, 0, st>>>(P);
-    else
-      apply_kernel_wide<T, C, HD, STYLE, R, PG><<<g, b, 0, st>>>(P);
+  static void launch(ApplyParams P, int64_t n_chunks, hipStream_t st) {
+    auto kern = apply_occ3<T, HD, R, PG>() ? apply_kernel<T, C, HD, STYLE, R, PG>
+                                           : apply_kernel_wide<T, C, HD, STYLE, R, PG>;
+    static const int per_cu = [&] {
+      int nb = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, kApplyBlock, 0) != hipSuccess ||
+          nb < 1)
+        nb = 1;
+      return nb;
+    }();
+    const int64_t resident = (int64_t)per_cu * device_cus();
+    const int64_t grid = n_chunks < resident ? n_chunks : resident;
+    const int64_t r0 = P.h_inner ? P.H : P.cpu, r1 = P.h_inner ? P.cpu : P.H;
+    P.g0 = (int32_t)(grid % r0);
+    P.g1 = (int32_t)(grid / r0 % r1);
+    P.g2 = (int32_t)(grid / r0 / r1 % P.L);
+    P.g3 = (int32_t)(grid / r0 / r1 / P.L);
+    kern<<<dim3((unsigned)grid), dim3(kApplyBlock), 0, st>>>(P);
   }
   template <bool PG>
   static void go(const ApplyParams& P, int rank_var, int64_t grid, hipStream_t st) {
@@ -881,11 +917,10 @@ extern "C" kvfix_status kvfix_apply(const kvfix_plane* reuse, const kvfix_plane*
   const int ch = apply_chunk_rows(reuse->dtype == KVFIX_F32 ? 4 : 8, reuse->head_dim);
   P.cpu = (reuse->n_tokens + ch - 1) / ch;
   const int64_t n_chunks = units * P.cpu;
-  const int64_t grid = n_chunks < kApplyGrid ? n_chunks : kApplyGrid;
-  P.gk = (int32_t)(grid % P.cpu);
-  P.gh = (int32_t)(grid / P.cpu % P.H);
-  P.gl = (int32_t)(grid / P.cpu / P.H % P.L);
-  P.gs = (int32_t)(grid / P.cpu / P.H / P.L);
+  // heads innermost when a token's heads sit closer together than a head's
+  // tokens (a paged pool, a token-major layout)
+  P.h_inner = reuse->s_head < reuse->s_token;
+  const int64_t grid = n_chunks;        // capped at the resident blocks by the launcher
   const int style = rope ? rope->style : kStyleNone;
   return dispatch_t_hd_style<ApplyLaunch>(reuse->dtype, reuse->head_dim, style, P,
                                           rank_variant(P.lr.rank), grid, (hipStream_t)stream);

@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "common.h"
 
 namespace kvfix {
@@ -111,5 +113,22 @@ inline DLowRank make_dlowrank(const kvfix_lowrank* lr) {
 inline int rank_variant(int r) { return r == 0 ? 0 : r <= 2 ? 2 : r <= 4 ? 4 : 8; }
 
 constexpr int64_t kMaxGrid = 0x7fffffffLL;
+
+// Compute units of the current device, cached per device id.
+inline int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    cus = 256;
+  if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
 
 }  // namespace kvfix
