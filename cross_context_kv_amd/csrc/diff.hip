@@ -57,50 +57,89 @@ __device__ __forceinline__ void load_table(const double2* tab, int seg, int g, d
   }
 }
 
+// Agents handled per pass over a block's master rows: their rotary tables
+// sit in LDS, and the master rows are read from HBM once per pass.
+constexpr int kAgentGroup = 16;
+
+// Copy the tables of agents [a0, a0 + na) into LDS (whole block).
+template <int HD>
+__device__ __forceinline__ void stage_tables(const double2* tab, int a0, int na,
+                                             double2 (*stab)[HD / 2]) {
+  for (int i = threadIdx.x; i < na * (HD / 2); i += blockDim.x)
+    stab[i / (HD / 2)][i % (HD / 2)] = tab[(int64_t)(a0 + i / (HD / 2)) * (HD / 2) + i % (HD / 2)];
+}
+
+template <int V>
+__device__ __forceinline__ void lds_table(const double2* row, int g, double* cs, double* sn) {
+#pragma unroll
+  for (int m = 0; m < V; ++m) {
+    const double2 e = row[g * V + m];
+    cs[m] = e.x;
+    sn[m] = e.y;
+  }
+}
+
 template <typename T, int HD, int STYLE>
 __global__ __launch_bounds__(kDiffBlock) void diff_flag_kernel(DiffShape D, const double2* tab,
                                                                uint8_t* flags) {
   using M = RowMap<T, HD, STYLE>;
   using Cd = Codec<T, double>;
   constexpr int V = M::V, G = M::G, RPB = kDiffBlock / G;
+  __shared__ double2 stab[kAgentGroup][HD / 2];
+  __shared__ uint32_t sover;
   const int g = threadIdx.x % G, rr = threadIdx.x / G;
   const int beta = blockIdx.x % D.nb;
   const int l = blockIdx.x / D.nb;
   const int t0 = beta * D.bt;
   const int tb = min(D.bt, D.n - t0);           // valid tokens of this block
   const int rows = D.H * tb;
-  for (int a = 0; a < D.A; ++a) {
-    double cs[V], sn[V];
-    load_table<HD, V>(tab, a, g, cs, sn);
-    int over = 0;
+  const double eps = (double)D.eps;
+  for (int a0 = 0; a0 < D.A; a0 += kAgentGroup) {
+    const int na = min(kAgentGroup, D.A - a0);
+    __syncthreads();                            // the previous group is done with stab, sover
+    stage_tables<HD>(tab, a0, na, stab);
+    if (threadIdx.x == 0) sover = 0;
+    __syncthreads();
+    uint32_t over = 0;                          // bit a: agent a0 + a differs on my rows
     for (int r = rr; r < rows; r += RPB) {
       const int h = r / tb, t = t0 + r % tb;
-      const T* mk = reinterpret_cast<const T*>(D.mk.data) + row_offset(D.mk, l, 0, h, t);
-      const T* mv = reinterpret_cast<const T*>(D.mv.data) + row_offset(D.mv, l, 0, h, t);
-      const T* sk = reinterpret_cast<const T*>(D.sk.data) + row_offset(D.sk, l, a, h, t);
-      const T* sv = reinterpret_cast<const T*>(D.sv.data) + row_offset(D.sv, l, a, h, t);
-      double p0[V], p1[V], xa[V], xb[V], ma[V], mb[V];
-      Cd::unpack(ld16(sk + M::off0(g)), p0);
-      Cd::unpack(ld16(sk + M::off1(g)), p1);
-      parts_to_pairs<STYLE, V>(p0, p1, xa, xb);
-      rotate_pairs<V>(xa, xb, cs, sn);
-      Cd::unpack(ld16_cached(mk + M::off0(g)), p0);
-      Cd::unpack(ld16_cached(mk + M::off1(g)), p1);
-      parts_to_pairs<STYLE, V>(p0, p1, ma, mb);
+      // the master row, once per group of agents
+      const T* mkp = reinterpret_cast<const T*>(D.mk.data) + row_offset(D.mk, l, 0, h, t);
+      const T* mvp = reinterpret_cast<const T*>(D.mv.data) + row_offset(D.mv, l, 0, h, t);
+      const vu4 mk0 = ld16(mkp + M::off0(g)), mk1 = ld16(mkp + M::off1(g));
+      const vu4 mv0 = ld16(mvp + M::off0(g)), mv1 = ld16(mvp + M::off1(g));
+      for (int a = 0; a < na; ++a) {
+        const T* sk = reinterpret_cast<const T*>(D.sk.data) + row_offset(D.sk, l, a0 + a, h, t);
+        const T* sv = reinterpret_cast<const T*>(D.sv.data) + row_offset(D.sv, l, a0 + a, h, t);
+        const vu4 k0 = ld16(sk + M::off0(g)), k1 = ld16(sk + M::off1(g));
+        const vu4 v0 = ld16(sv + M::off0(g)), v1 = ld16(sv + M::off1(g));
+        double cs[V], sn[V];
+        lds_table<V>(stab[a], g, cs, sn);
+        double p0[V], p1[V], xa[V], xb[V], ma[V], mb[V];
+        Cd::unpack(k0, p0);
+        Cd::unpack(k1, p1);
+        parts_to_pairs<STYLE, V>(p0, p1, xa, xb);
+        rotate_pairs<V>(xa, xb, cs, sn);
+        Cd::unpack(mk0, p0);
+        Cd::unpack(mk1, p1);
+        parts_to_pairs<STYLE, V>(p0, p1, ma, mb);
+        bool d = false;
 #pragma unroll
-      for (int m = 0; m < V; ++m)
-        over |= (fabs(xa[m] - ma[m]) > (double)D.eps) | (fabs(xb[m] - mb[m]) > (double)D.eps);
-      double q0[V], q1[V];
-      Cd::unpack(ld16(sv + M::off0(g)), p0);
-      Cd::unpack(ld16(sv + M::off1(g)), p1);
-      Cd::unpack(ld16_cached(mv + M::off0(g)), q0);
-      Cd::unpack(ld16_cached(mv + M::off1(g)), q1);
+        for (int m = 0; m < V; ++m) d |= (fabs(xa[m] - ma[m]) > eps) | (fabs(xb[m] - mb[m]) > eps);
+        double q0[V], q1[V];
+        Cd::unpack(v0, p0);
+        Cd::unpack(v1, p1);
+        Cd::unpack(mv0, q0);
+        Cd::unpack(mv1, q1);
 #pragma unroll
-      for (int m = 0; m < V; ++m)
-        over |= (fabs(p0[m] - q0[m]) > (double)D.eps) | (fabs(p1[m] - q1[m]) > (double)D.eps);
+        for (int m = 0; m < V; ++m) d |= (fabs(p0[m] - q0[m]) > eps) | (fabs(p1[m] - q1[m]) > eps);
+        over |= (uint32_t)d << a;
+      }
     }
-    const int any = __syncthreads_or(over);
-    if (threadIdx.x == 0) flags[((int64_t)a * D.L + l) * D.nb + beta] = any ? 1 : 0;
+    if (over) atomicOr(&sover, over);
+    __syncthreads();
+    if ((int)threadIdx.x < na)
+      flags[((int64_t)(a0 + threadIdx.x) * D.L + l) * D.nb + beta] = (sover >> threadIdx.x) & 1u;
   }
 }
 
@@ -248,55 +287,71 @@ __global__ __launch_bounds__(kDiffBlock) void diff_decode_kernel(DecodeParams P,
   using M = RowMap<T, HD, STYLE>;
   using Cd = Codec<T, double>;
   constexpr int V = M::V, G = M::G, RPB = kDiffBlock / G;
+  __shared__ double2 stab[kAgentGroup][HD / 2];
+  __shared__ int64_t sslot[kAgentGroup];       // packed slot of the agent's block, or -1
   const int g = threadIdx.x % G, rr = threadIdx.x / G;
   const int beta = blockIdx.x % P.nb;
   const int l = blockIdx.x / P.nb;
   const int t0 = beta * P.bt;
   const int tb = min(P.bt, P.n - t0);
   const int rows = P.H * tb;
-  for (int a = 0; a < P.A; ++a) {
-    const int arow = a * P.L + l;
-    const uint32_t* mrow = P.mask + (int64_t)arow * P.words;
-    bool listed = (mrow[beta >> 5] >> (beta & 31)) & 1u;
-    int64_t slot = -1;
-    if (listed) {
-      int64_t before = 0;
-      for (int w = 0; w < (beta >> 5); ++w) before += __popc(mrow[w]);
-      before += __popc(mrow[beta >> 5] & ((1u << (beta & 31)) - 1u));
-      slot = P.offsets[arow] + before;
-      listed = slot < P.capacity;      // never read past the packed values
+  for (int a0 = 0; a0 < P.A; a0 += kAgentGroup) {
+    const int na = min(kAgentGroup, P.A - a0);
+    __syncthreads();                            // the previous group is done with stab, sslot
+    stage_tables<HD>(tab, a0, na, stab);
+    if ((int)threadIdx.x < na) {
+      const int arow = (a0 + threadIdx.x) * P.L + l;
+      const uint32_t* mrow = P.mask + (int64_t)arow * P.words;
+      int64_t slot = -1;
+      if ((mrow[beta >> 5] >> (beta & 31)) & 1u) {
+        int64_t before = 0;
+        for (int w = 0; w < (beta >> 5); ++w) before += __popc(mrow[w]);
+        before += __popc(mrow[beta >> 5] & ((1u << (beta & 31)) - 1u));
+        slot = P.offsets[arow] + before;
+        if (slot >= P.capacity) slot = -1;      // never read past the packed values
+      }
+      sslot[threadIdx.x] = slot;
     }
-    double cs[V], sn[V];
-    load_table<HD, V>(tab, a, g, cs, sn);
+    __syncthreads();
     for (int r = rr; r < rows; r += RPB) {
       const int h = r / tb, t = r % tb;
-      const T* srck;
-      const T* srcv;
-      if (listed) {
-        const int64_t e = ((slot * P.H + h) * (int64_t)P.bt + t) * HD;
-        srck = reinterpret_cast<const T*>(P.vals_k) + e;
-        srcv = reinterpret_cast<const T*>(P.vals_v) + e;
-      } else {
-        srck = reinterpret_cast<const T*>(P.mk.data) + row_offset(P.mk, l, 0, h, t0 + t);
-        srcv = reinterpret_cast<const T*>(P.mv.data) + row_offset(P.mv, l, 0, h, t0 + t);
-      }
-      const int64_t ko = row_offset(P.ok, l, a, h, t0 + t);
-      const int64_t vo = row_offset(P.ov, l, a, h, t0 + t);
-      double p0[V], p1[V], xa[V], xb[V];
-      Cd::unpack(ld16_cached(srck + M::off0(g)), p0);
-      Cd::unpack(ld16_cached(srck + M::off1(g)), p1);
-      parts_to_pairs<STYLE, V>(p0, p1, xa, xb);
-      rotate_pairs<V>(xa, xb, cs, sn);
-      pairs_to_parts<STYLE, V>(xa, xb, p0, p1);
-      if (ko >= 0) {
-        T* dk = reinterpret_cast<T*>(P.ok.data) + ko;
-        st16(dk + M::off0(g), Cd::pack(p0));
-        st16(dk + M::off1(g), Cd::pack(p1));
-      }
-      if (vo >= 0) {
-        T* dv = reinterpret_cast<T*>(P.ov.data) + vo;
-        st16(dv + M::off0(g), ld16_cached(srcv + M::off0(g)));
-        st16(dv + M::off1(g), ld16_cached(srcv + M::off1(g)));
+      // the master row, once per group of agents
+      const T* mkp = reinterpret_cast<const T*>(P.mk.data) + row_offset(P.mk, l, 0, h, t0 + t);
+      const T* mvp = reinterpret_cast<const T*>(P.mv.data) + row_offset(P.mv, l, 0, h, t0 + t);
+      const vu4 mk0 = ld16(mkp + M::off0(g)), mk1 = ld16(mkp + M::off1(g));
+      const vu4 mv0 = ld16(mvp + M::off0(g)), mv1 = ld16(mvp + M::off1(g));
+      for (int a = 0; a < na; ++a) {
+        const int64_t slot = sslot[a];          // uniform over the block
+        vu4 k0 = mk0, k1 = mk1, v0 = mv0, v1 = mv1;
+        if (slot >= 0) {
+          const int64_t e = ((slot * P.H + h) * (int64_t)P.bt + t) * HD;
+          const T* pk = reinterpret_cast<const T*>(P.vals_k) + e;
+          const T* pv = reinterpret_cast<const T*>(P.vals_v) + e;
+          k0 = ld16(pk + M::off0(g));
+          k1 = ld16(pk + M::off1(g));
+          v0 = ld16(pv + M::off0(g));
+          v1 = ld16(pv + M::off1(g));
+        }
+        double cs[V], sn[V];
+        lds_table<V>(stab[a], g, cs, sn);
+        double p0[V], p1[V], xa[V], xb[V];
+        Cd::unpack(k0, p0);
+        Cd::unpack(k1, p1);
+        parts_to_pairs<STYLE, V>(p0, p1, xa, xb);
+        rotate_pairs<V>(xa, xb, cs, sn);
+        pairs_to_parts<STYLE, V>(xa, xb, p0, p1);
+        const int64_t ko = row_offset(P.ok, l, a0 + a, h, t0 + t);
+        const int64_t vo = row_offset(P.ov, l, a0 + a, h, t0 + t);
+        if (ko >= 0) {
+          T* dk = reinterpret_cast<T*>(P.ok.data) + ko;
+          st16(dk + M::off0(g), Cd::pack(p0));
+          st16(dk + M::off1(g), Cd::pack(p1));
+        }
+        if (vo >= 0) {
+          T* dv = reinterpret_cast<T*>(P.ov.data) + vo;
+          st16(dv + M::off0(g), v0);
+          st16(dv + M::off1(g), v1);
+        }
       }
     }
   }
