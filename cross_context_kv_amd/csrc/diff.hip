@@ -284,8 +284,11 @@ struct DecodeParams {
 template <typename T, int HD, int STYLE>
 __global__ __launch_bounds__(kDiffBlock) void diff_decode_kernel(DecodeParams P,
                                                                  const double2* tab) {
+  // Values are rotated in fp32 for bf16 storage (one rounding to bf16, as in
+  // apply) and in fp64 for fp32 storage.
+  using C = typename std::conditional<std::is_same<T, float>::value, double, float>::type;
   using M = RowMap<T, HD, STYLE>;
-  using Cd = Codec<T, double>;
+  using Cd = Codec<T, C>;
   constexpr int V = M::V, G = M::G, RPB = kDiffBlock / G;
   __shared__ double2 stab[kAgentGroup][HD / 2];
   __shared__ int64_t sslot[kAgentGroup];       // packed slot of the agent's block, or -1
@@ -332,9 +335,12 @@ __global__ __launch_bounds__(kDiffBlock) void diff_decode_kernel(DecodeParams P,
           v0 = ld16(pv + M::off0(g));
           v1 = ld16(pv + M::off1(g));
         }
-        double cs[V], sn[V];
-        lds_table<V>(stab[a], g, cs, sn);
-        double p0[V], p1[V], xa[V], xb[V];
+        double csd[V], snd[V];
+        lds_table<V>(stab[a], g, csd, snd);
+        C cs[V], sn[V];
+#pragma unroll
+        for (int m = 0; m < V; ++m) { cs[m] = (C)csd[m]; sn[m] = (C)snd[m]; }
+        C p0[V], p1[V], xa[V], xb[V];
         Cd::unpack(k0, p0);
         Cd::unpack(k1, p1);
         parts_to_pairs<STYLE, V>(p0, p1, xa, xb);
