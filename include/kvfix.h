@@ -188,7 +188,8 @@ kvfix_status kvfix_select_topb(const float* scores, int32_t n_rows, int32_t n, i
  * (device data is not checked on the host).
  * out may alias reuse (in-place correction).
  * ws: device workspace of kvfix_fit_mean_workspace(...) bytes, 16-byte
- * aligned (partial sums of 128-probe slices).
+ * aligned (fp64 partial sums of 256-probe slices); KVFIX_ERR_ARG when it is
+ * missing, short or misaligned.
  * Arithmetic: fp64 residuals and sums in a fixed order, rounded once to fp32.
  * ------------------------------------------------------------------------- */
 size_t kvfix_fit_mean_workspace(int32_t n_layers, int32_t n_segs, int32_t n_heads,
@@ -207,7 +208,10 @@ kvfix_status kvfix_fit_mean(const kvfix_plane* fresh, int32_t fresh_by_slot,
  * get reuse + w mu-hat; KVCMAS eq. 3 (selective recompute) and eq. 4 / eq. 8
  * (add the estimated deviation to the aligned source cache)]
  * mask: device uint32 [n_segs][ceil(n_tokens/32)] or NULL (no probes).
- * mu: device fp32 [n_layers][n_segs][n_heads][head_dim].
+ * mu: device fp32 [n_layers][n_segs][n_heads][head_dim], contiguous, 16-byte
+ * aligned (KVFIX_ERR_ALIGN otherwise).
+ * lowrank: A rows may use any 4-byte-aligned strides (16-byte-aligned rows
+ * of rank 4 or 8 are read as vectors); rank <= 8.
  * out may alias reuse exactly (in place; each row is read and written by the
  * same lanes).  rope == NULL for value planes.
  * Arithmetic: fp32 for bf16 planes, fp64 for fp32 planes; one rounding.

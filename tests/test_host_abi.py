@@ -84,6 +84,9 @@ def test_call_level_validation():
     # shapes must agree
     assert L.kvfix_apply(R(p), R(plane(n_heads=3)), None, None, 0.0, 1.0, mu, None, None, None) == 1
     assert L.kvfix_apply(R(p), R(p), None, None, 0.0, 1.0, None, None, None, None) == 1
+    # the mean must be 16-byte aligned (it is read as vectors)
+    assert L.kvfix_apply(R(p), R(p), None, None, 0.0, 1.0, ctypes.c_void_p(516), None, None,
+                         None) == 2
     # weights need lo <= hi
     assert L.kvfix_apply(R(p), R(p), None, ctypes.c_void_p(512), 2.0, 1.0, mu, None, None, None) == 1
     # rotary arguments
