@@ -759,8 +759,11 @@ struct ApplyLaunch {
   // are fewer chunks, so no block waits for another to finish.
   template <int R, bool PG>
   static void launch(ApplyParams P, int64_t n_chunks, hipStream_t st) {
-    auto kern = apply_occ3<T, HD, R, PG>() ? apply_kernel<T, C, HD, STYLE, R, PG>
-                                           : apply_kernel_wide<T, C, HD, STYLE, R, PG>;
+    // only the chosen instance is compiled
+    auto kern = [] {
+      if constexpr (apply_occ3<T, HD, R, PG>()) return apply_kernel<T, C, HD, STYLE, R, PG>;
+      else return apply_kernel_wide<T, C, HD, STYLE, R, PG>;
+    }();
     static const int per_cu = [&] {
       int nb = 0;
       if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, kApplyBlock, 0) != hipSuccess ||
