@@ -41,14 +41,17 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 METRIC = "corrected-KV GB/s (read+write) and % of HBM peak; segment-layers/s at 8B shape"
-KERNEL_SOURCES = ["cross_context_kv_amd/csrc/correct.hip", "cross_context_kv_amd/csrc/common.h",
-                  "cross_context_kv_amd/csrc/diff.hip", "cross_context_kv_amd/csrc/draft.hip",
-                  "cross_context_kv_amd/csrc/score_select.hip"]
+# Sources each roofline kernel is built from: a counter summary stays valid
+# while these files are unchanged.
+KERNEL_SOURCES = {
+    "apply": ["cross_context_kv_amd/csrc/correct.hip", "cross_context_kv_amd/csrc/common.h"],
+    "diff_decode": ["cross_context_kv_amd/csrc/diff.hip", "cross_context_kv_amd/csrc/common.h"],
+}
 
 
-def kernel_hash() -> str:
+def kernel_hash(kernel_tag: str) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in KERNEL_SOURCES[kernel_tag]:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -66,7 +69,7 @@ def read_traffic(workload: str):
         return None
     with open(p) as f:
         c = json.load(f)
-    if c.get("kernel_hash") != kernel_hash():
+    if c.get("kernel_hash") != kernel_hash(Workload.ALL[workload].kernel_tag):
         return None
     return c.get("traffic_bytes_per_launch")
 
