@@ -222,6 +222,147 @@ def mask_to_bool(mask_row: np.ndarray, n: int) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------
+# BCR layouts: the chunk budget, chunk scores, whole chunks as rows, grown
+# spans, and the coin control
+# (BCR §3 "The layouts": BCR-chunk repairs the best-scoring fixed chunks,
+#  BCR-grow seeds on the best row and widens the span while a neighbour scores
+#  at least tau of the seed, BCR-single spends the budget row by row; §3 "The
+#  repair": a group of rows scores the mean of its rows; §4.3: tau = 0.25;
+#  App. A.2 "The policy" step 2 (the mean keeps a short last chunk from being
+#  penalised) and "The random control" (chunks drawn by coin at the same
+#  budget); App. A.2 Table 8 (the budget kept by unit of choice:
+#  max(1, round(0.2 n_chunks)) chunks); App. B Algorithm 1 (skip rule
+#  M < 2B or rho M < B, else round(rho M / B) chunks of B = 64 rows))
+# ----------------------------------------------------------------------------
+
+
+def _round_half_up(x: Fraction) -> int:
+    """Nearest integer to x >= 0; a half rounds up (away from zero)."""
+    return int(math.floor(x + Fraction(1, 2)))
+
+
+def chunk_budget(M: int, B: int, rho_num: int, rho_den: int, rule: str) -> int:
+    """Chunks of B rows to repair among M cached rows at budget rho = rho_num / rho_den.
+
+    rule "alg1"  : 0 (serve unrepaired) when M < 2B or rho M < B, otherwise
+                   round(rho M / B)                      [BCR App. B Algorithm 1]
+    rule "table8": max(1, round(rho n_chunks)), n_chunks = ceil(M / B)
+                                                        [BCR App. A.2 Table 8]
+    Never more than n_chunks.  rho is exact (a fraction), so halves are exact.
+    """
+    if M < 0 or B < 1 or rho_den < 1 or not 0 <= rho_num <= rho_den:
+        raise ValueError("bad budget arguments")
+    rho = Fraction(rho_num, rho_den)
+    n_chunks = -(-M // B)
+    if rule == "alg1":
+        if M < 2 * B or rho * M < B:
+            return 0
+        c = _round_half_up(rho * M / B)
+    elif rule == "table8":
+        c = max(1, _round_half_up(rho * n_chunks))
+    else:
+        raise ValueError(rule)
+    return min(c, n_chunks)
+
+
+def chunk_means(scores: np.ndarray, B: int) -> np.ndarray:
+    """Chunk score a-bar_i = mean of a_j over the rows j of chunk i.
+
+    Chunk i holds rows [iB, min((i+1)B, n)); the last one may be short and is
+    divided by its own length.  The sum runs in float64 over the rows in
+    ascending order and the mean is rounded once to float32.
+    scores: float32 [rows][n].  Returns float32 [rows][ceil(n/B)].
+    """
+    scores = np.asarray(scores, dtype=np.float32)
+    rows, n = scores.shape
+    nc = -(-n // B)
+    out = np.zeros((rows, nc), dtype=np.float32)
+    for r in range(rows):
+        for i in range(nc):
+            lo, hi = i * B, min((i + 1) * B, n)
+            acc = 0.0
+            for j in range(lo, hi):
+                acc += float(scores[r, j])
+            out[r, i] = np.float32(acc / (hi - lo))
+    return out
+
+
+def expand_chunks(chunk_idx: np.ndarray, n: int, B: int):
+    """The rows of the chosen chunks.
+
+    chunk_idx: int32 [rows][c], ascending (as select_topb returns it).
+    Returns (idx int32 [rows][c*B]: the rows in ascending order, then -1 for
+    the rows a short last chunk does not have; counts int32 [rows]; mask
+    uint32 [rows][ceil(n/32)]).
+    """
+    rows, c = chunk_idx.shape
+    idx = np.full((rows, c * B), -1, dtype=np.int32)
+    counts = np.zeros(rows, dtype=np.int32)
+    mask = np.zeros((rows, (n + 31) // 32), dtype=np.uint32)
+    for r in range(rows):
+        k = 0
+        for ci in chunk_idx[r]:
+            for j in range(int(ci) * B, min((int(ci) + 1) * B, n)):
+                idx[r, k] = j
+                mask[r, j // 32] |= np.uint32(1) << np.uint32(j % 32)
+                k += 1
+        counts[r] = k
+    return idx, counts, mask
+
+
+def select_grow(scores: np.ndarray, b: int, tau: float):
+    """Exactly b rows per score row, spent in grown spans.
+
+    While fewer than b rows are chosen: the seed is the best-scoring row not
+    yet chosen (ties to the lower index); it is chosen, and its span then
+    widens one row at a time, taking the higher-scoring of the two rows just
+    outside it (the left one on a tie), as long as that row is not chosen yet
+    and scores at least tau times the seed (compared in float64), and rows
+    remain in the budget.
+    scores: float32 [rows][n] (no NaN).  Returns (idx int32 [rows][b]
+    ascending, mask uint32 [rows][ceil(n/32)]).
+    """
+    scores = np.asarray(scores, dtype=np.float32)
+    if np.isnan(scores).any():
+        raise ValueError("NaN score")
+    rows, n = scores.shape
+    if not 0 <= b <= n:
+        raise ValueError("b out of range")
+    idx = np.zeros((rows, b), dtype=np.int32)
+    mask = np.zeros((rows, (n + 31) // 32), dtype=np.uint32)
+    for r in range(rows):
+        a = scores[r].astype(np.float64)
+        chosen = np.zeros(n, dtype=bool)
+        left = b
+        for seed in np.lexsort((np.arange(n), -a)):     # score desc, then index asc
+            if left == 0:
+                break
+            if chosen[seed]:
+                continue
+            chosen[seed] = True
+            left -= 1
+            thr = float(tau) * a[seed]
+            lo = hi = int(seed)
+            while left > 0:
+                cl = lo - 1 if lo > 0 and not chosen[lo - 1] and a[lo - 1] >= thr else -1
+                cr = hi + 1 if hi + 1 < n and not chosen[hi + 1] and a[hi + 1] >= thr else -1
+                if cl < 0 and cr < 0:
+                    break
+                if cl >= 0 and (cr < 0 or a[cl] >= a[cr]):
+                    lo = cl
+                    chosen[cl] = True
+                else:
+                    hi = cr
+                    chosen[cr] = True
+                left -= 1
+        sel = np.nonzero(chosen)[0]
+        idx[r] = sel
+        for j in sel:
+            mask[r, j // 32] |= np.uint32(1) << np.uint32(j % 32)
+    return idx, mask
+
+
+# ----------------------------------------------------------------------------
 # a5: probe mean residual (+ fresh scatter)
 # (AKS step 3 and the equation for mu-hat: the mean of fresh minus reused over
 #  the probe set, re-estimated at every layer; KVCMAS eq. 7-8: a rank-r state
@@ -241,21 +382,25 @@ def fit_mean(fresh: np.ndarray, reuse: np.ndarray, dtype: str, idx: np.ndarray,
              deltas: Optional[Sequence[int]] = None, theta: float = 0.0, style: str = "half",
              A: Optional[np.ndarray] = None, B: Optional[np.ndarray] = None,
              fresh_by_slot: bool = False) -> np.ndarray:
-    """mu[l][s][h] = (1/b) sum_{j in S_s} (fresh_j - align(reuse_j) - A_j B).
+    """mu[l][s][h] = (1/|S_s|) sum_{j in S_s} (fresh_j - align(reuse_j) - A_j B).
 
-    idx: int32 [S][b].  fresh_by_slot: fresh holds only the probe rows, row k
-    of segment s being token idx[s][k].  b = 0 gives mu = 0.  Returns float32
-    [L][S][H][hd].
+    idx: int32 [S][w].  An entry outside [0, n) is padding, not a member of
+    the probe set S_s (a layout whose row count depends on the data, such as
+    whole chunks with a short last chunk, pads its fixed-width list with -1);
+    mu is the mean over the members, 0 when there are none.  fresh_by_slot:
+    fresh holds the probe rows by slot, row k of segment s being token
+    idx[s][k] (padding slots unused).  Returns float32 [L][S][H][hd].
     """
     L, S, H, n, hd = reuse.shape
-    b = idx.shape[1]
+    w = idx.shape[1]
     mu = np.zeros((L, S, H, hd), dtype=np.float64)
-    if b == 0:
-        return mu.astype(np.float32)
-    for l in range(L):
-        for s in range(S):
-            rows = idx[s].astype(np.int64)
-            fr_rows = np.arange(b) if fresh_by_slot else rows
+    for s in range(S):
+        slots = np.array([k for k in range(w) if 0 <= int(idx[s][k]) < n], dtype=np.int64)
+        if len(slots) == 0:
+            continue
+        rows = idx[s][slots].astype(np.int64)
+        fr_rows = slots if fresh_by_slot else rows
+        for l in range(L):
             for h in range(H):
                 f = to_f64(fresh[l, s, h][fr_rows], dtype)
                 r = to_f64(reuse[l, s, h][rows], dtype)
@@ -265,18 +410,22 @@ def fit_mean(fresh: np.ndarray, reuse: np.ndarray, dtype: str, idx: np.ndarray,
                 ab = lowrank_rows(A, B, l, s, h, rows)
                 if ab is not None:
                     res = res - ab
-                mu[l, s, h] = res.sum(axis=0) / b
+                mu[l, s, h] = res.sum(axis=0) / len(rows)
     return mu.astype(np.float32)
 
 
 def scatter_fresh(out: np.ndarray, fresh: np.ndarray, idx: np.ndarray,
                   fresh_by_slot: bool = False) -> None:
-    """Copy the fresh rows into the probe positions of `out` (in place, exact)."""
+    """Copy the fresh rows into the probe positions of `out` (in place, exact);
+    padding entries of idx (outside [0, n)) are skipped."""
     L, S, H, n, hd = out.shape
-    b = idx.shape[1]
+    w = idx.shape[1]
     for s in range(S):
-        rows = idx[s].astype(np.int64)
-        src = np.arange(b) if fresh_by_slot else rows
+        slots = np.array([k for k in range(w) if 0 <= int(idx[s][k]) < n], dtype=np.int64)
+        if len(slots) == 0:
+            continue
+        rows = idx[s][slots].astype(np.int64)
+        src = slots if fresh_by_slot else rows
         out[:, s][:, :, rows] = fresh[:, s][:, :, src]
 
 

@@ -194,6 +194,14 @@ def draw_draft_queries(cfg: WorkloadConfig, device="cpu") -> torch.Tensor:
     return q.to(torch.bfloat16)
 
 
+def draw_coin_keys(seed: int, rows: int, n_chunks: int, device="cpu", draw: int = 0) -> torch.Tensor:
+    """Uniform [0, 1) float32 keys [rows, n_chunks], one per chunk, for the
+    coin control (the chunks holding the largest keys form a uniformly random
+    subset of any fixed size).  `draw` tells repeated coins apart."""
+    g = make_gen(device, seed, "coin", draw)
+    return torch.rand(rows, n_chunks, generator=g, device=device, dtype=torch.float32)
+
+
 def draw_page_table(cfg: WorkloadConfig, device="cpu") -> torch.Tensor:
     """Seeded permutation of the page pool, int32 [n_segs, n_tokens / page_size]."""
     per_seg = -(-cfg.n_tokens // cfg.page_size)

@@ -608,3 +608,192 @@ def test_diff_roundtrip_lossless_fp32_storage():
     assert d["vals_k"].dtype == np.float32
     ok, ov = K.diff_decode(mk, mv, d, [0] * A, 1e4, A, bt, dtype="f32")
     assert np.array_equal(ok, sk) and np.array_equal(ov, sv)
+
+
+# ----------------------------------------------------------------------------
+# BCR layouts: chunk budget, chunk means, chunk rows, grown spans, coin
+# ----------------------------------------------------------------------------
+
+
+def test_chunk_budget_reproduces_the_printed_budget_column():
+    g = golden("bcr_table8_budget.json")
+    M, (num, den) = g["segment_rows"], g["rho"]
+    for unit, pct in zip(g["units"], g["budget_percent_printed"]):
+        c = K.chunk_budget(M, unit, num, den, "table8")
+        assert round(100.0 * c * unit / M, g["printed_decimals"]) == pct, (unit, c)
+
+
+def test_chunk_budget_algorithm1_skip_rule_and_rounding():
+    # skip when M < 2B ...
+    assert K.chunk_budget(127, 64, 1, 5, "alg1") == 0
+    # ... or when rho M < B (0.2 * 319 = 63.8 < 64); rho M = B is repaired
+    assert K.chunk_budget(319, 64, 1, 5, "alg1") == 0
+    assert K.chunk_budget(320, 64, 1, 5, "alg1") == 1
+    # round(rho M / B): 0.2 * 2048 / 64 = 6.4 -> 6, the 64-row line of the table
+    assert K.chunk_budget(2048, 64, 1, 5, "alg1") == 6 == K.chunk_budget(2048, 64, 1, 5, "table8")
+    # 0.2 * 2240 / 64 = 7.0 exactly; 0.5 * 192 / 64 = 1.5 rounds up
+    assert K.chunk_budget(2240, 64, 1, 5, "alg1") == 7
+    assert K.chunk_budget(192, 64, 1, 2, "alg1") == 2
+    # rho = 1 takes every chunk (1000 / 64 = 15.625 -> 16 = ceil(1000 / 64))
+    assert K.chunk_budget(1000, 64, 1, 1, "alg1") == 16
+    # rho = 0: Algorithm 1 serves unrepaired; the table's rule keeps one chunk
+    assert K.chunk_budget(2048, 64, 0, 1, "alg1") == 0
+    assert K.chunk_budget(2048, 64, 0, 1, "table8") == 1
+    assert K.chunk_budget(0, 64, 1, 5, "table8") == 0
+
+
+def test_chunk_means_closed_forms():
+    n, B = 100, 64
+    ramp = np.arange(n, dtype=np.float32)[None, :]
+    m = K.chunk_means(ramp, B)
+    # the mean of the integers lo..hi-1 is (lo + hi - 1) / 2; the short last
+    # chunk (rows 64..99) is divided by its own 36 rows, not by 64
+    assert m.tolist() == [[31.5, 81.5]]
+    const = np.full((2, 130), 0.375, dtype=np.float32)
+    assert np.all(K.chunk_means(const, 16) == np.float32(0.375))
+    # random: within one float32 ulp of the exactly rounded mean
+    rng = np.random.default_rng(21)
+    x = rng.random((3, 200)).astype(np.float32) * 10.0 ** rng.integers(-3, 3, (3, 200))
+    got = K.chunk_means(x.astype(np.float32), 48)
+    for r in range(3):
+        for i in range(got.shape[1]):
+            vals = [float(v) for v in x[r, i * 48:(i + 1) * 48]]
+            exact = np.float32(math.fsum(vals) / len(vals))
+            assert abs(float(got[r, i]) - float(exact)) <= float(np.spacing(exact))
+
+
+def test_expand_chunks_hand_example():
+    idx, counts, mask = K.expand_chunks(np.array([[1, 3]], dtype=np.int32), 100, 32)
+    # chunk 1 = rows 32..63, chunk 3 = rows 96..99 (a short last chunk), then padding
+    assert idx[0].tolist() == list(range(32, 64)) + [96, 97, 98, 99] + [-1] * 28
+    assert counts.tolist() == [36]
+    assert mask[0].tolist() == [0, 0xFFFFFFFF, 0, 0xF]
+
+
+def test_chunk_layout_keeps_the_best_means():
+    rng = np.random.default_rng(22)
+    a = rng.random((4, 1000)).astype(np.float32)
+    a[:, 300:364] += 5.0                       # one chunk of clearly higher scores
+    m = K.chunk_means(a, 64)
+    c = K.chunk_budget(1000, 64, 1, 5, "alg1")
+    cidx, _ = K.select_topb(m, c)
+    for r in range(4):
+        assert 300 // 64 in cidx[r] or 364 // 64 in cidx[r]
+        chosen = set(cidx[r].tolist())
+        worst_in = min(m[r, i] for i in chosen)
+        best_out = max(m[r, i] for i in range(m.shape[1]) if i not in chosen)
+        assert worst_in >= best_out
+
+
+def test_select_grow_hand_example():
+    # seed 3 (9), threshold 2.25: left 3 >= 2.25, right 2 < 2.25 -> row 2;
+    # left 8 -> row 1; left 1 and right 2 both fail; seed 1 is taken already;
+    # seed 5 (7) uses the last row of the budget of 4
+    idx, mask = K.select_grow(np.array([[1, 8, 3, 9, 2, 7, 0.5, 6]], np.float32), 4, 0.25)
+    assert idx.tolist() == [[1, 2, 3, 5]]
+    assert mask.tolist() == [[0b101110]]
+
+
+def test_select_grow_tie_goes_left_and_budget_stops_mid_span():
+    a = np.array([[5, 4, 10, 4, 1]], np.float32)
+    assert K.select_grow(a, 1, 0.25)[0].tolist() == [[2]]
+    assert K.select_grow(a, 2, 0.25)[0].tolist() == [[1, 2]]        # 4 | 4: the left one
+    assert K.select_grow(a, 3, 0.25)[0].tolist() == [[0, 1, 2]]     # 5 beats 4
+    assert K.select_grow(a, 4, 0.25)[0].tolist() == [[0, 1, 2, 3]]
+
+
+def test_select_grow_spans_stop_at_chosen_rows():
+    # seed 0 (9) cannot grow (0.1 < 4.5); seed 3 (8) takes row 2 (5 >= 4) and
+    # stops at 0.1 on both sides; row 2 is then skipped as a seed; seed 1
+    # (0.1, threshold 0.05) is boxed in by chosen rows 0 and 2
+    a = np.array([[9, 0.1, 5, 8, 0.1]], np.float32)
+    assert K.select_grow(a, 4, 0.5)[0].tolist() == [[0, 1, 2, 3]]
+    assert K.select_grow(a, 3, 0.5)[0].tolist() == [[0, 2, 3]]
+
+
+@pytest.mark.parametrize("b", [0, 1, 7, 40, 100])
+def test_select_grow_with_tau_above_one_is_topb(b):
+    # an unchosen neighbour never beats the seed, so no span grows
+    rng = np.random.default_rng(23 + b)
+    a = np.round(rng.random((3, 100)) * 20).astype(np.float32) + 1.0   # ties
+    gi, gm = K.select_grow(a, b, 1.5)
+    ti, tm = K.select_topb(a, b)
+    assert np.array_equal(gi, ti) and np.array_equal(gm, tm)
+
+
+def _window_by_prefix_minimum_merge(a, b):
+    """tau = 0: one window around the best row.  Its left and right parts are
+    the first b-1 rows of the merge of the two outward runs, where each run is
+    replaced by its running minimum (a non-increasing sequence) and equal
+    values go to the left run."""
+    s = int(np.lexsort((np.arange(len(a)), -a.astype(np.float64)))[0])
+    X = list(np.minimum.accumulate(a[:s][::-1].astype(np.float64))) if s > 0 else []
+    Y = list(np.minimum.accumulate(a[s + 1:].astype(np.float64))) if s + 1 < len(a) else []
+    i = j = 0
+    for _ in range(b - 1):
+        if j >= len(Y) or (i < len(X) and X[i] >= Y[j]):
+            i += 1
+        else:
+            j += 1
+    return list(range(s - i, s + j + 1))
+
+
+def test_select_grow_zero_tau_is_one_window_by_prefix_minimum_merge():
+    rng = np.random.default_rng(24)
+    for trial in range(20):
+        n = int(rng.integers(2, 60))
+        a = (rng.random(n) * 10).astype(np.float32)
+        if trial % 3 == 0:
+            a = np.round(a).astype(np.float32)       # ties
+        b = int(rng.integers(1, n + 1))
+        got = K.select_grow(a[None, :], b, 0.0)[0][0].tolist()
+        assert got == _window_by_prefix_minimum_merge(a, b)
+
+
+def test_select_grow_invariants():
+    rng = np.random.default_rng(25)
+    a = rng.random((5, 300)).astype(np.float32) ** 4
+    for b in [0, 1, 30, 299, 300]:
+        idx, mask = K.select_grow(a, b, 0.25)
+        assert idx.shape == (5, b)
+        for r in range(5):
+            assert np.all(np.diff(idx[r]) > 0)
+            assert K.mask_to_bool(mask[r], 300).sum() == b
+            if b:
+                assert int(np.argmax(a[r])) in idx[r]
+
+
+def test_fit_mean_padding_entries_are_not_probes():
+    rng = np.random.default_rng(26)
+    reuse = K.store(rng.standard_normal((2, 2, 2, 40, 8)), "bf16")
+    fresh = K.store(rng.standard_normal((2, 2, 2, 40, 8)), "bf16")
+    real = np.array([[3, 9, 20], [0, 5, 39]], dtype=np.int32)
+    padded = np.array([[3, 9, 20, -1, -1], [0, 5, 39, -1, 40]], dtype=np.int32)
+    a = K.fit_mean(fresh, reuse, "bf16", real, [4, 7], 1e4)
+    b = K.fit_mean(fresh, reuse, "bf16", padded, [4, 7], 1e4)
+    assert np.array_equal(a, b)
+    # a list of padding only is an empty probe set: mu = 0
+    z = K.fit_mean(fresh, reuse, "bf16", np.full((2, 4), -1, np.int32), [4, 7], 1e4)
+    assert not z.any()
+    # by slot: padding slots hold no fresh row
+    compact = np.zeros((2, 2, 2, 5, 8), dtype=fresh.dtype)
+    for s in range(2):
+        for k in range(5):
+            if 0 <= padded[s, k] < 40:
+                compact[:, s, :, k] = fresh[:, s, :, padded[s, k]]
+    c = K.fit_mean(compact, reuse, "bf16", padded, [4, 7], 1e4, fresh_by_slot=True)
+    assert np.array_equal(a, c)
+
+
+def test_coin_control_draws_exactly_c_uniform_chunks():
+    from synthetic.workloads import draw_coin_keys
+    nc, c, trials = 10, 3, 3000
+    hits = np.zeros(nc)
+    keys = draw_coin_keys(77, trials, nc).numpy()
+    idx, mask = K.select_topb(keys, c)
+    for r in range(trials):
+        assert len(set(idx[r].tolist())) == c
+        hits[idx[r]] += 1
+    p = c / nc
+    sd = math.sqrt(trials * p * (1 - p))
+    assert np.all(np.abs(hits - trials * p) < 5 * sd)
