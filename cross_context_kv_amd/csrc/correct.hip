@@ -116,6 +116,9 @@ __global__ __launch_bounds__(kBlock) void rope_shift_kernel(RopeShiftParams P) {
 
 constexpr int kFitRows = 256;
 constexpr int kFitMaxRank = 8;
+// A partial row: HD residual sums, kFitMaxRank sums of rank-state rows, and
+// the number of probe-set members (indices inside [0, n)) of the slice.
+__host__ __device__ constexpr int fit_row_width(int hd) { return hd + kFitMaxRank + 1; }
 
 struct FitParams {
   DPlane fresh, reuse, out;
@@ -124,7 +127,7 @@ struct FitParams {
   int32_t b, parts;
   DLowRank lr;
   RopeArgs rope;
-  double* partial;          // [units][parts][HD + kFitMaxRank]
+  double* partial;          // [units][parts][kFitRowWidth(HD)]
   int32_t S, H, n;
 };
 
@@ -133,7 +136,7 @@ __global__ __launch_bounds__(kBlock) void fit_partial_kernel(FitParams P) {
   using M = PartMap<T, HD, STYLE>;
   using Cd = Codec<T, double>;
   constexpr int V = M::V, G = M::G, RPW = M::RPW, U = 4;
-  constexpr int PW = HD + kFitMaxRank;         // partial row width
+  constexpr int PW = fit_row_width(HD);
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int g = lane % G, rw = lane / G;
   const int part = blockIdx.x % P.parts;
@@ -158,12 +161,14 @@ __global__ __launch_bounds__(kBlock) void fit_partial_kernel(FitParams P) {
   float arow[kFitMaxRank];
 #pragma unroll
   for (int k = 0; k < kFitMaxRank; ++k) arow[k] = 0.0f;
+  int member = 0;
   {
     const int i = threadIdx.x;
     if (i < nk) {
       const int k = k_begin + i;
       const int j = idx[k];
-      const bool ok = j >= 0 && j < P.n;            // an index out of range is dropped
+      const bool ok = j >= 0 && j < P.n;            // an index out of range is padding
+      member = ok;
       sj[i] = ok ? j : -1;
       spf[i] = ok ? page_of(P.fresh, s, P.fresh_by_slot ? k : j) : -1;
       spr[i] = ok ? page_of(P.reuse, s, j) : -1;
@@ -176,7 +181,7 @@ __global__ __launch_bounds__(kBlock) void fit_partial_kernel(FitParams P) {
       }
     }
   }
-  __syncthreads();
+  const int members = __syncthreads_count(member);
   static_assert(kFitRows <= kBlock, "one probe row per thread in the rank-state sum");
   double cs[V], ss[V];
   if constexpr (STYLE != kStyleNone) {
@@ -266,9 +271,11 @@ __global__ __launch_bounds__(kBlock) void fit_partial_kernel(FitParams P) {
     }
     outp[HD + threadIdx.x] = a;
   }
+  if (threadIdx.x == 0) outp[HD + kFitMaxRank] = (double)members;
 }
 
-// mu[unit][d] = (sum_p partial[p][d] - sum_k (sum_p partial[p][HD + k]) B[k][d]) / b
+// mu[unit][d] = (sum_p partial[p][d] - sum_k (sum_p partial[p][HD + k]) B[k][d]) / members,
+// members = the number of probe-set members over all slices (mu = 0 for none)
 struct FitFinishParams {
   const double* partial;
   DLowRank lr;
@@ -279,14 +286,21 @@ struct FitFinishParams {
 __global__ void fit_finish_kernel(FitFinishParams F) {
   __shared__ double sA[kFitMaxRank];
   const int unit = blockIdx.x;
-  const int pw = F.hd + kFitMaxRank;
+  const int pw = fit_row_width(F.hd);
+  __shared__ double s_members;
   const double* pp = F.partial + (int64_t)unit * F.parts * pw;
   if (threadIdx.x < kFitMaxRank) {
     double a = 0.0;
     for (int p = 0; p < F.parts; ++p) a += pp[(int64_t)p * pw + F.hd + threadIdx.x];
     sA[threadIdx.x] = a;
   }
+  if (threadIdx.x == 0) {
+    double c = 0.0;
+    for (int p = 0; p < F.parts; ++p) c += pp[(int64_t)p * pw + F.hd + kFitMaxRank];
+    s_members = c;
+  }
   __syncthreads();
+  const double members = s_members;
   const int h = unit % F.H, s = (unit / F.H) % F.S, l = unit / (F.H * F.S);
   const float* Bp = F.lr.rank > 0 ? F.lr.B + l * F.lr.sB_layer + s * F.lr.sB_seg + h * F.lr.sB_head
                                   : nullptr;
@@ -295,7 +309,7 @@ __global__ void fit_finish_kernel(FitFinishParams F) {
     for (int p = 0; p < F.parts; ++p) t += pp[(int64_t)p * pw + d];
     double ab = 0.0;
     for (int k = 0; k < F.lr.rank; ++k) ab = fma(sA[k], (double)Bp[k * F.hd + d], ab);
-    F.mu[(int64_t)unit * F.hd + d] = F.b > 0 ? (float)((t - ab) / (double)F.b) : 0.0f;
+    F.mu[(int64_t)unit * F.hd + d] = members > 0.0 ? (float)((t - ab) / members) : 0.0f;
   }
 }
 
@@ -827,7 +841,7 @@ static int fit_parts(int32_t b) { return b > 0 ? (b + kFitRows - 1) / kFitRows :
 extern "C" size_t kvfix_fit_mean_workspace(int32_t n_layers, int32_t n_segs, int32_t n_heads,
                                            int32_t head_dim, int32_t b) {
   if (n_layers < 0 || n_segs < 0 || n_heads < 0 || head_dim < 0 || b < 0) return 0;
-  return (size_t)n_layers * n_segs * n_heads * fit_parts(b) * (head_dim + kFitMaxRank) *
+  return (size_t)n_layers * n_segs * n_heads * fit_parts(b) * fit_row_width(head_dim) *
          sizeof(double);
 }
 
@@ -848,7 +862,7 @@ extern "C" kvfix_status kvfix_fit_mean(const kvfix_plane* fresh, int32_t fresh_b
       fresh->n_heads != reuse->n_heads || fresh->n_segs != reuse->n_segs ||
       fresh->n_layers != reuse->n_layers)
     return KVFIX_ERR_ARG;
-  if (b < 0 || b > reuse->n_tokens) return KVFIX_ERR_ARG;
+  if (b < 0) return KVFIX_ERR_ARG;                // b: the width of each index list
   if (b > 0 && idx == nullptr) return KVFIX_ERR_ARG;
   if (fresh_by_slot ? fresh->n_tokens < b : fresh->n_tokens != reuse->n_tokens)
     return KVFIX_ERR_ARG;

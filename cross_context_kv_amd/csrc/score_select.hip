@@ -15,6 +15,7 @@
 
 #include "common.h"
 #include "host_util.h"
+#include "select_common.h"
 
 namespace kvfix {
 
@@ -110,48 +111,6 @@ struct ScoreLaunch {
 // top-b selection
 // ---------------------------------------------------------------------------
 
-constexpr int kSelBlock = 1024;
-constexpr int kSelWaves = kSelBlock / 64;
-constexpr int kSelRegKeys = 32;        // keys held in registers per thread (n <= 32768)
-
-__device__ __forceinline__ uint32_t order_key(float f) {
-  if (f != f) return 0u;                                   // NaN ranks lowest
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) == 0u) u = 0u;                     // -0 == +0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// Exclusive prefix of a per-thread count over the block (integer, so order
-// does not matter): wave prefix by shuffles, then the wave totals.
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* lds,
-                                                        uint32_t* total) {
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  uint32_t incl = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_up(incl, off);
-    if (lane >= off) incl += y;
-  }
-  if (lane == 63) lds[wave] = incl;
-  __syncthreads();
-  if (wave == 0) {
-    const uint32_t wt = lane < kSelWaves ? lds[lane] : 0u;
-    uint32_t wi = wt;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t y = __shfl_up(wi, off);
-      if (lane >= off) wi += y;
-    }
-    if (lane < kSelWaves) lds[64 + lane] = wi - wt;        // exclusive prefix of wave totals
-    if (lane == kSelWaves - 1) lds[128] = wi;
-  }
-  __syncthreads();
-  const uint32_t r = lds[64 + wave] + incl - v;
-  *total = lds[128];
-  __syncthreads();
-  return r;
-}
-
 // One block per row.  Keys j = t + 1024 q live in registers (read once).
 // Four 8-bit radix passes over per-wave LDS histograms find the b-th largest
 // key T and how many keys equal to T are still needed; the compaction then
@@ -164,7 +123,7 @@ __global__ __launch_bounds__(kSelBlock) void select_topb_kernel(const float* __r
                                                                 int words) {
   __shared__ uint32_t hist[kSelWaves][256];
   __shared__ uint32_t scan[160];
-  __shared__ uint32_t sh_prefix, sh_remaining;
+  __shared__ uint32_t sh[2];
   const int row = blockIdx.x;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const float* sc = scores + (int64_t)row * n;
@@ -180,66 +139,8 @@ __global__ __launch_bounds__(kSelBlock) void select_topb_kernel(const float* __r
       key[q] = j < n ? order_key(sc[j]) : 0u;
     }
   }
-  if (t == 0) { sh_prefix = 0; sh_remaining = (uint32_t)b; }
-  __syncthreads();
-  uint32_t prefix = 0, pmask = 0;
-  if (b > 0) {
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int i = lane; i < 256; i += 64) hist[wave][i] = 0;
-      __syncthreads();
-      if (in_regs) {
-#pragma unroll
-        for (int q = 0; q < kSelRegKeys; ++q) {
-          const int j = t + q * kSelBlock;
-          if (j < n && (key[q] & pmask) == prefix) atomicAdd(&hist[wave][(key[q] >> shift) & 255u], 1u);
-        }
-      } else {
-        for (int j = t; j < n; j += kSelBlock) {
-          const uint32_t k = order_key(sc[j]);
-          if ((k & pmask) == prefix) atomicAdd(&hist[wave][(k >> shift) & 255u], 1u);
-        }
-      }
-      __syncthreads();
-      if (t < 256) {                                       // fold the wave histograms
-        uint32_t c = 0;
-#pragma unroll
-        for (int w = 0; w < kSelWaves; ++w) c += hist[w][t];
-        hist[0][t] = c;
-      }
-      __syncthreads();
-      if (t < 64) {
-        // lane L owns bins 255-4L .. 252-4L (descending); find the bin that
-        // holds the need-th largest key by a prefix over the lanes
-        const uint32_t need = sh_remaining;
-        uint32_t c[4], sum = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { c[i] = hist[0][255 - 4 * t - i]; sum += c[i]; }
-        uint32_t incl = sum;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const uint32_t y = __shfl_up(incl, off);
-          if (t >= off) incl += y;
-        }
-        const uint32_t excl = incl - sum;
-        if (excl < need && need <= incl) {
-          uint32_t above = excl;
-          int d = 255 - 4 * t - 3;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if (above + c[i] >= need) { d = 255 - 4 * t - i; break; }
-            above += c[i];
-          }
-          sh_remaining = need - above;
-          sh_prefix = prefix | ((uint32_t)d << shift);
-        }
-      }
-      __syncthreads();
-      prefix = sh_prefix;
-      pmask |= 255u << shift;
-    }
-  }
-  const uint32_t T = sh_prefix;
-  const uint32_t need_eq = b > 0 ? sh_remaining : 0u;
+  uint32_t T, need_eq;
+  radix_threshold(key, in_regs, sc, n, b, &hist[0][0], sh, &T, &need_eq);
 
   // Compaction in index order: chunk c covers keys [1024 c, 1024 c + 1024),
   // thread t holds key 1024 c + t (register q = c when in_regs).

@@ -21,7 +21,8 @@ STATUS = {0: "KVFIX_OK", 1: "KVFIX_ERR_ARG", 2: "KVFIX_ERR_ALIGN", 3: "KVFIX_ERR
           4: "KVFIX_ERR_HIP", 5: "KVFIX_ERR_UNSUPPORTED"}
 
 EXPORTS = ("kvfix_rope_shift", "kvfix_score", "kvfix_score_draft_workspace", "kvfix_score_draft",
-           "kvfix_select_topb", "kvfix_fit_mean_workspace", "kvfix_fit_mean", "kvfix_apply", "kvfix_diff_encode_workspace",
+           "kvfix_select_topb", "kvfix_chunk_budget", "kvfix_chunk_means", "kvfix_expand_chunks",
+           "kvfix_select_grow", "kvfix_fit_mean_workspace", "kvfix_fit_mean", "kvfix_apply", "kvfix_diff_encode_workspace",
            "kvfix_diff_encode", "kvfix_diff_decode_workspace", "kvfix_diff_decode",
            "kvfix_status_string", "kvfix_version")
 
@@ -81,6 +82,10 @@ def lib() -> ctypes.CDLL:
             "kvfix_score_draft_workspace": [I32, I32, I32, I32, I32, I32],
             "kvfix_score_draft": [P, I32, I32, P, I32, P, P, P, ctypes.c_size_t, P],
             "kvfix_select_topb": [P, I32, I32, I32, P, P, P],
+            "kvfix_chunk_budget": [I64, I32, I64, I64, I32],
+            "kvfix_chunk_means": [P, I32, I32, I32, P, P],
+            "kvfix_expand_chunks": [P, I32, I32, I32, I32, P, P, P, P],
+            "kvfix_select_grow": [P, I32, I32, I32, ctypes.c_double, P, P, P],
             "kvfix_fit_mean_workspace": [I32, I32, I32, I32, I32],
             "kvfix_fit_mean": [P, I32, P, P, P, I32, P, P, P, P, ctypes.c_size_t, P],
             "kvfix_apply": [P, P, P, P, F, F, P, P, P, P],
@@ -95,6 +100,7 @@ def lib() -> ctypes.CDLL:
             fn = getattr(L, name)
             fn.argtypes = args
             fn.restype = ctypes.c_int32
+        L.kvfix_chunk_budget.restype = ctypes.c_int64
         L.kvfix_score_draft_workspace.restype = ctypes.c_size_t
         L.kvfix_fit_mean_workspace.restype = ctypes.c_size_t
         L.kvfix_diff_encode_workspace.restype = ctypes.c_size_t
@@ -215,6 +221,37 @@ def kvfix_select_topb(scores: torch.Tensor, b: int, idx: torch.Tensor,
     n_rows, n = scores.shape
     _check("kvfix_select_topb", lib().kvfix_select_topb(_ptr(scores), n_rows, n, b, _ptr(idx),
                                                         _ptr(mask), _stream()))
+
+
+BUDGET_SKIP, BUDGET_AT_LEAST_ONE = 0, 1
+
+
+def kvfix_chunk_budget(n_tokens: int, chunk: int, rho_num: int, rho_den: int,
+                       rule: int = BUDGET_SKIP) -> int:
+    c = int(lib().kvfix_chunk_budget(n_tokens, chunk, rho_num, rho_den, rule))
+    if c < 0:
+        raise KvfixError("kvfix_chunk_budget", 1)
+    return c
+
+
+def kvfix_chunk_means(scores: torch.Tensor, chunk: int, means: torch.Tensor) -> None:
+    n_rows, n = scores.shape
+    _check("kvfix_chunk_means", lib().kvfix_chunk_means(_ptr(scores), n_rows, n, chunk,
+                                                        _ptr(means), _stream()))
+
+
+def kvfix_expand_chunks(chunk_idx: torch.Tensor, n: int, chunk: int, idx: torch.Tensor,
+                        counts: torch.Tensor, mask: torch.Tensor) -> None:
+    n_rows, c = chunk_idx.shape
+    _check("kvfix_expand_chunks", lib().kvfix_expand_chunks(
+        _ptr(chunk_idx), n_rows, c, n, chunk, _ptr(idx), _ptr(counts), _ptr(mask), _stream()))
+
+
+def kvfix_select_grow(scores: torch.Tensor, b: int, tau: float, idx: torch.Tensor,
+                      mask: torch.Tensor) -> None:
+    n_rows, n = scores.shape
+    _check("kvfix_select_grow", lib().kvfix_select_grow(_ptr(scores), n_rows, n, b, float(tau),
+                                                        _ptr(idx), _ptr(mask), _stream()))
 
 
 def kvfix_fit_mean_workspace(n_layers: int, n_segs: int, n_heads: int, head_dim: int,

@@ -10,6 +10,9 @@
  *   kvfix_score        fresh-vs-reused L2 divergence per token at a check layer
  *   kvfix_score_draft  attention mass that draft query rows pay each token
  *   kvfix_select_topb  exactly b tokens with the largest score (probe set)
+ *   kvfix_chunk_budget / kvfix_chunk_means / kvfix_expand_chunks
+ *                      probe sets of whole fixed-size chunks (BCR-chunk, coin)
+ *   kvfix_select_grow  probe sets of spans grown around the best rows (BCR-grow)
  *   kvfix_fit_mean     per-layer mean residual over the probe set (+ fresh scatter)
  *   kvfix_apply        fused re-align + weighted mean + rank-r correction
  *   kvfix_diff_encode  block-sparse diff of N sibling caches against a master
@@ -177,15 +180,83 @@ kvfix_status kvfix_select_topb(const float* scores, int32_t n_rows, int32_t n, i
                                int32_t* idx, uint32_t* mask, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * BCR layouts of the probe budget.  [BCR §3 "The layouts" and "The repair";
+ * §4.3; App. A.2 "The policy", "The random control" and Table 8; App. B
+ * Algorithm 1]
+ *
+ * Whole chunks (BCR-chunk): chunk i of a row of n scores holds tokens
+ * [i*chunk, min((i+1)*chunk, n)) and scores the mean of its tokens' scores.
+ * The layout is: kvfix_chunk_means, then kvfix_select_topb over the means with
+ * c = kvfix_chunk_budget(...) chunks, then kvfix_expand_chunks to token
+ * indices and the token mask, which kvfix_fit_mean and kvfix_apply take.  The
+ * coin control draws the chunks at random at the same budget: the same chain
+ * with kvfix_select_topb run over caller-drawn uniform random keys, one per
+ * chunk, instead of the means.
+ * ------------------------------------------------------------------------- */
+typedef enum {
+  KVFIX_BUDGET_SKIP = 0,          /* 0 when M < 2 chunk or rho M < chunk, else round(rho M / chunk) */
+  KVFIX_BUDGET_AT_LEAST_ONE = 1   /* max(1, round(rho * ceil(M / chunk))) */
+} kvfix_budget_rule;
+
+/* Number of chunks to repair among M = n_tokens cached tokens at budget
+ * rho = rho_num / rho_den (exact; a half rounds up), never more than
+ * ceil(M / chunk).  KVFIX_BUDGET_SKIP is BCR's Algorithm 1 (serve unrepaired
+ * when the segment is shorter than two chunks or the budget is less than one
+ * chunk); KVFIX_BUDGET_AT_LEAST_ONE is BCR's Table 8 rule.  Host-only (no
+ * device work).  Returns -1 for chunk < 1, n_tokens outside [0, 2^31],
+ * rho_den outside [1, 2^30], rho_num outside [0, rho_den] or another rule. */
+int64_t kvfix_chunk_budget(int64_t n_tokens, int32_t chunk, int64_t rho_num, int64_t rho_den,
+                           int32_t rule);
+
+/* means[r][i] = mean of scores[r][j] over the tokens j of chunk i, summed in
+ * fp64 in token order, divided by the chunk's own length (the last chunk may
+ * be short) and rounded once to fp32.
+ * scores: device fp32 [n_rows][n].  means: device fp32 [n_rows][ceil(n/chunk)]. */
+kvfix_status kvfix_chunk_means(const float* scores, int32_t n_rows, int32_t n, int32_t chunk,
+                               float* means, void* stream);
+
+/* The tokens of c listed chunks per row.  chunk_idx: device int32 [n_rows][c]
+ * (kvfix_select_topb's output: ascending); an id outside [0, ceil(n/chunk))
+ * lists no tokens.  idx: device int32 [n_rows][c*chunk]: the listed chunks'
+ * tokens in list order (ascending for an ascending list), then -1 padding
+ * for the tokens a short last chunk does not have (kvfix_fit_mean reads -1
+ * as padding).  counts: device int32 [n_rows], the tokens listed.  mask:
+ * device uint32 [n_rows][ceil(n/32)], all words written.  c * chunk < 2^31. */
+kvfix_status kvfix_expand_chunks(const int32_t* chunk_idx, int32_t n_rows, int32_t c, int32_t n,
+                                 int32_t chunk, int32_t* idx, int32_t* counts, uint32_t* mask,
+                                 void* stream);
+
+/* Grown spans (BCR-grow): exactly b tokens per row.  While fewer than b are
+ * chosen, the seed is the best-scoring token not yet chosen (equal scores:
+ * the lower index; -0 equals +0; NaN ranks lowest); it is chosen, and its
+ * span widens one token at a time to the higher-scoring of the two tokens
+ * just outside it (the left one on a tie), while that token is not chosen
+ * yet, scores at least tau times the seed (compared in fp64) and the budget
+ * lasts.  tau > 1 with positive scores gives kvfix_select_topb's set.
+ * scores: device fp32 [n_rows][n].  idx: device int32 [n_rows][b],
+ * ascending.  mask: as kvfix_select_topb.  0 <= b <= n; tau not NaN.
+ * KVFIX_ERR_UNSUPPORTED when the seed sort (8 bytes per seed, b rounded up
+ * to a power of two), the seeds (4 bytes each) and the chosen-token bitmap
+ * (n/8 bytes) exceed one block's LDS (with 160 KiB: b <= 8192 for n up to
+ * about 500 000).  The scores are staged in LDS as well when they fit. */
+kvfix_status kvfix_select_grow(const float* scores, int32_t n_rows, int32_t n, int32_t b,
+                               double tau, int32_t* idx, uint32_t* mask, void* stream);
+
+/* ---------------------------------------------------------------------------
  * a5. Probe mean residual, re-estimated per layer, and fresh scatter.
- *   mu[l][s][h][:] = (1/b) sum_{k<b} ( fresh_k - align(reuse_j) - A_j B ),  j = idx[s][k]
+ *   mu[l][s][h][:] = (1/m) sum_{k : j in [0, n)} ( fresh_k - align(reuse_j) - A_j B ),
+ *   j = idx[s][k],  m = the number of k < b with j in [0, n_tokens)
+ * An index outside [0, n_tokens) is padding, not a probe: a layout whose
+ * row count depends on the data (whole chunks, the last one short) pads its
+ * fixed-width list with -1.  m == 0 (b == 0, or padding only) gives mu = 0.
  * fresh_k is fresh row j (fresh_by_slot == 0) or fresh row k (fresh_by_slot
- * == 1: fresh holds only the probe rows, in idx order).  If out != NULL the
- * fresh rows are also copied into out at the probe positions (exact copy).
- * b == 0 gives mu = 0.  [AKS step 3 and the equation for mu-hat; KVCMAS eq. 7]
+ * == 1: fresh holds the probe rows by slot, in idx order).  If out != NULL
+ * the fresh rows are also copied into out at the probe positions (exact
+ * copy).  [AKS step 3 and the equation for mu-hat (the mean over the probe
+ * set); KVCMAS eq. 7]
  * mu: device fp32 [n_layers][n_segs][n_heads][head_dim], contiguous.
- * idx: device int32 [n_segs][b]; an index outside [0, n_tokens) is skipped
- * (device data is not checked on the host).
+ * idx: device int32 [n_segs][b]; b >= 0 is the list width and may exceed
+ * n_tokens (device data is not checked on the host).
  * out may alias reuse (in-place correction).
  * ws: device workspace of kvfix_fit_mean_workspace(...) bytes, 16-byte
  * aligned (fp64 partial sums of 256-probe slices); KVFIX_ERR_ARG when it is

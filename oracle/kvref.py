@@ -290,18 +290,21 @@ def chunk_means(scores: np.ndarray, B: int) -> np.ndarray:
 def expand_chunks(chunk_idx: np.ndarray, n: int, B: int):
     """The rows of the chosen chunks.
 
-    chunk_idx: int32 [rows][c], ascending (as select_topb returns it).
-    Returns (idx int32 [rows][c*B]: the rows in ascending order, then -1 for
+    chunk_idx: int32 [rows][c], ascending (as select_topb returns it); an id
+    outside [0, ceil(n/B)) names no chunk and lists no rows.  Returns (idx int32 [rows][c*B]: the rows in ascending order, then -1 for
     the rows a short last chunk does not have; counts int32 [rows]; mask
     uint32 [rows][ceil(n/32)]).
     """
     rows, c = chunk_idx.shape
+    nc = -(-n // B)
     idx = np.full((rows, c * B), -1, dtype=np.int32)
     counts = np.zeros(rows, dtype=np.int32)
     mask = np.zeros((rows, (n + 31) // 32), dtype=np.uint32)
     for r in range(rows):
         k = 0
         for ci in chunk_idx[r]:
+            if not 0 <= int(ci) < nc:          # not a chunk of the row: no rows
+                continue
             for j in range(int(ci) * B, min((int(ci) + 1) * B, n)):
                 idx[r, k] = j
                 mask[r, j // 32] |= np.uint32(1) << np.uint32(j % 32)

@@ -220,6 +220,108 @@ def test_c4_qwen25_14b_draft_full_size():
             log("c4 full: layer", l, p, "max rel err", e)
 
 
+def test_c4_bcr_layouts_full_size():
+    """The BCR layouts on the Qwen-14B-shaped draft scores (32768 tokens):
+    64-token chunks at r = 0.1 (51 chunks), the coin at the same budget, and
+    grown spans (b = 3277, tau = 0.25), each bit-exact against the oracle on
+    the GPU's scores; then the chunk-layout and grow-layout corrections of all
+    48 layers, checked on sampled layers."""
+    from helpers import to_np, torch_rotate, assert_values, rel_err
+    from oracle import kvref as K
+    from synthetic import draw_correction, draw_draft_queries, draw_deltas
+    from synthetic.workloads import draw_coin_keys
+    import cross_context_kv_amd.kvfix as kv
+    from cross_context_kv_amd.kvfix import Plane
+    cfg = CONFIGS["c4"]
+    L, S, H, Hq, T, n, hd, b = (cfg.n_layers, cfg.n_segs, cfg.n_kv_heads, cfg.n_q_heads,
+                                cfg.n_draft, cfg.n_tokens, cfg.head_dim, cfg.b)
+    B, tau = 64, 0.25
+    dev = "cuda"
+    deltas = [int(d) for d in draw_deltas(cfg).tolist()]
+    reuse = {p: torch.empty(L, S, H, n, hd, dtype=torch.bfloat16, device=dev) for p in "kv"}
+    fresh = {p: torch.empty(L, S, H, n, hd, dtype=torch.bfloat16, device=dev) for p in "kv"}
+    log("c4 bcr: drawing 48 layers")
+    for l in range(L):
+        raw = draw_correction(cfg, dev, layers=[l])
+        reuse["k"][l] = torch_rotate(raw["x_k"][0], [-d for d in deltas], cfg.theta).to(
+            torch.bfloat16)
+        reuse["v"][l] = raw["x_v"][0].to(torch.bfloat16)
+        fresh["k"][l] = raw["fresh_k"][0]
+        fresh["v"][l] = raw["fresh_v"][0]
+        del raw
+    q = draw_draft_queries(cfg, dev)[None].contiguous()
+    d_t = torch.tensor(deltas, dtype=torch.int64, device=dev)
+    ws = torch.empty(kv.kvfix_score_draft_workspace(S, L, cfg.first_layer, Hq, T, n) // 4 + 64,
+                     dtype=torch.float32, device=dev)
+    scores = torch.empty(S, n, dtype=torch.float32, device=dev)
+    log("c4 bcr: draft score and the three layouts")
+    kv.kvfix_score_draft(q, Plane.dense(reuse["k"]), cfg.first_layer, d_t, cfg.theta, scores, ws)
+    nc = n // B
+    c = kv.kvfix_chunk_budget(n, B, 1, 10, kv.BUDGET_SKIP)
+    assert c == K.chunk_budget(n, B, 1, 10, "alg1") == 51
+    words = (n + 31) // 32
+
+    def chunk_rows(keys):
+        cidx = torch.empty(S, c, dtype=torch.int32, device=dev)
+        cmask = torch.empty(S, (nc + 31) // 32, dtype=torch.int32, device=dev)
+        kv.kvfix_select_topb(keys, c, cidx, cmask)
+        idx = torch.empty(S, c * B, dtype=torch.int32, device=dev)
+        counts = torch.empty(S, dtype=torch.int32, device=dev)
+        mask = torch.empty(S, words, dtype=torch.int32, device=dev)
+        kv.kvfix_expand_chunks(cidx, n, B, idx, counts, mask)
+        return idx, counts, mask
+
+    means = torch.empty(S, nc, dtype=torch.float32, device=dev)
+    kv.kvfix_chunk_means(scores, B, means)
+    layouts = {"chunk": chunk_rows(means)}
+    keys = draw_coin_keys(cfg.seed, S, nc, dev)
+    layouts["coin"] = chunk_rows(keys)
+    g_idx = torch.empty(S, b, dtype=torch.int32, device=dev)
+    g_mask = torch.empty(S, words, dtype=torch.int32, device=dev)
+    kv.kvfix_select_grow(scores, b, tau, g_idx, g_mask)
+    torch.cuda.synchronize()
+    g_scores = scores.cpu().numpy()
+    o_means = K.chunk_means(g_scores, B)
+    assert np.array_equal(means.cpu().numpy().view(np.uint32), o_means.view(np.uint32))
+    for name, ks in (("chunk", o_means), ("coin", keys.cpu().numpy())):
+        o = K.expand_chunks(K.select_topb(ks, c)[0], n, B)
+        got = [t.cpu().numpy() for t in layouts[name]]
+        got[2] = got[2].view(np.uint32)
+        for a, e in zip(got, o):
+            assert np.array_equal(a, e), name
+        log("c4 bcr:", name, "rows", int(got[1][0]))
+    o_gi, o_gm = K.select_grow(g_scores, b, tau)
+    assert np.array_equal(g_idx.cpu().numpy(), o_gi)
+    assert np.array_equal(g_mask.cpu().numpy().view(np.uint32), o_gm)
+    spans = int(np.sum(np.diff(o_gi[0]) > 1)) + 1
+    log("c4 bcr: grow spans", spans)
+
+    for name, idx, width, mask in (("chunk", layouts["chunk"][0], c * B, layouts["chunk"][2]),
+                                   ("grow", g_idx, b, g_mask)):
+        out = {p: torch.empty_like(reuse[p]) for p in "kv"}
+        mu = torch.empty(2, L, S, H, hd, dtype=torch.float32, device=dev)
+        log("c4 bcr:", name, "correction of 48 layers")
+        for pi, p in enumerate("kv"):
+            d = d_t if p == "k" else None
+            kv.kvfix_fit_mean(Plane.dense(fresh[p]), Plane.dense(reuse[p]), Plane.dense(out[p]),
+                              idx, width, mu[pi], d, cfg.theta)
+            kv.kvfix_apply(Plane.dense(reuse[p]), Plane.dense(out[p]), mask, mu[pi], None, 0.0,
+                           1.0, d, cfg.theta)
+        torch.cuda.synchronize()
+        h_idx = idx.cpu().numpy()
+        h_mask = mask.cpu().numpy().view(np.uint32)
+        for l, p in ((0, "k"), (L - 1, "v")) if name == "chunk" else ((23, "k"),):
+            pi = "kv".index(p)
+            rope = (deltas, cfg.theta, "half") if p == "k" else (None, 0.0, "half")
+            fr, ru = to_np(fresh[p][l:l + 1]), to_np(reuse[p][l:l + 1])
+            o_out, o_mu = K.correct(fr, ru, "bf16", h_idx, h_mask, None, 0.0, 1.0, None, None,
+                                    rope[0], rope[1], rope[2])
+            assert rel_err(mu[pi, l:l + 1].cpu().numpy(), o_mu, "f32") <= 1e-5, (name, l, p)
+            e = assert_values(to_np(out[p][l:l + 1]), o_out, "bf16", f"{name} layer {l} {p}")
+            log("c4 bcr:", name, "layer", l, p, "max rel err", e)
+        del out
+
+
 # ----------------------------------------------------------------------------
 # Collective round: 16 agents x 32 layers x 8192 tokens, block-sparse diffs
 # against one master, then the fused restore of all 16 caches.

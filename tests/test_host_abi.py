@@ -109,16 +109,19 @@ def test_call_level_validation():
     assert L.kvfix_select_topb(sc, 1, 10, 11, ctypes.c_void_p(512), ctypes.c_void_p(512), None) == 1
     assert L.kvfix_select_topb(sc, 1, 10, -1, ctypes.c_void_p(512), ctypes.c_void_p(512), None) == 1
     assert L.kvfix_select_topb(None, 1, 10, 3, ctypes.c_void_p(512), ctypes.c_void_p(512), None) == 1
-    # fit_mean: b within n, idx needed when b > 0, fresh rows by slot need >= b rows
+    # fit_mean: b (the list width) >= 0, idx needed when b > 0, fresh rows by
+    # slot need >= b rows
     assert L.kvfix_fit_mean(R(p), 0, R(p), None, None, 3, None, None, mu, None, 0, None) == 1
-    assert L.kvfix_fit_mean(R(p), 0, R(p), None, ctypes.c_void_p(512), 65, None, None, mu, None, 0, None) == 1
+    assert L.kvfix_fit_mean(R(p), 0, R(p), None, ctypes.c_void_p(512), -1, None, None, mu, None, 0, None) == 1
     assert L.kvfix_fit_mean(R(plane(n_tokens=2)), 1, R(p), None, ctypes.c_void_p(512), 3, None,
                             None, mu, None, 0, None) == 1
     assert L.kvfix_fit_mean(R(plane(n_tokens=3)), 0, R(p), None, ctypes.c_void_p(512), 3, None,
                             None, mu, None, 0, None) == 1
     # the workspace must hold every slice's partial sums
     need = L.kvfix_fit_mean_workspace(2, 1, 2, 128, 3)
-    assert need == 2 * 1 * 2 * 1 * (128 + 8) * 8
+    assert need == 2 * 1 * 2 * 1 * (128 + 8 + 1) * 8      # sums, rank-state sums, member count
+    # a list wider than n (padded whole chunks) is accepted
+    assert L.kvfix_fit_mean_workspace(2, 1, 2, 128, 100) == need
     assert L.kvfix_fit_mean(R(p), 0, R(p), None, ctypes.c_void_p(512), 3, None, None, mu,
                             ctypes.c_void_p(4096), need - 8, None) == 1
     assert L.kvfix_fit_mean(R(p), 0, R(p), None, ctypes.c_void_p(512), 3, None, None, mu,
