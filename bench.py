@@ -23,8 +23,12 @@ rows, plus states, scores and indices), the dominant kernel's roofline from
 events recorded around its launches, and the CPU oracle timed on a bounded
 sample of the same workload.
 
+  c4 takes --layout: rows (top b), chunk (BCR-chunk: 64-token chunks by mean
+  draft mass), coin (the same budget in random chunks, no draft) or grow
+  (BCR-grow spans, tau 0.25).
+
   python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload c2]
-                  [--no-cpu-baseline]
+                  [--layout rows] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -364,20 +368,51 @@ class C5(Correction):
 class C4(Workload):
     name = "c4"
     kernel_tag = "apply"
+    # probe layout: top-b rows, whole 64-token chunks (BCR-chunk), chunks by
+    # coin at the same budget (no draft), or grown spans (BCR-grow)
+    layout = "rows"
+    CHUNK, TAU, RHO = 64, 0.25, (1, 10)
+    LAYOUT_TEXT = {
+        "rows": "top b=3277 rows (r=0.1) of the draft mass",
+        "chunk": "BCR-chunk: 64-token chunks by mean draft mass, round(0.1 n / 64) = 51 chunks",
+        "coin": "coin control: 51 random 64-token chunks (no draft)",
+        "grow": "BCR-grow: b=3277 rows in spans grown while a neighbour scores >= 0.25 x seed",
+    }
 
     def workload_text(self):
         return ("c4_qwen25_14b_draft: 48 layers x 8 KV heads (40 query heads) x 32768 tokens x "
-                "hd 128 bf16; draft mass of 2 query tokens over layers 1-47, b=3277 (r=0.1) for "
-                "both planes, w=1, no rank state, theta 1e6")
+                "hd 128 bf16; draft mass of 2 query tokens over layers 1-47; probes: "
+                f"{self.LAYOUT_TEXT[self.layout]}, for both planes; w=1, no rank state, theta 1e6")
+
+    def n_chunks(self):
+        return -(-self.cfg.n_tokens // self.CHUNK)
+
+    def chunk_budget(self):
+        from oracle import kvref as K
+        return K.chunk_budget(self.cfg.n_tokens, self.CHUNK, *self.RHO, "alg1")
+
+    def probe_rows(self):
+        """Probe rows per segment of the layout (whole chunks: c * 64 here,
+        the segment length being a multiple of 64)."""
+        if self.layout in ("chunk", "coin"):
+            return min(self.chunk_budget() * self.CHUNK, self.cfg.n_tokens)
+        return self.cfg.b
 
     def alg_bytes(self):
         c = self.cfg
-        L, S, H, Hq, T, n, hd, b = (c.n_layers, c.n_segs, c.n_kv_heads, c.n_q_heads, c.n_draft,
-                                    c.n_tokens, c.head_dim, c.b)
+        L, S, H, Hq, T, n, hd = (c.n_layers, c.n_segs, c.n_kv_heads, c.n_q_heads, c.n_draft,
+                                 c.n_tokens, c.head_dim)
+        b = self.probe_rows()
         row = hd * 2
         words = (n + 31) // 32
-        draft = (L - c.first_layer) * S * H * n * row + L * Hq * T * row * S + S * n * 4
-        select = S * n * 4 + S * b * 4 + S * words * 4
+        draft = 0 if self.layout == "coin" else (
+            (L - c.first_layer) * S * H * n * row + L * Hq * T * row * S + S * n * 4)
+        if self.layout in ("chunk", "coin"):
+            nc, ch = self.n_chunks(), self.chunk_budget()
+            select = (S * n * 4 if self.layout == "chunk" else 0) + 2 * S * nc * 4 + \
+                S * ch * 4 + S * (nc + 31) // 32 * 4 + S * (ch * self.CHUNK * 4 + words * 4 + 4)
+        else:
+            select = S * n * 4 + S * b * 4 + S * words * 4
         fit = 2 * (L * S * H * b * 3 * row + L * S * H * hd * 4 + S * b * 4)
         apply_one = L * S * H * (n - b) * 2 * row + L * S * H * hd * 4 + S * words * 4
         return {"draft": draft, "select": select, "fit_mean": fit, "apply": 2 * apply_one,
@@ -387,8 +422,10 @@ class C4(Workload):
     def build(self):
         torch, kv, c = self.torch, self.kv, self.cfg
         from synthetic import draw_correction, draw_deltas, draw_draft_queries
-        L, S, H, Hq, T, n, hd, b = (c.n_layers, c.n_segs, c.n_kv_heads, c.n_q_heads, c.n_draft,
-                                    c.n_tokens, c.head_dim, c.b)
+        from synthetic.workloads import draw_coin_keys
+        L, S, H, Hq, T, n, hd = (c.n_layers, c.n_segs, c.n_kv_heads, c.n_q_heads, c.n_draft,
+                                 c.n_tokens, c.head_dim)
+        b = self.probe_rows()
         t = {"delta": draw_deltas(c).to("cuda")}
         for p in "kv":
             t["reuse_" + p] = torch.empty(L, S, H, n, hd, dtype=torch.bfloat16, device="cuda")
@@ -408,23 +445,47 @@ class C4(Workload):
         t["scores"] = torch.empty(S, n, dtype=torch.float32, device="cuda")
         t["idx"] = torch.empty(S, b, dtype=torch.int32, device="cuda")
         t["mask"] = torch.empty(S, (n + 31) // 32, dtype=torch.int32, device="cuda")
+        if self.layout in ("chunk", "coin"):
+            nc, ch = self.n_chunks(), self.chunk_budget()
+            t["means"] = torch.empty(S, nc, dtype=torch.float32, device="cuda")
+            t["cidx"] = torch.empty(S, ch, dtype=torch.int32, device="cuda")
+            t["cmask"] = torch.empty(S, (nc + 31) // 32, dtype=torch.int32, device="cuda")
+            t["counts"] = torch.empty(S, dtype=torch.int32, device="cuda")
+            t["idx"] = torch.empty(S, ch * self.CHUNK, dtype=torch.int32, device="cuda")
+            t["keys"] = draw_coin_keys(c.seed, S, nc, "cuda")
         t["mu"] = torch.empty(2, L, S, H, hd, dtype=torch.float32, device="cuda")
-        t["ws_fit"] = torch.empty(kv.kvfix_fit_mean_workspace(L, S, H, hd, b), dtype=torch.uint8,
-                                  device="cuda")
+        t["ws_fit"] = torch.empty(kv.kvfix_fit_mean_workspace(L, S, H, hd, t["idx"].shape[1]),
+                                  dtype=torch.uint8, device="cuda")
         P = kv.Plane.dense
         self.planes = {k: P(t[k]) for k in ("reuse_k", "reuse_v", "fresh_k", "fresh_v", "out_k",
                                             "out_v")}
         self.t = t
         torch.cuda.synchronize()
 
+    def select(self):
+        kv, t, c = self.kv, self.t, self.cfg
+        if self.layout == "rows":
+            kv.kvfix_select_topb(t["scores"], c.b, t["idx"], t["mask"])
+        elif self.layout == "grow":
+            kv.kvfix_select_grow(t["scores"], c.b, self.TAU, t["idx"], t["mask"])
+        else:
+            if self.layout == "chunk":
+                kv.kvfix_chunk_means(t["scores"], self.CHUNK, t["means"])
+            keys = t["means"] if self.layout == "chunk" else t["keys"]
+            kv.kvfix_select_topb(keys, t["cidx"].shape[1], t["cidx"], t["cmask"])
+            kv.kvfix_expand_chunks(t["cidx"], c.n_tokens, self.CHUNK, t["idx"], t["counts"],
+                                   t["mask"])
+
     def step(self):
         kv, t, c, P = self.kv, self.t, self.cfg, self.planes
-        kv.kvfix_score_draft(t["q"], P["reuse_k"], c.first_layer, t["delta"], c.theta,
-                             t["scores"], t["ws_draft"])
-        kv.kvfix_select_topb(t["scores"], c.b, t["idx"], t["mask"])
+        if self.layout != "coin":
+            kv.kvfix_score_draft(t["q"], P["reuse_k"], c.first_layer, t["delta"], c.theta,
+                                 t["scores"], t["ws_draft"])
+        self.select()
+        width = t["idx"].shape[1]
         for i, p in enumerate("kv"):
             d = t["delta"] if p == "k" else None
-            kv.kvfix_fit_mean(P["fresh_" + p], P["reuse_" + p], P["out_" + p], t["idx"], c.b,
+            kv.kvfix_fit_mean(P["fresh_" + p], P["reuse_" + p], P["out_" + p], t["idx"], width,
                               t["mu"][i], d, c.theta, ws=t["ws_fit"])
         for i, p in enumerate("kv"):
             d = t["delta"] if p == "k" else None
@@ -433,8 +494,8 @@ class C4(Workload):
                                1.0, d, c.theta)
 
     def cpu_baseline(self, np):
-        """The oracle on a bounded sample: the draft mass over layers 1-3,
-        selection, and fit + apply of K and V on layers 0-3."""
+        """The oracle on a bounded sample: the draft mass over layers 1-3, the
+        same probe layout, and fit + apply of K and V on layers 0-3."""
         torch, c, t = self.torch, self.cfg, self.t
         from oracle import kvref as K
         L4 = 4
@@ -442,19 +503,31 @@ class C4(Workload):
                                                        "fresh_v")}
         q = host(t["q"][0, :L4], torch, np)
         deltas = [int(v) for v in t["delta"].tolist()]
+        keys = host(t["keys"], torch, np) if "keys" in t else None
 
         def run():
-            s = K.score_draft(q, data["reuse_k"], deltas, c.theta, c.first_layer)
-            idx, mask = K.select_topb(s, c.b)
+            s = None if self.layout == "coin" else K.score_draft(q, data["reuse_k"], deltas,
+                                                                  c.theta, c.first_layer)
+            if self.layout == "rows":
+                idx, mask = K.select_topb(s, c.b)
+            elif self.layout == "grow":
+                idx, mask = K.select_grow(s, c.b, self.TAU)
+            else:
+                ks = K.chunk_means(s, self.CHUNK) if self.layout == "chunk" else keys
+                idx, _, mask = K.expand_chunks(K.select_topb(ks, self.chunk_budget())[0],
+                                               c.n_tokens, self.CHUNK)
             for p in "kv":
                 K.correct(data["fresh_" + p], data["reuse_" + p], "bf16", idx, mask, None, 0.0,
                           1.0, None, None, deltas if p == "k" else None, c.theta)
 
         dt = timed_oracle(run, 1)
-        nbytes = C4.alg_bytes(type("X", (), {"cfg": c.replace(n_layers=L4)})())["total"]
+        sub = C4.__new__(C4)
+        sub.cfg, sub.layout = c.replace(n_layers=L4), self.layout
+        nbytes = sub.alg_bytes()["total"]
+        draft = "no draft; " if self.layout == "coin" else "draft mass over layers 1-3; "
         return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-                "sample": f"the whole step on layers 0-3 (4 of {c.n_layers}; draft mass over "
-                          f"layers 1-3) of the same input bytes ({nbytes / 1e6:.1f} MB "
+                "sample": f"the whole step on layers 0-3 (4 of {c.n_layers}; {draft}the same "
+                          f"probe layout) of the same input bytes ({nbytes / 1e6:.1f} MB "
                           f"algorithmic), one run of {dt:.1f} s, numpy fp64, one thread"}
 
 
@@ -582,8 +655,13 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c2", choices=sorted(Workload.ALL))
+    ap.add_argument("--layout", default="rows", choices=sorted(C4.LAYOUT_TEXT),
+                    help="probe layout of the c4 workload (BCR layouts and the coin control)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
+    if args.layout != "rows" and args.workload != "c4":
+        print("--layout applies to the c4 workload only", file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
               "(the correction path is sharded by segment/layer/head without exchange; "
@@ -596,6 +674,8 @@ def main():
     from synthetic import CONFIGS
     kv.lib()                          # fails loudly without the built library
     w = Workload.ALL[args.workload](CONFIGS[args.workload], torch, kv)
+    if args.layout != "rows":
+        w.layout = args.layout
     w.build()
     for _ in range(args.warmup):
         w.step()

@@ -16,13 +16,14 @@
 // is one of the b best rows (all rows ranked above a seed are taken already,
 // and fewer than b are taken), so the block finds the b best with the radix
 // search of the top-b selection, sorts them best first in LDS (bitonic, 64-bit
-// keys: score descending, then index ascending), and stages the row's scores
-// and a chosen-row bitmap in LDS.  One wave then walks the seeds.  A seed's
-// span holds a 64-row window of candidate rows on each side in registers
-// (a lane per row: its score, and whether it is free and scores at least
-// tau times the seed); each step of the span compares the two window heads
-// with readlane on block-uniform indices, so the walk costs one LDS round
-// trip per seed and per 64 rows rather than per row.
+// keys: score descending, then index ascending), flags the seeds that can
+// only span themselves (both neighbours below tau times the seed), and stages
+// the row's scores and a chosen-row bitmap in LDS.  One wave then walks the
+// seeds: a run of flagged seeds is taken 64 at a time (a bit test per lane
+// and a prefix count against the budget); a seed that may grow holds a
+// 64-row window of candidate rows on each side in registers and takes whole
+// runs of rows per comparison (see grow_walk), so a long span costs a few
+// ballots per 64 rows and a short one a single LDS round trip.
 #include <type_traits>
 
 #include "common.h"
@@ -158,61 +159,137 @@ __device__ __forceinline__ void mark_rows(uint32_t* bits, int lo, int hi, int la
   }
 }
 
+// Bit 31 of a seed entry: the seed spans itself alone whatever is chosen
+// around it (both neighbours score below tau times the seed, or lie outside
+// the row).
+constexpr uint32_t kSingle = 0x80000000u;
+// Steps a span takes one row at a time before it switches to whole runs.
+constexpr int kRawSteps = 16;
+
+__device__ __forceinline__ int ones_from(uint64_t m, int i) {   // consecutive set bits from bit i
+  const uint64_t inv = ~(m >> i);
+  return inv == 0 ? kWave - i : min((int)__builtin_ctzll(inv), kWave - i);
+}
+
+// One side of a growing span: a window of the 64 rows next to it (lane k:
+// the k-th row outward), whether each may join (a run of ones ending at the
+// first row that may not), how many are taken, and the running minimum of
+// the side's scores (prefix minima, computed when both sides are alive).
+struct Side {
+  float v, pm;
+  uint64_t ok;
+  int i;
+  float carry;               // minimum of the side's rows before this window
+  bool have_pm;
+};
+
 // The greedy walk over the seeds (one wave; every branch is wave-uniform).
+//
+// A span takes, at each step, the higher of the two rows just outside it
+// (the left one on a tie).  While both sides can grow this is the merge of
+// the two sides' sequences of scores; taking the larger head each time is
+// the same as merging the sequences' running minima (non-increasing), with
+// ties to the left, because a row above its side's running minimum follows
+// the row that set that minimum without the other side's head changing.  So
+// each comparison takes a whole run of rows: from the left side every row
+// whose running minimum is >= the right head, or from the right side every
+// row whose running minimum is > the left head.
 __device__ __forceinline__ void grow_walk(const float* A, uint32_t* bits,
-                                          const int32_t* seeds, int n, int b, double tau,
+                                          const uint32_t* seeds, int n, int b, double tau,
                                           int lane) {
+  const uint64_t below = (1ull << lane) - 1ull;
   int left = b;
   for (int k0 = 0; k0 < b && left > 0; k0 += kWave) {
-    const int mine = k0 + lane < b ? seeds[k0 + lane] : 0;
     const int kn = min(kWave, b - k0);
-    for (int q = 0; q < kn && left > 0; ++q) {
-      const int s = __builtin_amdgcn_readlane(mine, q);
+    const uint32_t e = lane < kn ? seeds[k0 + lane] : kSingle;
+    const int my_s = (int)(e & ~kSingle);
+    const float my_a = lane < kn ? A[my_s] : 0.0f;
+    const uint64_t singles = __ballot((e & kSingle) != 0u);
+    int q = 0;
+    while (q < kn && left > 0) {
+      // seeds q .. p-1 span themselves: take the ones not chosen yet, in order
+      const int p = min(kn, q + ones_from(singles, q));
+      if (p > q) {
+        const bool mine = lane >= q && lane < p;
+        const bool free_row = mine && !((bits[my_s >> 5] >> (my_s & 31)) & 1u);
+        const uint64_t fr = __ballot(free_row);
+        const bool take = free_row && __popcll(fr & below) < left;
+        if (take) atomicOr(&bits[my_s >> 5], 1u << (my_s & 31));
+        left -= min(__popcll(fr), left);
+        q = p;
+        continue;
+      }
+      // seed q may grow; its windows are read with its chosen bit (one round trip)
+      const int s = __builtin_amdgcn_readlane(my_s, q);
+      const double thr = tau * (double)lane_float(my_a, q);
+      ++q;
+      Side L, R;
+      auto load = [&](Side& S, int first, int dir) {
+        const int j = first + dir * lane;
+        bool ok = j >= 0 && j < n;
+        const float v = ok ? A[j] : 0.0f;
+        ok = ok && !((bits[j >> 5] >> (j & 31)) & 1u) && (double)v >= thr;
+        S.v = v;
+        S.ok = __ballot(ok);
+        S.i = 0;
+        S.have_pm = false;
+      };
+      // running minima of a side from its current head on (rows taken
+      // before the head are not part of the sequence still to merge)
+      auto prefix_min = [&](Side& S) {
+        if (S.have_pm) return;
+        float m = lane < S.i ? __int_as_float(0x7f800000) : S.v;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+          const float y = __shfl_up(m, off);
+          if (lane >= off) m = fminf(m, y);
+        }
+        S.pm = fminf(m, S.carry);
+        S.have_pm = true;
+      };
+      load(R, s + 1, 1);
+      load(L, s - 1, -1);
       const uint32_t wbits = __builtin_amdgcn_readfirstlane(bits[s >> 5]);
       if ((wbits >> (s & 31)) & 1u) continue;      // taken by an earlier span
-      const double thr = tau * (double)__int_as_float(__builtin_amdgcn_readfirstlane(
-                                   __float_as_int(A[s])));
       --left;
-      int lo = s, hi = s;
-      // window of the rows right of hi (lane k: row hi + 1 + k) and left of
-      // lo (lane k: row lo - 1 - k): score, and whether the row may join
-      float vr = 0.0f, vl = 0.0f;
-      uint64_t okr = 0, okl = 0;
-      int ir = 0, il = 0;
-      auto load_right = [&] {
-        const int j = hi + 1 + lane;
-        bool ok = j < n;
-        const float v = ok ? A[j] : 0.0f;
-        ok = ok && !((bits[j >> 5] >> (j & 31)) & 1u) && (double)v >= thr;
-        vr = v;
-        okr = __ballot(ok);
-        ir = 0;
-      };
-      auto load_left = [&] {
-        const int j = lo - 1 - lane;
-        bool ok = j >= 0;
-        const float v = ok ? A[j] : 0.0f;
-        ok = ok && !((bits[j >> 5] >> (j & 31)) & 1u) && (double)v >= thr;
-        vl = v;
-        okl = __ballot(ok);
-        il = 0;
-      };
-      if (left > 0) {
-        load_right();
-        load_left();
-      }
+      int lo = s, hi = s, raw = 0;
+      bool runs = false;
+      L.carry = R.carry = __int_as_float(0x7f800000);   // +inf
       while (left > 0) {
-        const bool r_ok = (okr >> ir) & 1u, l_ok = (okl >> il) & 1u;
-        if (!r_ok && !l_ok) break;
-        const bool take_left = l_ok && (!r_ok || lane_float(vl, il) >= lane_float(vr, ir));
-        if (take_left) {
-          --lo;
-          if (++il == kWave) load_left();
+        const bool la = (L.ok >> L.i) & 1u, ra = (R.ok >> R.i) & 1u;
+        if (!la && !ra) break;
+        bool take_left;
+        int k;
+        if (la && ra && !runs && raw < kRawSteps) {
+          // the first steps of a span one row at a time, on the raw scores
+          take_left = lane_float(L.v, L.i) >= lane_float(R.v, R.i);
+          k = 1;
+          ++raw;
+        } else if (la && ra) {
+          if (!runs) {                                 // from here on: whole runs
+            runs = true;
+            L.have_pm = R.have_pm = false;
+          }
+          prefix_min(L);
+          prefix_min(R);
+          const float xh = lane_float(L.pm, L.i), yh = lane_float(R.pm, R.i);
+          take_left = xh >= yh;
+          k = take_left ? ones_from(__ballot(L.pm >= yh) & L.ok, L.i)
+                        : ones_from(__ballot(R.pm > xh) & R.ok, R.i);
         } else {
-          ++hi;
-          if (++ir == kWave) load_right();
+          take_left = la;                              // one side left: take its run
+          k = take_left ? ones_from(L.ok, L.i) : ones_from(R.ok, R.i);
         }
-        --left;
+        k = min(k, left);
+        left -= k;
+        Side& S = take_left ? L : R;
+        if (take_left) lo -= k; else hi += k;
+        S.i += k;
+        if (S.i == kWave) {                            // window used up: the next 64 rows
+          const float carry = S.have_pm ? lane_float(S.pm, kWave - 1) : S.carry;
+          if (take_left) load(L, lo - 1, -1); else load(R, hi + 1, 1);
+          S.carry = carry;
+        }
       }
       mark_rows(bits, lo, hi, lane);
     }
@@ -225,13 +302,14 @@ __global__ __launch_bounds__(kSelBlock) void select_grow_kernel(const float* __r
                                                                 uint32_t* __restrict__ mask,
                                                                 int words, GrowShape G) {
   extern __shared__ __attribute__((aligned(16))) unsigned char glds[];
-  __shared__ uint32_t scan[160];
-  __shared__ uint32_t sh[2];
+  __shared__ uint64_t scan64[160];
+  __shared__ uint32_t ctab[2 * kCompactTab];
+  __shared__ uint32_t sh[3];
   uint32_t* hist = reinterpret_cast<uint32_t*>(glds);
   uint64_t* keys = reinterpret_cast<uint64_t*>(glds);
   float* s_scores = reinterpret_cast<float*>(glds);
   uint32_t* bits = reinterpret_cast<uint32_t*>(glds + G.a_bytes);
-  int32_t* seeds = reinterpret_cast<int32_t*>(glds + G.a_bytes + align16u((uint64_t)words * 4));
+  uint32_t* seeds = reinterpret_cast<uint32_t*>(glds + G.a_bytes + align16u((uint64_t)words * 4));
   const int row = blockIdx.x;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const float* sc = scores + (int64_t)row * n;
@@ -248,33 +326,13 @@ __global__ __launch_bounds__(kSelBlock) void select_grow_kernel(const float* __r
       key[q] = j < n ? order_key(sc[j]) : 0u;
     }
   }
-  uint32_t T, need_eq;
-  radix_threshold(key, in_regs, sc, n, b, hist, sh, &T, &need_eq);
-  uint32_t eq_base = 0, sel_base = 0;
-  const int n_tiles = (n + kSelBlock - 1) / kSelBlock;
-  for (int c = 0; c < n_tiles; ++c) {
-    const int j = c * kSelBlock + t;
-    uint32_t k = 0;
-    if (j < n) {
-      if (in_regs) {
-#pragma unroll
-        for (int q = 0; q < kSelRegKeys; ++q)
-          if (q == c) k = key[q];
-      } else {
-        k = order_key(sc[j]);
-      }
-    }
-    const bool valid = j < n && b > 0;
-    const uint32_t is_eq = valid && k == T;
-    uint32_t tot;
-    const uint32_t eq_rank = eq_base + block_exclusive_scan(is_eq, scan, &tot);
-    eq_base += tot;
-    const uint32_t sel = valid && (k > T || (is_eq && eq_rank < need_eq));
-    const uint32_t pos = sel_base + block_exclusive_scan(sel, scan, &tot);
-    sel_base += tot;
-    // ascending sort key: best score first, then the lower index
-    if (sel && pos < (uint32_t)b) keys[pos] = ((uint64_t)(~k) << 32) | (uint32_t)j;
-  }
+  uint32_t T, need_eq, eq_total;
+  radix_threshold(key, in_regs, sc, n, b, hist, sh, &T, &need_eq, &eq_total);
+  compact_topb(key, in_regs, sc, n, b, T, need_eq, eq_total, ctab,
+               [&](uint32_t pos, int j, uint32_t k) {   // best score first, then the lower index
+                 keys[pos] = ((uint64_t)(~k) << 32) | (uint32_t)j;
+               },
+               [](int, uint32_t) {});
   for (int i = b + t; i < G.P; i += kSelBlock) keys[i] = ~0ull;
   __syncthreads();
 
@@ -294,7 +352,13 @@ __global__ __launch_bounds__(kSelBlock) void select_grow_kernel(const float* __r
       __syncthreads();
     }
   }
-  for (int i = t; i < b; i += kSelBlock) seeds[i] = (int32_t)(uint32_t)(keys[i] & 0xFFFFFFFFull);
+  for (int i = t; i < b; i += kSelBlock) {
+    const int sd = (int)(uint32_t)(keys[i] & 0xFFFFFFFFull);
+    const double thr = tau * (double)sc[sd];
+    const bool grows = (sd > 0 && (double)sc[sd - 1] >= thr) ||
+                       (sd + 1 < n && (double)sc[sd + 1] >= thr);
+    seeds[i] = (uint32_t)sd | (grows ? 0u : kSingle);
+  }
   __syncthreads();
 
   // 3. stage the scores (the keys are dead), clear the bitmap
@@ -304,19 +368,26 @@ __global__ __launch_bounds__(kSelBlock) void select_grow_kernel(const float* __r
   __syncthreads();
 
   // 4. the walk
-  if (wave == 0) grow_walk(G.scores_in_lds ? s_scores : sc, bits, seeds, n, b, tau, lane);
+  // (two call sites, so that each reads its scores through a typed pointer:
+  // LDS or global, never a generic one)
+  if (wave == 0) {
+    if (G.scores_in_lds)
+      grow_walk(s_scores, bits, seeds, n, b, tau, lane);
+    else
+      grow_walk(sc, bits, seeds, n, b, tau, lane);
+  }
   __syncthreads();
 
   // 5. mask and ascending indices from the bitmap
-  uint32_t base = 0;
+  uint64_t base = 0;
   for (int w0 = 0; w0 < words; w0 += kSelBlock) {
     const int w = w0 + t;
     const uint32_t v = w < words ? bits[w] : 0u;
     if (w < words) out_mask[w] = v;
-    uint32_t tot;
-    uint32_t pos = base + block_exclusive_scan((uint32_t)__popc(v), scan, &tot);
+    uint64_t tot;
+    uint64_t pos = base + block_exclusive_scan64((uint64_t)__popc(v), scan64, &tot);
     for (uint32_t x = v; x; x &= x - 1) {
-      if (pos < (uint32_t)b) out_idx[pos] = (w << 5) + __ffs(x) - 1;
+      if (pos < (uint64_t)b) out_idx[pos] = (w << 5) + __ffs(x) - 1;
       ++pos;
     }
     base += tot;
@@ -401,7 +472,7 @@ extern "C" kvfix_status kvfix_select_grow(const float* scores, int32_t n_rows, i
   if (n_rows == 0 || n == 0) return KVFIX_OK;
   if (scores == nullptr || mask == nullptr || (b > 0 && idx == nullptr)) return KVFIX_ERR_ARG;
   if (n_rows > kMaxGrid) return KVFIX_ERR_ARG;
-  const int limit = max_lds_per_block() - 1024;     // room for the static LDS
+  const int limit = max_lds_per_block() - 8192;     // room for the static LDS
   GrowShape G = grow_shape(n, b, true);
   if (G.bytes > (uint32_t)limit) G = grow_shape(n, b, false);
   if (G.bytes > (uint32_t)limit) return KVFIX_ERR_UNSUPPORTED;

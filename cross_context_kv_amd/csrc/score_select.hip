@@ -7,10 +7,11 @@
 //
 // select: one 1024-thread block per row.  Scores become order-preserving
 // 32-bit keys (NaN lowest, -0 = +0).  Four 8-bit radix passes (LDS integer
-// histograms) find the key T of the b-th largest element and how many
-// elements equal to T are still needed; then a block scan over contiguous
-// per-thread index ranges keeps every key > T and the lowest-index keys == T,
-// writing indices in ascending order and the bitmask word by word.
+// histograms, wave-aggregated increments) find the key T of the b-th largest
+// element and how many elements equal to T are still needed; then the
+// compaction keeps every key > T and the lowest-index keys == T, placing
+// each by wave ballots and a scanned table of per-wave counts, and writes
+// indices in ascending order and the bitmask word by word.
 #include <type_traits>
 
 #include "common.h"
@@ -114,16 +115,17 @@ struct ScoreLaunch {
 // One block per row.  Keys j = t + 1024 q live in registers (read once).
 // Four 8-bit radix passes over per-wave LDS histograms find the b-th largest
 // key T and how many keys equal to T are still needed; the compaction then
-// walks the row in index order, 1024 keys at a time, so indices come out
-// ascending and the lowest-index keys equal to T are the ones taken.
+// places every kept key by wave ballots and a scanned table of per-wave
+// counts, so indices come out ascending and the lowest-index keys equal to
+// T are the ones taken.
 __global__ __launch_bounds__(kSelBlock) void select_topb_kernel(const float* __restrict__ scores,
                                                                 int n, int b,
                                                                 int32_t* __restrict__ idx,
                                                                 uint32_t* __restrict__ mask,
                                                                 int words) {
   __shared__ uint32_t hist[kSelWaves][256];
-  __shared__ uint32_t scan[160];
-  __shared__ uint32_t sh[2];
+  __shared__ uint32_t ctab[2 * kCompactTab];
+  __shared__ uint32_t sh[3];
   const int row = blockIdx.x;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const float* sc = scores + (int64_t)row * n;
@@ -139,39 +141,12 @@ __global__ __launch_bounds__(kSelBlock) void select_topb_kernel(const float* __r
       key[q] = j < n ? order_key(sc[j]) : 0u;
     }
   }
-  uint32_t T, need_eq;
-  radix_threshold(key, in_regs, sc, n, b, &hist[0][0], sh, &T, &need_eq);
+  uint32_t T, need_eq, eq_total;
+  radix_threshold(key, in_regs, sc, n, b, &hist[0][0], sh, &T, &need_eq, &eq_total);
 
-  // Compaction in index order: chunk c covers keys [1024 c, 1024 c + 1024),
-  // thread t holds key 1024 c + t (register q = c when in_regs).
-  uint32_t eq_base = 0, sel_base = 0;
-  const int n_chunks = (n + kSelBlock - 1) / kSelBlock;
-  for (int c = 0; c < n_chunks; ++c) {
-    const int j = c * kSelBlock + t;
-    uint32_t k = 0;
-    if (j < n) {
-      if (in_regs) {
-#pragma unroll
-        for (int q = 0; q < kSelRegKeys; ++q)
-          if (q == c) k = key[q];
-      } else {
-        k = order_key(sc[j]);
-      }
-    }
-    const bool valid = j < n && b > 0;
-    const uint32_t is_eq = valid && k == T;
-    uint32_t tot;
-    const uint32_t eq_rank = eq_base + block_exclusive_scan(is_eq, scan, &tot);
-    eq_base += tot;
-    const uint32_t sel = valid && (k > T || (is_eq && eq_rank < need_eq));
-    const uint32_t pos = sel_base + block_exclusive_scan(sel, scan, &tot);
-    sel_base += tot;
-    if (sel && pos < (uint32_t)b) out_idx[pos] = j;        // exactly b are selected
-    const uint64_t bal = __ballot(sel);
-    const int wbase = (c * kSelBlock + wave * 64) >> 5;    // first mask word of this wave
-    if (lane == 0 && wbase < words) out_mask[wbase] = (uint32_t)bal;
-    if (lane == 32 && wbase + 1 < words) out_mask[wbase + 1] = (uint32_t)(bal >> 32);
-  }
+  compact_topb(key, in_regs, sc, n, b, T, need_eq, eq_total, ctab,
+               [&](uint32_t pos, int j, uint32_t) { out_idx[pos] = j; },
+               [&](int w, uint32_t bits) { out_mask[w] = bits; });
 }
 
 }  // namespace kvfix
