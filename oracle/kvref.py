@@ -160,17 +160,19 @@ def rope_shift(plane: np.ndarray, dtype: str, deltas: Sequence[int], theta: floa
 
 def score_l2(fresh: np.ndarray, reuse: np.ndarray, dtype: str, check_layer: int,
              deltas: Optional[Sequence[int]] = None, theta: float = 0.0,
-             style: str = "half") -> np.ndarray:
+             style: str = "half", per_head: bool = False) -> np.ndarray:
     """d[s][j] = || fresh_j - align(reuse_j) || over all heads and dims of row j.
 
-    deltas=None scores a value plane (no rotation).  Returns float32 [S][n].
+    per_head: d[s][h][j] over the head_dim elements of head h alone (AKS
+    builds its correction for one attention head).  deltas=None scores a
+    value plane (no rotation).  Returns float32 [S][n], or [S][H][n].
     """
     f = to_f64(fresh[check_layer], dtype)          # [S][H][n][hd]
     r = to_f64(reuse[check_layer], dtype)
     if deltas is not None:
         r = np.stack([rope_rotate(r[s], deltas[s], theta, style) for s in range(r.shape[0])])
     diff = f - r
-    sq = (diff * diff).sum(axis=(1, 3))            # sum over heads and dims -> [S][n]
+    sq = (diff * diff).sum(axis=3 if per_head else (1, 3))
     return np.sqrt(sq).astype(np.float32)
 
 
@@ -381,30 +383,46 @@ def lowrank_rows(A: Optional[np.ndarray], B: Optional[np.ndarray], l: int, s: in
     return A[l, s, h][rows].astype(np.float64) @ B[l, s, h].astype(np.float64)
 
 
+def _probe_list(idx: np.ndarray, s: int, h: int, per_head: bool) -> np.ndarray:
+    return idx[s][h] if per_head else idx[s]
+
+
+def _covered(rows: np.ndarray, cover, s: int) -> np.ndarray:
+    """1.0 for rows inside segment s's covered prefix, 0.0 past it."""
+    if cover is None:
+        return np.ones(len(rows))
+    return (rows < int(cover[s])).astype(np.float64)
+
+
 def fit_mean(fresh: np.ndarray, reuse: np.ndarray, dtype: str, idx: np.ndarray,
              deltas: Optional[Sequence[int]] = None, theta: float = 0.0, style: str = "half",
              A: Optional[np.ndarray] = None, B: Optional[np.ndarray] = None,
-             fresh_by_slot: bool = False) -> np.ndarray:
-    """mu[l][s][h] = (1/|S_s|) sum_{j in S_s} (fresh_j - align(reuse_j) - A_j B).
+             fresh_by_slot: bool = False, per_head: bool = False,
+             cover: Optional[Sequence[int]] = None) -> np.ndarray:
+    """mu[l][s][h] = (1/|S|) sum_{j in S} (fresh_j - align(reuse_j) - A_j B).
 
-    idx: int32 [S][w].  An entry outside [0, n) is padding, not a member of
-    the probe set S_s (a layout whose row count depends on the data, such as
-    whole chunks with a short last chunk, pads its fixed-width list with -1);
-    mu is the mean over the members, 0 when there are none.  fresh_by_slot:
-    fresh holds the probe rows by slot, row k of segment s being token
-    idx[s][k] (padding slots unused).  Returns float32 [L][S][H][hd].
+    idx: int32 [S][w], or [S][H][w] with per_head (a probe set per head).  An
+    entry outside [0, n) is padding, not a member of the probe set S (a
+    layout whose row count depends on the data, such as whole chunks with a
+    short last chunk, pads its fixed-width list with -1); mu is the mean over
+    the members, 0 when there are none.  cover: rows at or past cover[s] have
+    no rank state (A_j = 0 there; KVCMAS App. A.3 "Variable Segment Lengths":
+    no extrapolation past the covered prefix).  fresh_by_slot: fresh holds
+    the probe rows by slot, row k being token idx[s]([h])[k] (padding slots
+    unused).  Returns float32 [L][S][H][hd].
     """
     L, S, H, n, hd = reuse.shape
-    w = idx.shape[1]
     mu = np.zeros((L, S, H, hd), dtype=np.float64)
     for s in range(S):
-        slots = np.array([k for k in range(w) if 0 <= int(idx[s][k]) < n], dtype=np.int64)
-        if len(slots) == 0:
-            continue
-        rows = idx[s][slots].astype(np.int64)
-        fr_rows = slots if fresh_by_slot else rows
-        for l in range(L):
-            for h in range(H):
+        for h in range(H):
+            lst = _probe_list(idx, s, h, per_head)
+            slots = np.array([k for k in range(len(lst)) if 0 <= int(lst[k]) < n], dtype=np.int64)
+            if len(slots) == 0:
+                continue
+            rows = lst[slots].astype(np.int64)
+            fr_rows = slots if fresh_by_slot else rows
+            cov = _covered(rows, cover, s)
+            for l in range(L):
                 f = to_f64(fresh[l, s, h][fr_rows], dtype)
                 r = to_f64(reuse[l, s, h][rows], dtype)
                 if deltas is not None:
@@ -412,24 +430,25 @@ def fit_mean(fresh: np.ndarray, reuse: np.ndarray, dtype: str, idx: np.ndarray,
                 res = f - r
                 ab = lowrank_rows(A, B, l, s, h, rows)
                 if ab is not None:
-                    res = res - ab
+                    res = res - cov[:, None] * ab
                 mu[l, s, h] = res.sum(axis=0) / len(rows)
     return mu.astype(np.float32)
 
 
 def scatter_fresh(out: np.ndarray, fresh: np.ndarray, idx: np.ndarray,
-                  fresh_by_slot: bool = False) -> None:
+                  fresh_by_slot: bool = False, per_head: bool = False) -> None:
     """Copy the fresh rows into the probe positions of `out` (in place, exact);
     padding entries of idx (outside [0, n)) are skipped."""
     L, S, H, n, hd = out.shape
-    w = idx.shape[1]
     for s in range(S):
-        slots = np.array([k for k in range(w) if 0 <= int(idx[s][k]) < n], dtype=np.int64)
-        if len(slots) == 0:
-            continue
-        rows = idx[s][slots].astype(np.int64)
-        src = slots if fresh_by_slot else rows
-        out[:, s][:, :, rows] = fresh[:, s][:, :, src]
+        for h in range(H):
+            lst = _probe_list(idx, s, h, per_head)
+            slots = np.array([k for k in range(len(lst)) if 0 <= int(lst[k]) < n], dtype=np.int64)
+            if len(slots) == 0:
+                continue
+            rows = lst[slots].astype(np.int64)
+            src = slots if fresh_by_slot else rows
+            out[:, s, h][:, rows] = fresh[:, s, h][:, src]
 
 
 # ----------------------------------------------------------------------------
@@ -452,44 +471,52 @@ def apply(reuse: np.ndarray, dtype: str, mask: Optional[np.ndarray], mu: np.ndar
           scores: Optional[np.ndarray] = None, w_lo: float = 0.0, w_hi: float = 1.0,
           A: Optional[np.ndarray] = None, B: Optional[np.ndarray] = None,
           deltas: Optional[Sequence[int]] = None, theta: float = 0.0, style: str = "half",
-          out: Optional[np.ndarray] = None) -> np.ndarray:
+          out: Optional[np.ndarray] = None, per_head: bool = False,
+          cover: Optional[Sequence[int]] = None) -> np.ndarray:
     """out_j = round(align(reuse_j) + w_j mu + A_j B) for every non-probe row j.
 
     Probe rows (mask bit set) are left as they are in `out` (a copy of `reuse`
     when out is None); the fresh scatter fills them.  mu: float32 [L][S][H][hd];
-    scores: float32 [S][n] or None (w = 1).
+    scores: float32 [S][n] or None (w = 1); mask [S][words].  per_head: mask
+    [S][H][words] and scores [S][H][n].  cover: rows at or past cover[s] are
+    only re-aligned, out_j = round(align(reuse_j)) (KVCMAS App. A.3 "Variable
+    Segment Lengths").
     """
     L, S, H, n, hd = reuse.shape
     res = reuse.copy() if out is None else out
     for s in range(S):
-        keep = np.ones(n, dtype=bool)
-        if mask is not None:
-            keep = ~mask_to_bool(mask[s], n)
-        rows = np.nonzero(keep)[0]
-        w = weights(None if scores is None else scores[s], w_lo, w_hi, n)[rows]
-        for l in range(L):
-            for h in range(H):
+        for h in range(H):
+            m = None if mask is None else (mask[s][h] if per_head else mask[s])
+            keep = np.ones(n, dtype=bool) if m is None else ~mask_to_bool(m, n)
+            rows = np.nonzero(keep)[0]
+            sc = None if scores is None else (scores[s][h] if per_head else scores[s])
+            cov = _covered(rows, cover, s)
+            w = weights(sc, w_lo, w_hi, n)[rows] * cov
+            for l in range(L):
                 x = to_f64(reuse[l, s, h][rows], dtype)
                 if deltas is not None:
                     x = rope_rotate(x, deltas[s], theta, style)
                 y = x + w[:, None] * mu[l, s, h].astype(np.float64)[None, :]
                 ab = lowrank_rows(A, B, l, s, h, rows)
                 if ab is not None:
-                    y = y + ab
+                    y = y + cov[:, None] * ab
                 res[l, s, h][rows] = store(y, dtype)
     return res
 
 
 def correct(fresh, reuse, dtype, idx, mask, scores=None, w_lo=0.0, w_hi=1.0, A=None, B=None,
-            deltas=None, theta=0.0, style="half", fresh_by_slot=False):
+            deltas=None, theta=0.0, style="half", fresh_by_slot=False, per_head=False,
+            cover=None):
     """The whole correction of one plane: fit the mean, scatter, apply.
 
     Returns (out plane, mu).
     """
-    mu = fit_mean(fresh, reuse, dtype, idx, deltas, theta, style, A, B, fresh_by_slot)
+    mu = fit_mean(fresh, reuse, dtype, idx, deltas, theta, style, A, B, fresh_by_slot,
+                  per_head, cover)
     out = reuse.copy()
-    scatter_fresh(out, fresh, idx, fresh_by_slot)
-    apply(reuse, dtype, mask, mu, scores, w_lo, w_hi, A, B, deltas, theta, style, out=out)
+    scatter_fresh(out, fresh, idx, fresh_by_slot, per_head)
+    apply(reuse, dtype, mask, mu, scores, w_lo, w_hi, A, B, deltas, theta, style, out=out,
+          per_head=per_head, cover=cover)
     return out, mu
 
 

@@ -797,3 +797,106 @@ def test_coin_control_draws_exactly_c_uniform_chunks():
     p = c / nc
     sd = math.sqrt(trials * p * (1 - p))
     assert np.all(np.abs(hits - trials * p) < 5 * sd)
+
+
+# ----------------------------------------------------------------------------
+# Probe granularity per head (AKS: the construction for one attention head)
+# and the covered prefix (KVCMAS App. A.3 "Variable Segment Lengths")
+# ----------------------------------------------------------------------------
+
+
+def _case(seed, L=2, S=2, H=3, n=40, hd=8, r=2, dtype="bf16"):
+    rng = np.random.default_rng(seed)
+    reuse = K.store(rng.standard_normal((L, S, H, n, hd)), dtype)
+    fresh = K.store(rng.standard_normal((L, S, H, n, hd)), dtype)
+    A = rng.standard_normal((L, S, H, n, r)).astype(np.float32)
+    B = rng.standard_normal((L, S, H, r, hd)).astype(np.float32)
+    return rng, reuse, fresh, A, B
+
+
+def test_per_head_scores_add_up_in_squares_to_the_shared_score():
+    rng, reuse, fresh, _, _ = _case(40)
+    d = K.score_l2(fresh, reuse, "bf16", 1, [3, 9], 1e4)
+    dh = K.score_l2(fresh, reuse, "bf16", 1, [3, 9], 1e4, per_head=True)
+    assert dh.shape == (2, 3, 40)
+    sq = (dh.astype(np.float64) ** 2).sum(axis=1)
+    assert np.allclose(np.sqrt(sq), d, rtol=2e-7, atol=0)
+    # one head: the per-head score is the shared score
+    d1 = K.score_l2(fresh[:, :, :1], reuse[:, :, :1], "bf16", 1, [3, 9], 1e4)
+    assert np.array_equal(K.score_l2(fresh[:, :, :1], reuse[:, :, :1], "bf16", 1, [3, 9], 1e4,
+                                     per_head=True)[:, 0], d1)
+
+
+def test_per_head_fit_with_one_probe_set_for_all_heads_is_the_shared_fit():
+    rng, reuse, fresh, A, B = _case(41)
+    idx = np.array([[1, 7, 30, 39], [0, 2, 3, 20]], np.int32)
+    idx_h = np.repeat(idx[:, None, :], 3, axis=1)
+    a = K.fit_mean(fresh, reuse, "bf16", idx, [4, -2], 1e4, "half", A, B)
+    b = K.fit_mean(fresh, reuse, "bf16", idx_h, [4, -2], 1e4, "half", A, B, per_head=True)
+    assert np.array_equal(a, b)
+
+
+def test_per_head_fit_and_apply_use_each_heads_own_probes():
+    rng, reuse, fresh, A, B = _case(42)
+    S, H, n = 2, 3, 40
+    idx_h = np.stack([np.stack([np.sort(rng.choice(n, 5, replace=False)) for _ in range(H)])
+                      for _ in range(S)]).astype(np.int32)
+    mask_h = np.zeros((S, H, (n + 31) // 32), np.uint32)
+    for s in range(S):
+        for h in range(H):
+            for j in idx_h[s, h]:
+                mask_h[s, h, j // 32] |= np.uint32(1) << np.uint32(j % 32)
+    out, mu = K.correct(fresh, reuse, "bf16", idx_h, mask_h, None, 0.0, 1.0, A, B, [5, 6], 1e4,
+                        per_head=True)
+    # each head equals the shared correction of that head alone with its probes
+    for h in range(H):
+        o1, m1 = K.correct(fresh[:, :, h:h + 1], reuse[:, :, h:h + 1], "bf16", idx_h[:, h],
+                           mask_h[:, h], None, 0.0, 1.0, A[:, :, h:h + 1], B[:, :, h:h + 1],
+                           [5, 6], 1e4)
+        assert np.array_equal(out[:, :, h:h + 1], o1) and np.array_equal(mu[:, :, h:h + 1], m1)
+
+
+def test_cover_full_is_no_cover_and_zero_is_pure_realignment():
+    rng, reuse, fresh, A, B = _case(43)
+    idx = np.array([[1, 7, 30, 39], [0, 2, 3, 20]], np.int32)
+    mask = np.zeros((2, 2), np.uint32)
+    for s in range(2):
+        for j in idx[s]:
+            mask[s, j // 32] |= np.uint32(1) << np.uint32(j % 32)
+    sc = rng.random((2, 40)).astype(np.float32) * 3
+    base = K.correct(fresh, reuse, "bf16", idx, mask, sc, 0.0, 2.0, A, B, [7, 8], 1e4)
+    full = K.correct(fresh, reuse, "bf16", idx, mask, sc, 0.0, 2.0, A, B, [7, 8], 1e4,
+                     cover=[40, 40])
+    assert np.array_equal(base[0], full[0]) and np.array_equal(base[1], full[1])
+    zero, mu0 = K.correct(fresh, reuse, "bf16", idx, mask, sc, 0.0, 2.0, A, B, [7, 8], 1e4,
+                          cover=[0, 0])
+    shifted = K.rope_shift(reuse, "bf16", [7, 8], 1e4)
+    for s in range(2):
+        rows = np.setdiff1d(np.arange(40), idx[s])
+        assert np.array_equal(zero[:, s][:, :, rows], shifted[:, s][:, :, rows])
+    # no rank state anywhere: the mean is the mean without A B
+    assert np.array_equal(mu0, K.fit_mean(fresh, reuse, "bf16", idx, [7, 8], 1e4))
+
+
+def test_cover_splits_the_segment_at_the_covered_prefix():
+    rng, reuse, fresh, A, B = _case(44)
+    idx = np.array([[1, 7, 30, 39], [0, 2, 3, 20]], np.int32)
+    mask = np.zeros((2, 2), np.uint32)
+    for s in range(2):
+        for j in idx[s]:
+            mask[s, j // 32] |= np.uint32(1) << np.uint32(j % 32)
+    cover = [25, 10]
+    out, mu = K.correct(fresh, reuse, "bf16", idx, mask, None, 0.0, 1.0, A, B, [7, 8], 1e4,
+                        cover=cover)
+    shifted = K.rope_shift(reuse, "bf16", [7, 8], 1e4)
+    # A rows past the prefix set to zero give the same mean (the state is absent there)
+    A0 = A.copy()
+    for s in range(2):
+        A0[:, s, :, cover[s]:] = 0.0
+    assert np.array_equal(mu, K.fit_mean(fresh, reuse, "bf16", idx, [7, 8], 1e4, "half", A0, B))
+    full, _ = K.correct(fresh, reuse, "bf16", idx, mask, None, 0.0, 1.0, A0, B, [7, 8], 1e4)
+    for s in range(2):
+        rows = np.setdiff1d(np.arange(40), idx[s])
+        inside, past = rows[rows < cover[s]], rows[rows >= cover[s]]
+        assert np.array_equal(out[:, s][:, :, past], shifted[:, s][:, :, past])
+        assert np.array_equal(out[:, s][:, :, inside], full[:, s][:, :, inside])
