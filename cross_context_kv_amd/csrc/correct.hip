@@ -129,6 +129,8 @@ struct FitParams {
   RopeArgs rope;
   double* partial;          // [units][parts][kFitRowWidth(HD)]
   int32_t S, H, n;
+  int32_t idx_heads;        // 1: idx [S][b]; H: idx [S][H][b] (per head)
+  const int32_t* cover;     // rank state only for rows j < cover[s] (NULL: all)
 };
 
 template <typename T, int HD, int STYLE>
@@ -155,7 +157,8 @@ __global__ __launch_bounds__(kBlock) void fit_partial_kernel(FitParams P) {
   // Stage the slice's probe indices and their page ids.  Thread t < nk also
   // loads the rank-state row of slot t now (summed after the main loop), so
   // that load shares a memory round trip with the staging.
-  const int32_t* idx = P.idx + (int64_t)s * P.b;
+  const int32_t* idx = P.idx + ((int64_t)s * P.idx_heads + (P.idx_heads > 1 ? h : 0)) * P.b;
+  const int cov = P.cover ? P.cover[s] : P.n;
   const int rank = P.lr.rank;
   double* outp = P.partial + (int64_t)blockIdx.x * PW;
   float arow[kFitMaxRank];
@@ -173,7 +176,7 @@ __global__ __launch_bounds__(kBlock) void fit_partial_kernel(FitParams P) {
       spf[i] = ok ? page_of(P.fresh, s, P.fresh_by_slot ? k : j) : -1;
       spr[i] = ok ? page_of(P.reuse, s, j) : -1;
       spo[i] = ok && P.has_out ? page_of(P.out, s, j) : 0;
-      if (ok && rank > 0) {
+      if (ok && rank > 0 && j < cov) {                // no rank state past the covered prefix
         const float* Ar = P.lr.A + l * P.lr.sA_layer + s * P.lr.sA_seg + h * P.lr.sA_head +
                           (int64_t)j * rank;
 #pragma unroll
@@ -353,6 +356,8 @@ struct ApplyParams {
   DLowRank lr;
   RopeArgs rope;
   int32_t S, L, H, n, cpu, mask_words;
+  int32_t per_head;            // mask [S][H][words] and scores [S][H][n]
+  const int32_t* cover;        // rows j >= cover[s] are only re-aligned (NULL: none)
   // Chunk order: c = ((s L + l) X + x) Y + y, where (x, y) = (head, chunk
   // of tokens) or, when a head's rows are farther apart than a token's
   // (paged pools, token-major layouts), (chunk of tokens, head), so that the
@@ -457,7 +462,9 @@ __device__ __forceinline__ void apply_body(const ApplyParams& P) {
     const int wb = (p.k * CH) >> 5;
 #pragma unroll
     for (int qq = 0; qq < NW; ++qq)
-      if (wb + qq < P.mask_words) w[qq] = P.mask[(int64_t)p.s * P.mask_words + wb + qq];
+      if (wb + qq < P.mask_words)
+        w[qq] = P.mask[((int64_t)p.s * (P.per_head ? P.H : 1) + (P.per_head ? p.h : 0)) *
+                           P.mask_words + wb + qq];
   };
   Pos pos;
   {
@@ -560,7 +567,10 @@ __device__ __forceinline__ void apply_body(const ApplyParams& P) {
     // Set-up loads: this thread's chunk row (weight, rank-state row) and the
     // lane's per-unit mean and B values.
     float wt = 1.0f;
-    if (P.scores && t < nrows) wt = P.scores[(int64_t)s * P.n + j_begin + t];
+    if (P.scores && t < nrows)
+      wt = P.scores[((int64_t)s * (P.per_head ? P.H : 1) + (P.per_head ? h : 0)) * P.n +
+                    j_begin + t];
+    const int cov = P.cover ? P.cover[s] : P.n;
     float arow[R];
 #pragma unroll
     for (int kk = 0; kk < R; ++kk) arow[kk] = 0.0f;
@@ -599,10 +609,14 @@ __device__ __forceinline__ void apply_body(const ApplyParams& P) {
       }
     }
     if (t < nrows) {
-      sw[buf][t] = fminf(fmaxf(wt, P.w_lo), P.w_hi);
+      // w = clamp(score) (1 without scores); past the covered prefix neither
+      // the mean nor the rank term applies: w = 0 and A row = 0
+      const bool covered = j_begin + t < cov;
+      sw[buf][t] = !covered ? 0.0f : P.scores ? fminf(fmaxf(wt, P.w_lo), P.w_hi) : 1.0f;
       if constexpr (MAXR > 0) {
 #pragma unroll
-        for (int kk = 0; kk < RS; ++kk) sa[buf][t * RS + kk] = kk < MAXR ? arow[kk] : 0.0f;
+        for (int kk = 0; kk < RS; ++kk)
+          sa[buf][t * RS + kk] = kk < MAXR && covered ? arow[kk] : 0.0f;
       }
     }
     __syncthreads();
@@ -845,11 +859,12 @@ extern "C" size_t kvfix_fit_mean_workspace(int32_t n_layers, int32_t n_segs, int
          sizeof(double);
 }
 
-extern "C" kvfix_status kvfix_fit_mean(const kvfix_plane* fresh, int32_t fresh_by_slot,
-                                       const kvfix_plane* reuse, const kvfix_plane* out,
-                                       const int32_t* idx, int32_t b, const kvfix_rope* rope,
-                                       const kvfix_lowrank* lowrank, float* mu, void* ws,
-                                       size_t ws_bytes, void* stream) {
+extern "C" kvfix_status kvfix_fit_mean_ex(const kvfix_plane* fresh, int32_t fresh_by_slot,
+                                          const kvfix_plane* reuse, const kvfix_plane* out,
+                                          const int32_t* idx, int32_t b, const kvfix_rope* rope,
+                                          const kvfix_lowrank* lowrank,
+                                          const kvfix_granularity* opt, float* mu, void* ws,
+                                          size_t ws_bytes, void* stream) {
   KVFIX_TRY(check_plane(fresh));
   KVFIX_TRY(check_plane(reuse));
   if (out) {
@@ -868,6 +883,7 @@ extern "C" kvfix_status kvfix_fit_mean(const kvfix_plane* fresh, int32_t fresh_b
     return KVFIX_ERR_ARG;
   KVFIX_TRY(check_rope(rope, reuse->head_dim));
   KVFIX_TRY(check_lowrank(lowrank));
+  if (opt && opt->per_head != 0 && opt->per_head != 1) return KVFIX_ERR_ARG;
   const int64_t units = (int64_t)reuse->n_layers * reuse->n_segs * reuse->n_heads;
   if (units == 0) return KVFIX_OK;
   const size_t need = kvfix_fit_mean_workspace(reuse->n_layers, reuse->n_segs, reuse->n_heads,
@@ -889,6 +905,8 @@ extern "C" kvfix_status kvfix_fit_mean(const kvfix_plane* fresh, int32_t fresh_b
   P.rope = make_rope_args(rope, reuse->head_dim);
   P.partial = static_cast<double*>(ws);
   P.S = reuse->n_segs; P.H = reuse->n_heads; P.n = reuse->n_tokens;
+  P.idx_heads = opt && opt->per_head ? reuse->n_heads : 1;
+  P.cover = opt ? opt->cover : nullptr;
   hipStream_t st = (hipStream_t)stream;
   const int style = rope ? rope->style : kStyleNone;
   KVFIX_TRY(dispatch_t_hd_style<FitLaunch>(reuse->dtype, reuse->head_dim, style, P, grid, st));
@@ -901,10 +919,20 @@ extern "C" kvfix_status kvfix_fit_mean(const kvfix_plane* fresh, int32_t fresh_b
   return launch_status();
 }
 
-extern "C" kvfix_status kvfix_apply(const kvfix_plane* reuse, const kvfix_plane* out,
-                                    const uint32_t* mask, const float* scores, float w_lo,
-                                    float w_hi, const float* mu, const kvfix_lowrank* lowrank,
-                                    const kvfix_rope* rope, void* stream) {
+extern "C" kvfix_status kvfix_fit_mean(const kvfix_plane* fresh, int32_t fresh_by_slot,
+                                       const kvfix_plane* reuse, const kvfix_plane* out,
+                                       const int32_t* idx, int32_t b, const kvfix_rope* rope,
+                                       const kvfix_lowrank* lowrank, float* mu, void* ws,
+                                       size_t ws_bytes, void* stream) {
+  return kvfix_fit_mean_ex(fresh, fresh_by_slot, reuse, out, idx, b, rope, lowrank, nullptr, mu,
+                           ws, ws_bytes, stream);
+}
+
+extern "C" kvfix_status kvfix_apply_ex(const kvfix_plane* reuse, const kvfix_plane* out,
+                                       const uint32_t* mask, const float* scores, float w_lo,
+                                       float w_hi, const float* mu, const kvfix_lowrank* lowrank,
+                                       const kvfix_rope* rope, const kvfix_granularity* opt,
+                                       void* stream) {
   KVFIX_TRY(check_plane(reuse));
   KVFIX_TRY(check_plane(out));
   KVFIX_TRY(same_rows(reuse, out));
@@ -912,6 +940,7 @@ extern "C" kvfix_status kvfix_apply(const kvfix_plane* reuse, const kvfix_plane*
   if (scores && !(w_lo <= w_hi)) return KVFIX_ERR_ARG;
   KVFIX_TRY(check_rope(rope, reuse->head_dim));
   KVFIX_TRY(check_lowrank(lowrank));
+  if (opt && opt->per_head != 0 && opt->per_head != 1) return KVFIX_ERR_ARG;
   const int64_t units = (int64_t)reuse->n_layers * reuse->n_segs * reuse->n_heads;
   if (units == 0 || reuse->n_tokens == 0) return KVFIX_OK;
   if (!aligned16(mu)) return KVFIX_ERR_ALIGN;
@@ -931,6 +960,8 @@ extern "C" kvfix_status kvfix_apply(const kvfix_plane* reuse, const kvfix_plane*
   P.rope = make_rope_args(rope, reuse->head_dim);
   P.S = reuse->n_segs; P.L = reuse->n_layers; P.H = reuse->n_heads; P.n = reuse->n_tokens;
   P.mask_words = (reuse->n_tokens + 31) / 32;
+  P.per_head = opt ? opt->per_head : 0;
+  P.cover = opt ? opt->cover : nullptr;
   const int ch = apply_chunk_rows(reuse->dtype == KVFIX_F32 ? 4 : 8, reuse->head_dim);
   P.cpu = (reuse->n_tokens + ch - 1) / ch;
   const int64_t n_chunks = units * P.cpu;
@@ -941,4 +972,11 @@ extern "C" kvfix_status kvfix_apply(const kvfix_plane* reuse, const kvfix_plane*
   const int style = rope ? rope->style : kStyleNone;
   return dispatch_t_hd_style<ApplyLaunch>(reuse->dtype, reuse->head_dim, style, P,
                                           rank_variant(P.lr.rank), grid, (hipStream_t)stream);
+}
+
+extern "C" kvfix_status kvfix_apply(const kvfix_plane* reuse, const kvfix_plane* out,
+                                    const uint32_t* mask, const float* scores, float w_lo,
+                                    float w_hi, const float* mu, const kvfix_lowrank* lowrank,
+                                    const kvfix_rope* rope, void* stream) {
+  return kvfix_apply_ex(reuse, out, mask, scores, w_lo, w_hi, mu, lowrank, rope, nullptr, stream);
 }

@@ -26,8 +26,9 @@ struct ScoreParams {
   DPlane fresh, reuse;
   int32_t fl, rl;                 // layer read in each plane
   RopeArgs rope;
-  float* scores;
+  float* scores;                  // [S][n], or [S][H][n] per head
   int32_t S, H, n, tok_blocks;
+  int32_t per_head;
 };
 
 template <typename T, int HD, int STYLE>
@@ -53,12 +54,14 @@ __global__ __launch_bounds__(kScoreBlock) void score_l2_kernel(ScoreParams P) {
     for (int m = 0; m < V; ++m) { cs[m] = tc[g * V + m]; sn[m] = ts[g * V + m]; }
   }
 
+  // Every lane runs the head loop (the per-head sums reduce across lanes
+  // inside it); a lane past n or on a bad page id adds nothing.
   double acc = 0.0;
-  if (j < P.n) {
-    for (int h = wave; h < P.H; h += W) {
-      const int64_t fo = row_offset(P.fresh, P.fl, s, h, j);
-      const int64_t ro = row_offset(P.reuse, P.rl, s, h, j);
-      if (fo < 0 || ro < 0) continue;
+  for (int h = wave; h < P.H; h += W) {
+    const int64_t fo = j < P.n ? row_offset(P.fresh, P.fl, s, h, j) : -1;
+    const int64_t ro = j < P.n ? row_offset(P.reuse, P.rl, s, h, j) : -1;
+    double hacc = 0.0;
+    if (fo >= 0 && ro >= 0) {
       const T* fr = reinterpret_cast<const T*>(P.fresh.data) + fo;
       const T* rr = reinterpret_cast<const T*>(P.reuse.data) + ro;
       const vu4 f0 = ld16(fr + M::off0(g)), f1 = ld16(fr + M::off1(g));
@@ -74,11 +77,19 @@ __global__ __launch_bounds__(kScoreBlock) void score_l2_kernel(ScoreParams P) {
 #pragma unroll
       for (int m = 0; m < V; ++m) {
         const double da = fa[m] - ra[m], db = fb[m] - rb[m];
-        acc = fma(da, da, acc);
-        acc = fma(db, db, acc);
+        hacc = fma(da, da, hacc);
+        hacc = fma(db, db, hacc);
       }
     }
+    if (P.per_head) {                              // uniform: this head's score of row j
+#pragma unroll
+      for (int off = 1; off < G; off <<= 1) hacc += __shfl_xor(hacc, off);
+      if (g == 0 && j < P.n) P.scores[((int64_t)s * P.H + h) * P.n + j] = (float)sqrt(hacc);
+    } else {
+      acc += hacc;
+    }
   }
+  if (P.per_head) return;                          // (uniform over the block)
 #pragma unroll
   for (int off = 1; off < G; off <<= 1) acc += __shfl_xor(acc, off);
   if (g == 0) part[wave][rw] = acc;
@@ -153,9 +164,10 @@ __global__ __launch_bounds__(kSelBlock) void select_topb_kernel(const float* __r
 
 using namespace kvfix;
 
-extern "C" kvfix_status kvfix_score(const kvfix_plane* fresh, int32_t fresh_layer,
-                                    const kvfix_plane* reuse, int32_t reuse_layer,
-                                    const kvfix_rope* rope, float* scores, void* stream) {
+extern "C" kvfix_status kvfix_score_ex(const kvfix_plane* fresh, int32_t fresh_layer,
+                                       const kvfix_plane* reuse, int32_t reuse_layer,
+                                       const kvfix_rope* rope, const kvfix_granularity* opt,
+                                       float* scores, void* stream) {
   KVFIX_TRY(check_plane(fresh));
   KVFIX_TRY(check_plane(reuse));
   KVFIX_TRY(same_rows(fresh, reuse));
@@ -164,7 +176,8 @@ extern "C" kvfix_status kvfix_score(const kvfix_plane* fresh, int32_t fresh_laye
       reuse_layer >= reuse->n_layers)
     return KVFIX_ERR_ARG;
   KVFIX_TRY(check_rope(rope, reuse->head_dim));
-  if (reuse->n_segs == 0 || reuse->n_tokens == 0) return KVFIX_OK;
+  if (opt && opt->per_head != 0 && opt->per_head != 1) return KVFIX_ERR_ARG;
+  if (reuse->n_segs == 0 || reuse->n_tokens == 0 || reuse->n_heads == 0) return KVFIX_OK;
   ScoreParams P;
   P.fresh = make_dplane(*fresh);
   P.reuse = make_dplane(*reuse);
@@ -174,6 +187,7 @@ extern "C" kvfix_status kvfix_score(const kvfix_plane* fresh, int32_t fresh_laye
   P.scores = scores;
   P.S = reuse->n_segs; P.H = reuse->n_heads; P.n = reuse->n_tokens;
   P.tok_blocks = 0;
+  P.per_head = opt ? opt->per_head : 0;
   const int style = rope ? rope->style : kStyleNone;
   // The dispatcher lives with the correction kernels; replicate it here.
 #define KVFIX_SCASE(T_, HD_, ST_)                                              \
@@ -187,6 +201,12 @@ extern "C" kvfix_status kvfix_score(const kvfix_plane* fresh, int32_t fresh_laye
 #undef KVFIX_SSTYLES
 #undef KVFIX_SCASE
   return KVFIX_ERR_UNSUPPORTED;
+}
+
+extern "C" kvfix_status kvfix_score(const kvfix_plane* fresh, int32_t fresh_layer,
+                                    const kvfix_plane* reuse, int32_t reuse_layer,
+                                    const kvfix_rope* rope, float* scores, void* stream) {
+  return kvfix_score_ex(fresh, fresh_layer, reuse, reuse_layer, rope, nullptr, scores, stream);
 }
 
 extern "C" kvfix_status kvfix_select_topb(const float* scores, int32_t n_rows, int32_t n,

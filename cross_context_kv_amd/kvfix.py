@@ -22,7 +22,8 @@ STATUS = {0: "KVFIX_OK", 1: "KVFIX_ERR_ARG", 2: "KVFIX_ERR_ALIGN", 3: "KVFIX_ERR
 
 EXPORTS = ("kvfix_rope_shift", "kvfix_score", "kvfix_score_draft_workspace", "kvfix_score_draft",
            "kvfix_select_topb", "kvfix_chunk_budget", "kvfix_chunk_means", "kvfix_expand_chunks",
-           "kvfix_select_grow", "kvfix_fit_mean_workspace", "kvfix_fit_mean", "kvfix_apply", "kvfix_diff_encode_workspace",
+           "kvfix_select_grow", "kvfix_score_ex", "kvfix_fit_mean_ex", "kvfix_apply_ex",
+           "kvfix_fit_mean_workspace", "kvfix_fit_mean", "kvfix_apply", "kvfix_diff_encode_workspace",
            "kvfix_diff_encode", "kvfix_diff_decode_workspace", "kvfix_diff_decode",
            "kvfix_status_string", "kvfix_version")
 
@@ -64,6 +65,17 @@ class c_diff(ctypes.Structure):
                 ("block_tokens", ctypes.c_int32)]
 
 
+class c_granularity(ctypes.Structure):
+    _fields_ = [("per_head", ctypes.c_int32), ("cover", ctypes.c_void_p)]
+
+
+def _granularity(per_head: bool, cover: Optional[torch.Tensor]):
+    """ctypes options for the _ex calls, or None for the plain calls."""
+    if not per_head and cover is None:
+        return None
+    return c_granularity(int(per_head), None if cover is None else cover.data_ptr())
+
+
 _lib = None
 
 
@@ -86,6 +98,9 @@ def lib() -> ctypes.CDLL:
             "kvfix_chunk_means": [P, I32, I32, I32, P, P],
             "kvfix_expand_chunks": [P, I32, I32, I32, I32, P, P, P, P],
             "kvfix_select_grow": [P, I32, I32, I32, ctypes.c_double, P, P, P],
+            "kvfix_score_ex": [P, I32, P, I32, P, P, P, P],
+            "kvfix_fit_mean_ex": [P, I32, P, P, P, I32, P, P, P, P, P, ctypes.c_size_t, P],
+            "kvfix_apply_ex": [P, P, P, P, F, F, P, P, P, P, P],
             "kvfix_fit_mean_workspace": [I32, I32, I32, I32, I32],
             "kvfix_fit_mean": [P, I32, P, P, P, I32, P, P, P, P, ctypes.c_size_t, P],
             "kvfix_apply": [P, P, P, P, F, F, P, P, P, P],
@@ -207,13 +222,20 @@ def kvfix_rope_shift(src: Plane, dst: Plane, delta: torch.Tensor, theta: float,
 
 def kvfix_score(fresh: Plane, fresh_layer: int, reuse: Plane, reuse_layer: int,
                 scores: torch.Tensor, delta: Optional[torch.Tensor] = None, theta: float = 0.0,
-                style: int = ROPE_HALF) -> None:
+                style: int = ROPE_HALF, per_head: bool = False) -> None:
+    """per_head: scores [n_segs][n_heads][n] (kvfix_score_ex)."""
     rr = None
     if delta is not None:
         r, _ = make_rope(delta, theta, style)
         rr = ctypes.byref(r)
-    _check("kvfix_score", lib().kvfix_score(fresh.ref(), fresh_layer, reuse.ref(), reuse_layer,
-                                            rr, _ptr(scores), _stream()))
+    g = _granularity(per_head, None)
+    if g is None:
+        _check("kvfix_score", lib().kvfix_score(fresh.ref(), fresh_layer, reuse.ref(),
+                                                reuse_layer, rr, _ptr(scores), _stream()))
+    else:
+        _check("kvfix_score_ex", lib().kvfix_score_ex(fresh.ref(), fresh_layer, reuse.ref(),
+                                                      reuse_layer, rr, ctypes.byref(g),
+                                                      _ptr(scores), _stream()))
 
 
 def kvfix_select_topb(scores: torch.Tensor, b: int, idx: torch.Tensor,
@@ -262,9 +284,11 @@ def kvfix_fit_mean_workspace(n_layers: int, n_segs: int, n_heads: int, head_dim:
 def kvfix_fit_mean(fresh: Plane, reuse: Plane, out: Optional[Plane], idx: torch.Tensor, b: int,
                    mu: torch.Tensor, delta: Optional[torch.Tensor] = None, theta: float = 0.0,
                    style: int = ROPE_HALF, A=None, B=None, fresh_by_slot: bool = False,
-                   ws: Optional[torch.Tensor] = None) -> None:
+                   ws: Optional[torch.Tensor] = None, per_head: bool = False,
+                   cover: Optional[torch.Tensor] = None) -> None:
     """ws: device workspace (any dtype) of at least kvfix_fit_mean_workspace bytes; a
-    fresh one is allocated through torch when omitted."""
+    fresh one is allocated through torch when omitted.  per_head / cover: the
+    kvfix_fit_mean_ex options (idx [n_segs][n_heads][b]; cover int32 [n_segs])."""
     rr = None
     if delta is not None:
         r, _ = make_rope(delta, theta, style)
@@ -275,24 +299,41 @@ def kvfix_fit_mean(fresh: Plane, reuse: Plane, out: Optional[Plane], idx: torch.
     need = kvfix_fit_mean_workspace(c.n_layers, c.n_segs, c.n_heads, c.head_dim, b)
     if ws is None:
         ws = torch.empty(max(need, 16), dtype=torch.uint8, device=mu.device)
-    _check("kvfix_fit_mean", lib().kvfix_fit_mean(
-        fresh.ref(), int(fresh_by_slot), reuse.ref(), out.ref() if out else None, _ptr(idx), b,
-        rr, lrp, _ptr(mu), _ptr(ws), ws.numel() * ws.element_size(), _stream()))
+    g = _granularity(per_head, cover)
+    if g is None:
+        _check("kvfix_fit_mean", lib().kvfix_fit_mean(
+            fresh.ref(), int(fresh_by_slot), reuse.ref(), out.ref() if out else None, _ptr(idx),
+            b, rr, lrp, _ptr(mu), _ptr(ws), ws.numel() * ws.element_size(), _stream()))
+    else:
+        _check("kvfix_fit_mean_ex", lib().kvfix_fit_mean_ex(
+            fresh.ref(), int(fresh_by_slot), reuse.ref(), out.ref() if out else None, _ptr(idx),
+            b, rr, lrp, ctypes.byref(g), _ptr(mu), _ptr(ws), ws.numel() * ws.element_size(),
+            _stream()))
 
 
 def kvfix_apply(reuse: Plane, out: Plane, mask: Optional[torch.Tensor], mu: torch.Tensor,
                 scores: Optional[torch.Tensor] = None, w_lo: float = 0.0, w_hi: float = 1.0,
                 delta: Optional[torch.Tensor] = None, theta: float = 0.0, style: int = ROPE_HALF,
-                A=None, B=None) -> None:
+                A=None, B=None, per_head: bool = False,
+                cover: Optional[torch.Tensor] = None) -> None:
+    """per_head / cover: the kvfix_apply_ex options (mask [n_segs][n_heads][words],
+    scores [n_segs][n_heads][n]; cover int32 [n_segs])."""
     rr = None
     if delta is not None:
         r, _ = make_rope(delta, theta, style)
         rr = ctypes.byref(r)
     lr = make_lowrank(A, B)
     lrp = ctypes.byref(lr[0]) if lr else None
-    _check("kvfix_apply", lib().kvfix_apply(reuse.ref(), out.ref(), _ptr(mask), _ptr(scores),
-                                            float(w_lo), float(w_hi), _ptr(mu), lrp, rr,
-                                            _stream()))
+    g = _granularity(per_head, cover)
+    if g is None:
+        _check("kvfix_apply", lib().kvfix_apply(reuse.ref(), out.ref(), _ptr(mask), _ptr(scores),
+                                                float(w_lo), float(w_hi), _ptr(mu), lrp, rr,
+                                                _stream()))
+    else:
+        _check("kvfix_apply_ex", lib().kvfix_apply_ex(reuse.ref(), out.ref(), _ptr(mask),
+                                                      _ptr(scores), float(w_lo), float(w_hi),
+                                                      _ptr(mu), lrp, rr, ctypes.byref(g),
+                                                      _stream()))
 
 
 def kvfix_score_draft_workspace(n_segs: int, n_layers: int, first_layer: int, n_q_heads: int,

@@ -15,6 +15,7 @@
  *   kvfix_select_grow  probe sets of spans grown around the best rows (BCR-grow)
  *   kvfix_fit_mean     per-layer mean residual over the probe set (+ fresh scatter)
  *   kvfix_apply        fused re-align + weighted mean + rank-r correction
+ *   kvfix_*_ex         the same with per-head probe sets and a covered prefix
  *   kvfix_diff_encode  block-sparse diff of N sibling caches against a master
  *   kvfix_diff_decode  fused restore: master + diff blocks + rotation, per sibling
  *
@@ -291,6 +292,45 @@ kvfix_status kvfix_apply(const kvfix_plane* reuse, const kvfix_plane* out,
                          const uint32_t* mask, const float* scores, float w_lo, float w_hi,
                          const float* mu, const kvfix_lowrank* lowrank,
                          const kvfix_rope* rope, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Probe granularity and covered prefix.  [AKS "Core idea and method": the
+ * construction is for one layer and one attention head; KVCMAS App. A.3
+ * "Variable Segment Lengths": when the correction state covers only a prefix
+ * of a segment, that prefix is corrected and the rest keeps the re-aligned
+ * source cache]
+ *
+ * The _ex calls take these options; the calls above are the _ex calls with
+ * opt == NULL (one probe set per segment, every row covered).
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  /* 0: one score row, probe list and mask per segment, shared by its heads
+   *    (scores [n_segs][n], idx [n_segs][b], mask [n_segs][ceil(n/32)]);
+   * 1: one per (segment, head): scores [n_segs][n_heads][n], idx
+   *    [n_segs][n_heads][b], mask [n_segs][n_heads][ceil(n/32)], and the
+   *    score of a token is taken over its head's head_dim elements only. */
+  int32_t per_head;
+  /* NULL, or device int32 [n_segs]: segment s is covered by the correction
+   * state for tokens j < cover[s] only.  kvfix_apply_ex writes
+   * round(align(reuse_j)) for non-probe tokens j >= cover[s] (no weighted
+   * mean, no rank term); kvfix_fit_mean_ex takes A_j = 0 for probes
+   * j >= cover[s].  Values outside [0, n_tokens] act as the nearest end. */
+  const int32_t* cover;
+} kvfix_granularity;
+
+kvfix_status kvfix_score_ex(const kvfix_plane* fresh, int32_t fresh_layer,
+                            const kvfix_plane* reuse, int32_t reuse_layer,
+                            const kvfix_rope* rope, const kvfix_granularity* opt, float* scores,
+                            void* stream);
+kvfix_status kvfix_fit_mean_ex(const kvfix_plane* fresh, int32_t fresh_by_slot,
+                               const kvfix_plane* reuse, const kvfix_plane* out,
+                               const int32_t* idx, int32_t b, const kvfix_rope* rope,
+                               const kvfix_lowrank* lowrank, const kvfix_granularity* opt,
+                               float* mu, void* ws, size_t ws_bytes, void* stream);
+kvfix_status kvfix_apply_ex(const kvfix_plane* reuse, const kvfix_plane* out,
+                            const uint32_t* mask, const float* scores, float w_lo, float w_hi,
+                            const float* mu, const kvfix_lowrank* lowrank,
+                            const kvfix_rope* rope, const kvfix_granularity* opt, void* stream);
 
 /* ---------------------------------------------------------------------------
  * a8 / a9. Master-mirror block-sparse diff.  [TD §4.3 master-mirror layout and
