@@ -629,7 +629,7 @@ ROOFLINE_KERNEL = {
     "c2": "kvfix apply_kernel<bf16, fp32, hd128, rotate-half, rank 4>",
     "c3": "kvfix diff_decode_kernel<bf16, hd128, rotate-half> (with its rotary-table pre-kernel)",
     "c4": "kvfix apply_kernel<bf16, fp32, hd128, rotate-half, rank 0>",
-    "c5": "kvfix apply_kernel_wide<bf16, fp32, hd128, rotate-half, rank 2, paged>",
+    "c5": "kvfix apply_kernel<bf16, fp32, hd128, rotate-half, rank 2, paged>",
 }
 
 
