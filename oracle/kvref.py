@@ -708,6 +708,34 @@ def diff_decode(master_k: np.ndarray, master_v: np.ndarray, diff: dict,
     return out_k, out_v
 
 
+def select_master(scores: np.ndarray):
+    """The group's master: the request with the lowest total deviation.
+
+    TD §4.2 "reuse plan output": the reuse path accumulates a deviation score
+    per request, and the master is the request whose restored cache is
+    closest to the group's shared structure, usually the one with the lowest
+    total deviation from the shared blocks.  Reading: the total of request a
+    is the sum of its per-token deviation scores (the check-layer divergence
+    of a2), added in float64 in token order; the master has the lowest total,
+    ties to the lower request index.  scores: float32 [A][n] (no NaN).
+    Returns (master, totals float64 [A]).
+    """
+    scores = np.asarray(scores, dtype=np.float32)
+    if np.isnan(scores).any():
+        raise ValueError("NaN score")
+    A, n = scores.shape
+    if A == 0:
+        raise ValueError("empty group")
+    totals = np.zeros(A, dtype=np.float64)
+    for a in range(A):
+        acc = 0.0
+        for j in range(n):
+            acc += float(scores[a, j])
+        totals[a] = acc
+    master = min(range(A), key=lambda a: (totals[a], a))
+    return master, totals
+
+
 def mirror_ratio(full_bytes: int, diff_bytes: int) -> float:
     """Compression R of one mirror: its dense size over its diff size
     (TD §6.4: R = 11.2 means a mirror costs about 9 % of a full cache)."""

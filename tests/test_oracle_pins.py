@@ -900,3 +900,45 @@ def test_cover_splits_the_segment_at_the_covered_prefix():
         inside, past = rows[rows < cover[s]], rows[rows >= cover[s]]
         assert np.array_equal(out[:, s][:, :, past], shifted[:, s][:, :, past])
         assert np.array_equal(out[:, s][:, :, inside], full[:, s][:, :, inside])
+
+
+# ----------------------------------------------------------------------------
+# Master selection (TD §4.2 "reuse plan output")
+# ----------------------------------------------------------------------------
+
+
+def test_select_master_hand_example_and_ties():
+    m, tot = K.select_master(np.array([[1, 2, 3], [0.5, 0.5, 0.5], [1, 1, 1]], np.float32))
+    assert m == 1 and tot.tolist() == [6.0, 1.5, 3.0]
+    # equal totals go to the lower request index
+    m, _ = K.select_master(np.array([[2, 2], [1, 3], [4, 0], [5, 5]], np.float32))
+    assert m == 0
+    m, _ = K.select_master(np.array([[9, 9], [1, 3], [4, 0]], np.float32))
+    assert m == 1
+
+
+def test_select_master_prefers_the_request_without_deviation():
+    # a request whose cache equals the shared blocks has zero divergence at
+    # every token: it is the master whatever the others look like
+    rng = np.random.default_rng(50)
+    sc = rng.random((6, 500)).astype(np.float32) + 0.01
+    sc[4] = 0.0
+    assert K.select_master(sc)[0] == 4
+
+
+def test_select_master_total_is_the_token_order_sum_of_the_l2_scores():
+    # the deviation of a request against the shared blocks: per-token L2
+    # divergence of its keys from the shared keys re-aligned to its frame
+    rng = np.random.default_rng(51)
+    A, H, n, hd = 4, 2, 64, 8
+    shared = K.store(rng.standard_normal((1, 1, H, n, hd)), "f32")
+    agents = np.repeat(shared, A, axis=1).copy()
+    planted = [5, 1, 3, 0]
+    for a, nb in enumerate(planted):
+        rows = rng.choice(n, nb * 4, replace=False)
+        agents[0, a][:, rows] += np.float32(0.5)
+    sc = K.score_l2(agents, np.repeat(shared, A, axis=1), "f32", 0)
+    m, tot = K.select_master(sc)
+    assert m == 3 and tot[3] == 0.0
+    assert np.argsort(tot, kind="stable").tolist() == np.argsort(planted, kind="stable").tolist()
+    assert tot[0] == sum(float(x) for x in sc[0])
