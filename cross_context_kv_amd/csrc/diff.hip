@@ -60,6 +60,7 @@ __device__ __forceinline__ void load_table(const double2* tab, int seg, int g, d
 // Agents handled per pass over a block's master rows: their rotary tables
 // sit in LDS, and the master rows are read from HBM once per pass.
 constexpr int kAgentGroup = 16;
+constexpr int kMaxBlockTokens = 64;      // the largest diff block (validated on the host)
 
 // Copy the tables of agents [a0, a0 + na) into LDS (whole block).
 template <int HD>
@@ -292,6 +293,9 @@ __global__ __launch_bounds__(kDiffBlock) void diff_decode_kernel(DecodeParams P,
   constexpr int V = M::V, G = M::G, RPB = kDiffBlock / G;
   __shared__ double2 stab[kAgentGroup][HD / 2];
   __shared__ int64_t sslot[kAgentGroup];       // packed slot of the agent's block, or -1
+  // page ids of the group's output rows (paged output planes: the slot
+  // mapping), staged once per group so that no store waits on a table read
+  __shared__ int32_t spk[kAgentGroup * kMaxBlockTokens], spv[kAgentGroup * kMaxBlockTokens];
   const int g = threadIdx.x % G, rr = threadIdx.x / G;
   const int beta = blockIdx.x % P.nb;
   const int l = blockIdx.x / P.nb;
@@ -314,6 +318,11 @@ __global__ __launch_bounds__(kDiffBlock) void diff_decode_kernel(DecodeParams P,
         if (slot >= P.capacity) slot = -1;      // never read past the packed values
       }
       sslot[threadIdx.x] = slot;
+    }
+    for (int i = threadIdx.x; i < na * tb; i += kDiffBlock) {
+      const int a = i / tb, t = i % tb;
+      spk[a * kMaxBlockTokens + t] = page_of(P.ok, a0 + a, t0 + t);
+      spv[a * kMaxBlockTokens + t] = page_of(P.ov, a0 + a, t0 + t);
     }
     __syncthreads();
     for (int r = rr; r < rows; r += RPB) {
@@ -346,8 +355,8 @@ __global__ __launch_bounds__(kDiffBlock) void diff_decode_kernel(DecodeParams P,
         parts_to_pairs<STYLE, V>(p0, p1, xa, xb);
         rotate_pairs<V>(xa, xb, cs, sn);
         pairs_to_parts<STYLE, V>(xa, xb, p0, p1);
-        const int64_t ko = row_offset(P.ok, l, a0 + a, h, t0 + t);
-        const int64_t vo = row_offset(P.ov, l, a0 + a, h, t0 + t);
+        const int64_t ko = row_offset_page(P.ok, l, a0 + a, h, t0 + t, spk[a * kMaxBlockTokens + t]);
+        const int64_t vo = row_offset_page(P.ov, l, a0 + a, h, t0 + t, spv[a * kMaxBlockTokens + t]);
         if (ko >= 0) {
           T* dk = reinterpret_cast<T*>(P.ok.data) + ko;
           st16(dk + M::off0(g), Cd::pack(p0));
@@ -360,6 +369,49 @@ __global__ __launch_bounds__(kDiffBlock) void diff_decode_kernel(DecodeParams P,
         }
       }
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// master selection (TD §4.2, reuse plan output): the request with the lowest
+// total deviation.  Lane 0 of wave w sums the scores of requests w, w + 16,
+// ... in token order in fp64 (the order of the definition, so the totals are
+// exact copies of a sequential sum; loads go in batches of 8); thread 0 then
+// takes the lowest total, ties to the lower index, a NaN total last.
+// ---------------------------------------------------------------------------
+
+constexpr int kMasterBlock = 1024;
+
+__global__ __launch_bounds__(kMasterBlock) void select_master_kernel(const float* __restrict__ scores,
+                                                                     int A, int n,
+                                                                     double* __restrict__ totals,
+                                                                     int32_t* __restrict__ master) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  for (int a = wave; a < A; a += kMasterBlock / kWave) {
+    if (lane == 0) {
+      const float* p = scores + (int64_t)a * n;
+      double acc = 0.0;
+      int j = 0;
+      for (; j + 8 <= n; j += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = p[j + u];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += (double)v[u];
+      }
+      for (; j < n; ++j) acc += (double)p[j];
+      totals[a] = acc;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int best = 0;
+    double bv = totals[0];
+    for (int a = 1; a < A; ++a) {
+      const double v = totals[a];
+      if (v < bv || (bv != bv && v == v)) { bv = v; best = a; }
+    }
+    *master = best;
   }
 }
 
@@ -435,7 +487,8 @@ inline kvfix_status check_group(const kvfix_plane* mk, const kvfix_plane* mv,
 
 inline kvfix_status check_diff(const kvfix_diff* d) {
   if (d == nullptr || d->offsets == nullptr) return KVFIX_ERR_ARG;
-  if (d->block_tokens < 1 || d->block_tokens > 64 || d->capacity_blocks < 0) return KVFIX_ERR_ARG;
+  if (d->block_tokens < 1 || d->block_tokens > kMaxBlockTokens || d->capacity_blocks < 0)
+    return KVFIX_ERR_ARG;
   if (d->capacity_blocks > 0 && (d->block_idx == nullptr || d->vals_k == nullptr ||
                                  d->vals_v == nullptr))
     return KVFIX_ERR_ARG;
@@ -551,4 +604,14 @@ extern "C" kvfix_status kvfix_diff_decode(const kvfix_plane* master_k, const kvf
   P.A = A; P.L = L; P.H = out_k->n_heads; P.n = n; P.bt = bt; P.nb = nb; P.words = words;
   return dispatch_rot<DecodeLaunch>(master_k->dtype, master_k->head_dim, from_master->style, P,
                                     (const double2*)tab, st);
+}
+
+extern "C" kvfix_status kvfix_select_master(const float* scores, int32_t n_agents, int32_t n,
+                                            double* totals, int32_t* master, void* stream) {
+  if (n_agents < 1 || n < 0 || (scores == nullptr && n > 0) || totals == nullptr ||
+      master == nullptr)
+    return KVFIX_ERR_ARG;
+  select_master_kernel<<<dim3(1), dim3(kMasterBlock), 0, (hipStream_t)stream>>>(
+      scores, n_agents, n, totals, master);
+  return launch_status();
 }

@@ -23,6 +23,7 @@ STATUS = {0: "KVFIX_OK", 1: "KVFIX_ERR_ARG", 2: "KVFIX_ERR_ALIGN", 3: "KVFIX_ERR
 EXPORTS = ("kvfix_rope_shift", "kvfix_score", "kvfix_score_draft_workspace", "kvfix_score_draft",
            "kvfix_select_topb", "kvfix_chunk_budget", "kvfix_chunk_means", "kvfix_expand_chunks",
            "kvfix_select_grow", "kvfix_score_ex", "kvfix_fit_mean_ex", "kvfix_apply_ex",
+           "kvfix_select_master",
            "kvfix_fit_mean_workspace", "kvfix_fit_mean", "kvfix_apply", "kvfix_diff_encode_workspace",
            "kvfix_diff_encode", "kvfix_diff_decode_workspace", "kvfix_diff_decode",
            "kvfix_status_string", "kvfix_version")
@@ -101,6 +102,7 @@ def lib() -> ctypes.CDLL:
             "kvfix_score_ex": [P, I32, P, I32, P, P, P, P],
             "kvfix_fit_mean_ex": [P, I32, P, P, P, I32, P, P, P, P, P, ctypes.c_size_t, P],
             "kvfix_apply_ex": [P, P, P, P, F, F, P, P, P, P, P],
+            "kvfix_select_master": [P, I32, I32, P, P, P],
             "kvfix_fit_mean_workspace": [I32, I32, I32, I32, I32],
             "kvfix_fit_mean": [P, I32, P, P, P, I32, P, P, P, P, ctypes.c_size_t, P],
             "kvfix_apply": [P, P, P, P, F, F, P, P, P, P],
@@ -274,6 +276,13 @@ def kvfix_select_grow(scores: torch.Tensor, b: int, tau: float, idx: torch.Tenso
     n_rows, n = scores.shape
     _check("kvfix_select_grow", lib().kvfix_select_grow(_ptr(scores), n_rows, n, b, float(tau),
                                                         _ptr(idx), _ptr(mask), _stream()))
+
+
+def kvfix_select_master(scores: torch.Tensor, totals: torch.Tensor, master: torch.Tensor) -> None:
+    """scores fp32 [n_agents][n]; totals fp64 [n_agents]; master int32 [1] (all device)."""
+    A, n = scores.shape
+    _check("kvfix_select_master", lib().kvfix_select_master(_ptr(scores), A, n, _ptr(totals),
+                                                            _ptr(master), _stream()))
 
 
 def kvfix_fit_mean_workspace(n_layers: int, n_segs: int, n_heads: int, head_dim: int,

@@ -18,6 +18,7 @@
  *   kvfix_*_ex         the same with per-head probe sets and a covered prefix
  *   kvfix_diff_encode  block-sparse diff of N sibling caches against a master
  *   kvfix_diff_decode  fused restore: master + diff blocks + rotation, per sibling
+ *   kvfix_select_master  the group's master: lowest total deviation
  *
  * Sources (page titles; sections named, not quoted):
  *   [KVCMAS] "KVCMAS: Efficient KV cache Correction for Shared Context in
@@ -292,6 +293,21 @@ kvfix_status kvfix_apply(const kvfix_plane* reuse, const kvfix_plane* out,
                          const uint32_t* mask, const float* scores, float w_lo, float w_hi,
                          const float* mu, const kvfix_lowrank* lowrank,
                          const kvfix_rope* rope, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Master selection.  [TD §4.2 "reuse plan output": the reuse path accumulates
+ * a deviation score per request, and the master of a group is the request
+ * closest to the group's shared structure, usually the one with the lowest
+ * total deviation from the shared blocks]
+ * totals[a] = sum over j of scores[a][j], added in fp64 in token order;
+ * *master = the a with the lowest total, ties to the lower index (a NaN
+ * total ranks last).  The scores are per-token deviation scores, e.g.
+ * kvfix_score of each request's cache against the shared blocks at the
+ * check layer.  scores: device fp32 [n_agents][n]; totals: device fp64
+ * [n_agents]; master: device int32 [1].  n_agents >= 1.
+ * ------------------------------------------------------------------------- */
+kvfix_status kvfix_select_master(const float* scores, int32_t n_agents, int32_t n,
+                                 double* totals, int32_t* master, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Probe granularity and covered prefix.  [AKS "Core idea and method": the

@@ -1,0 +1,116 @@
+"""GPU parity of the group's master selection and of the fused restore into a
+paged pool (TD §4.2 reuse plan output; TD Algorithm 1, the paged write
+through the slot mapping).
+
+Totals of the master selection are compared bit for bit (both sides add in
+fp64 in token order) and the master index exactly; the paged restore must
+equal the dense restore bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+from helpers import from_np, log, to_np
+from oracle import kvref as K
+from test_gpu_draft_diff import collective_case, gpu_encode
+
+import cross_context_kv_amd.kvfix as kv
+from cross_context_kv_amd.kvfix import Plane
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def gpu_master(sc: np.ndarray):
+    A = sc.shape[0]
+    t = torch.from_numpy(sc).to(DEV)
+    totals = torch.full((A,), float("nan"), dtype=torch.float64, device=DEV)
+    master = torch.full((1,), -7, dtype=torch.int32, device=DEV)
+    kv.kvfix_select_master(t, totals, master)
+    torch.cuda.synchronize()
+    return int(master.item()), totals.cpu().numpy()
+
+
+@pytest.mark.parametrize("A,n", [(1, 100), (3, 1), (16, 8192), (40, 8193), (5, 0), (17, 333)])
+def test_select_master_matches_oracle(A, n):
+    rng = np.random.default_rng(A * 1000 + n)
+    sc = (np.exp(rng.standard_normal((A, n))) * 10.0 ** rng.integers(-3, 3, (A, 1))).astype(np.float32)
+    log("select master", A, n)
+    m, tot = gpu_master(sc)
+    om, otot = K.select_master(sc)
+    assert np.array_equal(tot.view(np.uint64), otot.view(np.uint64))
+    assert m == om
+
+
+def test_select_master_ties_go_to_the_lower_index():
+    sc = np.array([[3, 1], [2, 2], [1, 3], [0, 5]], np.float32)   # totals 4, 4, 4, 5
+    assert gpu_master(sc)[0] == 0
+    sc = np.array([[9, 9], [2, 2], [1, 3], [0, 4]], np.float32)
+    assert gpu_master(sc)[0] == 1
+
+
+def test_select_master_on_collective_deviation_scores():
+    """Each agent's deviation from the shared blocks at the check layer: its
+    keys against the shared keys moved to the agent's frame.  The master is
+    an agent with the fewest planted blocks."""
+    cfg, raw, offs, mk, mv, sk, sv = collective_case(A=6, L=2, H=2, n=200)
+    A, n, c = cfg.n_segs, cfg.n_tokens, 1
+    shared = from_np(mk, DEV).expand(-1, A, -1, -1, -1)         # s_seg = 0: one source
+    agents = from_np(sk, DEV)
+    delta = torch.tensor(offs, dtype=torch.int64, device=DEV)
+    scores = torch.empty(A, n, dtype=torch.float32, device=DEV)
+    log("collective deviation scores", A, n)
+    kv.kvfix_score(Plane.dense(agents), c, Plane.dense(shared), c, scores, delta, cfg.theta)
+    torch.cuda.synchronize()
+    g_sc = scores.cpu().numpy()
+    m, tot = gpu_master(g_sc)
+    om, otot = K.select_master(g_sc)
+    assert m == om and np.array_equal(tot.view(np.uint64), otot.view(np.uint64))
+    planted = raw["planted"].numpy().sum(axis=1)
+    assert planted[m] == planted.min(), (m, planted.tolist(), tot.tolist())
+
+
+@pytest.mark.parametrize("page_size", [16, 8, 5])
+def test_decode_into_paged_pool_equals_dense(page_size):
+    cfg, raw, offs, mk, mv, sk, sv = collective_case(A=5, L=2, H=2, n=101)
+    A, L, H, n, hd, bt = cfg.n_segs, cfg.n_layers, cfg.n_kv_heads, cfg.n_tokens, cfg.head_dim, \
+        cfg.block_tokens
+    o = K.diff_encode(mk, mv, sk, sv, [-x for x in offs], cfg.theta, cfg.eps, bt, "half", "bf16")
+    diff, status, t = gpu_encode(mk, mv, sk, sv, [-x for x in offs], cfg.theta, cfg.eps, bt,
+                                 o["total"] + 3)
+    assert status == 0
+    ws = torch.empty(kv.kvfix_diff_decode_workspace(A, hd) + 256, dtype=torch.uint8, device=DEV)
+    d = torch.tensor(offs, dtype=torch.int64, device=DEV)
+    ok = torch.full((L, A, H, n, hd), float("nan"), dtype=torch.bfloat16, device=DEV)
+    ov = torch.full_like(ok, float("nan"))
+    log("decode dense", page_size)
+    kv.kvfix_diff_decode(Plane.dense(t["mk"]), Plane.dense(t["mv"]), diff, d, cfg.theta,
+                         Plane.dense(ok), Plane.dense(ov), ws)
+    pps = -(-n // page_size)
+    n_pages = A * pps + 7
+    rng = np.random.default_rng(page_size)
+    pt_np = rng.permutation(n_pages)[: A * pps].reshape(A, pps).astype(np.int32)
+    pt_np[2, 3] = -1                       # bad page ids: those rows are not written
+    pt_np[4, 0] = n_pages + 5
+    pt = torch.from_numpy(pt_np).to(DEV)
+    pool_k = torch.full((L, n_pages, page_size, H, hd), float("nan"), dtype=torch.bfloat16,
+                        device=DEV)
+    pool_v = torch.full_like(pool_k, float("nan"))
+    log("decode paged", page_size)
+    kv.kvfix_diff_decode(Plane.dense(t["mk"]), Plane.dense(t["mv"]), diff, d, cfg.theta,
+                         Plane.paged(pool_k, pt, page_size, n), Plane.paged(pool_v, pt, page_size, n),
+                         ws)
+    torch.cuda.synchronize()
+    dk, dv = to_np(ok), to_np(ov)
+    pk, pv = to_np(pool_k), to_np(pool_v)
+    nan_bits = to_np(torch.full((1,), float("nan"), dtype=torch.bfloat16))[0]
+    for a in range(A):
+        for j in range(n):
+            page = pt_np[a, j // page_size]
+            if 0 <= page < n_pages:
+                assert np.array_equal(pk[:, page, j % page_size], dk[:, a, :, j]), (a, j)
+                assert np.array_equal(pv[:, page, j % page_size], dv[:, a, :, j]), (a, j)
+    # the pages no row maps to, and the rows of bad ids, are untouched
+    used = set(int(p) for p in pt_np.ravel() if 0 <= p < n_pages)
+    for p in range(n_pages):
+        if p not in used:
+            assert np.all(pk[:, p] == nan_bits) and np.all(pv[:, p] == nan_bits)
