@@ -25,7 +25,9 @@ sample of the same workload.
 
   c4 takes --layout: rows (top b), chunk (BCR-chunk: 64-token chunks by mean
   draft mass), coin (the same budget in random chunks, no draft) or grow
-  (BCR-grow spans, tau 0.25).
+  (BCR-grow spans, tau 0.25).  c3 takes --layout: dense (default), paged
+  (restore into a paged pool through a slot mapping) or plan (the reuse plan
+  first: deviation scores of every agent and the master selection).
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload c2]
                   [--layout rows] [--no-cpu-baseline]
@@ -539,11 +541,22 @@ class C4(Workload):
 class C3(Workload):
     name = "c3"
     kernel_tag = "diff_decode"
+    # restore into dense planes, into a paged pool through a slot mapping
+    # (page 16, seeded permutation), or with the reuse plan first (deviation
+    # score of every agent against the shared blocks at check layer 1, then
+    # the master selection)
+    layout = "dense"
+    LAYOUT_TEXT = {"dense": "restore of all 16 caches into dense planes",
+                   "paged": "restore of all 16 caches into a paged pool (16-token pages, seeded "
+                            "slot mapping)",
+                   "plan": "reuse plan first (every agent's check-layer deviation from the shared "
+                           "blocks, master = lowest total), then restore into dense planes"}
+    CHECK = 1
 
     def workload_text(self):
         return ("c3_collective: 16 agents x 32 layers x 8 KV heads x 8192 tokens x hd 128 bf16 at "
                 "distinct offsets in [0,16384]; 16-token blocks, 3-9 % planted, eps 0.0625; "
-                "diff encode against the master, then restore of all 16 caches, theta 5e5")
+                f"diff encode against the master, then {self.LAYOUT_TEXT[self.layout]}, theta 5e5")
 
     def alg_bytes(self, total_blocks=None):
         c = self.cfg
@@ -556,8 +569,14 @@ class C3(Workload):
         meta = A * L * (-(-nb // 32)) * 4 + (A * L + 1) * 8 + tot * 4
         encode = 2 * A * plane + 2 * plane + 2 * tot * blk + meta
         decode = 2 * plane + 2 * tot * blk + meta + 2 * A * plane
-        return {"encode": encode, "decode": decode, "roofline_per_launch": decode,
-                "roofline_units": A * L * H * n, "total": encode + decode}
+        if self.layout == "paged":
+            decode += A * (-(-n // 16)) * 4                  # the slot mapping
+        plan = 0
+        if self.layout == "plan":                            # one layer of K, agents and shared
+            layer = H * n * hd * 2
+            plan = 2 * A * layer + A * n * 4 + A * n * 4 + A * 8 + 4
+        return {"plan": plan, "encode": encode, "decode": decode, "roofline_per_launch": decode,
+                "roofline_units": A * L * H * n, "total": plan + encode + decode}
 
     def build(self):
         torch, kv, c = self.torch, self.kv, self.cfg
@@ -565,10 +584,20 @@ class C3(Workload):
         L, A, H, n, hd, bt = (c.n_layers, c.n_segs, c.n_kv_heads, c.n_tokens, c.head_dim,
                               c.block_tokens)
         t = {}
+        pps = -(-n // 16)
         for p in "kv":
             t["m_" + p] = torch.empty(L, 1, H, n, hd, dtype=torch.bfloat16, device="cuda")
             t["s_" + p] = torch.empty(L, A, H, n, hd, dtype=torch.bfloat16, device="cuda")
-            t["o_" + p] = torch.empty(L, A, H, n, hd, dtype=torch.bfloat16, device="cuda")
+            if self.layout == "paged":
+                t["o_" + p] = torch.empty(L, A * pps, 16, H, hd, dtype=torch.bfloat16,
+                                          device="cuda")
+            else:
+                t["o_" + p] = torch.empty(L, A, H, n, hd, dtype=torch.bfloat16, device="cuda")
+        if self.layout == "paged":
+            from synthetic.workloads import make_gen
+            g = make_gen("cpu", c.seed, "restore_pages")
+            t["pt"] = torch.randperm(A * pps, generator=g).to(torch.int32).reshape(A, pps).to(
+                "cuda")
         planted = offs = None
         for l in range(L):
             raw = draw_collective(c, "cuda", layers=[l])
@@ -587,12 +616,24 @@ class C3(Workload):
         t["ws_d"] = torch.empty(kv.kvfix_diff_decode_workspace(A, hd) + 256, dtype=torch.uint8,
                                 device="cuda")
         P = kv.Plane.dense
-        self.planes = {k: P(t[k]) for k in ("m_k", "m_v", "s_k", "s_v", "o_k", "o_v")}
+        self.planes = {k: P(t[k]) for k in ("m_k", "m_v", "s_k", "s_v")}
+        for k in ("o_k", "o_v"):
+            self.planes[k] = (kv.Plane.paged(t[k], t["pt"], 16, n) if self.layout == "paged"
+                              else P(t[k]))
+        if self.layout == "plan":
+            self.planes["shared_k"] = P(t["m_k"].expand(-1, A, -1, -1, -1))
+            t["dev"] = torch.empty(A, n, dtype=torch.float32, device="cuda")
+            t["totals"] = torch.empty(A, dtype=torch.float64, device="cuda")
+            t["master"] = torch.empty(1, dtype=torch.int32, device="cuda")
         self.t = t
         torch.cuda.synchronize()
 
     def step(self):
         kv, t, c, P = self.kv, self.t, self.cfg, self.planes
+        if self.layout == "plan":
+            kv.kvfix_score(P["s_k"], self.CHECK, P["shared_k"], self.CHECK, t["dev"],
+                           t["from_m"], c.theta)
+            kv.kvfix_select_master(t["dev"], t["totals"], t["master"])
         kv.kvfix_diff_encode(P["m_k"], P["m_v"], P["s_k"], P["s_v"], t["to_m"], c.theta, c.eps,
                              self.diff, t["status"], t["ws_e"])
         with self.timed:
@@ -606,21 +647,31 @@ class C3(Workload):
         from oracle import kvref as K
         d = {k: host(t[k][:1], torch, np) for k in ("m_k", "m_v", "s_k", "s_v")}
         offs = [int(v) for v in t["from_m"].tolist()]
+        plan = self.layout == "plan"
+        if plan:
+            ck = {k: host(t[k][self.CHECK:self.CHECK + 1], torch, np) for k in ("m_k", "s_k")}
         box = {}
 
         def run():
+            if plan:
+                A = c.n_segs
+                dev = K.score_l2(ck["s_k"], np.repeat(ck["m_k"], A, axis=1), "bf16", 0, offs,
+                                 c.theta)
+                K.select_master(dev)
             o = K.diff_encode(d["m_k"], d["m_v"], d["s_k"], d["s_v"], [-x for x in offs],
                               c.theta, c.eps, c.block_tokens)
             K.diff_decode(d["m_k"], d["m_v"], o, offs, c.theta, c.n_segs, c.block_tokens)
             box["total"] = o["total"]
 
         dt = timed_oracle(run, 1)
-        sub = C3.alg_bytes(type("X", (), {"cfg": c.replace(n_layers=1), "total": box["total"]})())
-        nbytes = sub["total"]
+        sub = C3.__new__(C3)
+        sub.cfg, sub.total, sub.layout = c.replace(n_layers=1), box["total"], self.layout
+        nbytes = sub.alg_bytes()["total"]
+        what = "the reuse plan (check layer) and " if plan else ""
         return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-                "sample": f"encode + restore of layer 0 (1 of {c.n_layers}) for all {c.n_segs} "
-                          f"agents ({nbytes / 1e6:.1f} MB algorithmic), one run of {dt:.1f} s, "
-                          f"numpy fp64, one thread"}
+                "sample": f"{what}encode + restore of layer 0 (1 of {c.n_layers}) for all "
+                          f"{c.n_segs} agents ({nbytes / 1e6:.1f} MB algorithmic), one run of "
+                          f"{dt:.1f} s, numpy fp64, one thread"}
 
 
 Workload.ALL = {"c2": C2, "c3": C3, "c4": C4, "c5": C5}
@@ -655,12 +706,14 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c2", choices=sorted(Workload.ALL))
-    ap.add_argument("--layout", default="rows", choices=sorted(C4.LAYOUT_TEXT),
-                    help="probe layout of the c4 workload (BCR layouts and the coin control)")
+    ap.add_argument("--layout", default=None,
+                    help="c4: probe layout rows|chunk|coin|grow (BCR layouts and the coin "
+                         "control); c3: restore target dense|paged, or plan (reuse plan first)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
-    if args.layout != "rows" and args.workload != "c4":
-        print("--layout applies to the c4 workload only", file=sys.stderr)
+    W = Workload.ALL[args.workload]
+    if args.layout is not None and args.layout not in getattr(W, "LAYOUT_TEXT", {}):
+        print(f"--layout {args.layout} does not apply to {args.workload}", file=sys.stderr)
         sys.exit(2)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
@@ -673,8 +726,8 @@ def main():
     import cross_context_kv_amd.kvfix as kv
     from synthetic import CONFIGS
     kv.lib()                          # fails loudly without the built library
-    w = Workload.ALL[args.workload](CONFIGS[args.workload], torch, kv)
-    if args.layout != "rows":
+    w = W(CONFIGS[args.workload], torch, kv)
+    if args.layout is not None:
         w.layout = args.layout
     w.build()
     for _ in range(args.warmup):

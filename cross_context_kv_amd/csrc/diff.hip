@@ -374,10 +374,10 @@ __global__ __launch_bounds__(kDiffBlock) void diff_decode_kernel(DecodeParams P,
 
 // ---------------------------------------------------------------------------
 // master selection (TD §4.2, reuse plan output): the request with the lowest
-// total deviation.  Lane 0 of wave w sums the scores of requests w, w + 16,
-// ... in token order in fp64 (the order of the definition, so the totals are
-// exact copies of a sequential sum; loads go in batches of 8); thread 0 then
-// takes the lowest total, ties to the lower index, a NaN total last.
+// total deviation.  Wave w sums the scores of requests w, w + 16, ... in
+// fp64 in the order the definition fixes: lane k sums whole 64-token blocks
+// in token order, then the block sums are added in block order; thread 0
+// then takes the lowest total, ties to the lower index, a NaN total last.
 // ---------------------------------------------------------------------------
 
 constexpr int kMasterBlock = 1024;
@@ -387,21 +387,37 @@ __global__ __launch_bounds__(kMasterBlock) void select_master_kernel(const float
                                                                      double* __restrict__ totals,
                                                                      int32_t* __restrict__ master) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int nblk = (n + 63) / 64;
   for (int a = wave; a < A; a += kMasterBlock / kWave) {
-    if (lane == 0) {
-      const float* p = scores + (int64_t)a * n;
-      double acc = 0.0;
-      int j = 0;
-      for (; j + 8 <= n; j += 8) {
-        float v[8];
+    const float* p = scores + (int64_t)a * n;
+    double total = 0.0;
+    for (int b0 = 0; b0 < nblk; b0 += kWave) {
+      // lane k: the sum of block b0 + k, its tokens in order
+      const int bk = b0 + lane;
+      double blk = 0.0;
+      if (bk < nblk) {
+        const int j0 = bk * 64, j1 = min(j0 + 64, n);
+        for (int j = j0; j < j1; j += 8) {
+          float v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = p[j + u];
+          for (int u = 0; u < 8; ++u) v[u] = j + u < j1 ? p[j + u] : 0.0f;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) acc += (double)v[u];
+          for (int u = 0; u < 8; ++u)
+            if (j + u < j1) blk += (double)v[u];
+        }
       }
-      for (; j < n; ++j) acc += (double)p[j];
-      totals[a] = acc;
+      // the block sums, in block order
+      const int cnt = min(kWave, nblk - b0);
+      for (int k = 0; k < cnt; ++k) {
+        const uint64_t bits = (uint64_t)(uint32_t)__builtin_amdgcn_readlane(
+                                  (int)(uint32_t)__double_as_longlong(blk), k) |
+                              (uint64_t)(uint32_t)__builtin_amdgcn_readlane(
+                                  (int)(uint32_t)(__double_as_longlong(blk) >> 32), k)
+                                  << 32;
+        total += __longlong_as_double((long long)bits);
+      }
     }
+    if (lane == 0) totals[a] = total;
   }
   __syncthreads();
   if (threadIdx.x == 0) {

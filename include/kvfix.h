@@ -299,7 +299,8 @@ kvfix_status kvfix_apply(const kvfix_plane* reuse, const kvfix_plane* out,
  * a deviation score per request, and the master of a group is the request
  * closest to the group's shared structure, usually the one with the lowest
  * total deviation from the shared blocks]
- * totals[a] = sum over j of scores[a][j], added in fp64 in token order;
+ * totals[a] = sum over j of scores[a][j] in fp64, added in a fixed order:
+ * each 64-token block in token order, then the block sums in block order;
  * *master = the a with the lowest total, ties to the lower index (a NaN
  * total ranks last).  The scores are per-token deviation scores, e.g.
  * kvfix_score of each request's cache against the shared blocks at the

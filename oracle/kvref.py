@@ -716,9 +716,11 @@ def select_master(scores: np.ndarray):
     closest to the group's shared structure, usually the one with the lowest
     total deviation from the shared blocks.  Reading: the total of request a
     is the sum of its per-token deviation scores (the check-layer divergence
-    of a2), added in float64 in token order; the master has the lowest total,
-    ties to the lower request index.  scores: float32 [A][n] (no NaN).
-    Returns (master, totals float64 [A]).
+    of a2) in float64, added in this order: the tokens of each 64-token block
+    in token order, then the block sums in block order (the pages fix no
+    order; this one is fixed so that both sides add the same numbers the same
+    way).  The master has the lowest total, ties to the lower request index.
+    scores: float32 [A][n] (no NaN).  Returns (master, totals float64 [A]).
     """
     scores = np.asarray(scores, dtype=np.float32)
     if np.isnan(scores).any():
@@ -728,10 +730,13 @@ def select_master(scores: np.ndarray):
         raise ValueError("empty group")
     totals = np.zeros(A, dtype=np.float64)
     for a in range(A):
-        acc = 0.0
-        for j in range(n):
-            acc += float(scores[a, j])
-        totals[a] = acc
+        total = 0.0
+        for j0 in range(0, n, 64):
+            block = 0.0
+            for j in range(j0, min(j0 + 64, n)):
+                block += float(scores[a, j])
+            total += block
+        totals[a] = total
     master = min(range(A), key=lambda a: (totals[a], a))
     return master, totals
 

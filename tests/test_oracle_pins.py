@@ -941,4 +941,6 @@ def test_select_master_total_is_the_token_order_sum_of_the_l2_scores():
     m, tot = K.select_master(sc)
     assert m == 3 and tot[3] == 0.0
     assert np.argsort(tot, kind="stable").tolist() == np.argsort(planted, kind="stable").tolist()
-    assert tot[0] == sum(float(x) for x in sc[0])
+    # the total: 64-token block sums in token order, then the blocks in order
+    assert tot[0] == sum(sum(float(x) for x in sc[0][j:j + 64]) for j in range(0, n, 64))
+    assert abs(tot[0] - math.fsum(float(x) for x in sc[0])) <= 1e-12 * tot[0]
