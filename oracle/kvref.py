@@ -521,6 +521,160 @@ def correct(fresh, reuse, dtype, idx, mask, scores=None, w_lo=0.0, w_hi=1.0, A=N
 
 
 # ----------------------------------------------------------------------------
+# Anchor-blended low-rank correction and the reliability gate
+# (KVCMAS eq. 7: low-rank factors A B of each anchor's base cache and delta
+#  correction; eq. 8: the correction is the weighted sum of the anchors'
+#  deltas; App. A.3 "Reliability Gate" eq. 9-11, "Correction Weighting and
+#  Positional Alignment" (token-wise weights from the mean absolute source
+#  distance, softmax with T = 1, keys compared in canonical positions) and
+#  "Variable Segment Lengths"; eq. 4, 6 and 12: the correction is added to
+#  the aligned source cache)
+#
+# Layouts: an anchor pool of V anchors holds, per anchor v, layer l and plane
+# p (0 = K, 1 = V), A factors a[v][l][p][n_max][r] and the transposed B
+# factors bt[v][l][p][H*hd][r], both bf16 bit patterns; a row's feature
+# index is h*hd + d (all heads of a token).  Factors are in canonical
+# (segment-relative) positions; the source plane holds one segment.
+# ----------------------------------------------------------------------------
+
+
+def anchor_eligible(lengths: Sequence[int], n: int):
+    """Anchors that correct an n-token segment, and the covered prefix: those
+    covering the whole segment; if none does, those covering the longest
+    prefix, which is then the covered prefix."""
+    full = [v for v, ln in enumerate(lengths) if ln >= n]
+    if full:
+        return full, n
+    m = max(list(lengths) + [0])
+    if m <= 0:
+        return [], 0
+    return [v for v, ln in enumerate(lengths) if ln == m], m
+
+
+def anchor_recon(a: np.ndarray, bt: np.ndarray, v: int, l: int, p: int, rows) -> np.ndarray:
+    """Anchor v's reconstruction A B (eq. 7) of `rows` at layer l, plane p:
+    float64 [len(rows)][H*hd]."""
+    A = bf16_to_f64(a[v, l, p][np.asarray(rows, dtype=np.int64)])     # [m][r]
+    Bt = bf16_to_f64(bt[v, l, p])                                       # [D][r]
+    return A @ Bt.T
+
+
+def _token_rows(x: np.ndarray) -> np.ndarray:
+    """[H][n][hd] -> [n][H*hd] (all heads of a token in one row)."""
+    H, n, hd = x.shape
+    return x.transpose(1, 0, 2).reshape(n, H * hd)
+
+
+def anchor_gate_decide(d: Sequence[float], tau: float) -> dict:
+    """Gate weights, normalized entropy and decision from the distances of
+    the compared anchors (KVCMAS eq. 10-11 and the rule after them):
+    g = softmax(-d / T) with T = 1; Hbar = -sum g log2 g / log2 |A_k|,
+    clamped to [0, 1], its mathematical range, so that tau >= 1 never
+    refuses; accept iff |A_k| >= 2 and Hbar <= tau."""
+    d = np.asarray(d, dtype=np.float64)
+    if d.size < 2:
+        return {"g": np.ones(d.size), "hbar": float("nan"), "accept": False}
+    z = -d
+    e = np.exp(z - z.max())
+    g = e / e.sum()
+    terms = np.where(g > 0, g * np.log2(np.where(g > 0, g, 1.0)), 0.0)
+    hbar = float(min(1.0, max(0.0, -terms.sum() / math.log2(d.size))))
+    return {"g": g, "hbar": hbar, "accept": hbar <= tau}
+
+
+def anchor_gate(src_v: np.ndarray, a_base: np.ndarray, bt_base: np.ndarray,
+                lengths: Sequence[int], k: int, tau: float, dtype: str) -> dict:
+    """The reliability gate (KVCMAS App. A.3, eq. 9-11).
+
+    The comparison prefix is the first k tokens of the segment (k is clamped
+    to the segment length).  Compared anchors A_k: those storing at least k
+    tokens.  d_v = the Frobenius norm, over all layers, of the source value
+    states of the prefix (all heads and dims) minus anchor v's reconstructed
+    base value states (eq. 9).  src_v: value plane [L][1][H][n][hd].
+    Returns the compared anchors, d [V] (NaN outside A_k), g, Hbar, accept.
+    """
+    L, _, H, n, hd = src_v.shape
+    k = max(0, min(int(k), n))
+    Ak = [v for v, ln in enumerate(lengths) if ln >= k]
+    d = np.full(len(lengths), np.nan)
+    for v in Ak:
+        acc = 0.0
+        for l in range(L):
+            x = _token_rows(to_f64(src_v[l, 0], dtype))[:k]
+            diff = x - anchor_recon(a_base, bt_base, v, l, 1, np.arange(k))
+            acc += float((diff * diff).sum())
+        d[v] = math.sqrt(acc)
+    dec = anchor_gate_decide(d[Ak], tau)
+    return {"Ak": Ak, "d": d, "g": dec["g"], "hbar": dec["hbar"], "accept": dec["accept"]}
+
+
+def anchor_weights(src_k: np.ndarray, src_v: np.ndarray, a_base: np.ndarray,
+                   bt_base: np.ndarray, lengths: Sequence[int], src_off: int,
+                   theta: float, style: str, dtype: str) -> np.ndarray:
+    """Token-wise interpolation weights (KVCMAS App. A.3).
+
+    For each layer, plane and covered token j: dist_v = the mean, over all
+    heads and dims, of |source row - anchor v's reconstructed base row| for
+    the eligible anchors (source keys, cached at positions src_off + j, are
+    first turned to canonical, segment-relative positions: rotated by
+    -src_off), and w_v = softmax(-dist / T), T = 1.  Returns float64
+    w [L][2][n][V], zero for anchors outside the eligible set and for rows
+    past the covered prefix.
+    """
+    L, _, H, n, hd = src_k.shape
+    V = len(lengths)
+    E, cover = anchor_eligible(lengths, n)
+    w = np.zeros((L, 2, n, V))
+    if not E:
+        return w
+    for l in range(L):
+        for p, plane in enumerate((src_k, src_v)):
+            x = to_f64(plane[l, 0], dtype)
+            if p == 0:
+                x = rope_rotate(x, -src_off, theta, style)
+            rows = _token_rows(x)[:cover]
+            dist = np.stack([np.abs(rows - anchor_recon(a_base, bt_base, v, l, p, np.arange(cover)))
+                             .mean(axis=1) for v in E], axis=1)
+            z = -dist
+            e = np.exp(z - z.max(axis=1, keepdims=True))
+            wl = w[l, p]
+            for i, v in enumerate(E):
+                wl[:cover, v] = e[:, i] / e.sum(axis=1)
+    return w
+
+
+def anchor_apply(src: np.ndarray, plane: int, a_delta: np.ndarray, bt_delta: np.ndarray,
+                 w: np.ndarray, lengths: Sequence[int], src_off: int, tgt_off: int,
+                 theta: float, style: str, dtype: str) -> np.ndarray:
+    """The corrected target cache (KVCMAS eq. 8 with the token-wise weights,
+    added to the aligned source cache, eq. 4 / 6 / 12).
+
+    delta_hat_j = sum over eligible v of w[l][plane][j][v] A_v[j] B_v, in
+    canonical positions.  Keys: out_j = R(tgt_off) (R(-src_off) x_j +
+    delta_hat_j) = R(tgt_off - src_off) x_j + R(tgt_off) delta_hat_j; values:
+    out_j = x_j + delta_hat_j; rows past the covered prefix keep the
+    re-aligned source row.  Rounded once.  src: [L][1][H][n][hd].
+    """
+    L, _, H, n, hd = src.shape
+    E, cover = anchor_eligible(lengths, n)
+    out = np.empty_like(src)
+    for l in range(L):
+        x = to_f64(src[l, 0], dtype)
+        dhat = np.zeros((n, H * hd))
+        for v in E:
+            dhat[:cover] += w[l, plane, :cover, v][:, None] * anchor_recon(
+                a_delta, bt_delta, v, l, plane, np.arange(cover))
+        dh = dhat.reshape(n, H, hd).transpose(1, 0, 2)
+        if plane == 0:
+            y = rope_rotate(x, tgt_off - src_off, theta, style) + rope_rotate(dh, tgt_off, theta,
+                                                                              style)
+        else:
+            y = x + dh
+        out[l, 0] = store(y, dtype)
+    return out
+
+
+# ----------------------------------------------------------------------------
 # a3: draft attention-mass score
 # (BCR §3 "The repair": a_j = sum over layers l > 1 of the attention the two
 #  kept draft query rows pay row j, softmax(Q K~^T / sqrt(d_head)), with

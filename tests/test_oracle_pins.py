@@ -944,3 +944,241 @@ def test_select_master_total_is_the_token_order_sum_of_the_l2_scores():
     # the total: 64-token block sums in token order, then the blocks in order
     assert tot[0] == sum(sum(float(x) for x in sc[0][j:j + 64]) for j in range(0, n, 64))
     assert abs(tot[0] - math.fsum(float(x) for x in sc[0])) <= 1e-12 * tot[0]
+
+
+# ----------------------------------------------------------------------------
+# Anchor-blended correction and the reliability gate (KVCMAS eq. 8-11,
+# App. A.3).  Pools are built from small exactly representable factors so that
+# reconstructions, distances and corrected rows have closed forms.
+# ----------------------------------------------------------------------------
+
+
+def _rows_to_plane(rows, H, hd):
+    """[n][H*hd] float64 -> [H][n][hd]."""
+    n = rows.shape[0]
+    return rows.reshape(n, H, hd).transpose(1, 0, 2)
+
+
+def _const_pool(V, L, n_max, H, hd, r, fill):
+    """Pool whose anchor v reconstructs, at (l, p), every row as the vector
+    fill(v, l, p) [H*hd]: A rows = e_0, B row 0 = that vector.  All values
+    must be bf16-exact."""
+    D = H * hd
+    a = np.zeros((V, L, 2, n_max, r))
+    bt = np.zeros((V, L, 2, D, r))
+    a[..., 0] = 1.0
+    for v in range(V):
+        for l in range(L):
+            for p in range(2):
+                bt[v, l, p, :, 0] = fill(v, l, p)
+    return K.f64_to_bf16(a), K.f64_to_bf16(bt)
+
+
+def test_anchor_eligible_full_cover_else_longest_prefix():
+    assert K.anchor_eligible([5, 10, 10, 3], 8) == ([1, 2], 8)
+    assert K.anchor_eligible([5, 10, 10, 3], 10) == ([1, 2], 10)
+    assert K.anchor_eligible([5, 10, 12, 3], 8) == ([1, 2], 8)
+    assert K.anchor_eligible([5, 10, 10, 3], 12) == ([1, 2], 10)   # longest covered prefix
+    assert K.anchor_eligible([5, 7, 3], 12) == ([1], 7)
+    assert K.anchor_eligible([0, 0], 4) == ([], 0)
+    assert K.anchor_eligible([], 4) == ([], 0)
+
+
+def test_anchor_gate_decide_closed_forms():
+    # g = (3/4, 1/4): binary entropy of 1/4 = 2 - (3/4) log2 3
+    r = K.anchor_gate_decide([0.0, math.log(3.0)], 0.9)
+    assert np.allclose(r["g"], [0.75, 0.25], rtol=0, atol=1e-15)
+    assert abs(r["hbar"] - (2 - 0.75 * math.log2(3))) < 1e-14 and r["accept"]
+    assert not K.anchor_gate_decide([0.0, math.log(3.0)], 0.8)["accept"]
+    # g = (1/2, 1/4, 1/4): 1.5 bits out of log2 3
+    r = K.anchor_gate_decide([0.0, math.log(2.0), math.log(2.0)], 0.95)
+    assert abs(r["hbar"] - 1.5 / math.log2(3)) < 1e-14 and r["accept"]
+    # equal distances: the flat distribution, Hbar = 1; tau = 1 never refuses
+    for V in (2, 3, 7, 10):
+        r = K.anchor_gate_decide([2.5] * V, 1.0)
+        assert r["hbar"] == 1.0 and r["accept"]
+        assert not K.anchor_gate_decide([2.5] * V, 0.999)["accept"]
+    # a distinctive match: entropy near 0
+    r = K.anchor_gate_decide([0.0, 50.0, 60.0], 0.01)
+    assert r["hbar"] < 1e-15 and r["accept"]
+    # fewer than two compared anchors: dense
+    assert not K.anchor_gate_decide([0.0], 1.0)["accept"]
+    assert not K.anchor_gate_decide([], 1.0)["accept"]
+
+
+def test_anchor_gate_distance_is_the_frobenius_norm_over_layers_and_prefix():
+    L, H, n, hd, r = 3, 2, 7, 4, 2
+    D = H * hd
+    rng = np.random.default_rng(11)
+    base = np.round(rng.standard_normal(D) * 4) / 4                 # bf16-exact
+    off = [0.0, 0.5, -0.25, 1.0]
+    # value factors reconstruct base + off[v]; key factors hold unrelated data
+    a, bt = _const_pool(4, L, 9, H, hd, r,
+                        lambda v, l, p: base + off[v] if p == 1 else base * 3 - 7 + v)
+    src_v = K.f64_to_bf16(np.stack([_rows_to_plane(np.tile(base, (n, 1)), H, hd)[None]] * L))
+    lengths = [9, 9, 5, 9]
+    k = 5
+    g = K.anchor_gate(src_v, a, bt, lengths, k, 1.0, "bf16")
+    assert g["Ak"] == [0, 1, 2, 3]
+    for v in range(4):
+        assert abs(g["d"][v] - abs(off[v]) * math.sqrt(L * k * D)) < 1e-12
+    # the rows past the prefix do not matter
+    src2 = src_v.copy()
+    src2[:, :, :, k:] = K.f64_to_bf16(np.full(src2[:, :, :, k:].shape, 9.0))
+    assert np.array_equal(K.anchor_gate(src2, a, bt, lengths, k, 1.0, "bf16")["d"], g["d"])
+    # a longer prefix drops the short anchor; k past the segment is the segment
+    g6 = K.anchor_gate(src_v, a, bt, lengths, 6, 1.0, "bf16")
+    assert g6["Ak"] == [0, 1, 3] and np.isnan(g6["d"][2])
+    g99 = K.anchor_gate(src_v, a, bt, [9, 9, 7, 9], 99, 1.0, "bf16")
+    assert g99["Ak"] == [0, 1, 2, 3]
+    assert abs(g99["d"][3] - math.sqrt(L * n * D)) < 1e-12
+    # decision: distances above give a distinctive match to anchor 0
+    assert g["accept"] == (g["hbar"] <= 1.0)
+    one = K.anchor_gate(src_v, a, bt, [9, 2, 2, 2], 5, 1.0, "bf16")
+    assert one["Ak"] == [0] and not one["accept"]
+
+
+def test_anchor_gate_flat_when_anchors_are_equally_far():
+    L, H, n, hd, r = 2, 1, 4, 4, 2
+    a, bt = _const_pool(3, L, n, H, hd, r, lambda v, l, p: np.full(hd, 0.5 if v < 2 else -0.5))
+    src_v = K.f64_to_bf16(np.zeros((L, 1, H, n, hd)))
+    g = K.anchor_gate(src_v, a, bt, [n] * 3, n, 1.0, "bf16")
+    assert g["hbar"] == 1.0 and g["accept"]
+    assert not K.anchor_gate(src_v, a, bt, [n] * 3, n, 0.99, "bf16")["accept"]
+
+
+def test_anchor_weights_closed_form_mean_absolute_distance():
+    L, H, n, hd, r = 2, 2, 6, 4, 2
+    D = H * hd
+    rng = np.random.default_rng(12)
+    base = np.round(rng.standard_normal(D) * 4) / 4
+    # anchor 0 exact; anchor 1 off by 0.5 in head 0 only (mean 0.25 over all
+    # heads); anchor 2 off by 1 everywhere; anchor 3 too short to be eligible
+    def fill(v, l, p):
+        x = base.copy()
+        if v == 1:
+            x[:hd] += 0.5
+        if v >= 2:
+            x += 1.0
+        return x
+    a, bt = _const_pool(4, L, n, H, hd, r, fill)
+    plane = K.f64_to_bf16(np.stack([_rows_to_plane(np.tile(base, (n, 1)), H, hd)[None]] * L))
+    w = K.anchor_weights(plane, plane, a, bt, [n, n, n, n - 1], 0, 1e4, "half", "bf16")
+    e = np.exp(-np.array([0.0, 0.25, 1.0]))
+    want = e / e.sum()
+    for l in range(L):
+        for p in range(2):
+            assert np.allclose(w[l, p, :, :3], want, rtol=0, atol=1e-15)
+            assert np.all(w[l, p, :, 3] == 0)
+    assert np.allclose(w.sum(axis=3), 1.0, rtol=0, atol=1e-15)
+
+
+def test_anchor_weights_compare_keys_in_canonical_positions():
+    L, H, n, hd, r = 1, 2, 5, 8, 2
+    D = H * hd
+    rng = np.random.default_rng(13)
+    base = np.round(rng.standard_normal(D) * 4) / 4
+    a, bt = _const_pool(2, L, n, H, hd, r,
+                        lambda v, l, p: base if v == 0 else base + 0.75)
+    src_off, theta = 37, 100.0
+    canon = _rows_to_plane(np.tile(base, (n, 1)), H, hd)
+    keys = K.rope_rotate(canon, src_off, theta, "half")[None, None].astype(np.float32)
+    vals = canon[None, None].astype(np.float32)
+    w = K.anchor_weights(keys, vals, a, bt, [n, n], src_off, theta, "half", "f32")
+    e = np.exp(-np.array([0.0, 0.75]))
+    assert np.allclose(w[0, 0], e / e.sum(), rtol=0, atol=1e-6)      # keys: f32 rounding only
+    assert np.allclose(w[0, 1], e / e.sum(), rtol=0, atol=1e-15)
+    # matched at the cached positions instead, the keys would not fit anchor 0
+    w_wrong = K.anchor_weights(keys, vals, a, bt, [n, n], 0, theta, "half", "f32")
+    assert w_wrong[0, 0, :, 0].max() < 0.6
+
+
+def test_anchor_weights_are_token_wise_and_stop_at_the_covered_prefix():
+    L, H, n, hd, r = 1, 1, 6, 4, 2
+    rng = np.random.default_rng(14)
+    rows = np.round(rng.standard_normal((n, hd)) * 4) / 4
+    # anchor 0 reconstructs the first three rows exactly, anchor 1 the last three
+    a = np.zeros((2, L, 2, 8, r))
+    bt = np.zeros((2, L, 2, hd, r))
+    for v, sl in ((0, slice(0, 3)), (1, slice(3, 6))):
+        a[v, 0, :, sl, 0] = 1.0
+        bt[v, 0, :, :, 0] = rows[sl][0]
+    rows[1:3] = rows[0]
+    rows[4:6] = rows[3]
+    a, bt = K.f64_to_bf16(a), K.f64_to_bf16(bt)
+    plane = K.f64_to_bf16(rows[None, None, None])
+    w = K.anchor_weights(plane, plane, a, bt, [8, 8], 0, 1e4, "half", "bf16")
+    assert np.all(w[0, :, :3, 0] > 0.5) and np.all(w[0, :, 3:, 1] > 0.5)
+    # no anchor covers the segment: weights only on the longest covered prefix
+    w4 = K.anchor_weights(plane, plane, a, bt, [4, 2], 0, 1e4, "half", "bf16")
+    assert np.all(w4[0, :, :4, 0] == 1.0) and np.all(w4[0, :, 4:] == 0) and np.all(w4[..., 1] == 0)
+
+
+def _integer_delta_pool(V, L, n_max, H, hd, r, rng):
+    a = rng.integers(-2, 3, (V, L, 2, n_max, r)).astype(np.float64)
+    bt = rng.integers(-2, 3, (V, L, 2, H * hd, r)).astype(np.float64)
+    return a, bt, K.f64_to_bf16(a), K.f64_to_bf16(bt)
+
+
+def test_anchor_apply_values_add_the_weighted_low_rank_deltas_exactly():
+    L, H, n, hd, r, V = 2, 2, 5, 4, 3, 3
+    rng = np.random.default_rng(15)
+    af, btf, a, bt = _integer_delta_pool(V, L, n, H, hd, r, rng)
+    x = rng.integers(-8, 9, (L, 1, H, n, hd)).astype(np.float32)
+    w = np.zeros((L, 2, n, V))
+    w[:, :, :, 0] = 0.25
+    w[:, :, :, 2] = 0.75
+    w[:, :, :, 1] = 0.5          # anchor 1 is too short to be eligible: ignored
+    out = K.anchor_apply(x, 1, a, bt, w, [n, n - 1, n], 3, 9, 1e4, "half", "f32")
+    for l in range(L):
+        dhat = 0.25 * af[0, l, 1] @ btf[0, l, 1].T + 0.75 * af[2, l, 1] @ btf[2, l, 1].T
+        want = x[l, 0].astype(np.float64) + _rows_to_plane(dhat, H, hd)
+        assert np.array_equal(out[l, 0], want.astype(np.float32))
+    # one anchor at full weight
+    w1 = np.zeros((L, 2, n, V))
+    w1[:, :, :, 1] = 1.0
+    out1 = K.anchor_apply(x, 1, a, bt, w1, [n - 2, n, n - 1], 0, 0, 1e4, "half", "f32")
+    for l in range(L):
+        want = x[l, 0].astype(np.float64) + _rows_to_plane(af[1, l, 1] @ btf[1, l, 1].T, H, hd)
+        assert np.array_equal(out1[l, 0], want.astype(np.float32))
+
+
+def test_anchor_apply_keys_add_the_delta_in_canonical_positions():
+    L, H, n, hd, r, V = 1, 2, 6, 8, 2, 2
+    rng = np.random.default_rng(16)
+    af, btf, a, bt = _integer_delta_pool(V, L, n, H, hd, r, rng)
+    x = rng.standard_normal((L, 1, H, n, hd)).astype(np.float32)
+    w = np.zeros((L, 2, n, V))
+    w[..., 0] = 0.375
+    w[..., 1] = 0.625
+    src_off, tgt_off, theta = 19, 301, 50.0
+    out = K.anchor_apply(x, 0, a, bt, w, [n, n], src_off, tgt_off, theta, "half", "f32")
+    dhat = 0.375 * af[0, 0, 0] @ btf[0, 0, 0].T + 0.625 * af[1, 0, 0] @ btf[1, 0, 0].T
+    canon = K.rope_rotate(x[0, 0].astype(np.float64), -src_off, theta, "half") + \
+        _rows_to_plane(dhat, H, hd)
+    back = K.rope_rotate(out[0, 0].astype(np.float64), -tgt_off, theta, "half")
+    assert np.abs(back - canon).max() < 1e-5 * np.abs(canon).max()
+    # with no delta the keys are the rotary shift alone
+    z = np.zeros_like(w)
+    o0 = K.anchor_apply(x, 0, a, bt, z, [n, n], src_off, tgt_off, theta, "half", "f32")
+    assert np.array_equal(o0, K.rope_shift(x, "f32", [tgt_off - src_off], theta))
+    o0v = K.anchor_apply(x, 1, a, bt, z, [n, n], src_off, tgt_off, theta, "half", "f32")
+    assert np.array_equal(o0v, x)
+
+
+def test_anchor_apply_rows_past_the_covered_prefix_are_only_realigned():
+    L, H, n, hd, r, V = 1, 1, 8, 4, 2, 2
+    rng = np.random.default_rng(17)
+    af, btf, a, bt = _integer_delta_pool(V, L, n, H, hd, r, rng)
+    x = rng.integers(-8, 9, (L, 1, H, n, hd)).astype(np.float32)
+    w = np.full((L, 2, n, V), 0.5)                   # nonzero past the prefix too
+    src_off, tgt_off, theta = 4, 10, 1e4
+    out = K.anchor_apply(x, 0, a, bt, w, [5, 3], src_off, tgt_off, theta, "half", "f32")
+    shifted = K.rope_shift(x, "f32", [tgt_off - src_off], theta)
+    assert np.array_equal(out[:, :, :, 5:], shifted[:, :, :, 5:])
+    assert not np.array_equal(out[:, :, :, :5], shifted[:, :, :, :5])
+    # only anchor 0 covers the prefix: its delta at full weight 0.5 on rows < 5
+    outv = K.anchor_apply(x, 1, a, bt, w, [5, 3], 0, 0, theta, "half", "f32")
+    want = x[0, 0].astype(np.float64)
+    want[:, :5] += 0.5 * _rows_to_plane(af[0, 0, 1, :5] @ btf[0, 0, 1].T, H, hd)
+    assert np.array_equal(outv[0, 0], want.astype(np.float32))
