@@ -23,7 +23,8 @@ BUILD = os.path.join(os.path.dirname(PKG), "_build")
 LIB = os.path.join(PKG, "libkvfix.so")
 ARCH = os.environ.get("KVFIX_ARCH", "gfx950")
 
-SOURCES = ["correct.hip", "score_select.hip", "bcr.hip", "draft.hip", "diff.hip", "api.hip"]
+SOURCES = ["correct.hip", "score_select.hip", "bcr.hip", "draft.hip", "diff.hip", "anchor.hip",
+           "api.hip"]
 
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",

@@ -1,0 +1,655 @@
+// Anchor-blended low-rank correction and the reliability gate.
+//
+// [KVCMAS eq. 7-8: each anchor of a placeholder slot stores rank-r factors
+//  A B of its base cache and of its delta correction; the correction is the
+//  weighted sum of the anchors' deltas.  App. A.3 "Reliability Gate" eq. 9-11,
+//  "Correction Weighting and Positional Alignment" and "Variable Segment
+//  Lengths".]
+//
+// Two passes over the source segment:
+//   match  reconstructs every eligible anchor's base rows A_v B_v with bf16
+//          MFMA and, per (layer, plane, token), takes the mean absolute
+//          distance to the source row over all heads (keys first turned to
+//          canonical positions) and the softmax over anchors (T = 1): the
+//          token-wise weights.  On the value plane the same pass accumulates
+//          the squared distances over the gate prefix; a one-block finish
+//          turns them into the gate distances, the normalized entropy and
+//          the decision.
+//   apply  reconstructs the delta rows A_v B_v with MFMA, blends them with
+//          the token weights in fp32 and adds them to the re-aligned source:
+//          keys R(p_t - p_s) x + R(p_t) delta, values x + delta; rows past
+//          the covered prefix are only re-aligned.
+//
+// MFMA mapping (v_mfma_f32_16x16x32_bf16, K = 32 = the rank).  The output
+// tile is 16 features x 16 tokens: operand A holds 16 rows of the transposed
+// right factor (feature x rank), operand B the left-factor rows of 16 tokens.
+// Output row m of feature tile c (c = 0..7 over one 128-dim head) is mapped to
+// dim 64 (c / 4) + 16 (m / 4) + 4 (c % 4) + m % 4, so that output lane group
+// g (lanes 16g..16g+15, rows 4g..4g+3) ends up holding dims [16g, 16g+16) and
+// [64+16g, 64+16g+16) of its token: two 32-byte pieces of the source row, and
+// both members of every rotary pair in either pairing.
+#include <algorithm>
+#include <initializer_list>
+
+#include "common.h"
+#include "host_util.h"
+
+namespace kvfix {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kAnchorMax = KVFIX_ANCHOR_MAX;
+constexpr int kRank = KVFIX_ANCHOR_RANK;
+constexpr int kHD = 128;
+constexpr int kTiles = 8;                       // 16-dim MFMA tiles per head
+constexpr int kMatchWaves = 4, kMatchBands = 2;
+constexpr int kMatchTokens = kMatchWaves * kMatchBands * 16;    // 128
+constexpr int kApplyWaves = 4, kApplyBands = 4;
+constexpr int kApplyTokens = kApplyWaves * kApplyBands * 16;    // 256
+constexpr int kXcds = 8;
+constexpr int64_t kMaxOffset = int64_t(1) << 23;   // rotary angles stay accurate below this
+
+__device__ __forceinline__ int tile_dim(int c, int m) {
+  return (c >> 2) * 64 + (m >> 2) * 16 + (c & 3) * 4 + (m & 3);
+}
+
+// Factor slabs of one pool: A [V][L][2][n_max][r], Bt [V][L][2][D][r].
+struct Pool {
+  const bf16_t* a;
+  const bf16_t* bt;
+  int64_t n_max;
+  int32_t L, D;
+  int32_t len[kAnchorMax];
+};
+
+__device__ __forceinline__ const bf16_t* a_row(const Pool& G, int v, int l, int p, int j) {
+  return G.a + ((((int64_t)v * G.L + l) * 2 + p) * G.n_max + j) * kRank;
+}
+__device__ __forceinline__ const bf16_t* bt_row(const Pool& G, int v, int l, int p, int f) {
+  return G.bt + ((((int64_t)v * G.L + l) * 2 + p) * G.D + f) * kRank;
+}
+
+__device__ __forceinline__ bf16x8 ld_op(const bf16_t* p) {
+  return __builtin_bit_cast(bf16x8, ld16(p));
+}
+
+// The lane's 32 dims of row (l, seg, h, j) in fp32: x[0..15] = dims
+// [16g, 16g+16), x[16..31] = dims [64+16g, 64+16g+16).  Zeros for a row
+// outside the segment or on a bad page.
+__device__ __forceinline__ void load_lane_row(const DPlane& S, int l, int seg, int h, int j, int n,
+                                              int g, float* x) {
+  int64_t off = j < n ? row_offset(S, l, seg, h, j) : -1;
+  if (off < 0) {
+#pragma unroll
+    for (int e = 0; e < 32; ++e) x[e] = 0.0f;
+    return;
+  }
+  const bf16_t* row = reinterpret_cast<const bf16_t*>(S.data) + off;
+#pragma unroll
+  for (int part = 0; part < 2; ++part) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const vu4 u = ld16(row + part * 64 + 16 * g + 8 * q);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        x[16 * part + 8 * q + 2 * w] = bf16_lo(u[w]);
+        x[16 * part + 8 * q + 2 * w + 1] = bf16_hi(u[w]);
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void store_lane_row(const DPlane& O, int l, int seg, int h, int j,
+                                               int g, const float* y) {
+  const int64_t off = row_offset(O, l, seg, h, j);
+  if (off < 0) return;
+  bf16_t* row = reinterpret_cast<bf16_t*>(O.data) + off;
+#pragma unroll
+  for (int part = 0; part < 2; ++part) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      vu4 u;
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        u[w] = pack_bf16x2(y[16 * part + 8 * q + 2 * w], y[16 * part + 8 * q + 2 * w + 1]);
+      st16(row + part * 64 + 16 * g + 8 * q, u);
+    }
+  }
+}
+
+// Rotate the lane's 32 dims by the table's angles (cos tc, sin ts per pair).
+template <int STYLE>
+__device__ __forceinline__ void rotate_lane(float* x, const float* tc, const float* ts, int g) {
+  if (STYLE == kStyleHalf) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int q = 16 * g + e;
+      const float a = x[e], b = x[16 + e], c = tc[q], s = ts[q];
+      x[e] = fmaf(a, c, -(b * s));
+      x[16 + e] = fmaf(b, c, a * s);
+    }
+  } else {
+#pragma unroll
+    for (int part = 0; part < 2; ++part) {
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        const int q = 32 * part + 8 * g + e / 2;
+        const float a = x[16 * part + e], b = x[16 * part + e + 1], c = tc[q], s = ts[q];
+        x[16 * part + e] = fmaf(a, c, -(b * s));
+        x[16 * part + e + 1] = fmaf(b, c, a * s);
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// match: token weights and gate partial sums
+// ----------------------------------------------------------------------------
+
+struct MatchParams {
+  DPlane src[2];
+  Pool G;
+  RopeArgs rope;
+  int64_t src_off;
+  int32_t seg, n, H, V;
+  uint32_t elig, gate_set;
+  int32_t cover, k_gate;
+  int32_t n_pairs, n_tiles;
+  float D;          // features per token row (all heads)
+  float* w;          // [L][2][n][V]
+  double* part;      // [L][n_tiles][V]
+};
+
+// Per-lane distance sums live in LDS, one slot per (wave, anchor, band,
+// lane): acc1 the absolute, acc2 the squared distances.  A lane only ever
+// touches its own slots inside the head loop.
+__host__ __device__ constexpr int match_lds_floats(int V) {
+  return 2 * kMatchWaves * V * kMatchBands * 64;
+}
+
+template <int STYLE, bool GATE>
+__device__ __forceinline__ void match_body(const MatchParams& P, int l, int tile, float* acc1,
+                                           float* acc2, float* tc, float* ts, double* gsum) {
+  constexpr int p = GATE ? 1 : 0;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, t = lane & 15;
+  const int V = P.V;
+  auto slot = [&](int v, int b) { return (((wave * V + v) * kMatchBands + b) << 6) + lane; };
+  for (int v = 0; v < V; ++v)
+#pragma unroll
+    for (int b = 0; b < kMatchBands; ++b) acc1[slot(v, b)] = acc2[slot(v, b)] = 0.0f;
+  if (STYLE != kStyleNone) rope_table<kHD, float>(P.rope, -P.src_off, tc, ts);
+  __syncthreads();
+
+  const int jw = tile * kMatchTokens + wave * kMatchBands * 16;
+  const uint32_t set = GATE ? (P.elig | P.gate_set) : P.elig;
+  const int lim = GATE ? max(P.cover, P.k_gate) : P.cover;
+  const DPlane& S = P.src[p];
+
+  if (jw < lim) {
+    for (int h = 0; h < P.H; ++h) {
+      float nx[kMatchBands][32];
+#pragma unroll
+      for (int b = 0; b < kMatchBands; ++b) {
+        load_lane_row(S, l, P.seg, h, jw + 16 * b + t, P.n, g, nx[b]);
+        if (STYLE != kStyleNone) rotate_lane<STYLE>(nx[b], tc, ts, g);
+#pragma unroll
+        for (int e = 0; e < 32; ++e) nx[b][e] = -nx[b][e];
+      }
+      for (int v = 0; v < V; ++v) {
+        if (!((set >> v) & 1u)) continue;
+        const int len = P.G.len[v];
+        const int lv = min(len, lim);
+        if (jw >= lv) continue;
+        bf16x8 bop[kTiles];
+#pragma unroll
+        for (int c = 0; c < kTiles; ++c)
+          bop[c] = ld_op(bt_row(P.G, v, l, p, h * kHD + tile_dim(c, t)) + 8 * g);
+#pragma unroll
+        for (int b = 0; b < kMatchBands; ++b) {
+          if (jw + 16 * b >= lv) continue;
+          const int j = jw + 16 * b + t;
+          bf16x8 aop = {};
+          if (j < len) aop = ld_op(a_row(P.G, v, l, p, j) + 8 * g);
+          float s1[4] = {0, 0, 0, 0}, s2[4] = {0, 0, 0, 0};
+#pragma unroll
+          for (int c = 0; c < kTiles; ++c) {
+            const f32x4 cx = {nx[b][4 * c], nx[b][4 * c + 1], nx[b][4 * c + 2], nx[b][4 * c + 3]};
+            const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bop[c], aop, cx, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              s1[i] += fabsf(d[i]);
+              if (GATE) s2[i] = fmaf(d[i], d[i], s2[i]);
+            }
+          }
+          acc1[slot(v, b)] += (s1[0] + s1[1]) + (s1[2] + s1[3]);
+          if (GATE) acc2[slot(v, b)] += (s2[0] + s2[1]) + (s2[2] + s2[3]);
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // Column totals: the four lane groups of token t, added in group order.
+  auto total = [&](const float* acc, int v, int b) {
+    const int base = (((wave * V + v) * kMatchBands + b) << 6) + t;
+    return ((acc[base] + acc[base + 16]) + acc[base + 32]) + acc[base + 48];
+  };
+
+  // Token weights: softmax of minus the mean absolute distance over E.
+  if (g == 0) {
+#pragma unroll
+    for (int b = 0; b < kMatchBands; ++b) {
+      const int j = jw + 16 * b + t;
+      if (j >= P.n) continue;
+      float* wr = P.w + (((int64_t)l * 2 + p) * P.n + j) * V;
+      if (j >= P.cover) {
+        for (int v = 0; v < V; ++v) wr[v] = 0.0f;
+        continue;
+      }
+      float m = INFINITY;
+      for (int v = 0; v < V; ++v)
+        if ((P.elig >> v) & 1u) m = fminf(m, total(acc1, v, b) / P.D);
+      float sum = 0.0f;
+      for (int v = 0; v < V; ++v)
+        if ((P.elig >> v) & 1u) sum += expf(m - total(acc1, v, b) / P.D);
+      for (int v = 0; v < V; ++v)
+        wr[v] = ((P.elig >> v) & 1u) ? expf(m - total(acc1, v, b) / P.D) / sum : 0.0f;
+    }
+  }
+
+  if (GATE) {
+    // Per block and anchor of the gate set: the squared distances of the
+    // prefix rows in fp64, added in a fixed order (band, lane tree, wave).
+    for (int v = 0; v < V; ++v) {
+      if (!((P.gate_set >> v) & 1u)) continue;
+      double s = 0.0;
+#pragma unroll
+      for (int b = 0; b < kMatchBands; ++b)
+        if (jw + 16 * b + t < P.k_gate) s += (double)total(acc2, v, b);
+      s += __shfl_xor(s, 1);
+      s += __shfl_xor(s, 2);
+      s += __shfl_xor(s, 4);
+      s += __shfl_xor(s, 8);
+      if (lane == 0) gsum[wave * kAnchorMax + v] = s;
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < V) {
+      const int v = threadIdx.x;
+      double s = 0.0;
+      if ((P.gate_set >> v) & 1u)
+        for (int w = 0; w < kMatchWaves; ++w) s += gsum[w * kAnchorMax + v];
+      P.part[((int64_t)l * P.n_tiles + tile) * V + v] = s;
+    }
+  }
+}
+
+// Blocks of one (layer, plane) run on one XCD, so the plane's right factors
+// (all anchors: V * D * r bf16) are fetched into that XCD's L2 once.
+template <int STYLE>
+__global__ __launch_bounds__(kMatchWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void anchor_match_kernel(MatchParams P) {
+  extern __shared__ float match_lds[];
+  __shared__ float tc[kHD / 2], ts[kHD / 2];
+  __shared__ double gsum[kMatchWaves * kAnchorMax];
+  const int id = blockIdx.x, xcd = id % kXcds, k = id / kXcds;
+  const int tile = k % P.n_tiles;
+  const int pair = (k / P.n_tiles) * kXcds + xcd;
+  if (pair >= P.n_pairs) return;
+  const int l = pair >> 1;
+  float* acc1 = match_lds;
+  float* acc2 = match_lds + match_lds_floats(P.V) / 2;
+  if ((pair & 1) == 0)
+    match_body<STYLE, false>(P, l, tile, acc1, acc2, tc, ts, gsum);
+  else
+    match_body<kStyleNone, true>(P, l, tile, acc1, acc2, tc, ts, gsum);
+}
+
+// Gate finish: d_v = sqrt of the summed partials (fp64, fixed order), then
+// g = softmax(-d), Hbar = -sum g log2 g / log2 |A_k| clamped to [0, 1], and
+// the decision Hbar <= tau with at least two compared anchors.
+__global__ __launch_bounds__(1024) void anchor_gate_kernel(const double* part, int n_parts, int V,
+                                                           uint32_t gate_set, double tau,
+                                                           double* gate, int32_t* accept) {
+  __shared__ double sd[kAnchorMax];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (wave < V) {
+    double s = 0.0;
+    for (int i = lane; i < n_parts; i += 64) s += part[(int64_t)i * V + wave];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+    if (lane == 0) sd[wave] = ((gate_set >> wave) & 1u) ? sqrt(s) : __builtin_nan("");
+  }
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  int na = 0;
+  double dmin = INFINITY;
+  for (int v = 0; v < V; ++v) {
+    gate[v] = sd[v];
+    if ((gate_set >> v) & 1u) {
+      ++na;
+      dmin = fmin(dmin, sd[v]);
+    }
+  }
+  if (na < 2) {
+    gate[V] = __builtin_nan("");
+    *accept = 0;
+    return;
+  }
+  double sum = 0.0;
+  for (int v = 0; v < V; ++v)
+    if ((gate_set >> v) & 1u) sum += exp(dmin - sd[v]);
+  double hsum = 0.0;
+  for (int v = 0; v < V; ++v) {
+    if (!((gate_set >> v) & 1u)) continue;
+    const double gv = exp(dmin - sd[v]) / sum;
+    if (gv > 0.0) hsum += gv * log2(gv);
+  }
+  double hbar = -hsum / log2((double)na);
+  hbar = fmin(1.0, fmax(0.0, hbar));
+  gate[V] = hbar;
+  *accept = hbar <= tau ? 1 : 0;
+}
+
+// ----------------------------------------------------------------------------
+// apply: blended deltas added to the re-aligned source
+// ----------------------------------------------------------------------------
+
+struct AnchorApplyParams {
+  DPlane src[2], out[2];
+  Pool G;
+  RopeArgs rope;
+  int64_t src_off, tgt_off;
+  int32_t seg, n, H, V;
+  uint32_t elig;
+  int32_t cover;
+  int32_t n_pairs, n_tiles;
+  const float* w;    // [L][2][n][V]
+};
+
+template <int STYLE>
+__device__ __forceinline__ void apply_body(const AnchorApplyParams& P, int l, int p, int h,
+                                           int tile) {
+  __shared__ float tc1[kHD / 2], ts1[kHD / 2], tc2[kHD / 2], ts2[kHD / 2];
+  if (STYLE != kStyleNone) {
+    rope_table<kHD, float>(P.rope, P.tgt_off - P.src_off, tc1, ts1);
+    rope_table<kHD, float>(P.rope, P.tgt_off, tc2, ts2);
+  }
+  __syncthreads();
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, t = lane & 15;
+  const int jw = tile * kApplyTokens + wave * kApplyBands * 16;
+  f32x4 acc[kApplyBands][kTiles];
+#pragma unroll
+  for (int b = 0; b < kApplyBands; ++b)
+#pragma unroll
+    for (int c = 0; c < kTiles; ++c) acc[b][c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  if (jw < P.cover) {
+    const float* wl = P.w + ((int64_t)l * 2 + p) * P.n * P.V;
+#pragma unroll
+    for (int v = 0; v < kAnchorMax; ++v) {
+      if (!((P.elig >> v) & 1u)) continue;
+      bf16x8 bop[kTiles];
+#pragma unroll
+      for (int c = 0; c < kTiles; ++c)
+        bop[c] = ld_op(bt_row(P.G, v, l, p, h * kHD + tile_dim(c, t)) + 8 * g);
+#pragma unroll
+      for (int b = 0; b < kApplyBands; ++b) {
+        if (jw + 16 * b >= P.cover) continue;
+        const int j = jw + 16 * b + t;
+        bf16x8 aop = {};
+        float wv = 0.0f;
+        if (j < P.cover) {
+          aop = ld_op(a_row(P.G, v, l, p, j) + 8 * g);
+          wv = wl[(int64_t)j * P.V + v];
+        }
+#pragma unroll
+        for (int c = 0; c < kTiles; ++c) {
+          const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              bop[c], aop, f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[b][c][i] = fmaf(wv, d[i], acc[b][c][i]);
+        }
+      }
+    }
+  }
+
+#pragma unroll
+  for (int b = 0; b < kApplyBands; ++b) {
+    const int j = jw + 16 * b + t;
+    if (j >= P.n) continue;
+    float x[32], dl[32];
+    load_lane_row(P.src[p], l, P.seg, h, j, P.n, g, x);
+#pragma unroll
+    for (int c = 0; c < kTiles; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dl[4 * c + i] = acc[b][c][i];
+    if (STYLE != kStyleNone) {
+      rotate_lane<STYLE>(x, tc1, ts1, g);
+      rotate_lane<STYLE>(dl, tc2, ts2, g);
+    }
+#pragma unroll
+    for (int e = 0; e < 32; ++e) x[e] += dl[e];
+    store_lane_row(P.out[p], l, P.seg, h, j, g, x);
+  }
+}
+
+// Blocks of one (layer, plane) run on one XCD and walk its heads fastest, so
+// the delta left factors and weights of a token tile are read from HBM once
+// and reused from L2 by every head.
+template <int STYLE>
+__global__ __launch_bounds__(kApplyWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void anchor_apply_kernel(AnchorApplyParams P) {
+  const int id = blockIdx.x, xcd = id % kXcds, k = id / kXcds;
+  const int h = k % P.H, k2 = k / P.H;
+  const int tile = k2 % P.n_tiles;
+  const int pair = (k2 / P.n_tiles) * kXcds + xcd;
+  if (pair >= P.n_pairs) return;
+  const int l = pair >> 1;
+  if ((pair & 1) == 0)
+    apply_body<STYLE>(P, l, 0, h, tile);
+  else
+    apply_body<kStyleNone>(P, l, 1, h, tile);
+}
+
+// ----------------------------------------------------------------------------
+// host side
+// ----------------------------------------------------------------------------
+
+struct Eligible {
+  uint32_t elig = 0, gate_set = 0;
+  int32_t cover = 0, k_gate = 0;
+};
+
+// E and the covered prefix [KVCMAS App. A.3 "Variable Segment Lengths"]: the
+// anchors storing the whole segment, else those storing the longest prefix;
+// the gate set A_k: anchors storing at least k tokens (k clamped to [0, n]).
+Eligible eligible(const kvfix_anchor_pool* pool, int32_t n, int64_t k_gate) {
+  Eligible e;
+  int32_t longest = 0;
+  for (int v = 0; v < pool->n_anchors; ++v) longest = std::max(longest, pool->lengths[v]);
+  for (int v = 0; v < pool->n_anchors; ++v)
+    if (pool->lengths[v] >= n) e.elig |= 1u << v;
+  if (e.elig) {
+    e.cover = n;
+  } else if (longest > 0) {
+    e.cover = longest;
+    for (int v = 0; v < pool->n_anchors; ++v)
+      if (pool->lengths[v] == longest) e.elig |= 1u << v;
+  }
+  e.k_gate = (int32_t)std::min<int64_t>(std::max<int64_t>(k_gate, 0), n);
+  for (int v = 0; v < pool->n_anchors; ++v)
+    if (pool->lengths[v] >= e.k_gate) e.gate_set |= 1u << v;
+  return e;
+}
+
+kvfix_status check_pool(const kvfix_anchor_pool* pool) {
+  if (pool == nullptr) return KVFIX_ERR_ARG;
+  if (pool->n_anchors < 0 || pool->n_anchors > kAnchorMax || pool->n_max < 0) return KVFIX_ERR_ARG;
+  if (pool->rank != kRank) return KVFIX_ERR_UNSUPPORTED;
+  if (pool->n_anchors == 0) return KVFIX_OK;
+  if (pool->lengths == nullptr || pool->a == nullptr || pool->bt == nullptr) return KVFIX_ERR_ARG;
+  if (!aligned16(pool->a) || !aligned16(pool->bt)) return KVFIX_ERR_ALIGN;
+  for (int v = 0; v < pool->n_anchors; ++v)
+    if (pool->lengths[v] < 0 || pool->lengths[v] > pool->n_max) return KVFIX_ERR_ARG;
+  return KVFIX_OK;
+}
+
+kvfix_status check_anchor_planes(const kvfix_plane* k, const kvfix_plane* v, int32_t seg) {
+  KVFIX_TRY(check_plane(k));
+  KVFIX_TRY(check_plane(v));
+  KVFIX_TRY(same_rows(k, v));
+  if (k->n_layers != v->n_layers) return KVFIX_ERR_ARG;
+  if (k->dtype != KVFIX_BF16 || k->head_dim != kHD) return KVFIX_ERR_UNSUPPORTED;
+  if (seg < 0 || seg >= k->n_segs) return KVFIX_ERR_ARG;
+  return KVFIX_OK;
+}
+
+kvfix_status check_rotary(double theta, int32_t style, std::initializer_list<int64_t> offsets) {
+  if (style != KVFIX_ROPE_HALF && style != KVFIX_ROPE_INTERLEAVED) return KVFIX_ERR_ARG;
+  if (!(theta > 0.0) || !isfinite(theta)) return KVFIX_ERR_ARG;
+  for (int64_t o : offsets)
+    if (o > kMaxOffset || o < -kMaxOffset) return KVFIX_ERR_ARG;
+  return KVFIX_OK;
+}
+
+Pool make_pool(const kvfix_anchor_pool* pool, int32_t L, int32_t D) {
+  Pool G;
+  memset(&G, 0, sizeof(G));
+  G.a = static_cast<const bf16_t*>(pool->a);
+  G.bt = static_cast<const bf16_t*>(pool->bt);
+  G.n_max = pool->n_max;
+  G.L = L;
+  G.D = D;
+  for (int v = 0; v < pool->n_anchors; ++v) G.len[v] = pool->lengths[v];
+  return G;
+}
+
+RopeArgs rope_freqs(double theta, int32_t style) {
+  kvfix_rope r;
+  r.theta = theta;
+  r.style = style;
+  r.delta = nullptr;
+  return make_rope_args(&r, kHD);
+}
+
+int64_t n_match_tiles(int64_t n) { return (n + kMatchTokens - 1) / kMatchTokens; }
+
+}  // namespace
+}  // namespace kvfix
+
+using namespace kvfix;
+
+extern "C" size_t kvfix_anchor_match_workspace(int32_t n_layers, int32_t n_tokens,
+                                               int32_t n_anchors) {
+  if (n_layers < 0 || n_tokens < 0 || n_anchors < 0) return 0;
+  return (size_t)n_layers * (size_t)n_match_tiles(n_tokens) * (size_t)n_anchors * sizeof(double) +
+         256;
+}
+
+extern "C" kvfix_status kvfix_anchor_match(const kvfix_plane* src_k, const kvfix_plane* src_v,
+                                           int32_t seg, const kvfix_anchor_pool* base,
+                                           int64_t src_off, double theta, int32_t rope_style,
+                                           int64_t k_gate, double tau, float* weights,
+                                           double* gate, int32_t* accept, void* ws,
+                                           size_t ws_bytes, void* stream) {
+  KVFIX_TRY(check_anchor_planes(src_k, src_v, seg));
+  KVFIX_TRY(check_pool(base));
+  KVFIX_TRY(check_rotary(theta, rope_style, {src_off}));
+  if (gate == nullptr || accept == nullptr || ws == nullptr) return KVFIX_ERR_ARG;
+  if (!(tau == tau)) return KVFIX_ERR_ARG;
+  const int32_t L = src_k->n_layers, n = src_k->n_tokens, V = base->n_anchors;
+  if (V > 0 && n > 0 && L > 0 && weights == nullptr) return KVFIX_ERR_ARG;
+  if (ws_bytes < kvfix_anchor_match_workspace(L, n, V)) return KVFIX_ERR_ARG;
+  if ((reinterpret_cast<uintptr_t>(ws) & 7u) != 0) return KVFIX_ERR_ALIGN;
+  const hipStream_t st = (hipStream_t)stream;
+  const Eligible e = eligible(base, n, k_gate);
+
+  MatchParams P;
+  memset(&P, 0, sizeof(P));
+  P.src[0] = make_dplane(*src_k);
+  P.src[1] = make_dplane(*src_v);
+  P.G = make_pool(base, L, src_k->n_heads * kHD);
+  P.rope = rope_freqs(theta, rope_style);
+  P.src_off = src_off;
+  P.seg = seg;
+  P.n = n;
+  P.H = src_k->n_heads;
+  P.V = V;
+  P.elig = e.elig;
+  P.gate_set = e.gate_set;
+  P.cover = e.cover;
+  P.k_gate = e.k_gate;
+  P.n_pairs = 2 * L;
+  P.n_tiles = (int32_t)n_match_tiles(n);
+  P.D = (float)(src_k->n_heads * kHD);
+  P.w = weights;
+  P.part = static_cast<double*>(ws);
+  if (V > 0 && n > 0 && L > 0) {
+    const int64_t grid = (int64_t)P.n_tiles * ((P.n_pairs + kXcds - 1) / kXcds) * kXcds;
+    const size_t lds = sizeof(float) * match_lds_floats(V);
+    const void* kern = rope_style == KVFIX_ROPE_HALF
+                           ? reinterpret_cast<const void*>(&anchor_match_kernel<kStyleHalf>)
+                           : reinterpret_cast<const void*>(&anchor_match_kernel<kStyleInter>);
+    if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
+        hipSuccess)
+      return KVFIX_ERR_HIP;
+    if (rope_style == KVFIX_ROPE_HALF)
+      anchor_match_kernel<kStyleHalf><<<dim3((unsigned)grid), dim3(kMatchWaves * 64), lds, st>>>(P);
+    else
+      anchor_match_kernel<kStyleInter><<<dim3((unsigned)grid), dim3(kMatchWaves * 64), lds, st>>>(P);
+    KVFIX_TRY(launch_status());
+  }
+  const int n_parts = (V > 0 && n > 0) ? L * P.n_tiles : 0;
+  anchor_gate_kernel<<<dim3(1), dim3(1024), 0, st>>>(P.part, n_parts, V, e.gate_set, tau, gate,
+                                                      accept);
+  return launch_status();
+}
+
+extern "C" kvfix_status kvfix_anchor_apply(const kvfix_plane* src_k, const kvfix_plane* src_v,
+                                           int32_t seg, const kvfix_anchor_pool* delta,
+                                           const float* weights, int64_t src_off,
+                                           int64_t tgt_off, double theta, int32_t rope_style,
+                                           const kvfix_plane* out_k, const kvfix_plane* out_v,
+                                           void* stream) {
+  KVFIX_TRY(check_anchor_planes(src_k, src_v, seg));
+  KVFIX_TRY(check_anchor_planes(out_k, out_v, seg));
+  KVFIX_TRY(same_rows(src_k, out_k));
+  if (src_k->n_layers != out_k->n_layers) return KVFIX_ERR_ARG;
+  KVFIX_TRY(check_pool(delta));
+  KVFIX_TRY(check_rotary(theta, rope_style, {src_off, tgt_off, tgt_off - src_off}));
+  const int32_t L = src_k->n_layers, n = src_k->n_tokens, V = delta->n_anchors;
+  const Eligible e = eligible(delta, n, 0);
+  if (e.elig != 0 && weights == nullptr) return KVFIX_ERR_ARG;
+  if (L == 0 || n == 0 || src_k->n_heads == 0) return KVFIX_OK;
+
+  AnchorApplyParams P;
+  memset(&P, 0, sizeof(P));
+  P.src[0] = make_dplane(*src_k);
+  P.src[1] = make_dplane(*src_v);
+  P.out[0] = make_dplane(*out_k);
+  P.out[1] = make_dplane(*out_v);
+  P.G = make_pool(delta, L, src_k->n_heads * kHD);
+  P.rope = rope_freqs(theta, rope_style);
+  P.src_off = src_off;
+  P.tgt_off = tgt_off;
+  P.seg = seg;
+  P.n = n;
+  P.H = src_k->n_heads;
+  P.V = V;
+  P.elig = e.elig;
+  P.cover = e.cover;
+  P.n_pairs = 2 * L;
+  P.n_tiles = (n + kApplyTokens - 1) / kApplyTokens;
+  P.w = weights;
+  const int64_t grid =
+      (int64_t)P.H * P.n_tiles * ((P.n_pairs + kXcds - 1) / kXcds) * kXcds;
+  const hipStream_t st = (hipStream_t)stream;
+  if (rope_style == KVFIX_ROPE_HALF)
+    anchor_apply_kernel<kStyleHalf><<<dim3((unsigned)grid), dim3(kApplyWaves * 64), 0, st>>>(P);
+  else
+    anchor_apply_kernel<kStyleInter><<<dim3((unsigned)grid), dim3(kApplyWaves * 64), 0, st>>>(P);
+  return launch_status();
+}

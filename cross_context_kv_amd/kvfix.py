@@ -23,7 +23,8 @@ STATUS = {0: "KVFIX_OK", 1: "KVFIX_ERR_ARG", 2: "KVFIX_ERR_ALIGN", 3: "KVFIX_ERR
 EXPORTS = ("kvfix_rope_shift", "kvfix_score", "kvfix_score_draft_workspace", "kvfix_score_draft",
            "kvfix_select_topb", "kvfix_chunk_budget", "kvfix_chunk_means", "kvfix_expand_chunks",
            "kvfix_select_grow", "kvfix_score_ex", "kvfix_fit_mean_ex", "kvfix_apply_ex",
-           "kvfix_select_master",
+           "kvfix_select_master", "kvfix_anchor_match_workspace", "kvfix_anchor_match",
+           "kvfix_anchor_apply",
            "kvfix_fit_mean_workspace", "kvfix_fit_mean", "kvfix_apply", "kvfix_diff_encode_workspace",
            "kvfix_diff_encode", "kvfix_diff_decode_workspace", "kvfix_diff_decode",
            "kvfix_status_string", "kvfix_version")
@@ -66,6 +67,12 @@ class c_diff(ctypes.Structure):
                 ("block_tokens", ctypes.c_int32)]
 
 
+class c_anchor_pool(ctypes.Structure):
+    _fields_ = [("n_anchors", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("n_max", ctypes.c_int64), ("lengths", ctypes.c_void_p),
+                ("a", ctypes.c_void_p), ("bt", ctypes.c_void_p)]
+
+
 class c_granularity(ctypes.Structure):
     _fields_ = [("per_head", ctypes.c_int32), ("cover", ctypes.c_void_p)]
 
@@ -103,6 +110,10 @@ def lib() -> ctypes.CDLL:
             "kvfix_fit_mean_ex": [P, I32, P, P, P, I32, P, P, P, P, P, ctypes.c_size_t, P],
             "kvfix_apply_ex": [P, P, P, P, F, F, P, P, P, P, P],
             "kvfix_select_master": [P, I32, I32, P, P, P],
+            "kvfix_anchor_match_workspace": [I32, I32, I32],
+            "kvfix_anchor_match": [P, P, I32, P, I64, ctypes.c_double, I32, I64, ctypes.c_double,
+                                   P, P, P, P, ctypes.c_size_t, P],
+            "kvfix_anchor_apply": [P, P, I32, P, P, I64, I64, ctypes.c_double, I32, P, P, P],
             "kvfix_fit_mean_workspace": [I32, I32, I32, I32, I32],
             "kvfix_fit_mean": [P, I32, P, P, P, I32, P, P, P, P, ctypes.c_size_t, P],
             "kvfix_apply": [P, P, P, P, F, F, P, P, P, P],
@@ -122,6 +133,7 @@ def lib() -> ctypes.CDLL:
         L.kvfix_fit_mean_workspace.restype = ctypes.c_size_t
         L.kvfix_diff_encode_workspace.restype = ctypes.c_size_t
         L.kvfix_diff_decode_workspace.restype = ctypes.c_size_t
+        L.kvfix_anchor_match_workspace.restype = ctypes.c_size_t
         L.kvfix_status_string.restype = ctypes.c_char_p
         _lib = L
     return _lib
@@ -412,3 +424,51 @@ def kvfix_diff_decode(master_k: Plane, master_v: Plane, diff: Diff, from_master:
     _check("kvfix_diff_decode", lib().kvfix_diff_decode(
         master_k.ref(), master_v.ref(), ctypes.byref(d), ctypes.byref(r), out_k.ref(),
         out_v.ref(), _ptr(ws), ws.numel() * ws.element_size(), _stream()))
+
+
+ANCHOR_MAX, ANCHOR_RANK = 16, 32
+
+
+class AnchorPool:
+    """Factors of an anchor pool: a [V, L, 2, n_max, r] and bt [V, L, 2, H*hd, r],
+    device tensors of bfloat16 (or their uint16/int16 bit patterns), plus the
+    host list of stored lengths."""
+
+    def __init__(self, a: torch.Tensor, bt: torch.Tensor, lengths: Sequence[int]):
+        if a.dim() != 5 or bt.dim() != 5 or not a.is_contiguous() or not bt.is_contiguous():
+            raise ValueError("a and bt must be contiguous 5-d tensors")
+        if a.element_size() != 2 or bt.element_size() != 2:
+            raise ValueError("a and bt must hold bf16 values")
+        V = a.shape[0]
+        if bt.shape[0] != V or len(lengths) != V:
+            raise ValueError("a, bt and lengths disagree on the anchor count")
+        self.a, self.bt = a, bt
+        self.lengths = [int(x) for x in lengths]
+        self._len = (ctypes.c_int32 * max(V, 1))(*self.lengths)
+        self.c = c_anchor_pool(V, a.shape[4], a.shape[3], ctypes.addressof(self._len),
+                               a.data_ptr(), bt.data_ptr())
+
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+def kvfix_anchor_match_workspace(n_layers: int, n_tokens: int, n_anchors: int) -> int:
+    return int(lib().kvfix_anchor_match_workspace(n_layers, n_tokens, n_anchors))
+
+
+def kvfix_anchor_match(src_k: Plane, src_v: Plane, seg: int, base: AnchorPool, src_off: int,
+                       theta: float, k_gate: int, tau: float, weights: torch.Tensor,
+                       gate: torch.Tensor, accept: torch.Tensor, ws: torch.Tensor,
+                       style: int = ROPE_HALF) -> None:
+    _check("kvfix_anchor_match", lib().kvfix_anchor_match(
+        src_k.ref(), src_v.ref(), seg, base.ref(), int(src_off), float(theta), style, int(k_gate),
+        float(tau), _ptr(weights), _ptr(gate), _ptr(accept), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream()))
+
+
+def kvfix_anchor_apply(src_k: Plane, src_v: Plane, seg: int, delta: AnchorPool,
+                       weights: Optional[torch.Tensor], src_off: int, tgt_off: int, theta: float,
+                       out_k: Plane, out_v: Plane, style: int = ROPE_HALF) -> None:
+    _check("kvfix_anchor_apply", lib().kvfix_anchor_apply(
+        src_k.ref(), src_v.ref(), seg, delta.ref(), _ptr(weights), int(src_off), int(tgt_off),
+        float(theta), style, out_k.ref(), out_v.ref(), _stream()))

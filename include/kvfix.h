@@ -19,6 +19,9 @@
  *   kvfix_diff_encode  block-sparse diff of N sibling caches against a master
  *   kvfix_diff_decode  fused restore: master + diff blocks + rotation, per sibling
  *   kvfix_select_master  the group's master: lowest total deviation
+ *   kvfix_anchor_match / kvfix_anchor_apply
+ *                      anchor-pool token weights, reliability gate, and the
+ *                      blended low-rank correction
  *
  * Sources (page titles; sections named, not quoted):
  *   [KVCMAS] "KVCMAS: Efficient KV cache Correction for Shared Context in
@@ -404,6 +407,83 @@ kvfix_status kvfix_diff_decode(const kvfix_plane* master_k, const kvfix_plane* m
                                const kvfix_diff* diff, const kvfix_rope* from_master,
                                const kvfix_plane* out_k, const kvfix_plane* out_v,
                                void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Anchor-blended low-rank correction and the reliability gate.
+ * [KVCMAS eq. 7: an anchor stores rank-r factors A B (A: rows x r, B: r x D)
+ *  of its base cache and of its delta correction; eq. 8: the correction is
+ *  the weighted sum of the anchors' deltas; App. A.3 "Reliability Gate"
+ *  eq. 9-11, "Correction Weighting and Positional Alignment", "Variable
+ *  Segment Lengths"; eq. 4 / 6 / 12: the correction is added to the aligned
+ *  source cache.]
+ *
+ * A pool holds the factors of V <= KVFIX_ANCHOR_MAX anchors of one shared
+ * segment slot, in canonical (segment-relative) positions, rank
+ * KVFIX_ANCHOR_RANK (a lower rank is passed zero-padded, which is exact):
+ *   a   device bf16 [V][n_layers][2][n_max][r]   (plane 0 = K, 1 = V)
+ *   bt  device bf16 [V][n_layers][2][n_heads*128][r]   B transposed: row
+ *       h*128 + d holds column (h, d) of B
+ *   lengths  HOST int32 [V]: tokens stored by each anchor, 0..n_max
+ * The base factors (the anchors' source caches) feed kvfix_anchor_match,
+ * the delta factors of the consuming agent feed kvfix_anchor_apply, with the
+ * same lengths.  Both pointers 16-byte aligned (KVFIX_ERR_ALIGN otherwise).
+ *
+ * Eligible anchors E: those storing the whole n-token segment; if none does,
+ * those storing the longest prefix, and the covered prefix is then that
+ * length (else n).  The source segment is segment `seg` of bf16 planes with
+ * head_dim 128 (KVFIX_ERR_UNSUPPORTED otherwise); its keys are cached at
+ * positions src_off + j.  Offsets (and their differences) up to 2^23.
+ * ------------------------------------------------------------------------- */
+#define KVFIX_ANCHOR_MAX 16
+#define KVFIX_ANCHOR_RANK 32
+
+typedef struct {
+  int32_t        n_anchors;      /* V, 0..KVFIX_ANCHOR_MAX */
+  int32_t        rank;           /* must be KVFIX_ANCHOR_RANK */
+  int64_t        n_max;
+  const int32_t* lengths;        /* host */
+  const void*    a;
+  const void*    bt;
+} kvfix_anchor_pool;
+
+/* Match: token weights and the gate.
+ * weights: device fp32 [n_layers][2][n][V].  For covered rows j and plane p,
+ *   w[l][p][j][v] = softmax over v in E of -dist_v (T = 1), dist_v = the mean
+ *   over all heads and dims of |source row - A_v[j] B_v| (keys first rotated
+ *   by -src_off to canonical positions); 0 for v outside E and for rows past
+ *   the covered prefix.
+ * gate: device fp64 [V + 1].  The comparison prefix is the first k_gate
+ *   tokens (clamped to [0, n]); A_k = anchors storing at least that many.
+ *   gate[v] = d_v = sqrt(sum over layers, prefix rows, heads, dims of
+ *   (value - A_v B_v)^2) for v in A_k, NaN otherwise; gate[V] = the
+ *   normalized entropy of softmax(-d) over A_k, clamped to [0, 1] (NaN with
+ *   fewer than two compared anchors).
+ * accept: device int32, 1 iff |A_k| >= 2 and gate[V] <= tau (else dense
+ *   prefill is due).
+ * ws: device workspace of kvfix_anchor_match_workspace(...) bytes, 8-byte
+ *   aligned (the per-block partial sums of the gate).
+ * Arithmetic: bf16 MFMA products, fp32 sums of distances, fp64 gate totals. */
+size_t kvfix_anchor_match_workspace(int32_t n_layers, int32_t n_tokens, int32_t n_anchors);
+kvfix_status kvfix_anchor_match(const kvfix_plane* src_k, const kvfix_plane* src_v, int32_t seg,
+                                const kvfix_anchor_pool* base, int64_t src_off, double theta,
+                                int32_t rope_style, int64_t k_gate, double tau, float* weights,
+                                double* gate, int32_t* accept, void* ws, size_t ws_bytes,
+                                void* stream);
+
+/* Apply: the corrected target segment.  For covered rows j:
+ *   delta_j = sum over v in E of weights[l][p][j][v] A_v[j] B_v (canonical),
+ *   keys    out = R(tgt_off - src_off) x + R(tgt_off) delta_j
+ *   values  out = x + delta_j
+ * and past the covered prefix out = R(tgt_off - src_off) x (keys), x (values).
+ * out_k/out_v: bf16 planes of the same shape (dense or paged), written at
+ * segment `seg`; they may alias src_k/src_v exactly (in place: each row is
+ * read and written by the same lanes).  weights: as produced by
+ * kvfix_anchor_match (may be NULL when E is empty).
+ * Arithmetic: bf16 MFMA products, fp32 blend and rotation, one rounding. */
+kvfix_status kvfix_anchor_apply(const kvfix_plane* src_k, const kvfix_plane* src_v, int32_t seg,
+                                const kvfix_anchor_pool* delta, const float* weights,
+                                int64_t src_off, int64_t tgt_off, double theta, int32_t rope_style,
+                                const kvfix_plane* out_k, const kvfix_plane* out_v, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* kvfix_status_string(kvfix_status status);

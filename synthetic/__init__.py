@@ -8,6 +8,7 @@ Both the oracle tests and the GPU benchmark draw their inputs from here.
 from .workloads import (  # noqa: F401
     CONFIGS,
     WorkloadConfig,
+    draw_anchor_pool,
     draw_correction,
     draw_collective,
     draw_draft_queries,

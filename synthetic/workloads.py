@@ -248,3 +248,53 @@ def draw_collective(cfg: WorkloadConfig, device="cpu", layers: Optional[Iterable
         out["master_" + plane] = torch.stack(ms)
         out["y_" + plane] = torch.stack(ys)
     return out
+
+
+def draw_anchor_pool(cfg: WorkloadConfig, n_anchors: int, device="cpu",
+                     layers: Optional[Iterable[int]] = None, n_max: Optional[int] = None,
+                     rank: int = 32, spread: float = 0.25, delta_std: float = 0.1) -> dict:
+    """Raw draws of an anchor pool and of a source segment that resembles it.
+
+    Per (layer, plane): shared factors A0 [n_max, rank] ~ N(0, 1) and
+    B0 [D, rank] ~ N(0, 1/sqrt(rank)) (D = H * hd); anchor v's base factors
+    are A0 + s_v N(0, 1) and B0 + s_v N(0, 1/sqrt(rank)) with s_v = spread *
+    (v + 1) / V, so the anchors sit at graded distances from the shared
+    structure; the source content is A_s B_s^T + N(0, noise_std) with its
+    own perturbation of strength spread / 2.  Delta factors are independent:
+    A ~ N(0, delta_std), B ~ N(0, 1/sqrt(rank)).
+
+    Returns
+      src_k, src_v         float32 [len(layers), 1, H, n, hd]: the source
+                           content in canonical (segment-relative) positions
+                           (storing keys at an offset needs a rotation, left to
+                           the caller)
+      a_base, bt_base      bf16 [V, len(layers), 2, n_max, rank] and
+      a_delta, bt_delta    bf16 [V, len(layers), 2, D, rank] (B transposed)
+    """
+    L = list(range(cfg.n_layers)) if layers is None else list(layers)
+    H, n, hd, V = cfg.n_kv_heads, cfg.n_tokens, cfg.head_dim, n_anchors
+    n_max = n if n_max is None else n_max
+    D = H * hd
+    bs = 1.0 / rank ** 0.5
+    out = {k: torch.empty(shape, dtype=torch.bfloat16, device=device) for k, shape in (
+        ("a_base", (V, len(L), 2, n_max, rank)), ("bt_base", (V, len(L), 2, D, rank)),
+        ("a_delta", (V, len(L), 2, n_max, rank)), ("bt_delta", (V, len(L), 2, D, rank)))}
+    src = {p: torch.empty((len(L), 1, H, n, hd), dtype=torch.float32, device=device)
+           for p in ("k", "v")}
+    for li, l in enumerate(L):
+        for pi, plane in enumerate(("k", "v")):
+            key = (cfg.seed, "anchor", plane, l)
+            A0 = _normal((max(n, n_max), rank), 1.0, device, *key, "A0")
+            B0 = _normal((D, rank), bs, device, *key, "B0")
+            for v in range(V):
+                s_v = spread * (v + 1) / V
+                out["a_base"][v, li, pi] = A0[:n_max] + _normal((n_max, rank), s_v, device, *key, v, "A")
+                out["bt_base"][v, li, pi] = B0 + _normal((D, rank), s_v * bs, device, *key, v, "B")
+                out["a_delta"][v, li, pi] = _normal((n_max, rank), delta_std, device, *key, v, "dA")
+                out["bt_delta"][v, li, pi] = _normal((D, rank), bs, device, *key, v, "dB")
+            As = A0[:n] + _normal((n, rank), spread / 2, device, *key, "As")
+            Bs = B0 + _normal((D, rank), spread / 2 * bs, device, *key, "Bs")
+            x = As @ Bs.T + _normal((n, D), cfg.noise_std, device, *key, "xs")
+            src[plane][li, 0] = x.reshape(n, H, hd).transpose(0, 1)
+    out["src_k"], out["src_v"] = src["k"], src["v"]
+    return out
