@@ -27,7 +27,9 @@ sample of the same workload.
   draft mass), coin (the same budget in random chunks, no draft) or grow
   (BCR-grow spans, tau 0.25).  c3 takes --layout: dense (default), paged
   (restore into a paged pool through a slot mapping) or plan (the reuse plan
-  first: deviation scores of every agent and the master selection).
+  first: deviation scores of every agent and the master selection).  c2 takes
+  --layout anchor: the same segment corrected through an anchor pool of 10
+  anchors at rank 32 (reliability gate, token weights, blended delta apply).
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload c2]
                   [--layout rows] [--no-cpu-baseline]
@@ -52,6 +54,7 @@ METRIC = "corrected-KV GB/s (read+write) and % of HBM peak; segment-layers/s at 
 KERNEL_SOURCES = {
     "apply": ["cross_context_kv_amd/csrc/correct.hip", "cross_context_kv_amd/csrc/common.h"],
     "diff_decode": ["cross_context_kv_amd/csrc/diff.hip", "cross_context_kv_amd/csrc/common.h"],
+    "anchor_apply": ["cross_context_kv_amd/csrc/anchor.hip", "cross_context_kv_amd/csrc/common.h"],
 }
 
 
@@ -63,19 +66,19 @@ def kernel_hash(kernel_tag: str) -> str:
     return h.hexdigest()[:16]
 
 
-def counters_path(workload: str) -> str:
-    return os.path.join(ROOT, "profiles", f"{Workload.ALL[workload].kernel_tag}_{workload}_counters.json")
+def counters_path(W) -> str:
+    return os.path.join(ROOT, "profiles", f"{W.kernel_tag}_{W.counter_name}_counters.json")
 
 
-def read_traffic(workload: str):
+def read_traffic(W):
     """HBM bytes per launch of the roofline kernel from the committed counter
     summary, or None when the kernel sources changed since it was taken."""
-    p = counters_path(workload)
+    p = counters_path(W)
     if not os.path.exists(p):
         return None
     with open(p) as f:
         c = json.load(f)
-    if c.get("kernel_hash") != kernel_hash(Workload.ALL[workload].kernel_tag):
+    if c.get("kernel_hash") != kernel_hash(W.kernel_tag):
         return None
     return c.get("traffic_bytes_per_launch")
 
@@ -134,6 +137,11 @@ def timed_oracle(fn, repeats):
 class Workload:
     ALL = {}
     kernel_tag = "apply"
+    extra_timed = {}
+
+    @property
+    def counter_name(self):
+        return self.name
 
     def __init__(self, cfg, torch, kv):
         self.cfg, self.torch, self.kv = cfg, torch, kv
@@ -674,13 +682,113 @@ class C3(Workload):
                           f"{dt:.1f} s, numpy fp64, one thread"}
 
 
+class C2Anchor(Workload):
+    """The c2 segment corrected through an anchor pool (KVCMAS eq. 8-11, App.
+    A.3): match (gate + token weights of K and V) and the blended apply."""
+    name = "c2"
+    counter_name = "c2_anchor"
+    kernel_tag = "anchor_apply"
+    V, RANK, SRC_OFF, TAU = 10, 32, 2048, 0.5
+
+    def workload_text(self):
+        return ("c2_llama3_8b segment (32 layers x 8 KV heads x 4096 tokens x hd 128 bf16) "
+                f"corrected through an anchor pool: V={self.V} anchors, rank {self.RANK}, "
+                "gate over the whole segment, token weights of K and V, blended delta apply "
+                "with re-alignment, theta 5e5")
+
+    def mfma_flops(self):
+        c = self.cfg
+        D = c.n_kv_heads * c.head_dim
+        return 2 * (self.V * c.n_layers * 2 * c.n_tokens * D * self.RANK * 2)
+
+    def alg_bytes(self):
+        c = self.cfg
+        L, H, n, hd, V, r = c.n_layers, c.n_kv_heads, c.n_tokens, c.head_dim, self.V, self.RANK
+        plane = L * H * n * hd * 2
+        a = V * L * 2 * n * r * 2
+        bt = V * L * 2 * H * hd * r * 2
+        wts = L * 2 * n * V * 4
+        parts = L * -(-n // 128) * V * 8
+        match = 2 * plane + a + bt + wts + parts
+        apply = 4 * plane + a + bt + wts
+        return {"match": match, "apply": apply, "roofline_per_launch": apply,
+                "roofline_units": 2 * L * H * n, "total": match + apply}
+
+    def build(self):
+        torch, kv, c = self.torch, self.kv, self.cfg
+        from synthetic import draw_anchor_pool, draw_deltas
+        L, n, V = c.n_layers, c.n_tokens, self.V
+        raw = draw_anchor_pool(c, V, "cuda", rank=self.RANK)
+        t = {k: raw[k] for k in ("a_base", "bt_base", "a_delta", "bt_delta")}
+        self.tgt_off = self.SRC_OFF + int(draw_deltas(c)[0])
+        # keys stored at positions SRC_OFF + j: the canonical content rotated forward
+        canon = raw["src_k"].to(torch.bfloat16)
+        t["src_k"] = torch.empty_like(canon)
+        off = torch.full((1,), self.SRC_OFF, dtype=torch.int64, device="cuda")
+        kv.kvfix_rope_shift(kv.Plane.dense(canon), kv.Plane.dense(t["src_k"]), off, c.theta)
+        t["src_v"] = raw["src_v"].to(torch.bfloat16)
+        del raw, canon
+        t["out_k"], t["out_v"] = torch.empty_like(t["src_k"]), torch.empty_like(t["src_v"])
+        t["w"] = torch.empty(L, 2, V, n, dtype=torch.float32, device="cuda")
+        t["gate"] = torch.empty(V + 1, dtype=torch.float64, device="cuda")
+        t["accept"] = torch.empty(1, dtype=torch.int32, device="cuda")
+        t["ws"] = torch.empty(kv.kvfix_anchor_match_workspace(L, n, V), dtype=torch.uint8,
+                              device="cuda")
+        lengths = [n] * V
+        self.base = kv.AnchorPool(t["a_base"], t["bt_base"], lengths)
+        self.delta = kv.AnchorPool(t["a_delta"], t["bt_delta"], lengths)
+        self.planes = {k: kv.Plane.dense(t[k]) for k in ("src_k", "src_v", "out_k", "out_v")}
+        self.extra_timed = {"anchor_match_kernel + gate finish": Timed(torch)}
+        self.t = t
+        torch.cuda.synchronize()
+
+    def step(self):
+        kv, t, c, P = self.kv, self.t, self.cfg, self.planes
+        with self.extra_timed["anchor_match_kernel + gate finish"]:
+            kv.kvfix_anchor_match(P["src_k"], P["src_v"], 0, self.base, self.SRC_OFF, c.theta,
+                                  c.n_tokens, self.TAU, t["w"], t["gate"], t["accept"], t["ws"])
+        with self.timed:
+            kv.kvfix_anchor_apply(P["src_k"], P["src_v"], 0, self.delta, t["w"], self.SRC_OFF,
+                                  self.tgt_off, c.theta, P["out_k"], P["out_v"])
+
+    def cpu_baseline(self, np):
+        """The oracle on a bounded sample: gate, token weights and apply of K
+        and V on layers 0-3 of the same input bytes (all tokens, all anchors)."""
+        torch, c, t = self.torch, self.cfg, self.t
+        from oracle import kvref as K
+        LS = 4
+        d = {k: host(t[k][:LS], torch, np) for k in ("src_k", "src_v")}
+        d.update({k: host(t[k][:, :LS], torch, np) for k in ("a_base", "bt_base", "a_delta",
+                                                             "bt_delta")})
+        lengths = [c.n_tokens] * self.V
+
+        def run():
+            K.anchor_gate(d["src_v"], d["a_base"], d["bt_base"], lengths, c.n_tokens, self.TAU,
+                          "bf16")
+            w = K.anchor_weights(d["src_k"], d["src_v"], d["a_base"], d["bt_base"], lengths,
+                                 self.SRC_OFF, c.theta, "half", "bf16")
+            for p, key in ((0, "src_k"), (1, "src_v")):
+                K.anchor_apply(d[key], p, d["a_delta"], d["bt_delta"], w, lengths, self.SRC_OFF,
+                               self.tgt_off, c.theta, "half", "bf16")
+
+        dt = timed_oracle(run, 1)
+        nbytes = self.alg_bytes()["total"] * LS // c.n_layers
+        return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "sample": f"gate, weights and apply of layers 0-{LS - 1} ({LS} of {c.n_layers}), "
+                          f"all {c.n_tokens} tokens and {self.V} anchors ({nbytes / 1e6:.1f} MB "
+                          f"algorithmic), one run of {dt:.1f} s, numpy fp64, one thread"}
+
+
 Workload.ALL = {"c2": C2, "c3": C3, "c4": C4, "c5": C5}
+# workload variants chosen by --layout
+VARIANTS = {("c2", "anchor"): C2Anchor}
 
 ROOFLINE_KERNEL = {
     "c2": "kvfix apply_kernel<bf16, fp32, hd128, rotate-half, rank 4>",
     "c3": "kvfix diff_decode_kernel<bf16, hd128, rotate-half> (with its rotary-table pre-kernel)",
     "c4": "kvfix apply_kernel<bf16, fp32, hd128, rotate-half, rank 0>",
     "c5": "kvfix apply_kernel<bf16, fp32, hd128, rotate-half, rank 2, paged>",
+    "c2_anchor": "kvfix anchor_apply_kernel<rotate-half> (V=10, rank 32, K and V planes)",
 }
 
 
@@ -708,11 +816,14 @@ def main():
     ap.add_argument("--workload", default="c2", choices=sorted(Workload.ALL))
     ap.add_argument("--layout", default=None,
                     help="c4: probe layout rows|chunk|coin|grow (BCR layouts and the coin "
-                         "control); c3: restore target dense|paged, or plan (reuse plan first)")
+                         "control); c3: restore target dense|paged, or plan (reuse plan first); "
+                         "c2: anchor (the segment corrected through an anchor pool)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     W = Workload.ALL[args.workload]
-    if args.layout is not None and args.layout not in getattr(W, "LAYOUT_TEXT", {}):
+    if (args.workload, args.layout) in VARIANTS:
+        W = VARIANTS[(args.workload, args.layout)]
+    elif args.layout is not None and args.layout not in getattr(W, "LAYOUT_TEXT", {}):
         print(f"--layout {args.layout} does not apply to {args.workload}", file=sys.stderr)
         sys.exit(2)
     if args.gpus != 1:
@@ -727,7 +838,7 @@ def main():
     from synthetic import CONFIGS
     kv.lib()                          # fails loudly without the built library
     w = W(CONFIGS[args.workload], torch, kv)
-    if args.layout is not None:
+    if args.layout is not None and W is Workload.ALL[args.workload]:
         w.layout = args.layout
     w.build()
     for _ in range(args.warmup):
@@ -746,6 +857,8 @@ def main():
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
     w.timed.on = True
+    for tm in w.extra_timed.values():
+        tm.on = True
     torch.cuda.synchronize()
     for _ in range(args.steps):
         w.step()
@@ -780,17 +893,21 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": ROOFLINE_KERNEL[args.workload],
+            "kernel": ROOFLINE_KERNEL[w.counter_name],
             "achieved": round(roof_gbs, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(roof_gbs / HBM_PEAK_GBS, 4),
-            "traffic": read_traffic(args.workload),
+            "traffic": read_traffic(w),
             "alg_bytes_per_launch": ab["roofline_per_launch"],
             "avg_launch_ms": round(roof_ms, 5),
         },
         "cpu_baseline": None,
     }
+    for label, tm in w.extra_timed.items():
+        line["config"][f"avg_ms {label}"] = round(tm.avg_ms(), 5)
+    if hasattr(w, "mfma_flops"):
+        line["config"]["mfma_TFLOPs"] = round(w.mfma_flops() / (ms * 1e-3) / 1e12, 1)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = w.cpu_baseline(np)
     print(json.dumps(line), flush=True)

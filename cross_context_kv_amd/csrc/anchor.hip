@@ -48,6 +48,7 @@ constexpr int kMatchWaves = 4, kMatchBands = 2;
 constexpr int kMatchTokens = kMatchWaves * kMatchBands * 16;    // 128
 constexpr int kApplyWaves = 4, kApplyBands = 4;
 constexpr int kApplyTokens = kApplyWaves * kApplyBands * 16;    // 256
+constexpr int kSlice = kTiles * 16 * kRank;   // one head's right factor, bf16 elements (8 KiB)
 constexpr int kXcds = 8;
 constexpr int64_t kMaxOffset = int64_t(1) << 23;   // rotary angles stay accurate below this
 
@@ -71,34 +72,37 @@ __device__ __forceinline__ const bf16_t* bt_row(const Pool& G, int v, int l, int
   return G.bt + ((((int64_t)v * G.L + l) * 2 + p) * G.D + f) * kRank;
 }
 
+// Factor rows are re-read by many blocks: ordinary (cached) loads.
 __device__ __forceinline__ bf16x8 ld_op(const bf16_t* p) {
-  return __builtin_bit_cast(bf16x8, ld16(p));
+  return __builtin_bit_cast(bf16x8, ld16_cached(p));
 }
 
-// The lane's 32 dims of row (l, seg, h, j) in fp32: x[0..15] = dims
-// [16g, 16g+16), x[16..31] = dims [64+16g, 64+16g+16).  Zeros for a row
-// outside the segment or on a bad page.
-__device__ __forceinline__ void load_lane_row(const DPlane& S, int l, int seg, int h, int j, int n,
-                                              int g, float* x) {
-  int64_t off = j < n ? row_offset(S, l, seg, h, j) : -1;
+// The lane's 32 dims of row (l, seg, h, j) as four raw 16-byte pieces:
+// dims [16g, 16g+8), [16g+8, 16g+16), [64+16g, ..+8), [64+16g+8, ..+16).
+// Zeros for a row outside the segment or on a bad page.
+__device__ __forceinline__ void load_lane_raw(const DPlane& S, int l, int seg, int h, int j, int n,
+                                              int g, vu4* r) {
+  const int64_t off = j < n ? row_offset(S, l, seg, h, j) : -1;
   if (off < 0) {
 #pragma unroll
-    for (int e = 0; e < 32; ++e) x[e] = 0.0f;
+    for (int q = 0; q < 4; ++q) r[q] = vu4{0u, 0u, 0u, 0u};
     return;
   }
   const bf16_t* row = reinterpret_cast<const bf16_t*>(S.data) + off;
 #pragma unroll
-  for (int part = 0; part < 2; ++part) {
+  for (int q = 0; q < 4; ++q) r[q] = ld16(row + (q >> 1) * 64 + 16 * g + 8 * (q & 1));
+}
+
+// Raw pieces -> fp32: x[0..15] = dims [16g, 16g+16), x[16..31] = dims
+// [64+16g, 64+16g+16).
+__device__ __forceinline__ void unpack_lane(const vu4* r, float* x) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const vu4 u = ld16(row + part * 64 + 16 * g + 8 * q);
+  for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        x[16 * part + 8 * q + 2 * w] = bf16_lo(u[w]);
-        x[16 * part + 8 * q + 2 * w + 1] = bf16_hi(u[w]);
-      }
+    for (int w = 0; w < 4; ++w) {
+      x[8 * q + 2 * w] = bf16_lo(r[q][w]);
+      x[8 * q + 2 * w + 1] = bf16_hi(r[q][w]);
     }
-  }
 }
 
 __device__ __forceinline__ void store_lane_row(const DPlane& O, int l, int seg, int h, int j,
@@ -157,8 +161,10 @@ struct MatchParams {
   uint32_t elig, gate_set;
   int32_t cover, k_gate;
   int32_t n_pairs, n_tiles;
+  int32_t n_list[2];               // anchors computed per plane, in order,
+  uint64_t list[2];                // 4 bits per anchor id
   float D;          // features per token row (all heads)
-  float* w;          // [L][2][n][V]
+  float* w;          // [L][2][V][n]
   double* part;      // [L][n_tiles][V]
 };
 
@@ -171,7 +177,8 @@ __host__ __device__ constexpr int match_lds_floats(int V) {
 
 template <int STYLE, bool GATE>
 __device__ __forceinline__ void match_body(const MatchParams& P, int l, int tile, float* acc1,
-                                           float* acc2, float* tc, float* ts, double* gsum) {
+                                           float* acc2, bf16_t* sbt, float* tc, float* ts,
+                                           double* gsum) {
   constexpr int p = GATE ? 1 : 0;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, t = lane & 15;
   const int V = P.V;
@@ -187,46 +194,117 @@ __device__ __forceinline__ void match_body(const MatchParams& P, int l, int tile
   const int lim = GATE ? max(P.cover, P.k_gate) : P.cover;
   const DPlane& S = P.src[p];
 
-  if (jw < lim) {
-    for (int h = 0; h < P.H; ++h) {
-      float nx[kMatchBands][32];
+  // One flat loop over the (head, listed anchor) pairs q = h * nl + i.  The
+  // right-factor slice of pair q + 1 is staged in LDS (two buffers, in the
+  // MFMA row order) and its left rows loaded while pair q computes, one
+  // barrier per pair; the source rows of the next head are loaded while the
+  // current head computes.  Indices are clamped at the end, so every load is
+  // unconditional.  The loop runs for every wave of the block (rows past the
+  // limit compute values nobody reads).
+  const int nl = P.n_list[p];
+  if (tile * kMatchTokens < lim && nl > 0) {
+    const uint64_t list = P.list[p];
+    const int total = P.H * nl;
+    const int tid = threadIdx.x;
+    vu4 xr[kMatchBands][4];
+    float nx[kMatchBands][32];
+    auto next_rows = [&](int h) {
+#pragma unroll
+      for (int b = 0; b < kMatchBands; ++b)
+        load_lane_raw(S, l, P.seg, h, jw + 16 * b + t, P.n, g, xr[b]);
+    };
+    auto take_rows = [&]() {
 #pragma unroll
       for (int b = 0; b < kMatchBands; ++b) {
-        load_lane_row(S, l, P.seg, h, jw + 16 * b + t, P.n, g, nx[b]);
+        unpack_lane(xr[b], nx[b]);
         if (STYLE != kStyleNone) rotate_lane<STYLE>(nx[b], tc, ts, g);
 #pragma unroll
         for (int e = 0; e < 32; ++e) nx[b][e] = -nx[b][e];
       }
-      for (int v = 0; v < V; ++v) {
-        if (!((set >> v) & 1u)) continue;
-        const int len = P.G.len[v];
-        const int lv = min(len, lim);
-        if (jw >= lv) continue;
-        bf16x8 bop[kTiles];
+    };
+    auto pair_hv = [&](int q, int& h, int& v) {
+      q = min(q, total - 1);
+      h = q / nl;
+      v = (int)((list >> (4 * (q - h * nl))) & 15u);
+    };
+    auto stage_load = [&](int q, vu4* r) {
+      int h, v;
+      pair_hv(q, h, v);
+      const bf16_t* src = bt_row(P.G, v, l, p, h * kHD);
+      r[0] = ld16_cached(src + 8 * tid);
+      r[1] = ld16_cached(src + 8 * (tid + 256));
+    };
+    auto stage_store = [&](const vu4* r, bf16_t* buf) {
 #pragma unroll
-        for (int c = 0; c < kTiles; ++c)
-          bop[c] = ld_op(bt_row(P.G, v, l, p, h * kHD + tile_dim(c, t)) + 8 * g);
-#pragma unroll
-        for (int b = 0; b < kMatchBands; ++b) {
-          if (jw + 16 * b >= lv) continue;
-          const int j = jw + 16 * b + t;
-          bf16x8 aop = {};
-          if (j < len) aop = ld_op(a_row(P.G, v, l, p, j) + 8 * g);
-          float s1[4] = {0, 0, 0, 0}, s2[4] = {0, 0, 0, 0};
-#pragma unroll
-          for (int c = 0; c < kTiles; ++c) {
-            const f32x4 cx = {nx[b][4 * c], nx[b][4 * c + 1], nx[b][4 * c + 2], nx[b][4 * c + 3]};
-            const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bop[c], aop, cx, 0, 0, 0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              s1[i] += fabsf(d[i]);
-              if (GATE) s2[i] = fmaf(d[i], d[i], s2[i]);
-            }
-          }
-          acc1[slot(v, b)] += (s1[0] + s1[1]) + (s1[2] + s1[3]);
-          if (GATE) acc2[slot(v, b)] += (s2[0] + s2[1]) + (s2[2] + s2[3]);
-        }
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const int u = tid + 256 * k2, f = u >> 2, qq = u & 3;
+        const int c = ((f >> 6) << 2) | ((f >> 2) & 3), m = (((f >> 4) & 3) << 2) | (f & 3);
+        *reinterpret_cast<vu4*>(buf + (c * 16 + m) * kRank + 8 * qq) = r[k2];
       }
+    };
+    auto load_a = [&](int q, bf16x8* a) {
+      int h, v;
+      pair_hv(q, h, v);
+      const int last = P.G.len[v] - 1;        // a listed anchor stores >= 1 row
+#pragma unroll
+      for (int b = 0; b < kMatchBands; ++b)
+        a[b] = ld_op(a_row(P.G, v, l, p, min(jw + 16 * b + t, last)) + 8 * g);
+    };
+    auto compute = [&](const bf16_t* buf, const bf16x8* a, int q) {
+      int h, v;
+      pair_hv(q, h, v);
+      bf16x8 bop[kTiles];
+#pragma unroll
+      for (int c = 0; c < kTiles; ++c)
+        bop[c] = *reinterpret_cast<const bf16x8*>(buf + (c * 16 + t) * kRank + 8 * g);
+#pragma unroll
+      for (int b = 0; b < kMatchBands; ++b) {
+        float s1[4] = {0, 0, 0, 0}, s2[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int c = 0; c < kTiles; ++c) {
+          const f32x4 cx = {nx[b][4 * c], nx[b][4 * c + 1], nx[b][4 * c + 2], nx[b][4 * c + 3]};
+          const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bop[c], a[b], cx, 0, 0, 0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            s1[e] += fabsf(d[e]);
+            if (GATE) s2[e] = fmaf(d[e], d[e], s2[e]);
+          }
+        }
+        acc1[slot(v, b)] += (s1[0] + s1[1]) + (s1[2] + s1[3]);
+        if (GATE) acc2[slot(v, b)] += (s2[0] + s2[1]) + (s2[2] + s2[3]);
+      }
+      // last anchor of head h: switch the rows to head h + 1
+      if (q - h * nl == nl - 1 && h + 1 < P.H) {
+        take_rows();
+        next_rows(min(h + 2, P.H - 1));
+      }
+    };
+
+    // Iteration q stores the slice of pair q + 1 (loaded one iteration
+    // earlier) into the buffer pair q - 1 used, loads the slice of pair q + 2
+    // and the left rows of pair q + 1, computes pair q, and ends on the
+    // barrier that publishes pair q + 1.
+    vu4 sr[2];
+    bf16x8 a0[kMatchBands], a1[kMatchBands];
+    next_rows(0);
+    stage_load(0, sr);
+    load_a(0, a0);
+    stage_store(sr, sbt);
+    stage_load(1, sr);
+    take_rows();
+    next_rows(min(1, P.H - 1));
+    __syncthreads();
+    for (int q = 0; q < total; q += 2) {
+      stage_store(sr, sbt + kSlice);
+      stage_load(q + 2, sr);
+      load_a(q + 1, a1);
+      compute(sbt, a0, q);
+      __syncthreads();
+      stage_store(sr, sbt);
+      stage_load(q + 3, sr);
+      load_a(q + 2, a0);
+      if (q + 1 < total) compute(sbt + kSlice, a1, q + 1);
+      __syncthreads();
     }
   }
   __syncthreads();
@@ -243,9 +321,9 @@ __device__ __forceinline__ void match_body(const MatchParams& P, int l, int tile
     for (int b = 0; b < kMatchBands; ++b) {
       const int j = jw + 16 * b + t;
       if (j >= P.n) continue;
-      float* wr = P.w + (((int64_t)l * 2 + p) * P.n + j) * V;
+      float* wr = P.w + ((int64_t)l * 2 + p) * V * P.n + j;
       if (j >= P.cover) {
-        for (int v = 0; v < V; ++v) wr[v] = 0.0f;
+        for (int v = 0; v < V; ++v) wr[(int64_t)v * P.n] = 0.0f;
         continue;
       }
       float m = INFINITY;
@@ -255,7 +333,8 @@ __device__ __forceinline__ void match_body(const MatchParams& P, int l, int tile
       for (int v = 0; v < V; ++v)
         if ((P.elig >> v) & 1u) sum += expf(m - total(acc1, v, b) / P.D);
       for (int v = 0; v < V; ++v)
-        wr[v] = ((P.elig >> v) & 1u) ? expf(m - total(acc1, v, b) / P.D) / sum : 0.0f;
+        wr[(int64_t)v * P.n] =
+            ((P.elig >> v) & 1u) ? expf(m - total(acc1, v, b) / P.D) / sum : 0.0f;
     }
   }
 
@@ -291,6 +370,7 @@ template <int STYLE>
 __global__ __launch_bounds__(kMatchWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void anchor_match_kernel(MatchParams P) {
   extern __shared__ float match_lds[];
+  __shared__ __attribute__((aligned(16))) bf16_t sbt[2 * kSlice];
   __shared__ float tc[kHD / 2], ts[kHD / 2];
   __shared__ double gsum[kMatchWaves * kAnchorMax];
   const int id = blockIdx.x, xcd = id % kXcds, k = id / kXcds;
@@ -301,9 +381,9 @@ void anchor_match_kernel(MatchParams P) {
   float* acc1 = match_lds;
   float* acc2 = match_lds + match_lds_floats(P.V) / 2;
   if ((pair & 1) == 0)
-    match_body<STYLE, false>(P, l, tile, acc1, acc2, tc, ts, gsum);
+    match_body<STYLE, false>(P, l, tile, acc1, acc2, sbt, tc, ts, gsum);
   else
-    match_body<kStyleNone, true>(P, l, tile, acc1, acc2, tc, ts, gsum);
+    match_body<kStyleNone, true>(P, l, tile, acc1, acc2, sbt, tc, ts, gsum);
 }
 
 // Gate finish: d_v = sqrt of the summed partials (fp64, fixed order), then
@@ -365,54 +445,98 @@ struct AnchorApplyParams {
   uint32_t elig;
   int32_t cover;
   int32_t n_pairs, n_tiles;
-  const float* w;    // [L][2][n][V]
+  int32_t n_list;                  // the eligible anchors, in order,
+  uint64_t list;                   // 4 bits per anchor id
+  const float* w;    // [L][2][V][n]
 };
 
 template <int STYLE>
 __device__ __forceinline__ void apply_body(const AnchorApplyParams& P, int l, int p, int h,
-                                           int tile) {
-  __shared__ float tc1[kHD / 2], ts1[kHD / 2], tc2[kHD / 2], ts2[kHD / 2];
+                                           int tile, bf16_t* sbt, float* tab) {
+  float *tc1 = tab, *ts1 = tab + 64, *tc2 = tab + 128, *ts2 = tab + 192;
   if (STYLE != kStyleNone) {
     rope_table<kHD, float>(P.rope, P.tgt_off - P.src_off, tc1, ts1);
     rope_table<kHD, float>(P.rope, P.tgt_off, tc2, ts2);
   }
   __syncthreads();
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, t = lane & 15;
-  const int jw = tile * kApplyTokens + wave * kApplyBands * 16;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, t = lane & 15;
+  const int j0 = tile * kApplyTokens, jw = j0 + wave * kApplyBands * 16;
   f32x4 acc[kApplyBands][kTiles];
 #pragma unroll
   for (int b = 0; b < kApplyBands; ++b)
 #pragma unroll
     for (int c = 0; c < kTiles; ++c) acc[b][c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  if (jw < P.cover) {
-    const float* wl = P.w + ((int64_t)l * 2 + p) * P.n * P.V;
+  // The eligible anchors in order.  The head's right-factor slice of anchor
+  // i + 1 is staged in LDS (two buffers, in the MFMA row order) and its left
+  // rows and weights loaded while anchor i computes; one barrier per anchor.
+  // Indices are clamped at the end, so every load is unconditional; rows past
+  // the covered prefix read the last covered row and get weight 0.
+  const int nl = P.n_list;
+  if (j0 < P.cover && nl > 0) {
+    const float* wl = P.w + ((int64_t)l * 2 + p) * P.V * P.n;
+    const int last = P.cover - 1;
+    auto anchor = [&](int i) { return (int)((P.list >> (4 * min(i, nl - 1))) & 15u); };
+    auto stage_load = [&](int v, vu4* r) {
+      const bf16_t* src = bt_row(P.G, v, l, p, h * kHD);
+      r[0] = ld16_cached(src + 8 * tid);
+      r[1] = ld16_cached(src + 8 * (tid + 256));
+    };
+    auto stage_store = [&](const vu4* r, bf16_t* buf) {
 #pragma unroll
-    for (int v = 0; v < kAnchorMax; ++v) {
-      if (!((P.elig >> v) & 1u)) continue;
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const int u = tid + 256 * k2, f = u >> 2, q = u & 3;
+        const int c = ((f >> 6) << 2) | ((f >> 2) & 3), m = (((f >> 4) & 3) << 2) | (f & 3);
+        *reinterpret_cast<vu4*>(buf + (c * 16 + m) * kRank + 8 * q) = r[k2];
+      }
+    };
+    struct AOps {
+      bf16x8 a[kApplyBands];
+      float w[kApplyBands];
+    };
+    auto load_a = [&](int v, AOps& o) {
+#pragma unroll
+      for (int b = 0; b < kApplyBands; ++b) {
+        const int j = jw + 16 * b + t;
+        const int jr = min(j, last);
+        o.a[b] = ld_op(a_row(P.G, v, l, p, jr) + 8 * g);
+        const float wv = wl[(int64_t)v * P.n + jr];
+        o.w[b] = j < P.cover ? wv : 0.0f;
+      }
+    };
+    auto compute = [&](const bf16_t* buf, const AOps& o) {
       bf16x8 bop[kTiles];
 #pragma unroll
       for (int c = 0; c < kTiles; ++c)
-        bop[c] = ld_op(bt_row(P.G, v, l, p, h * kHD + tile_dim(c, t)) + 8 * g);
+        bop[c] = *reinterpret_cast<const bf16x8*>(buf + (c * 16 + t) * kRank + 8 * g);
 #pragma unroll
-      for (int b = 0; b < kApplyBands; ++b) {
-        if (jw + 16 * b >= P.cover) continue;
-        const int j = jw + 16 * b + t;
-        bf16x8 aop = {};
-        float wv = 0.0f;
-        if (j < P.cover) {
-          aop = ld_op(a_row(P.G, v, l, p, j) + 8 * g);
-          wv = wl[(int64_t)j * P.V + v];
-        }
+      for (int b = 0; b < kApplyBands; ++b)
 #pragma unroll
         for (int c = 0; c < kTiles; ++c) {
           const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              bop[c], aop, f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+              bop[c], o.a[b], f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[b][c][i] = fmaf(wv, d[i], acc[b][c][i]);
+          for (int e = 0; e < 4; ++e) acc[b][c][e] = fmaf(o.w[b], d[e], acc[b][c][e]);
         }
-      }
+    };
+    vu4 sr[2];
+    AOps A0, A1;
+    stage_load(anchor(0), sr);
+    load_a(anchor(0), A0);
+    stage_store(sr, sbt);
+    __syncthreads();
+    for (int i = 0; i < nl; i += 2) {
+      stage_load(anchor(i + 1), sr);
+      load_a(anchor(i + 1), A1);
+      compute(sbt, A0);
+      stage_store(sr, sbt + kSlice);
+      __syncthreads();
+      stage_load(anchor(i + 2), sr);
+      load_a(anchor(i + 2), A0);
+      if (i + 1 < nl) compute(sbt + kSlice, A1);
+      stage_store(sr, sbt);
+      __syncthreads();
     }
   }
 
@@ -420,12 +544,14 @@ __device__ __forceinline__ void apply_body(const AnchorApplyParams& P, int l, in
   for (int b = 0; b < kApplyBands; ++b) {
     const int j = jw + 16 * b + t;
     if (j >= P.n) continue;
+    vu4 xr[4];
     float x[32], dl[32];
-    load_lane_row(P.src[p], l, P.seg, h, j, P.n, g, x);
+    load_lane_raw(P.src[p], l, P.seg, h, j, P.n, g, xr);
+    unpack_lane(xr, x);
 #pragma unroll
     for (int c = 0; c < kTiles; ++c)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dl[4 * c + i] = acc[b][c][i];
+      for (int e = 0; e < 4; ++e) dl[4 * c + e] = acc[b][c][e];
     if (STYLE != kStyleNone) {
       rotate_lane<STYLE>(x, tc1, ts1, g);
       rotate_lane<STYLE>(dl, tc2, ts2, g);
@@ -442,6 +568,8 @@ __device__ __forceinline__ void apply_body(const AnchorApplyParams& P, int l, in
 template <int STYLE>
 __global__ __launch_bounds__(kApplyWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void anchor_apply_kernel(AnchorApplyParams P) {
+  __shared__ __attribute__((aligned(16))) bf16_t sbt[2 * kSlice];
+  __shared__ float tab[4 * (kHD / 2)];
   const int id = blockIdx.x, xcd = id % kXcds, k = id / kXcds;
   const int h = k % P.H, k2 = k / P.H;
   const int tile = k2 % P.n_tiles;
@@ -449,9 +577,9 @@ void anchor_apply_kernel(AnchorApplyParams P) {
   if (pair >= P.n_pairs) return;
   const int l = pair >> 1;
   if ((pair & 1) == 0)
-    apply_body<STYLE>(P, l, 0, h, tile);
+    apply_body<STYLE>(P, l, 0, h, tile, sbt, tab);
   else
-    apply_body<kStyleNone>(P, l, 1, h, tile);
+    apply_body<kStyleNone>(P, l, 1, h, tile, sbt, tab);
 }
 
 // ----------------------------------------------------------------------------
@@ -585,6 +713,12 @@ extern "C" kvfix_status kvfix_anchor_match(const kvfix_plane* src_k, const kvfix
   P.n_pairs = 2 * L;
   P.n_tiles = (int32_t)n_match_tiles(n);
   P.D = (float)(src_k->n_heads * kHD);
+  for (int v = 0; v < V; ++v) {
+    const bool in_e = (e.elig >> v) & 1u;
+    const bool in_gate = e.k_gate > 0 && ((e.gate_set >> v) & 1u);
+    if (in_e) P.list[0] |= (uint64_t)v << (4 * P.n_list[0]++);
+    if (in_e || in_gate) P.list[1] |= (uint64_t)v << (4 * P.n_list[1]++);
+  }
   P.w = weights;
   P.part = static_cast<double*>(ws);
   if (V > 0 && n > 0 && L > 0) {
@@ -643,6 +777,8 @@ extern "C" kvfix_status kvfix_anchor_apply(const kvfix_plane* src_k, const kvfix
   P.cover = e.cover;
   P.n_pairs = 2 * L;
   P.n_tiles = (n + kApplyTokens - 1) / kApplyTokens;
+  for (int v = 0; v < V; ++v)
+    if ((e.elig >> v) & 1u) P.list |= (uint64_t)v << (4 * P.n_list++);
   P.w = weights;
   const int64_t grid =
       (int64_t)P.H * P.n_tiles * ((P.n_pairs + kXcds - 1) / kXcds) * kXcds;

@@ -447,8 +447,8 @@ typedef struct {
 } kvfix_anchor_pool;
 
 /* Match: token weights and the gate.
- * weights: device fp32 [n_layers][2][n][V].  For covered rows j and plane p,
- *   w[l][p][j][v] = softmax over v in E of -dist_v (T = 1), dist_v = the mean
+ * weights: device fp32 [n_layers][2][V][n].  For covered rows j and plane p,
+ *   w[l][p][v][j] = softmax over v in E of -dist_v (T = 1), dist_v = the mean
  *   over all heads and dims of |source row - A_v[j] B_v| (keys first rotated
  *   by -src_off to canonical positions); 0 for v outside E and for rows past
  *   the covered prefix.
@@ -471,7 +471,7 @@ kvfix_status kvfix_anchor_match(const kvfix_plane* src_k, const kvfix_plane* src
                                 void* stream);
 
 /* Apply: the corrected target segment.  For covered rows j:
- *   delta_j = sum over v in E of weights[l][p][j][v] A_v[j] B_v (canonical),
+ *   delta_j = sum over v in E of weights[l][p][v][j] A_v[j] B_v (canonical),
  *   keys    out = R(tgt_off - src_off) x + R(tgt_off) delta_j
  *   values  out = x + delta_j
  * and past the covered prefix out = R(tgt_off - src_off) x (keys), x (values).

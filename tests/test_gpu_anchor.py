@@ -54,7 +54,7 @@ def gpu_match(case, lengths, k_gate, tau, src_k=None, src_v=None):
     pk = Plane.dense(tk) if src_k is None else src_k
     pv = Plane.dense(tv) if src_v is None else src_v
     base = AnchorPool(from_np(case["a_base"], DEV), from_np(case["bt_base"], DEV), lengths)
-    w = torch.full((L, 2, n, V), float("nan"), dtype=torch.float32, device=DEV)
+    w = torch.full((L, 2, V, n), float("nan"), dtype=torch.float32, device=DEV)
     gate = torch.full((V + 1,), -1.0, dtype=torch.float64, device=DEV)
     acc = torch.full((1,), -7, dtype=torch.int32, device=DEV)
     ws = torch.empty(kv.kvfix_anchor_match_workspace(L, n, V), dtype=torch.uint8, device=DEV)
@@ -94,8 +94,13 @@ def check_gate(case, lengths, k_gate, tau, g_gate, g_acc):
     return o
 
 
+def weights_np(w):
+    """GPU weights [L][2][V][n] -> the oracle's layout [L][2][n][V]."""
+    return w.cpu().numpy().transpose(0, 1, 3, 2)
+
+
 def check_weights(case, lengths, w):
-    g = w.cpu().numpy()
+    g = weights_np(w)
     o = K.anchor_weights(case["src_k"], case["src_v"], case["a_base"], case["bt_base"], lengths,
                          case["src_off"], case["theta"], case["style"], "bf16")
     err = np.abs(g.astype(np.float64) - o).max() if g.size else 0.0
@@ -112,7 +117,7 @@ def check_weights(case, lengths, w):
 
 def check_apply(case, lengths, w, tgt_off):
     gk, gv = gpu_apply(case, lengths, w, tgt_off)
-    wn = w.cpu().numpy().astype(np.float64)
+    wn = weights_np(w).astype(np.float64)
     errs = []
     for plane, src, g in ((0, case["src_k"], gk), (1, case["src_v"], gv)):
         o = K.anchor_apply(src, plane, case["a_delta"], case["bt_delta"], wn, lengths,
@@ -243,7 +248,7 @@ def test_llama3_8b_shape_ten_anchors_sampled():
     lengths = [n] * V
     base = AnchorPool(raw["a_base"], raw["bt_base"], lengths)
     delta = AnchorPool(raw["a_delta"], raw["bt_delta"], lengths)
-    w = torch.empty((L, 2, n, V), dtype=torch.float32, device=DEV)
+    w = torch.empty((L, 2, V, n), dtype=torch.float32, device=DEV)
     gate = torch.empty((V + 1,), dtype=torch.float64, device=DEV)
     acc = torch.empty((1,), dtype=torch.int32, device=DEV)
     ws = torch.empty(kv.kvfix_anchor_match_workspace(L, n, V), dtype=torch.uint8, device=DEV)
@@ -278,7 +283,7 @@ def test_llama3_8b_shape_ten_anchors_sampled():
     m = len(toks)
     o_w = K.anchor_weights(sk, sv, fac["a_base"], bt["bt_base"], [m] * V, src_off, theta, "half",
                            "bf16")
-    g_w = w[layers][:, :, toks].cpu().numpy().astype(np.float64)
+    g_w = weights_np(w[layers][:, :, :, toks]).astype(np.float64)
     err = np.abs(g_w - o_w).max()
     log("8B-shape weights max abs err", err)
     assert err <= W_TOL
