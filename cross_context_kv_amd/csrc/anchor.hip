@@ -168,11 +168,13 @@ struct MatchParams {
   double* part;      // [L][n_tiles][V]
 };
 
-// Per-lane distance sums live in LDS, one slot per (wave, anchor, band,
-// lane): acc1 the absolute, acc2 the squared distances.  A lane only ever
-// touches its own slots inside the head loop.
+// Distance sums live in LDS, one slot per (wave, anchor, band, token
+// column): acc1 the absolute, acc2 the squared distances.  Each pair's
+// partial sums are first added across the four lane groups of a column
+// (fixed order), then lane group 0 adds them to the column's slot; no other
+// lane touches that slot inside the head loop.
 __host__ __device__ constexpr int match_lds_floats(int V) {
-  return 2 * kMatchWaves * V * kMatchBands * 64;
+  return 2 * kMatchWaves * V * kMatchBands * 16;
 }
 
 template <int STYLE, bool GATE>
@@ -182,10 +184,11 @@ __device__ __forceinline__ void match_body(const MatchParams& P, int l, int tile
   constexpr int p = GATE ? 1 : 0;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, t = lane & 15;
   const int V = P.V;
-  auto slot = [&](int v, int b) { return (((wave * V + v) * kMatchBands + b) << 6) + lane; };
-  for (int v = 0; v < V; ++v)
+  auto slot = [&](int v, int b) { return (((wave * V + v) * kMatchBands + b) << 4) + t; };
+  if (g == 0)
+    for (int v = 0; v < V; ++v)
 #pragma unroll
-    for (int b = 0; b < kMatchBands; ++b) acc1[slot(v, b)] = acc2[slot(v, b)] = 0.0f;
+      for (int b = 0; b < kMatchBands; ++b) acc1[slot(v, b)] = acc2[slot(v, b)] = 0.0f;
   if (STYLE != kStyleNone) rope_table<kHD, float>(P.rope, -P.src_off, tc, ts);
   __syncthreads();
 
@@ -197,10 +200,10 @@ __device__ __forceinline__ void match_body(const MatchParams& P, int l, int tile
   // One flat loop over the (head, listed anchor) pairs q = h * nl + i.  The
   // right-factor slice of pair q + 1 is staged in LDS (two buffers, in the
   // MFMA row order) and its left rows loaded while pair q computes, one
-  // barrier per pair; the source rows of the next head are loaded while the
-  // current head computes.  Indices are clamped at the end, so every load is
-  // unconditional.  The loop runs for every wave of the block (rows past the
-  // limit compute values nobody reads).
+  // barrier per pair; the source rows of a head are loaded after its last
+  // pair (three waves per SIMD cover that wait).  Indices are clamped at the
+  // end, so every load is unconditional.  The loop runs for every wave of the
+  // block (rows past the limit compute values nobody reads).
   const int nl = P.n_list[p];
   if (tile * kMatchTokens < lim && nl > 0) {
     const uint64_t list = P.list[p];
@@ -270,13 +273,24 @@ __device__ __forceinline__ void match_body(const MatchParams& P, int l, int tile
             if (GATE) s2[e] = fmaf(d[e], d[e], s2[e]);
           }
         }
-        acc1[slot(v, b)] += (s1[0] + s1[1]) + (s1[2] + s1[3]);
-        if (GATE) acc2[slot(v, b)] += (s2[0] + s2[1]) + (s2[2] + s2[3]);
+        float c1 = (s1[0] + s1[1]) + (s1[2] + s1[3]);
+        c1 += __shfl_xor(c1, 16);
+        c1 += __shfl_xor(c1, 32);
+        float c2 = 0.0f;
+        if (GATE) {
+          c2 = (s2[0] + s2[1]) + (s2[2] + s2[3]);
+          c2 += __shfl_xor(c2, 16);
+          c2 += __shfl_xor(c2, 32);
+        }
+        if (g == 0) {
+          acc1[slot(v, b)] += c1;
+          if (GATE) acc2[slot(v, b)] += c2;
+        }
       }
       // last anchor of head h: switch the rows to head h + 1
       if (q - h * nl == nl - 1 && h + 1 < P.H) {
+        next_rows(h + 1);
         take_rows();
-        next_rows(min(h + 2, P.H - 1));
       }
     };
 
@@ -292,7 +306,6 @@ __device__ __forceinline__ void match_body(const MatchParams& P, int l, int tile
     stage_store(sr, sbt);
     stage_load(1, sr);
     take_rows();
-    next_rows(min(1, P.H - 1));
     __syncthreads();
     for (int q = 0; q < total; q += 2) {
       stage_store(sr, sbt + kSlice);
@@ -309,11 +322,7 @@ __device__ __forceinline__ void match_body(const MatchParams& P, int l, int tile
   }
   __syncthreads();
 
-  // Column totals: the four lane groups of token t, added in group order.
-  auto total = [&](const float* acc, int v, int b) {
-    const int base = (((wave * V + v) * kMatchBands + b) << 6) + t;
-    return ((acc[base] + acc[base + 16]) + acc[base + 32]) + acc[base + 48];
-  };
+  auto total = [&](const float* acc, int v, int b) { return acc[slot(v, b)]; };
 
   // Token weights: softmax of minus the mean absolute distance over E.
   if (g == 0) {
@@ -367,7 +376,7 @@ __device__ __forceinline__ void match_body(const MatchParams& P, int l, int tile
 // Blocks of one (layer, plane) run on one XCD, so the plane's right factors
 // (all anchors: V * D * r bf16) are fetched into that XCD's L2 once.
 template <int STYLE>
-__global__ __launch_bounds__(kMatchWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(kMatchWaves * 64) __attribute__((amdgpu_waves_per_eu(3)))
 void anchor_match_kernel(MatchParams P) {
   extern __shared__ float match_lds[];
   __shared__ __attribute__((aligned(16))) bf16_t sbt[2 * kSlice];
