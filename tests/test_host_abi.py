@@ -137,3 +137,61 @@ def test_empty_shapes_are_noops_without_launch():
         assert L.kvfix_rope_shift(R(p), R(p), R(rope()), None) == 0
     assert L.kvfix_select_topb(None, 0, 10, 3, None, None, None) == 0
     assert L.kvfix_select_topb(None, 4, 0, 0, None, None, None) == 0
+
+
+def anchor_pool(V=3, rank=32, n_max=64, lengths=None, a=4096, bt=8192):
+    lens = (ctypes.c_int32 * max(V, 1))(*(lengths if lengths is not None else [n_max] * V))
+    pool = kv.c_anchor_pool(V, rank, n_max, ctypes.addressof(lens), a, bt)
+    pool._lens = lens                   # keep the host array alive
+    return pool
+
+
+def test_anchor_call_validation():
+    L = kv.lib()
+    p = plane()
+    w, gate, acc = ctypes.c_void_p(512), ctypes.c_void_p(1024), ctypes.c_void_p(2048)
+    need = L.kvfix_anchor_match_workspace(2, 64, 3)
+    assert need == 2 * 1 * 3 * 8 + 256
+    assert L.kvfix_anchor_match_workspace(2, 200, 3) == 2 * 2 * 3 * 8 + 256
+    ws = ctypes.c_void_p(4096)
+
+    def match(pk=p, pv=p, seg=0, pool=None, src_off=100, theta=1e4, style=kv.ROPE_HALF, k=64,
+              tau=0.5, wts=w, g=gate, a=acc, wsp=ws, wsb=need):
+        pool = anchor_pool() if pool is None else pool
+        return L.kvfix_anchor_match(R(pk), R(pv), seg, R(pool), src_off, theta, style, k, tau,
+                                    wts, g, a, wsp, wsb, None)
+
+    def apply(pk=p, pv=p, seg=0, pool=None, wts=w, src_off=100, tgt_off=900, theta=1e4,
+              style=kv.ROPE_HALF, ok=p, ov=p):
+        pool = anchor_pool() if pool is None else pool
+        return L.kvfix_anchor_apply(R(pk), R(pv), seg, R(pool), wts, src_off, tgt_off, theta,
+                                    style, R(ok), R(ov), None)
+
+    for call in (match, apply):
+        assert call(pool=anchor_pool(rank=16)) == 5                 # rank must be 32
+        assert call(pool=anchor_pool(V=17)) == 1                    # at most 16 anchors
+        assert call(pool=anchor_pool(lengths=[64, 65, 3])) == 1     # a length past n_max
+        assert call(pool=anchor_pool(lengths=[64, -1, 3])) == 1
+        assert call(pool=anchor_pool(a=None)) == 1
+        assert call(pool=anchor_pool(bt=8200)) == 2                 # factors 16-byte aligned
+        assert call(pk=plane(dtype=kv.F32, s_layer=4 * 64 * 128, s_seg=4 * 64 * 128,
+                             s_head=64 * 128, s_token=128)) == 1    # K and V must agree
+        f32 = plane(dtype=kv.F32)
+        assert call(pk=f32, pv=f32) == 5                            # bf16 planes only
+        hd64 = plane(head_dim=64, s_token=64)
+        assert call(pk=hd64, pv=hd64) == 5                          # head_dim 128 only
+        assert call(seg=1) == 1 and call(seg=-1) == 1
+        assert call(pv=plane(n_tokens=32)) == 1
+        assert call(style=3) == 1 and call(theta=0.0) == 1
+        assert call(src_off=(1 << 23) + 1) == 1                     # rotary angle range
+    assert match(g=None) == 1 and match(a=None) == 1 and match(wsp=None) == 1
+    assert match(wsb=need - 8) == 1
+    assert match(wsp=ctypes.c_void_p(4100)) == 2
+    assert match(tau=float("nan")) == 1
+    assert match(wts=None) == 1                                     # weights needed with anchors
+    assert apply(tgt_off=-(1 << 23) - 50) == 1                      # tgt - src out of range too
+    assert apply(wts=None) == 1                                     # eligible anchors need weights
+    assert apply(ok=plane(n_heads=3)) == 1
+    # no eligible anchor and no rows: nothing to launch
+    assert apply(wts=None, pool=anchor_pool(lengths=[0, 0, 0]), pk=plane(n_layers=0),
+                 pv=plane(n_layers=0), ok=plane(n_layers=0), ov=plane(n_layers=0)) == 0
