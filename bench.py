@@ -177,26 +177,38 @@ class Correction(Workload):
                 "roofline_per_launch": apply_one, "roofline_units": L * S * H * (n - b),
                 "total": score + select + fit + 2 * apply_one}
 
-    def step(self):
+    def _prep(self, i, p):
+        """Score, select and fit of one plane (on the current stream)."""
         kv, t, c = self.kv, self.t, self.cfg
-        S, n, b, ck = c.n_segs, c.n_tokens, c.b, c.check_layer
-        F, R = self.fresh_check_planes, self.reuse_planes
-        fl = self.fresh_check_layer
-        kv.kvfix_score(F["k"], fl, R["k"], ck, t["scores"][0], t["delta"], c.theta)
-        kv.kvfix_score(F["v"], fl, R["v"], ck, t["scores"][1])
-        kv.kvfix_select_topb(t["scores"].view(2 * S, n), b, t["idx"].view(2 * S, b),
-                             t["mask"].view(2 * S, -1))
+        R = self.reuse_planes
+        d = t["delta"] if p == "k" else None
+        kv.kvfix_score(self.fresh_check_planes[p], self.fresh_check_layer, R[p], c.check_layer,
+                       t["scores"][i], d, c.theta)
+        kv.kvfix_select_topb(t["scores"][i], c.b, t["idx"][i], t["mask"][i])
+        kv.kvfix_fit_mean(self.fit_fresh_planes[p], R[p], self.out_planes[p], t["idx"][i], c.b,
+                          t["mu"][i], d, c.theta, A=t["A_" + p], B=t["B_" + p],
+                          fresh_by_slot=self.paged, ws=t["ws_fit_" + p])
+
+    def step(self):
+        """The K and V chains are independent: the V plane's score, selection
+        and fit run on a second stream while the K plane's run and its apply
+        streams; the V apply follows the K apply on the main stream."""
+        kv, t, c, torch = self.kv, self.t, self.cfg, self.torch
+        main = torch.cuda.current_stream()
+        self.ev_fork.record(main)
+        self.side.wait_event(self.ev_fork)
+        with torch.cuda.stream(self.side):
+            self._prep(1, "v")
+            self.ev_join.record(self.side)
+        self._prep(0, "k")
         for i, p in enumerate("kv"):
-            d = t["delta"] if p == "k" else None
-            kv.kvfix_fit_mean(self.fit_fresh_planes[p], R[p], self.out_planes[p], t["idx"][i], b,
-                              t["mu"][i], d, c.theta, A=t["A_" + p], B=t["B_" + p],
-                              fresh_by_slot=self.paged, ws=t["ws_fit"])
-        for i, p in enumerate("kv"):
+            if p == "v":
+                main.wait_event(self.ev_join)
             d = t["delta"] if p == "k" else None
             sc = t["scores"][i] if c.weight == "clip" else None
             with self.timed:
-                kv.kvfix_apply(R[p], self.out_planes[p], t["mask"][i], t["mu"][i], sc, c.w_lo,
-                               c.w_hi, d, c.theta, A=t["A_" + p], B=t["B_" + p])
+                kv.kvfix_apply(self.reuse_planes[p], self.out_planes[p], t["mask"][i], t["mu"][i],
+                               sc, c.w_lo, c.w_hi, d, c.theta, A=t["A_" + p], B=t["B_" + p])
 
 
 class C2(Correction):
@@ -242,7 +254,10 @@ class C2(Correction):
         t["mask"] = torch.empty(2, S, (n + 31) // 32, dtype=torch.int32, device="cuda")
         t["mu"] = torch.empty(2, L, S, H, hd, dtype=torch.float32, device="cuda")
         ws = kv.kvfix_fit_mean_workspace(L, S, H, hd, b)
-        t["ws_fit"] = torch.empty(max(ws, 16), dtype=torch.uint8, device="cuda")
+        for p in "kv":             # one workspace per plane: the two chains run concurrently
+            t["ws_fit_" + p] = torch.empty(max(ws, 16), dtype=torch.uint8, device="cuda")
+        self.side = torch.cuda.Stream()
+        self.ev_fork, self.ev_join = torch.cuda.Event(), torch.cuda.Event()
 
     def cpu_baseline(self, np):
         """The oracle (as it stands, one thread) on the same input bytes: the
@@ -466,8 +481,12 @@ class C4(Workload):
             t["idx"] = torch.empty(S, ch * self.CHUNK, dtype=torch.int32, device="cuda")
             t["keys"] = draw_coin_keys(c.seed, S, nc, "cuda")
         t["mu"] = torch.empty(2, L, S, H, hd, dtype=torch.float32, device="cuda")
-        t["ws_fit"] = torch.empty(kv.kvfix_fit_mean_workspace(L, S, H, hd, t["idx"].shape[1]),
-                                  dtype=torch.uint8, device="cuda")
+        for p in "kv":             # one workspace per plane: the two fits run concurrently
+            t["ws_fit_" + p] = torch.empty(
+                kv.kvfix_fit_mean_workspace(L, S, H, hd, t["idx"].shape[1]), dtype=torch.uint8,
+                device="cuda")
+        self.side = torch.cuda.Stream()
+        self.ev_fork, self.ev_join = torch.cuda.Event(), torch.cuda.Event()
         P = kv.Plane.dense
         self.planes = {k: P(t[k]) for k in ("reuse_k", "reuse_v", "fresh_k", "fresh_v", "out_k",
                                             "out_v")}
@@ -495,11 +514,24 @@ class C4(Workload):
                                  t["scores"], t["ws_draft"])
         self.select()
         width = t["idx"].shape[1]
-        for i, p in enumerate("kv"):
+        torch = self.torch
+        main = torch.cuda.current_stream()
+
+        def fit(i, p):
             d = t["delta"] if p == "k" else None
             kv.kvfix_fit_mean(P["fresh_" + p], P["reuse_" + p], P["out_" + p], t["idx"], width,
-                              t["mu"][i], d, c.theta, ws=t["ws_fit"])
+                              t["mu"][i], d, c.theta, ws=t["ws_fit_" + p])
+
+        # the V fit runs on a second stream beside the K fit and apply
+        self.ev_fork.record(main)
+        self.side.wait_event(self.ev_fork)
+        with torch.cuda.stream(self.side):
+            fit(1, "v")
+            self.ev_join.record(self.side)
+        fit(0, "k")
         for i, p in enumerate("kv"):
+            if p == "v":
+                main.wait_event(self.ev_join)
             d = t["delta"] if p == "k" else None
             with self.timed:
                 kv.kvfix_apply(P["reuse_" + p], P["out_" + p], t["mask"], t["mu"][i], None, 0.0,

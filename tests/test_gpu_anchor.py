@@ -292,3 +292,20 @@ def test_llama3_8b_shape_ten_anchors_sampled():
                            tgt_off, theta, "half", "bf16")
         e = assert_values(sel(out), o, "bf16", f"8B-shape plane {plane}")
         log("8B-shape plane", plane, "max rel err", e)
+
+
+def test_sixteen_anchors_and_single_token_segment():
+    """The largest pool (16 anchors, lengths mixed around n) and a one-token
+    segment (one ragged tile, every wave but one idle)."""
+    case = anchor_case(L=2, H=3, n=129, V=16, n_max=140, seed=67)
+    lengths = [129, 140, 135, 129, 60, 129, 140, 2, 129, 130, 131, 129, 129, 100, 140, 129]
+    log("sixteen anchors")
+    w, gate, acc = gpu_match(case, lengths, 100, 0.7)
+    check_weights(case, lengths, w)
+    check_gate(case, lengths, 100, 0.7, gate, acc)
+    check_apply(case, lengths, w, tgt_off=31)
+    one = anchor_case(L=1, H=1, n=1, V=2, n_max=4, seed=68)
+    w, gate, acc = gpu_match(one, [1, 4], 1, 1.0)
+    check_weights(one, [1, 4], w)
+    check_gate(one, [1, 4], 1, 1.0, gate, acc)
+    check_apply(one, [1, 4], w, tgt_off=7)
