@@ -723,7 +723,7 @@ class C2Anchor(Workload):
     counter_name = "c2_anchor"
     kernel_tag = "anchor_match"
     V, RANK, SRC_OFF, TAU = 10, 32, 2048, 0.5
-    # The match kernel dominates and is bound by vector ALU work: one absolute
+    # The match call (three kernels) dominates and is bound by vector ALU work: one absolute
     # add per element and anchor on the key plane, an absolute add and a
     # fused multiply-add on the value plane (4 flops per element and anchor
     # over both planes), against the fp32 vector peak of 157.3 TFLOP/s.
@@ -772,8 +772,8 @@ class C2Anchor(Workload):
         t["w"] = torch.empty(L, 2, V, n, dtype=torch.float32, device="cuda")
         t["gate"] = torch.empty(V + 1, dtype=torch.float64, device="cuda")
         t["accept"] = torch.empty(1, dtype=torch.int32, device="cuda")
-        t["ws"] = torch.empty(kv.kvfix_anchor_match_workspace(L, n, V), dtype=torch.uint8,
-                              device="cuda")
+        t["ws"] = torch.empty(kv.kvfix_anchor_match_workspace(L, c.n_kv_heads, n, V),
+                              dtype=torch.uint8, device="cuda")
         lengths = [n] * V
         self.base = kv.AnchorPool(t["a_base"], t["bt_base"], lengths)
         self.delta = kv.AnchorPool(t["a_delta"], t["bt_delta"], lengths)
@@ -828,8 +828,8 @@ ROOFLINE_KERNEL = {
     "c3": "kvfix diff_decode_kernel<bf16, hd128, rotate-half> (with its rotary-table pre-kernel)",
     "c4": "kvfix apply_kernel<bf16, fp32, hd128, rotate-half, rank 0>",
     "c5": "kvfix apply_kernel<bf16, fp32, hd128, rotate-half, rank 2, paged>",
-    "c2_anchor": "kvfix anchor_match_kernel<rotate-half> + anchor_gate_kernel (V=10, rank 32, "
-                 "K and V planes)",
+    "c2_anchor": "kvfix_anchor_match: anchor_match_kernel<rotate-half> + anchor_finish_kernel + "
+                 "anchor_gate_kernel (V=10, rank 32, K and V planes)",
 }
 
 

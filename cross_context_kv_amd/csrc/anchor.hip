@@ -163,236 +163,221 @@ struct MatchParams {
   int32_t n_pairs, n_tiles;
   int32_t n_list[2];               // anchors computed per plane, in order,
   uint64_t list[2];                // 4 bits per anchor id
-  float D;          // features per token row (all heads)
-  float* w;          // [L][2][V][n]
-  double* part;      // [L][n_tiles][V]
+  float* part1;      // [L][2][V][H][n] per-head sums of |source - A_v B_v|
+  float* part2;      // [L][V][H][n] per-head sums of squares (value plane)
 };
 
-// Distance sums live in LDS, one slot per (wave, anchor, band, token
-// column): acc1 the absolute, acc2 the squared distances.  Each pair's
-// partial sums are first added across the four lane groups of a column
-// (fixed order), then lane group 0 adds them to the column's slot; no other
-// lane touches that slot inside the head loop.
-__host__ __device__ constexpr int match_lds_floats(int V) {
-  return 2 * kMatchWaves * V * kMatchBands * 16;
-}
-
+// One block = 128 tokens (4 waves x 2 bands of 16) of one (layer, plane,
+// head).  Blocks of one (layer, plane) run on one XCD with the heads of a
+// token tile next to each other, so the left-factor rows of the tile are read
+// from HBM once and from L2 by every head.  The head's source rows sit in
+// registers as fp32 (keys rotated by -src_off to canonical positions),
+// negated, and serve as the MFMA accumulator input, so the MFMA returns
+// A_v B_v - x directly.  Per listed anchor: the head's right-factor slice is
+// staged in LDS (two buffers, one barrier per anchor, the next anchor's slice
+// and left rows loaded while the current one computes; indices clamped at
+// the end so every load is unconditional); absolute values (and squares on
+// the value plane) are summed per lane, added across the four lane groups of
+// a token column in a fixed order, and written as the head's sums.
 template <int STYLE, bool GATE>
-__device__ __forceinline__ void match_body(const MatchParams& P, int l, int tile, float* acc1,
-                                           float* acc2, bf16_t* sbt, float* tc, float* ts,
-                                           double* gsum) {
+__device__ __forceinline__ void match_body(const MatchParams& P, int l, int h, int tile,
+                                           bf16_t* sbt, float* tc, float* ts) {
   constexpr int p = GATE ? 1 : 0;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, t = lane & 15;
-  const int V = P.V;
-  auto slot = [&](int v, int b) { return (((wave * V + v) * kMatchBands + b) << 4) + t; };
-  if (g == 0)
-    for (int v = 0; v < V; ++v)
-#pragma unroll
-      for (int b = 0; b < kMatchBands; ++b) acc1[slot(v, b)] = acc2[slot(v, b)] = 0.0f;
   if (STYLE != kStyleNone) rope_table<kHD, float>(P.rope, -P.src_off, tc, ts);
   __syncthreads();
 
-  const int jw = tile * kMatchTokens + wave * kMatchBands * 16;
-  const uint32_t set = GATE ? (P.elig | P.gate_set) : P.elig;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, t = lane & 15;
+  const int j0 = tile * kMatchTokens, jw = j0 + wave * kMatchBands * 16;
   const int lim = GATE ? max(P.cover, P.k_gate) : P.cover;
-  const DPlane& S = P.src[p];
-
-  // One flat loop over the (head, listed anchor) pairs q = h * nl + i.  The
-  // right-factor slice of pair q + 1 is staged in LDS (two buffers, in the
-  // MFMA row order) and its left rows loaded while pair q computes, one
-  // barrier per pair; the source rows of a head are loaded after its last
-  // pair (three waves per SIMD cover that wait).  Indices are clamped at the
-  // end, so every load is unconditional.  The loop runs for every wave of the
-  // block (rows past the limit compute values nobody reads).
   const int nl = P.n_list[p];
-  if (tile * kMatchTokens < lim && nl > 0) {
-    const uint64_t list = P.list[p];
-    const int total = P.H * nl;
-    const int tid = threadIdx.x;
-    vu4 xr[kMatchBands][4];
-    float nx[kMatchBands][32];
-    auto next_rows = [&](int h) {
-#pragma unroll
-      for (int b = 0; b < kMatchBands; ++b)
-        load_lane_raw(S, l, P.seg, h, jw + 16 * b + t, P.n, g, xr[b]);
-    };
-    auto take_rows = [&]() {
-#pragma unroll
-      for (int b = 0; b < kMatchBands; ++b) {
-        unpack_lane(xr[b], nx[b]);
-        if (STYLE != kStyleNone) rotate_lane<STYLE>(nx[b], tc, ts, g);
-#pragma unroll
-        for (int e = 0; e < 32; ++e) nx[b][e] = -nx[b][e];
-      }
-    };
-    auto pair_hv = [&](int q, int& h, int& v) {
-      q = min(q, total - 1);
-      h = q / nl;
-      v = (int)((list >> (4 * (q - h * nl))) & 15u);
-    };
-    auto stage_load = [&](int q, vu4* r) {
-      int h, v;
-      pair_hv(q, h, v);
-      const bf16_t* src = bt_row(P.G, v, l, p, h * kHD);
-      r[0] = ld16_cached(src + 8 * tid);
-      r[1] = ld16_cached(src + 8 * (tid + 256));
-    };
-    auto stage_store = [&](const vu4* r, bf16_t* buf) {
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        const int u = tid + 256 * k2, f = u >> 2, qq = u & 3;
-        const int c = ((f >> 6) << 2) | ((f >> 2) & 3), m = (((f >> 4) & 3) << 2) | (f & 3);
-        *reinterpret_cast<vu4*>(buf + (c * 16 + m) * kRank + 8 * qq) = r[k2];
-      }
-    };
-    auto load_a = [&](int q, bf16x8* a) {
-      int h, v;
-      pair_hv(q, h, v);
-      const int last = P.G.len[v] - 1;        // a listed anchor stores >= 1 row
-#pragma unroll
-      for (int b = 0; b < kMatchBands; ++b)
-        a[b] = ld_op(a_row(P.G, v, l, p, min(jw + 16 * b + t, last)) + 8 * g);
-    };
-    auto compute = [&](const bf16_t* buf, const bf16x8* a, int q) {
-      int h, v;
-      pair_hv(q, h, v);
-      bf16x8 bop[kTiles];
-#pragma unroll
-      for (int c = 0; c < kTiles; ++c)
-        bop[c] = *reinterpret_cast<const bf16x8*>(buf + (c * 16 + t) * kRank + 8 * g);
-#pragma unroll
-      for (int b = 0; b < kMatchBands; ++b) {
-        float s1[4] = {0, 0, 0, 0}, s2[4] = {0, 0, 0, 0};
-#pragma unroll
-        for (int c = 0; c < kTiles; ++c) {
-          const f32x4 cx = {nx[b][4 * c], nx[b][4 * c + 1], nx[b][4 * c + 2], nx[b][4 * c + 3]};
-          const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bop[c], a[b], cx, 0, 0, 0);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            s1[e] += fabsf(d[e]);
-            if (GATE) s2[e] = fmaf(d[e], d[e], s2[e]);
-          }
-        }
-        float c1 = (s1[0] + s1[1]) + (s1[2] + s1[3]);
-        c1 += __shfl_xor(c1, 16);
-        c1 += __shfl_xor(c1, 32);
-        float c2 = 0.0f;
-        if (GATE) {
-          c2 = (s2[0] + s2[1]) + (s2[2] + s2[3]);
-          c2 += __shfl_xor(c2, 16);
-          c2 += __shfl_xor(c2, 32);
-        }
-        if (g == 0) {
-          acc1[slot(v, b)] += c1;
-          if (GATE) acc2[slot(v, b)] += c2;
-        }
-      }
-      // last anchor of head h: switch the rows to head h + 1
-      if (q - h * nl == nl - 1 && h + 1 < P.H) {
-        next_rows(h + 1);
-        take_rows();
-      }
-    };
+  if (j0 >= lim || nl == 0) return;          // block-uniform: no barrier follows
+  const uint64_t list = P.list[p];
+  const int V = P.V, H = P.H, n = P.n;
 
-    // Iteration q stores the slice of pair q + 1 (loaded one iteration
-    // earlier) into the buffer pair q - 1 used, loads the slice of pair q + 2
-    // and the left rows of pair q + 1, computes pair q, and ends on the
-    // barrier that publishes pair q + 1.
-    vu4 sr[2];
-    bf16x8 a0[kMatchBands], a1[kMatchBands];
-    next_rows(0);
-    stage_load(0, sr);
-    load_a(0, a0);
-    stage_store(sr, sbt);
-    stage_load(1, sr);
-    take_rows();
-    __syncthreads();
-    for (int q = 0; q < total; q += 2) {
-      stage_store(sr, sbt + kSlice);
-      stage_load(q + 2, sr);
-      load_a(q + 1, a1);
-      compute(sbt, a0, q);
-      __syncthreads();
-      stage_store(sr, sbt);
-      stage_load(q + 3, sr);
-      load_a(q + 2, a0);
-      if (q + 1 < total) compute(sbt + kSlice, a1, q + 1);
-      __syncthreads();
-    }
+  float nx[kMatchBands][32];
+#pragma unroll
+  for (int b = 0; b < kMatchBands; ++b) {
+    vu4 xr[4];
+    load_lane_raw(P.src[p], l, P.seg, h, jw + 16 * b + t, n, g, xr);
+    unpack_lane(xr, nx[b]);
+    if (STYLE != kStyleNone) rotate_lane<STYLE>(nx[b], tc, ts, g);
+#pragma unroll
+    for (int e = 0; e < 32; ++e) nx[b][e] = -nx[b][e];
   }
-  __syncthreads();
 
-  auto total = [&](const float* acc, int v, int b) { return acc[slot(v, b)]; };
-
-  // Token weights: softmax of minus the mean absolute distance over E.
-  if (g == 0) {
+  auto anchor = [&](int i) { return (int)((list >> (4 * min(i, nl - 1))) & 15u); };
+  auto stage_load = [&](int v, vu4* r) {
+    const bf16_t* src = bt_row(P.G, v, l, p, h * kHD);
+    r[0] = ld16_cached(src + 8 * tid);
+    r[1] = ld16_cached(src + 8 * (tid + 256));
+  };
+  auto stage_store = [&](const vu4* r, bf16_t* buf) {
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      const int u = tid + 256 * k2, f = u >> 2, q = u & 3;
+      const int c = ((f >> 6) << 2) | ((f >> 2) & 3), m = (((f >> 4) & 3) << 2) | (f & 3);
+      *reinterpret_cast<vu4*>(buf + (c * 16 + m) * kRank + 8 * q) = r[k2];
+    }
+  };
+  auto load_a = [&](int v, bf16x8* a) {
+    const int last = P.G.len[v] - 1;          // a listed anchor stores >= 1 row
+#pragma unroll
+    for (int b = 0; b < kMatchBands; ++b)
+      a[b] = ld_op(a_row(P.G, v, l, p, min(jw + 16 * b + t, last)) + 8 * g);
+  };
+  auto compute = [&](const bf16_t* buf, const bf16x8* a, int v) {
+    bf16x8 bop[kTiles];
+#pragma unroll
+    for (int c = 0; c < kTiles; ++c)
+      bop[c] = *reinterpret_cast<const bf16x8*>(buf + (c * 16 + t) * kRank + 8 * g);
+    float* o1 = P.part1 + ((((int64_t)l * 2 + p) * V + v) * H + h) * n;
+    float* o2 = P.part2 + (((int64_t)l * V + v) * H + h) * n;
 #pragma unroll
     for (int b = 0; b < kMatchBands; ++b) {
-      const int j = jw + 16 * b + t;
-      if (j >= P.n) continue;
-      float* wr = P.w + ((int64_t)l * 2 + p) * V * P.n + j;
-      if (j >= P.cover) {
-        for (int v = 0; v < V; ++v) wr[(int64_t)v * P.n] = 0.0f;
-        continue;
-      }
-      float m = INFINITY;
-      for (int v = 0; v < V; ++v)
-        if ((P.elig >> v) & 1u) m = fminf(m, total(acc1, v, b) / P.D);
-      float sum = 0.0f;
-      for (int v = 0; v < V; ++v)
-        if ((P.elig >> v) & 1u) sum += expf(m - total(acc1, v, b) / P.D);
-      for (int v = 0; v < V; ++v)
-        wr[(int64_t)v * P.n] =
-            ((P.elig >> v) & 1u) ? expf(m - total(acc1, v, b) / P.D) / sum : 0.0f;
-    }
-  }
-
-  if (GATE) {
-    // Per block and anchor of the gate set: the squared distances of the
-    // prefix rows in fp64, added in a fixed order (band, lane tree, wave).
-    for (int v = 0; v < V; ++v) {
-      if (!((P.gate_set >> v) & 1u)) continue;
-      double s = 0.0;
+      float s1[4] = {0, 0, 0, 0}, s2[4] = {0, 0, 0, 0};
 #pragma unroll
-      for (int b = 0; b < kMatchBands; ++b)
-        if (jw + 16 * b + t < P.k_gate) s += (double)total(acc2, v, b);
-      s += __shfl_xor(s, 1);
-      s += __shfl_xor(s, 2);
-      s += __shfl_xor(s, 4);
-      s += __shfl_xor(s, 8);
-      if (lane == 0) gsum[wave * kAnchorMax + v] = s;
+      for (int c = 0; c < kTiles; ++c) {
+        const f32x4 cx = {nx[b][4 * c], nx[b][4 * c + 1], nx[b][4 * c + 2], nx[b][4 * c + 3]};
+        const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bop[c], a[b], cx, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s1[e] += fabsf(d[e]);
+          if (GATE) s2[e] = fmaf(d[e], d[e], s2[e]);
+        }
+      }
+      float c1 = (s1[0] + s1[1]) + (s1[2] + s1[3]);
+      c1 += __shfl_xor(c1, 16);
+      c1 += __shfl_xor(c1, 32);
+      float c2 = 0.0f;
+      if (GATE) {
+        c2 = (s2[0] + s2[1]) + (s2[2] + s2[3]);
+        c2 += __shfl_xor(c2, 16);
+        c2 += __shfl_xor(c2, 32);
+      }
+      const int j = jw + 16 * b + t;
+      if (g == 0 && j < n) {
+        o1[j] = c1;
+        if (GATE) o2[j] = c2;
+      }
     }
+  };
+
+  vu4 sr[2];
+  bf16x8 a0[kMatchBands], a1[kMatchBands];
+  stage_load(anchor(0), sr);
+  load_a(anchor(0), a0);
+  stage_store(sr, sbt);
+  __syncthreads();
+  for (int i = 0; i < nl; i += 2) {
+    stage_load(anchor(i + 1), sr);
+    load_a(anchor(i + 1), a1);
+    compute(sbt, a0, anchor(i));
+    stage_store(sr, sbt + kSlice);
     __syncthreads();
-    if ((int)threadIdx.x < V) {
-      const int v = threadIdx.x;
-      double s = 0.0;
-      if ((P.gate_set >> v) & 1u)
-        for (int w = 0; w < kMatchWaves; ++w) s += gsum[w * kAnchorMax + v];
-      P.part[((int64_t)l * P.n_tiles + tile) * V + v] = s;
-    }
+    stage_load(anchor(i + 2), sr);
+    load_a(anchor(i + 2), a0);
+    if (i + 1 < nl) compute(sbt + kSlice, a1, anchor(i + 1));
+    stage_store(sr, sbt);
+    __syncthreads();
   }
 }
 
-// Blocks of one (layer, plane) run on one XCD, so the plane's right factors
-// (all anchors: V * D * r bf16) are fetched into that XCD's L2 once.
 template <int STYLE>
 __global__ __launch_bounds__(kMatchWaves * 64) __attribute__((amdgpu_waves_per_eu(3)))
 void anchor_match_kernel(MatchParams P) {
-  extern __shared__ float match_lds[];
   __shared__ __attribute__((aligned(16))) bf16_t sbt[2 * kSlice];
   __shared__ float tc[kHD / 2], ts[kHD / 2];
-  __shared__ double gsum[kMatchWaves * kAnchorMax];
   const int id = blockIdx.x, xcd = id % kXcds, k = id / kXcds;
-  const int tile = k % P.n_tiles;
-  const int pair = (k / P.n_tiles) * kXcds + xcd;
+  const int h = k % P.H, k2 = k / P.H;
+  const int tile = k2 % P.n_tiles;
+  const int pair = (k2 / P.n_tiles) * kXcds + xcd;
   if (pair >= P.n_pairs) return;
   const int l = pair >> 1;
-  float* acc1 = match_lds;
-  float* acc2 = match_lds + match_lds_floats(P.V) / 2;
   if ((pair & 1) == 0)
-    match_body<STYLE, false>(P, l, tile, acc1, acc2, sbt, tc, ts, gsum);
+    match_body<STYLE, false>(P, l, h, tile, sbt, tc, ts);
   else
-    match_body<kStyleNone, true>(P, l, tile, acc1, acc2, sbt, tc, ts, gsum);
+    match_body<kStyleNone, true>(P, l, h, tile, sbt, tc, ts);
+}
+
+// Per token: the head sums added in head order give the distance sums;
+// weights = softmax over E of minus the mean absolute distance (T = 1); on
+// the value plane the squared sums of the gate prefix are added per block in
+// fp64 in a fixed order (token tree inside a wave, then waves).
+constexpr int kFinishTokens = 256;
+
+struct FinishParams {
+  const float* part1;
+  const float* part2;
+  int32_t n, H, V;
+  uint32_t elig, gate_set;
+  int32_t cover, k_gate;
+  int32_t n_tiles;                 // token tiles of kFinishTokens
+  float D;                         // features per token row (all heads)
+  float* w;                        // [L][2][V][n]
+  double* gpart;                   // [L][n_tiles][V]
+};
+
+__global__ __launch_bounds__(kFinishTokens) void anchor_finish_kernel(FinishParams P) {
+  __shared__ double gsum[kFinishTokens / 64][kAnchorMax];
+  const int tile = blockIdx.x, p = blockIdx.y & 1, l = blockIdx.y >> 1;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int j = tile * kFinishTokens + tid;
+  const int V = P.V, H = P.H, n = P.n;
+  // Sums over heads, head by head (fixed order); the anchors' loads of one
+  // head are independent and issued together.
+  auto head_sums = [&](const float* base, uint32_t set, bool rows, float* s) {
+#pragma unroll
+    for (int v = 0; v < kAnchorMax; ++v) s[v] = 0.0f;
+    if (!rows) return;
+    for (int hh = 0; hh < H; ++hh) {
+      float x[kAnchorMax];
+#pragma unroll
+      for (int v = 0; v < kAnchorMax; ++v)
+        x[v] = (v < V && ((set >> v) & 1u)) ? base[((int64_t)v * H + hh) * n + j] : 0.0f;
+#pragma unroll
+      for (int v = 0; v < kAnchorMax; ++v) s[v] += x[v];
+    }
+  };
+  {
+    float s[kAnchorMax];
+    head_sums(P.part1 + ((int64_t)l * 2 + p) * V * H * n, P.elig, j < P.cover, s);
+    if (j < n) {
+      float* wr = P.w + ((int64_t)l * 2 + p) * V * n + j;
+      if (j < P.cover) {
+        float m = INFINITY;
+#pragma unroll
+        for (int v = 0; v < kAnchorMax; ++v)
+          if (v < V && ((P.elig >> v) & 1u)) m = fminf(m, s[v] / P.D);
+        float sum = 0.0f;
+#pragma unroll
+        for (int v = 0; v < kAnchorMax; ++v)
+          if (v < V && ((P.elig >> v) & 1u)) sum += expf(m - s[v] / P.D);
+#pragma unroll
+        for (int v = 0; v < kAnchorMax; ++v)
+          if (v < V) wr[(int64_t)v * n] = ((P.elig >> v) & 1u) ? expf(m - s[v] / P.D) / sum : 0.0f;
+      } else {
+        for (int v = 0; v < V; ++v) wr[(int64_t)v * n] = 0.0f;
+      }
+    }
+  }
+  if (p == 0) return;                        // block-uniform
+  float s2[kAnchorMax];
+  head_sums(P.part2 + (int64_t)l * V * H * n, P.gate_set, j < P.k_gate, s2);
+#pragma unroll
+  for (int v = 0; v < kAnchorMax; ++v) {
+    if (v >= V || !((P.gate_set >> v) & 1u)) continue;
+    double d = (double)s2[v];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) d += __shfl_xor(d, off);
+    if (lane == 0) gsum[wave][v] = d;
+  }
+  __syncthreads();
+  if (tid < V) {
+    double d = 0.0;
+    if ((P.gate_set >> tid) & 1u)
+      for (int w = 0; w < kFinishTokens / 64; ++w) d += gsum[w][tid];
+    P.gpart[((int64_t)l * P.n_tiles + tile) * V + tid] = d;
+  }
 }
 
 // Gate finish: d_v = sqrt of the summed partials (fp64, fixed order), then
@@ -672,18 +657,31 @@ RopeArgs rope_freqs(double theta, int32_t style) {
   return make_rope_args(&r, kHD);
 }
 
-int64_t n_match_tiles(int64_t n) { return (n + kMatchTokens - 1) / kMatchTokens; }
+// Workspace: the per-head distance sums of both planes, the per-head squared
+// sums of the value plane, and the gate's per-block partial sums.
+struct MatchWs {
+  size_t part1, part2, gpart, total;
+};
+
+MatchWs match_ws(int64_t L, int64_t H, int64_t n, int64_t V) {
+  MatchWs w;
+  auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+  w.part1 = up((size_t)(L * 2 * V * H * n) * sizeof(float));
+  w.part2 = up((size_t)(L * V * H * n) * sizeof(float));
+  w.gpart = up((size_t)(L * ((n + kFinishTokens - 1) / kFinishTokens) * V) * sizeof(double));
+  w.total = w.part1 + w.part2 + w.gpart + 256;
+  return w;
+}
 
 }  // namespace
 }  // namespace kvfix
 
 using namespace kvfix;
 
-extern "C" size_t kvfix_anchor_match_workspace(int32_t n_layers, int32_t n_tokens,
-                                               int32_t n_anchors) {
-  if (n_layers < 0 || n_tokens < 0 || n_anchors < 0) return 0;
-  return (size_t)n_layers * (size_t)n_match_tiles(n_tokens) * (size_t)n_anchors * sizeof(double) +
-         256;
+extern "C" size_t kvfix_anchor_match_workspace(int32_t n_layers, int32_t n_heads,
+                                               int32_t n_tokens, int32_t n_anchors) {
+  if (n_layers < 0 || n_heads < 0 || n_tokens < 0 || n_anchors < 0) return 0;
+  return match_ws(n_layers, n_heads, n_tokens, n_anchors).total;
 }
 
 extern "C" kvfix_status kvfix_anchor_match(const kvfix_plane* src_k, const kvfix_plane* src_v,
@@ -698,55 +696,71 @@ extern "C" kvfix_status kvfix_anchor_match(const kvfix_plane* src_k, const kvfix
   if (gate == nullptr || accept == nullptr || ws == nullptr) return KVFIX_ERR_ARG;
   if (!(tau == tau)) return KVFIX_ERR_ARG;
   const int32_t L = src_k->n_layers, n = src_k->n_tokens, V = base->n_anchors;
+  const int32_t H = src_k->n_heads;
   if (V > 0 && n > 0 && L > 0 && weights == nullptr) return KVFIX_ERR_ARG;
-  if (ws_bytes < kvfix_anchor_match_workspace(L, n, V)) return KVFIX_ERR_ARG;
-  if ((reinterpret_cast<uintptr_t>(ws) & 7u) != 0) return KVFIX_ERR_ALIGN;
+  const MatchWs W = match_ws(L, H, n, V);
+  if (ws_bytes < W.total) return KVFIX_ERR_ARG;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return KVFIX_ERR_ALIGN;
   const hipStream_t st = (hipStream_t)stream;
   const Eligible e = eligible(base, n, k_gate);
+  char* wsb = static_cast<char*>(ws);
+  double* gpart = reinterpret_cast<double*>(wsb + W.part1 + W.part2);
+  const int32_t n_fin = (n + kFinishTokens - 1) / kFinishTokens;
 
-  MatchParams P;
-  memset(&P, 0, sizeof(P));
-  P.src[0] = make_dplane(*src_k);
-  P.src[1] = make_dplane(*src_v);
-  P.G = make_pool(base, L, src_k->n_heads * kHD);
-  P.rope = rope_freqs(theta, rope_style);
-  P.src_off = src_off;
-  P.seg = seg;
-  P.n = n;
-  P.H = src_k->n_heads;
-  P.V = V;
-  P.elig = e.elig;
-  P.gate_set = e.gate_set;
-  P.cover = e.cover;
-  P.k_gate = e.k_gate;
-  P.n_pairs = 2 * L;
-  P.n_tiles = (int32_t)n_match_tiles(n);
-  P.D = (float)(src_k->n_heads * kHD);
-  for (int v = 0; v < V; ++v) {
-    const bool in_e = (e.elig >> v) & 1u;
-    const bool in_gate = e.k_gate > 0 && ((e.gate_set >> v) & 1u);
-    if (in_e) P.list[0] |= (uint64_t)v << (4 * P.n_list[0]++);
-    if (in_e || in_gate) P.list[1] |= (uint64_t)v << (4 * P.n_list[1]++);
-  }
-  P.w = weights;
-  P.part = static_cast<double*>(ws);
-  if (V > 0 && n > 0 && L > 0) {
-    const int64_t grid = (int64_t)P.n_tiles * ((P.n_pairs + kXcds - 1) / kXcds) * kXcds;
-    const size_t lds = sizeof(float) * match_lds_floats(V);
-    const void* kern = rope_style == KVFIX_ROPE_HALF
-                           ? reinterpret_cast<const void*>(&anchor_match_kernel<kStyleHalf>)
-                           : reinterpret_cast<const void*>(&anchor_match_kernel<kStyleInter>);
-    if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
-        hipSuccess)
-      return KVFIX_ERR_HIP;
+  if (V > 0 && n > 0 && L > 0 && H > 0) {
+    MatchParams P;
+    memset(&P, 0, sizeof(P));
+    P.src[0] = make_dplane(*src_k);
+    P.src[1] = make_dplane(*src_v);
+    P.G = make_pool(base, L, H * kHD);
+    P.rope = rope_freqs(theta, rope_style);
+    P.src_off = src_off;
+    P.seg = seg;
+    P.n = n;
+    P.H = H;
+    P.V = V;
+    P.elig = e.elig;
+    P.gate_set = e.gate_set;
+    P.cover = e.cover;
+    P.k_gate = e.k_gate;
+    P.n_pairs = 2 * L;
+    P.n_tiles = (n + kMatchTokens - 1) / kMatchTokens;
+    for (int v = 0; v < V; ++v) {
+      const bool in_e = (e.elig >> v) & 1u;
+      const bool in_gate = e.k_gate > 0 && ((e.gate_set >> v) & 1u);
+      if (in_e) P.list[0] |= (uint64_t)v << (4 * P.n_list[0]++);
+      if (in_e || in_gate) P.list[1] |= (uint64_t)v << (4 * P.n_list[1]++);
+    }
+    P.part1 = reinterpret_cast<float*>(wsb);
+    P.part2 = reinterpret_cast<float*>(wsb + W.part1);
+    const int64_t grid =
+        (int64_t)H * P.n_tiles * ((P.n_pairs + kXcds - 1) / kXcds) * kXcds;
     if (rope_style == KVFIX_ROPE_HALF)
-      anchor_match_kernel<kStyleHalf><<<dim3((unsigned)grid), dim3(kMatchWaves * 64), lds, st>>>(P);
+      anchor_match_kernel<kStyleHalf><<<dim3((unsigned)grid), dim3(kMatchWaves * 64), 0, st>>>(P);
     else
-      anchor_match_kernel<kStyleInter><<<dim3((unsigned)grid), dim3(kMatchWaves * 64), lds, st>>>(P);
+      anchor_match_kernel<kStyleInter><<<dim3((unsigned)grid), dim3(kMatchWaves * 64), 0, st>>>(P);
+    KVFIX_TRY(launch_status());
+
+    FinishParams F;
+    F.part1 = P.part1;
+    F.part2 = P.part2;
+    F.n = n;
+    F.H = H;
+    F.V = V;
+    F.elig = e.elig;
+    F.gate_set = e.gate_set;
+    F.cover = e.cover;
+    F.k_gate = e.k_gate;
+    F.n_tiles = n_fin;
+    F.D = (float)(H * kHD);
+    F.w = weights;
+    F.gpart = gpart;
+    anchor_finish_kernel<<<dim3((unsigned)n_fin, (unsigned)(2 * L)), dim3(kFinishTokens), 0,
+                           st>>>(F);
     KVFIX_TRY(launch_status());
   }
-  const int n_parts = (V > 0 && n > 0) ? L * P.n_tiles : 0;
-  anchor_gate_kernel<<<dim3(1), dim3(1024), 0, st>>>(P.part, n_parts, V, e.gate_set, tau, gate,
+  const int n_parts = (V > 0 && n > 0 && H > 0) ? L * n_fin : 0;
+  anchor_gate_kernel<<<dim3(1), dim3(1024), 0, st>>>(gpart, n_parts, V, e.gate_set, tau, gate,
                                                       accept);
   return launch_status();
 }

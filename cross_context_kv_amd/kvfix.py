@@ -110,7 +110,7 @@ def lib() -> ctypes.CDLL:
             "kvfix_fit_mean_ex": [P, I32, P, P, P, I32, P, P, P, P, P, ctypes.c_size_t, P],
             "kvfix_apply_ex": [P, P, P, P, F, F, P, P, P, P, P],
             "kvfix_select_master": [P, I32, I32, P, P, P],
-            "kvfix_anchor_match_workspace": [I32, I32, I32],
+            "kvfix_anchor_match_workspace": [I32, I32, I32, I32],
             "kvfix_anchor_match": [P, P, I32, P, I64, ctypes.c_double, I32, I64, ctypes.c_double,
                                    P, P, P, P, ctypes.c_size_t, P],
             "kvfix_anchor_apply": [P, P, I32, P, P, I64, I64, ctypes.c_double, I32, P, P, P],
@@ -452,8 +452,9 @@ class AnchorPool:
         return ctypes.byref(self.c)
 
 
-def kvfix_anchor_match_workspace(n_layers: int, n_tokens: int, n_anchors: int) -> int:
-    return int(lib().kvfix_anchor_match_workspace(n_layers, n_tokens, n_anchors))
+def kvfix_anchor_match_workspace(n_layers: int, n_heads: int, n_tokens: int,
+                                 n_anchors: int) -> int:
+    return int(lib().kvfix_anchor_match_workspace(n_layers, n_heads, n_tokens, n_anchors))
 
 
 def kvfix_anchor_match(src_k: Plane, src_v: Plane, seg: int, base: AnchorPool, src_off: int,

@@ -460,10 +460,14 @@ typedef struct {
  *   fewer than two compared anchors).
  * accept: device int32, 1 iff |A_k| >= 2 and gate[V] <= tau (else dense
  *   prefill is due).
- * ws: device workspace of kvfix_anchor_match_workspace(...) bytes, 8-byte
- *   aligned (the per-block partial sums of the gate).
- * Arithmetic: bf16 MFMA products, fp32 sums of distances, fp64 gate totals. */
-size_t kvfix_anchor_match_workspace(int32_t n_layers, int32_t n_tokens, int32_t n_anchors);
+ * ws: device workspace of kvfix_anchor_match_workspace(...) bytes, 256-byte
+ *   aligned: per-head distance sums of both planes (fp32 [L][2][V][H][n]), the
+ *   value plane's per-head squared sums (fp32 [L][V][H][n]) and the gate's
+ *   per-block partial sums.
+ * Arithmetic: bf16 MFMA products, fp32 distance sums (per head, then the
+ * heads added in order), fp64 gate totals. */
+size_t kvfix_anchor_match_workspace(int32_t n_layers, int32_t n_heads, int32_t n_tokens,
+                                    int32_t n_anchors);
 kvfix_status kvfix_anchor_match(const kvfix_plane* src_k, const kvfix_plane* src_v, int32_t seg,
                                 const kvfix_anchor_pool* base, int64_t src_off, double theta,
                                 int32_t rope_style, int64_t k_gate, double tau, float* weights,

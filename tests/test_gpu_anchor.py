@@ -57,7 +57,8 @@ def gpu_match(case, lengths, k_gate, tau, src_k=None, src_v=None):
     w = torch.full((L, 2, V, n), float("nan"), dtype=torch.float32, device=DEV)
     gate = torch.full((V + 1,), -1.0, dtype=torch.float64, device=DEV)
     acc = torch.full((1,), -7, dtype=torch.int32, device=DEV)
-    ws = torch.empty(kv.kvfix_anchor_match_workspace(L, n, V), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(kv.kvfix_anchor_match_workspace(L, case["H"], n, V), dtype=torch.uint8,
+                     device=DEV)
     kv.kvfix_anchor_match(pk, pv, 0, base, case["src_off"], case["theta"], k_gate, tau, w, gate,
                           acc, ws, STYLES[case["style"]])
     torch.cuda.synchronize()
@@ -251,7 +252,7 @@ def test_llama3_8b_shape_ten_anchors_sampled():
     w = torch.empty((L, 2, V, n), dtype=torch.float32, device=DEV)
     gate = torch.empty((V + 1,), dtype=torch.float64, device=DEV)
     acc = torch.empty((1,), dtype=torch.int32, device=DEV)
-    ws = torch.empty(kv.kvfix_anchor_match_workspace(L, n, V), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(kv.kvfix_anchor_match_workspace(L, H, n, V), dtype=torch.uint8, device=DEV)
     out_k, out_v = torch.empty_like(src_k), torch.empty_like(src_v)
     log("anchor match + apply, 8B shape")
     kv.kvfix_anchor_match(Plane.dense(src_k), Plane.dense(src_v), 0, base, src_off, theta, n, 0.5,

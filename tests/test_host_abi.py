@@ -150,9 +150,11 @@ def test_anchor_call_validation():
     L = kv.lib()
     p = plane()
     w, gate, acc = ctypes.c_void_p(512), ctypes.c_void_p(1024), ctypes.c_void_p(2048)
-    need = L.kvfix_anchor_match_workspace(2, 64, 3)
-    assert need == 2 * 1 * 3 * 8 + 256
-    assert L.kvfix_anchor_match_workspace(2, 200, 3) == 2 * 2 * 3 * 8 + 256
+    up = lambda x: (x + 255) // 256 * 256                       # noqa: E731
+    need = L.kvfix_anchor_match_workspace(2, 2, 64, 3)
+    assert need == up(2 * 2 * 3 * 2 * 64 * 4) + up(2 * 3 * 2 * 64 * 4) + up(2 * 1 * 3 * 8) + 256
+    assert L.kvfix_anchor_match_workspace(2, 2, 300, 3) == \
+        up(2 * 2 * 3 * 2 * 300 * 4) + up(2 * 3 * 2 * 300 * 4) + up(2 * 2 * 3 * 8) + 256
     ws = ctypes.c_void_p(4096)
 
     def match(pk=p, pv=p, seg=0, pool=None, src_off=100, theta=1e4, style=kv.ROPE_HALF, k=64,
@@ -186,7 +188,7 @@ def test_anchor_call_validation():
         assert call(src_off=(1 << 23) + 1) == 1                     # rotary angle range
     assert match(g=None) == 1 and match(a=None) == 1 and match(wsp=None) == 1
     assert match(wsb=need - 8) == 1
-    assert match(wsp=ctypes.c_void_p(4100)) == 2
+    assert match(wsp=ctypes.c_void_p(4096 + 128)) == 2              # 256-byte aligned
     assert match(tau=float("nan")) == 1
     assert match(wts=None) == 1                                     # weights needed with anchors
     assert apply(tgt_off=-(1 << 23) - 50) == 1                      # tgt - src out of range too
