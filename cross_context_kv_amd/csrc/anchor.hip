@@ -118,7 +118,9 @@ __device__ __forceinline__ void store_lane_row(const DPlane& O, int l, int seg, 
 #pragma unroll
       for (int w = 0; w < 4; ++w)
         u[w] = pack_bf16x2(y[16 * part + 8 * q + 2 * w], y[16 * part + 8 * q + 2 * w + 1]);
-      st16(row + part * 64 + 16 * g + 8 * q, u);
+      // an ordinary store: the four lane groups of a token write a row's
+      // 64-byte lines in two instructions, which L2 merges before writing back
+      *reinterpret_cast<vu4*>(row + part * 64 + 16 * g + 8 * q) = u;
     }
   }
 }
