@@ -73,6 +73,15 @@ __device__ __forceinline__ const bf16_t* bt_row(const Pool& G, int v, int l, int
 }
 
 // Factor rows are re-read by many blocks: ordinary (cached) loads.
+// LDS position (bf16 elements) of 16-byte chunk q (rank coefficients 8q..8q+7)
+// of MFMA row m of feature tile c in a staged right-factor slice.  A wave's
+// operand read for one tile (lanes: q = lane group, m = lane in group) then
+// covers one contiguous KiB, and the XOR spreads the staging writes (four
+// chunks of one row, several rows) over the banks.
+__device__ __forceinline__ int slice_chunk(int c, int q, int m) {
+  return ((c * 4 + q) * 16 + (m ^ (q << 2))) * 8;
+}
+
 __device__ __forceinline__ bf16x8 ld_op(const bf16_t* p) {
   return __builtin_bit_cast(bf16x8, ld16_cached(p));
 }
@@ -218,7 +227,7 @@ __device__ __forceinline__ void match_body(const MatchParams& P, int l, int h, i
     for (int k2 = 0; k2 < 2; ++k2) {
       const int u = tid + 256 * k2, f = u >> 2, q = u & 3;
       const int c = ((f >> 6) << 2) | ((f >> 2) & 3), m = (((f >> 4) & 3) << 2) | (f & 3);
-      *reinterpret_cast<vu4*>(buf + (c * 16 + m) * kRank + 8 * q) = r[k2];
+      *reinterpret_cast<vu4*>(buf + slice_chunk(c, q, m)) = r[k2];
     }
   };
   auto load_a = [&](int v, bf16x8* a) {
@@ -231,7 +240,7 @@ __device__ __forceinline__ void match_body(const MatchParams& P, int l, int h, i
     bf16x8 bop[kTiles];
 #pragma unroll
     for (int c = 0; c < kTiles; ++c)
-      bop[c] = *reinterpret_cast<const bf16x8*>(buf + (c * 16 + t) * kRank + 8 * g);
+      bop[c] = *reinterpret_cast<const bf16x8*>(buf + slice_chunk(c, g, t));
     float* o1 = P.part1 + ((((int64_t)l * 2 + p) * V + v) * H + h) * n;
     float* o2 = P.part2 + (((int64_t)l * V + v) * H + h) * n;
 #pragma unroll
@@ -465,7 +474,7 @@ __device__ __forceinline__ void apply_body(const AnchorApplyParams& P, int l, in
     for (int c = 0; c < kTiles; ++c) acc[b][c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   // The eligible anchors in order.  The head's right-factor slice of anchor
-  // i + 1 is staged in LDS (two buffers, in the MFMA row order) and its left
+  // i + 1 is staged in LDS (two buffers, in MFMA operand order) and its left
   // rows and weights loaded while anchor i computes; one barrier per anchor.
   // Indices are clamped at the end, so every load is unconditional; rows past
   // the covered prefix read the last covered row and get weight 0.
@@ -484,7 +493,7 @@ __device__ __forceinline__ void apply_body(const AnchorApplyParams& P, int l, in
       for (int k2 = 0; k2 < 2; ++k2) {
         const int u = tid + 256 * k2, f = u >> 2, q = u & 3;
         const int c = ((f >> 6) << 2) | ((f >> 2) & 3), m = (((f >> 4) & 3) << 2) | (f & 3);
-        *reinterpret_cast<vu4*>(buf + (c * 16 + m) * kRank + 8 * q) = r[k2];
+        *reinterpret_cast<vu4*>(buf + slice_chunk(c, q, m)) = r[k2];
       }
     };
     struct AOps {
@@ -505,7 +514,7 @@ __device__ __forceinline__ void apply_body(const AnchorApplyParams& P, int l, in
       bf16x8 bop[kTiles];
 #pragma unroll
       for (int c = 0; c < kTiles; ++c)
-        bop[c] = *reinterpret_cast<const bf16x8*>(buf + (c * 16 + t) * kRank + 8 * g);
+        bop[c] = *reinterpret_cast<const bf16x8*>(buf + slice_chunk(c, g, t));
 #pragma unroll
       for (int b = 0; b < kApplyBands; ++b)
 #pragma unroll
