@@ -248,7 +248,7 @@ def test_rope_shift_batched(dtype, hd, style):
 # ----------------------------------------------------------------------------
 
 
-@pytest.mark.parametrize("n", [1, 31, 32, 33, 300, 4096, 32768, 40000, 70001])
+@pytest.mark.parametrize("n", [1, 31, 32, 33, 300, 4095, 4096, 4097, 32768, 40000, 70001])
 def test_select_topb_matches_oracle(n):
     rng = np.random.default_rng(n)
     rows = 3
