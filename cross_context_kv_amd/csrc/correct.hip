@@ -320,12 +320,13 @@ __global__ void fit_finish_kernel(FitFinishParams F) {
 // apply
 // ---------------------------------------------------------------------------
 //
-// Persistent blocks sweep the plane: the rows are cut into chunks of CH rows
-// (one batch of U rows per lane), and block b takes chunks b, b + grid,
-// b + 2 grid, ...  At any moment the whole chip therefore streams one compact
-// window of HBM instead of one separate stream per block, which keeps the
-// memory system close to its copy rate.  Chunks are numbered segment-major,
-// so a block recomputes its rotary table only when the segment changes.
+// The rows are cut into chunks of CH rows (one batch of U rows per lane), and
+// block b takes chunks b, b + grid, b + 2 grid, ...  On dense planes the grid
+// is one block per chunk; on paged pools it is what the chip holds at once,
+// so the persistent blocks stream one compact window of the pool.  Either
+// way the chunks in flight cover neighbouring bytes.  Chunks are numbered
+// segment-major, so a block recomputes its rotary table only when the
+// segment changes.
 //
 // Per chunk, a block issues its row loads first, then the chunk's set-up
 // loads (probe bits, weights, rank-state rows; the lane's mean and B
@@ -504,19 +505,11 @@ __device__ __forceinline__ void apply_body(const ApplyParams& P) {
     const int j_begin = k * CH;
     const int j_end = min(P.n, j_begin + CH);
     const int nrows = j_end - j_begin;
-    // A new segment needs its rotary table; it is computed first, while
-    // nothing else of the chunk is live (chunks are segment-major, so this
-    // is rare).  Its shift was fetched one chunk ahead.
+    // A new segment needs its rotary table.  It is computed after the
+    // chunk's loads are issued (their latency covers it) and published by
+    // the chunk's barrier; its shift was fetched one chunk ahead.
     const bool new_seg = STYLE != kStyleNone && s != cur_s;      // uniform over the block
-    if (new_seg) {
-      ++gen;
-      if (t < HD / 2) {
-        double sv, cv;
-        rope_sincos((double)delta_cur * sfreq[t], &sv, &cv);
-        tab_c[gen & 1][t] = (C)cv;
-        tab_s[gen & 1][t] = (C)sv;
-      }
-    }
+    if (new_seg) ++gen;
     const Pos next = advance(pos);
     uint32_t mw_next[NW];
     chunk_words(next, mw_next);
@@ -606,6 +599,19 @@ __device__ __forceinline__ void apply_body(const ApplyParams& P) {
         else
 #pragma unroll
           for (int m = 0; m < V; ++m) Bv[kk][m] = (C)0;
+      }
+    }
+    if (new_seg && t < HD / 2) {
+      if constexpr (std::is_same<C, float>::value) {     // fp32 table (bf16 planes)
+        float sv, cv;
+        rope_sincos_f32((double)delta_cur * sfreq[t], &sv, &cv);
+        tab_c[gen & 1][t] = cv;
+        tab_s[gen & 1][t] = sv;
+      } else {
+        double sv, cv;
+        rope_sincos((double)delta_cur * sfreq[t], &sv, &cv);
+        tab_c[gen & 1][t] = (C)cv;
+        tab_s[gen & 1][t] = (C)sv;
       }
     }
     if (t < nrows) {
@@ -782,9 +788,9 @@ struct FitLaunch {
 template <typename T, int HD, int STYLE>
 struct ApplyLaunch {
   using C = typename std::conditional<std::is_same<T, float>::value, double, float>::type;
-  // The blocks are persistent: the grid is what the chip holds at once
-  // (resident blocks per CU of this instance x CUs), or fewer when there
-  // are fewer chunks, so no block waits for another to finish.
+  // Paged pools: persistent blocks, the grid being what the chip holds at
+  // once (resident blocks per CU of this instance x CUs, or fewer when there
+  // are fewer chunks).  Dense planes: one block per chunk.
   template <int R, bool PG>
   static void launch(ApplyParams P, int64_t n_chunks, hipStream_t st) {
     // only the chosen instance is compiled
@@ -800,7 +806,11 @@ struct ApplyLaunch {
       return nb;
     }();
     const int64_t resident = (int64_t)per_cu * device_cus();
-    const int64_t grid = n_chunks < resident ? n_chunks : resident;
+    // Dense planes: one block per chunk, dispatched in address order (the
+    // hardware then streams HBM like a plain one-pass copy).  Paged pools:
+    // persistent blocks sweeping the chunks, which keeps the blocks in
+    // flight on neighbouring pages.
+    const int64_t grid = !PG ? n_chunks : n_chunks < resident ? n_chunks : resident;
     const int64_t r0 = P.h_inner ? P.H : P.cpu, r1 = P.h_inner ? P.cpu : P.H;
     P.g0 = (int32_t)(grid % r0);
     P.g1 = (int32_t)(grid / r0 % r1);
