@@ -322,9 +322,9 @@ __global__ void fit_finish_kernel(FitFinishParams F) {
 //
 // The rows are cut into chunks of CH rows (one batch of U rows per lane), and
 // block b takes chunks b, b + grid, b + 2 grid, ...  On dense planes the grid
-// is one block per chunk; on paged pools it is what the chip holds at once,
-// so the persistent blocks stream one compact window of the pool.  Either
-// way the chunks in flight cover neighbouring bytes.  Chunks are numbered
+// is one block per chunk; on paged pools a block takes about sixteen chunks,
+// fetching each next chunk's page ids while it works on the current one.
+// Either way the chunks in flight cover neighbouring bytes.  Chunks are numbered
 // segment-major, so a block recomputes its rotary table only when the
 // segment changes.
 //
@@ -342,6 +342,7 @@ __global__ void fit_finish_kernel(FitFinishParams F) {
 constexpr int kApplyBlock = 256;
 constexpr int kApplyWaves = kApplyBlock / kWave;
 constexpr int kApplyU = 4;
+constexpr int kPagedChunksPerBlock = 16;
 
 // Rows per chunk for storage type T and head_dim HD (host and device).
 __host__ __device__ constexpr int apply_chunk_rows(int vec, int hd) {
@@ -788,9 +789,9 @@ struct FitLaunch {
 template <typename T, int HD, int STYLE>
 struct ApplyLaunch {
   using C = typename std::conditional<std::is_same<T, float>::value, double, float>::type;
-  // Paged pools: persistent blocks, the grid being what the chip holds at
-  // once (resident blocks per CU of this instance x CUs, or fewer when there
-  // are fewer chunks).  Dense planes: one block per chunk.
+  // Dense planes: one block per chunk.  Paged pools: about sixteen chunks
+  // per block, and never fewer blocks than the chip holds at once (resident
+  // blocks per CU of this instance x CUs) unless there are fewer chunks.
   template <int R, bool PG>
   static void launch(ApplyParams P, int64_t n_chunks, hipStream_t st) {
     // only the chosen instance is compiled
@@ -808,9 +809,13 @@ struct ApplyLaunch {
     const int64_t resident = (int64_t)per_cu * device_cus();
     // Dense planes: one block per chunk, dispatched in address order (the
     // hardware then streams HBM like a plain one-pass copy).  Paged pools:
-    // persistent blocks sweeping the chunks, which keeps the blocks in
-    // flight on neighbouring pages.
-    const int64_t grid = !PG ? n_chunks : n_chunks < resident ? n_chunks : resident;
+    // blocks of about kPagedChunksPerBlock chunks each (at least the
+    // resident count), so each block's page ids are fetched a chunk ahead
+    // while the blocks in flight still sweep neighbouring pages.
+    const int64_t per_block = n_chunks / kPagedChunksPerBlock;
+    const int64_t grid = !PG ? n_chunks
+                             : per_block > resident ? per_block
+                                                    : n_chunks < resident ? n_chunks : resident;
     const int64_t r0 = P.h_inner ? P.H : P.cpu, r1 = P.h_inner ? P.cpu : P.H;
     P.g0 = (int32_t)(grid % r0);
     P.g1 = (int32_t)(grid / r0 % r1);
