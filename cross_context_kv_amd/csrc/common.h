@@ -194,6 +194,11 @@ __device__ __forceinline__ void st16(void* p, vu4 v) {
   __builtin_nontemporal_store(v, reinterpret_cast<vu4*>(p));
 }
 
+// Completes the load that produced v here, once.  vmcnt counts stores as
+// well as loads, so a loop that reads registers loaded before it would
+// otherwise wait, every iteration, for all of its own earlier stores.
+__device__ __forceinline__ void settle(vu4& v) { asm volatile("" : "+v"(v)); }
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 

@@ -342,7 +342,7 @@ __global__ void fit_finish_kernel(FitFinishParams F) {
 constexpr int kApplyBlock = 256;
 constexpr int kApplyWaves = kApplyBlock / kWave;
 constexpr int kApplyU = 4;
-constexpr int kPagedChunksPerBlock = 16;
+constexpr int kPagedChunksPerBlock = 32;
 
 // Rows per chunk for storage type T and head_dim HD (host and device).
 __host__ __device__ constexpr int apply_chunk_rows(int vec, int hd) {
@@ -363,10 +363,11 @@ struct ApplyParams {
   // Chunk order: c = ((s L + l) X + x) Y + y, where (x, y) = (head, chunk
   // of tokens) or, when a head's rows are farther apart than a token's
   // (paged pools, token-major layouts), (chunk of tokens, head), so that the
-  // chunks in flight together cover neighbouring bytes.  g0..g3: the grid
-  // stride in the same digits (innermost first).
+  // chunks in flight together cover neighbouring bytes.  Block b takes the
+  // per_block chunks from b per_block on, one after another (a paged pool
+  // then reuses its rotary table across them).
   int32_t h_inner;
-  int32_t g0, g1, g2, g3;
+  int32_t per_block;
   int32_t a_vec;               // A rows may be read as whole 16-byte vectors
   int32_t b_vec;               // B rows may be read as whole 16-byte vectors
 };
@@ -438,19 +439,18 @@ __device__ __forceinline__ void apply_body(const ApplyParams& P) {
   const int64_t out_step = (int64_t)kStep * P.out.s_token;
   int cur_s = -1, gen = 0;
   const bool first_half = STYLE == kStyleHalf && g < M::X;
-  // Chunk coordinates (block-uniform).  The block advances by the grid
-  // stride, added digit by digit with carries: no division in the loop.
+  // Chunk coordinates (block-uniform).  The block steps to the next chunk
+  // digit by digit with carries: no division in the loop.
   struct Pos { int k, h, l, s; };
   const int r0 = P.h_inner ? P.H : P.cpu, r1 = P.h_inner ? P.cpu : P.H;
   auto advance = [&](Pos p) {
     int d0 = P.h_inner ? p.h : p.k, d1 = P.h_inner ? p.k : p.h;
-    d0 += P.g0;
-    int cy = d0 >= r0; if (cy) d0 -= r0;
-    d1 += P.g1 + cy;
-    cy = d1 >= r1; if (cy) d1 -= r1;
-    p.l += P.g2 + cy;
-    cy = p.l >= P.L; if (cy) p.l -= P.L;
-    p.s += P.g3 + cy;
+    int cy = ++d0 >= r0; if (cy) d0 = 0;
+    d1 += cy;
+    cy = d1 >= r1; if (cy) d1 = 0;
+    p.l += cy;
+    cy = p.l >= P.L; if (cy) p.l = 0;
+    p.s += cy;
     p.h = P.h_inner ? d0 : d1;
     p.k = P.h_inner ? d1 : d0;
     return p;
@@ -470,7 +470,7 @@ __device__ __forceinline__ void apply_body(const ApplyParams& P) {
   };
   Pos pos;
   {
-    unsigned q = blockIdx.x;
+    unsigned q = blockIdx.x * (unsigned)P.per_block;     // below 2^31 (host check)
     const int d0 = (int)(q % (unsigned)r0); q /= (unsigned)r0;
     const int d1 = (int)(q % (unsigned)r1); q /= (unsigned)r1;
     pos.l = (int)(q % (unsigned)P.L);
@@ -500,7 +500,7 @@ __device__ __forceinline__ void apply_body(const ApplyParams& P) {
   int64_t delta_cur = STYLE != kStyleNone && pos.s < P.S ? P.rope.delta[pos.s] : 0;
 
   int it = 0;
-  for (; pos.s < P.S; ++it) {
+  for (; pos.s < P.S && it < P.per_block; ++it) {
     const int buf = it & 1;
     const int k = pos.k, h = pos.h, l = pos.l, s = pos.s;
     const int j_begin = k * CH;
@@ -726,16 +726,16 @@ __device__ __forceinline__ void apply_body(const ApplyParams& P) {
   }
 }
 
-// Register budget: the bf16 / hd 128 / rank <= 4 instances fit in 168 VGPRs
-// without spilling (3 waves per SIMD, so 3 resident blocks per CU); the other
+// Register budget: the bf16 / hd 128 / rank <= 4 instances fit in 128 VGPRs
+// without spilling (4 waves per SIMD, so 4 resident blocks per CU); the other
 // instances keep the compiler's own choice.
 template <typename T, int HD, int MAXR, bool PAGED>
-constexpr bool apply_occ3() {
+constexpr bool apply_occ4() {
   return std::is_same<T, bf16_t>::value && HD == 128 && MAXR <= 4;
 }
 
 template <typename T, typename C, int HD, int STYLE, int MAXR, bool PAGED>
-__global__ __launch_bounds__(kApplyBlock) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ __launch_bounds__(kApplyBlock) __attribute__((amdgpu_waves_per_eu(4)))
 void apply_kernel(ApplyParams P) {
   apply_body<T, C, HD, STYLE, MAXR, PAGED>(P);
 }
@@ -789,14 +789,14 @@ struct FitLaunch {
 template <typename T, int HD, int STYLE>
 struct ApplyLaunch {
   using C = typename std::conditional<std::is_same<T, float>::value, double, float>::type;
-  // Dense planes: one block per chunk.  Paged pools: about sixteen chunks
+  // Dense planes: one block per chunk.  Paged pools: about 32 consecutive chunks
   // per block, and never fewer blocks than the chip holds at once (resident
   // blocks per CU of this instance x CUs) unless there are fewer chunks.
   template <int R, bool PG>
   static void launch(ApplyParams P, int64_t n_chunks, hipStream_t st) {
     // only the chosen instance is compiled
     auto kern = [] {
-      if constexpr (apply_occ3<T, HD, R, PG>()) return apply_kernel<T, C, HD, STYLE, R, PG>;
+      if constexpr (apply_occ4<T, HD, R, PG>()) return apply_kernel<T, C, HD, STYLE, R, PG>;
       else return apply_kernel_wide<T, C, HD, STYLE, R, PG>;
     }();
     static const int per_cu = [&] {
@@ -809,18 +809,15 @@ struct ApplyLaunch {
     const int64_t resident = (int64_t)per_cu * device_cus();
     // Dense planes: one block per chunk, dispatched in address order (the
     // hardware then streams HBM like a plain one-pass copy).  Paged pools:
-    // blocks of about kPagedChunksPerBlock chunks each (at least the
-    // resident count), so each block's page ids are fetched a chunk ahead
-    // while the blocks in flight still sweep neighbouring pages.
-    const int64_t per_block = n_chunks / kPagedChunksPerBlock;
-    const int64_t grid = !PG ? n_chunks
-                             : per_block > resident ? per_block
-                                                    : n_chunks < resident ? n_chunks : resident;
-    const int64_t r0 = P.h_inner ? P.H : P.cpu, r1 = P.h_inner ? P.cpu : P.H;
-    P.g0 = (int32_t)(grid % r0);
-    P.g1 = (int32_t)(grid / r0 % r1);
-    P.g2 = (int32_t)(grid / r0 / r1 % P.L);
-    P.g3 = (int32_t)(grid / r0 / r1 / P.L);
+    // runs of about kPagedChunksPerBlock consecutive chunks per block (and
+    // never fewer blocks than the chip holds at once), so each block's page
+    // ids are fetched a chunk ahead and its rotary table serves the run.
+    int64_t blocks = !PG ? n_chunks : n_chunks / kPagedChunksPerBlock;
+    if (blocks < resident) blocks = resident;
+    if (blocks > n_chunks) blocks = n_chunks;
+    const int64_t per = (n_chunks + blocks - 1) / blocks;
+    const int64_t grid = (n_chunks + per - 1) / per;
+    P.per_block = (int32_t)per;
     kern<<<dim3((unsigned)grid), dim3(kApplyBlock), 0, st>>>(P);
   }
   template <bool PG>
@@ -983,7 +980,8 @@ extern "C" kvfix_status kvfix_apply_ex(const kvfix_plane* reuse, const kvfix_pla
   // heads innermost when a token's heads sit closer together than a head's
   // tokens (a paged pool, a token-major layout)
   P.h_inner = reuse->s_head < reuse->s_token;
-  const int64_t grid = n_chunks;        // capped at the resident blocks by the launcher
+  if (n_chunks > kMaxGrid) return KVFIX_ERR_ARG;
+  const int64_t grid = n_chunks;        // the launcher derives the grid from the chunk count
   const int style = rope ? rope->style : kStyleNone;
   return dispatch_t_hd_style<ApplyLaunch>(reuse->dtype, reuse->head_dim, style, P,
                                           rank_variant(P.lr.rank), grid, (hipStream_t)stream);

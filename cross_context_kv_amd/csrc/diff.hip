@@ -330,8 +330,9 @@ __global__ __launch_bounds__(kDiffBlock) void diff_decode_kernel(DecodeParams P,
       // the master row, once per group of agents
       const T* mkp = reinterpret_cast<const T*>(P.mk.data) + row_offset(P.mk, l, 0, h, t0 + t);
       const T* mvp = reinterpret_cast<const T*>(P.mv.data) + row_offset(P.mv, l, 0, h, t0 + t);
-      const vu4 mk0 = ld16(mkp + M::off0(g)), mk1 = ld16(mkp + M::off1(g));
-      const vu4 mv0 = ld16(mvp + M::off0(g)), mv1 = ld16(mvp + M::off1(g));
+      vu4 mk0 = ld16(mkp + M::off0(g)), mk1 = ld16(mkp + M::off1(g));
+      vu4 mv0 = ld16(mvp + M::off0(g)), mv1 = ld16(mvp + M::off1(g));
+      settle(mk0); settle(mk1); settle(mv0); settle(mv1);
       for (int a = 0; a < na; ++a) {
         const int64_t slot = sslot[a];          // uniform over the block
         vu4 k0 = mk0, k1 = mk1, v0 = mv0, v1 = mv1;
@@ -343,6 +344,8 @@ __global__ __launch_bounds__(kDiffBlock) void diff_decode_kernel(DecodeParams P,
           k1 = ld16(pk + M::off1(g));
           v0 = ld16(pv + M::off0(g));
           v1 = ld16(pv + M::off1(g));
+          // consumed on this path, so that no later iteration waits on them
+          settle(k0); settle(k1); settle(v0); settle(v1);
         }
         double csd[V], snd[V];
         lds_table<V>(stab[a], g, csd, snd);
