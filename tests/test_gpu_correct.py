@@ -323,11 +323,19 @@ def test_paged_tagging_maps_every_row_exactly():
     assert np.array_equal(to_np(pool2).ravel(), pool)
 
 
-def test_paged_in_place_correction_equals_dense():
-    cfg = CONFIGS["c5"].replace(n_layers=3, n_segs=4, n_kv_heads=2, n_tokens=70, b=7,
-                                n_pages=29, check_layer=1)
+@pytest.mark.parametrize("L,S,H,n,b,n_pages", [
+    (3, 4, 2, 70, 7, 29),
+    # 1,161 chunks of 64 rows (43 per head, the last of 52 rows): more than
+    # the chip holds at once, so each paged block takes a run of two chunks
+    # (crossing head, layer and segment boundaries; the last run is a single
+    # chunk), while the dense apply takes one chunk per block
+    (3, 3, 3, 2740, 270, 540),
+])
+def test_paged_in_place_correction_equals_dense(L, S, H, n, b, n_pages):
+    cfg = CONFIGS["c5"].replace(n_layers=L, n_segs=S, n_kv_heads=H, n_tokens=n, b=b,
+                                n_pages=n_pages, check_layer=1)
     case = correction_case(cfg)
-    L, S, H, n, hd, ps = 3, 4, 2, 70, 128, 16
+    hd, ps = 128, 16
     pt, pps = paged_case(L, S, H, n, hd, ps, cfg.n_pages)
     # dense reference chain
     g = gpu_chain(cfg, case)
