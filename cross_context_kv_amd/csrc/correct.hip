@@ -499,8 +499,14 @@ __device__ __forceinline__ void apply_body(const ApplyParams& P) {
   if (STYLE != kStyleNone && t < HD / 2) sfreq[t] = P.rope.inv_freq[t];
   int64_t delta_cur = STYLE != kStyleNone && pos.s < P.S ? P.rope.delta[pos.s] : 0;
 
+  // Dense planes take exactly one chunk per block (the launcher's grid).
+  // The rotating MFMA instance then compiles the body once, with no
+  // next-chunk fetches: the loop's state would spill its scalar registers
+  // and leave it at four waves per SIMD.  The other dense instances keep
+  // the loop (run once); compiled straight, they measured slower.
+  constexpr bool kOne = !PAGED && kMfma && STYLE != kStyleNone;
   int it = 0;
-  for (; pos.s < P.S && it < P.per_block; ++it) {
+  for (; pos.s < P.S && it < (kOne ? 1 : P.per_block); ++it) {
     const int buf = it & 1;
     const int k = pos.k, h = pos.h, l = pos.l, s = pos.s;
     const int j_begin = k * CH;
@@ -511,11 +517,12 @@ __device__ __forceinline__ void apply_body(const ApplyParams& P) {
     // the chunk's barrier; its shift was fetched one chunk ahead.
     const bool new_seg = STYLE != kStyleNone && s != cur_s;      // uniform over the block
     if (new_seg) ++gen;
-    const Pos next = advance(pos);
+    const Pos next = kOne ? pos : advance(pos);
     uint32_t mw_next[NW];
-    chunk_words(next, mw_next);
+    if constexpr (!kOne) chunk_words(next, mw_next);
     int64_t delta_next = 0;
-    if (STYLE != kStyleNone && next.s < P.S && next.s != s) delta_next = P.rope.delta[next.s];
+    if constexpr (!kOne)
+      if (STYLE != kStyleNone && next.s < P.S && next.s != s) delta_next = P.rope.delta[next.s];
     // live rows of this lane: in range and not a probe
     bool live[U];
 #pragma unroll
@@ -715,6 +722,7 @@ __device__ __forceinline__ void apply_body(const ApplyParams& P) {
         st16(out_row(u), Cc::pack(x));
       }
     }
+    if constexpr (kOne) break;
 #pragma unroll
     for (int qq = 0; qq < NW; ++qq) mw[qq] = mw_next[qq];
     if constexpr (PAGED) {
