@@ -129,6 +129,7 @@ struct ScoreLaunch {
 // places every kept key by wave ballots and a scanned table of per-wave
 // counts, so indices come out ascending and the lowest-index keys equal to
 // T are the ones taken.
+template <int KR>
 __global__ __launch_bounds__(kSelBlock) void select_topb_kernel(const float* __restrict__ scores,
                                                                 int n, int b,
                                                                 int32_t* __restrict__ idx,
@@ -138,26 +139,26 @@ __global__ __launch_bounds__(kSelBlock) void select_topb_kernel(const float* __r
   __shared__ uint32_t ctab[2 * kCompactTab];
   __shared__ uint32_t sh[3];
   const int row = blockIdx.x;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x;
   const float* sc = scores + (int64_t)row * n;
   int32_t* out_idx = idx + (int64_t)row * b;
   uint32_t* out_mask = mask + (int64_t)row * words;
-  const bool in_regs = n <= kSelBlock * kSelRegKeys;
+  const bool in_regs = n <= kSelBlock * KR;
 
-  uint32_t key[kSelRegKeys];
+  uint32_t key[KR];
   if (in_regs) {
 #pragma unroll
-    for (int q = 0; q < kSelRegKeys; ++q) {
+    for (int q = 0; q < KR; ++q) {
       const int j = t + q * kSelBlock;
       key[q] = j < n ? order_key(sc[j]) : 0u;
     }
   }
   uint32_t T, need_eq, eq_total;
-  radix_threshold(key, in_regs, sc, n, b, &hist[0][0], sh, &T, &need_eq, &eq_total);
+  radix_threshold<KR>(key, in_regs, sc, n, b, &hist[0][0], sh, &T, &need_eq, &eq_total);
 
-  compact_topb(key, in_regs, sc, n, b, T, need_eq, eq_total, ctab,
-               [&](uint32_t pos, int j, uint32_t) { out_idx[pos] = j; },
-               [&](int w, uint32_t bits) { out_mask[w] = bits; });
+  compact_topb<KR>(key, in_regs, sc, n, b, T, need_eq, eq_total, ctab,
+                   [&](uint32_t pos, int j, uint32_t) { out_idx[pos] = j; },
+                   [&](int w, uint32_t bits) { out_mask[w] = bits; });
 }
 
 }  // namespace kvfix
@@ -217,7 +218,16 @@ extern "C" kvfix_status kvfix_select_topb(const float* scores, int32_t n_rows, i
   if (scores == nullptr || mask == nullptr || (b > 0 && idx == nullptr)) return KVFIX_ERR_ARG;
   if (n_rows > kMaxGrid) return KVFIX_ERR_ARG;
   const int words = (n + 31) / 32;
-  select_topb_kernel<<<dim3((unsigned)n_rows), dim3(kSelBlock), 0, (hipStream_t)stream>>>(
-      scores, n, b, idx, mask, words);
+  // register keys per thread: the fewest columns (a power of two) that hold
+  // the row; longer rows stream from memory through the 32-column path
+  const int cols = (n + kSelBlock - 1) / kSelBlock;
+  const dim3 grid((unsigned)n_rows), block(kSelBlock);
+  hipStream_t st = (hipStream_t)stream;
+  if (cols <= 1) select_topb_kernel<1><<<grid, block, 0, st>>>(scores, n, b, idx, mask, words);
+  else if (cols <= 2) select_topb_kernel<2><<<grid, block, 0, st>>>(scores, n, b, idx, mask, words);
+  else if (cols <= 4) select_topb_kernel<4><<<grid, block, 0, st>>>(scores, n, b, idx, mask, words);
+  else if (cols <= 8) select_topb_kernel<8><<<grid, block, 0, st>>>(scores, n, b, idx, mask, words);
+  else if (cols <= 16) select_topb_kernel<16><<<grid, block, 0, st>>>(scores, n, b, idx, mask, words);
+  else select_topb_kernel<kSelRegKeys><<<grid, block, 0, st>>>(scores, n, b, idx, mask, words);
   return launch_status();
 }

@@ -100,7 +100,9 @@ __device__ __forceinline__ void hist_add(uint32_t* whist, uint32_t bin, bool val
 // words of LDS.  Every thread of the 1024-thread block
 // calls it; it returns with the block synchronised.  b == 0 gives need_eq 0.
 // eq_total_out: the number of keys equal to T (all of them are kept when it
-// equals need_eq).  sh: 3 words of LDS.
+// equals need_eq).  sh: 3 words of LDS.  KR: the register keys per thread
+// (n <= 1024 KR when in_regs); a short row compiles only the columns it has.
+template <int KR = kSelRegKeys>
 __device__ __forceinline__ void radix_threshold(const uint32_t* key, bool in_regs,
                                                 const float* __restrict__ sc, int n, int b,
                                                 uint32_t* hist, uint32_t* sh, uint32_t* T_out,
@@ -116,7 +118,7 @@ __device__ __forceinline__ void radix_threshold(const uint32_t* key, bool in_reg
       if (in_regs) {
         const int cols = (n + kSelBlock - 1) / kSelBlock;   // columns holding keys
 #pragma unroll
-        for (int q = 0; q < kSelRegKeys; ++q) {
+        for (int q = 0; q < KR; ++q) {
           if (q < cols) {
             const int j = t + q * kSelBlock;
             hist_add(hist + wave * 256, (key[q] >> shift) & 255u,
@@ -208,7 +210,7 @@ constexpr int kCompactTab = 520;       // words of each of the two count tables
 // emit(pos, j, key) receives every kept key; word(w, bits) every mask word
 // (all ceil(n/32) words).  tab: 2 x kCompactTab words of LDS.  Every thread
 // of the 1024-thread block calls it; it returns with the block synchronised.
-template <typename Emit, typename Word>
+template <int KR = kSelRegKeys, typename Emit, typename Word>
 __device__ __forceinline__ void compact_topb(const uint32_t* key_regs, bool in_regs,
                                              const float* __restrict__ sc, int n, int b,
                                              uint32_t T, uint32_t need_eq, uint32_t eq_total,
@@ -218,15 +220,15 @@ __device__ __forceinline__ void compact_topb(const uint32_t* key_regs, bool in_r
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const uint64_t below = (1ull << lane) - 1ull;
   const int words = (n + 31) >> 5;
-  constexpr int kSpan = kSelBlock * kSelRegKeys;
+  constexpr int kSpan = kSelBlock * KR;
   uint32_t* teq = tab;
   uint32_t* tkeep = tab + kCompactTab;
   uint32_t eq_carry = 0, pos_carry = 0;
   for (int base = 0; base < n; base += kSpan) {
-    const int cols = min(kSelRegKeys, (n - base + kSelBlock - 1) / kSelBlock);
-    uint32_t key[kSelRegKeys];
+    const int cols = min(KR, (n - base + kSelBlock - 1) / kSelBlock);
+    uint32_t key[KR];
 #pragma unroll
-    for (int q = 0; q < kSelRegKeys; ++q) {
+    for (int q = 0; q < KR; ++q) {
       const int j = base + q * kSelBlock + t;
       key[q] = in_regs ? key_regs[q] : (q < cols && j < n ? order_key(sc[j]) : 0u);
     }
@@ -234,7 +236,7 @@ __device__ __forceinline__ void compact_topb(const uint32_t* key_regs, bool in_r
     // keys == T per (column, wave), when their rank decides
     if (!all_eq) {
 #pragma unroll
-      for (int q = 0; q < kSelRegKeys; ++q) {
+      for (int q = 0; q < KR; ++q) {
         const uint64_t em = q < cols ? __ballot(is_eq(q)) : 0ull;
         if (lane == 0) teq[q * kSelWaves + wave] = (uint32_t)__popcll(em);
       }
@@ -251,7 +253,7 @@ __device__ __forceinline__ void compact_topb(const uint32_t* key_regs, bool in_r
     };
     // kept keys per (column, wave)
 #pragma unroll
-    for (int q = 0; q < kSelRegKeys; ++q) {
+    for (int q = 0; q < KR; ++q) {
       const uint64_t km = q < cols ? __ballot(keep(q)) : 0ull;
       if (lane == 0) tkeep[q * kSelWaves + wave] = (uint32_t)__popcll(km);
     }
@@ -259,7 +261,7 @@ __device__ __forceinline__ void compact_topb(const uint32_t* key_regs, bool in_r
     scan512(tkeep, t);
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < kSelRegKeys; ++q) {
+    for (int q = 0; q < KR; ++q) {
       if (q >= cols) continue;
       const bool k = keep(q);
       const uint64_t km = __ballot(k);
