@@ -43,8 +43,11 @@ __device__ __forceinline__ bf16_t bf16_bits_rne(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
+// Three waves per SIMD: the instance fits in 168 VGPRs without spilling
+// (the compiler's own choice, 176, leaves two).
 template <int STYLE>
-__global__ __launch_bounds__(kDraftBlock) void draft_logits_kernel(DraftParams P) {
+__global__ __launch_bounds__(kDraftBlock) __attribute__((amdgpu_waves_per_eu(3)))
+void draft_logits_kernel(DraftParams P) {
   constexpr int HD = kDraftHD;
   __shared__ double tc[HD / 2], ts[HD / 2];
   __shared__ __attribute__((aligned(16))) bf16_t qs[3][16][HD];   // hi, mid, lo parts of the query tile
