@@ -81,8 +81,8 @@ __device__ __forceinline__ void lds_table(const double2* row, int g, double* cs,
 }
 
 template <typename T, int HD, int STYLE>
-__global__ __launch_bounds__(kDiffBlock) void diff_flag_kernel(DiffShape D, const double2* tab,
-                                                               uint8_t* flags) {
+__global__ __launch_bounds__(kDiffBlock) __attribute__((amdgpu_waves_per_eu(3)))
+void diff_flag_kernel(DiffShape D, const double2* tab, uint8_t* flags) {
   using M = RowMap<T, HD, STYLE>;
   using Cd = Codec<T, double>;
   constexpr int V = M::V, G = M::G, RPB = kDiffBlock / G;
@@ -109,11 +109,19 @@ __global__ __launch_bounds__(kDiffBlock) void diff_flag_kernel(DiffShape D, cons
       const T* mvp = reinterpret_cast<const T*>(D.mv.data) + row_offset(D.mv, l, 0, h, t);
       const vu4 mk0 = ld16(mkp + M::off0(g)), mk1 = ld16(mkp + M::off1(g));
       const vu4 mv0 = ld16(mvp + M::off0(g)), mv1 = ld16(mvp + M::off1(g));
-      for (int a = 0; a < na; ++a) {
+      // the next agent's rows load while this agent's compare (the last
+      // agent loads its own rows again)
+      auto load_agent = [&](int a, vu4* r) {
         const T* sk = reinterpret_cast<const T*>(D.sk.data) + row_offset(D.sk, l, a0 + a, h, t);
         const T* sv = reinterpret_cast<const T*>(D.sv.data) + row_offset(D.sv, l, a0 + a, h, t);
-        const vu4 k0 = ld16(sk + M::off0(g)), k1 = ld16(sk + M::off1(g));
-        const vu4 v0 = ld16(sv + M::off0(g)), v1 = ld16(sv + M::off1(g));
+        r[0] = ld16(sk + M::off0(g)); r[1] = ld16(sk + M::off1(g));
+        r[2] = ld16(sv + M::off0(g)); r[3] = ld16(sv + M::off1(g));
+      };
+      vu4 nxt[4];
+      load_agent(0, nxt);
+      for (int a = 0; a < na; ++a) {
+        const vu4 k0 = nxt[0], k1 = nxt[1], v0 = nxt[2], v1 = nxt[3];
+        load_agent(a + 1 < na ? a + 1 : a, nxt);
         double cs[V], sn[V];
         lds_table<V>(stab[a], g, cs, sn);
         double p0[V], p1[V], xa[V], xb[V], ma[V], mb[V];
