@@ -248,7 +248,11 @@ def test_rope_shift_batched(dtype, hd, style):
 # ----------------------------------------------------------------------------
 
 
-@pytest.mark.parametrize("n", [1, 31, 32, 33, 300, 4095, 4096, 4097, 32768, 40000, 70001])
+# row lengths on both sides of every register key-column count the selection
+# is compiled for (1, 2, 4, 8, 16, 32 columns of 1024 keys), and past them
+# (keys streamed from memory)
+@pytest.mark.parametrize("n", [1, 31, 32, 33, 300, 1024, 1025, 2048, 2049, 4095, 4096, 4097, 8192,
+                               8193, 16384, 16385, 32768, 32769, 40000, 70001])
 def test_select_topb_matches_oracle(n):
     rng = np.random.default_rng(n)
     rows = 3
