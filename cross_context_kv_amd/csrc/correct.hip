@@ -320,13 +320,12 @@ __global__ void fit_finish_kernel(FitFinishParams F) {
 // apply
 // ---------------------------------------------------------------------------
 //
-// The rows are cut into chunks of CH rows (one batch of U rows per lane), and
-// block b takes chunks b, b + grid, b + 2 grid, ...  On dense planes the grid
-// is one block per chunk; on paged pools a block takes about sixteen chunks,
-// fetching each next chunk's page ids while it works on the current one.
-// Either way the chunks in flight cover neighbouring bytes.  Chunks are numbered
-// segment-major, so a block recomputes its rotary table only when the
-// segment changes.
+// The rows are cut into chunks of CH rows (one batch of U rows per lane).  On
+// dense planes each block takes one chunk, in address order, so the chunks
+// in flight cover neighbouring bytes; on paged pools a block takes a run of
+// about 32 consecutive chunks, fetching each next chunk's page ids while it
+// works on the current one.  Chunks are numbered segment-major, so a block
+// recomputes its rotary table only when the segment changes.
 //
 // Per chunk, a block issues its row loads first, then the chunk's set-up
 // loads (probe bits, weights, rank-state rows; the lane's mean and B
