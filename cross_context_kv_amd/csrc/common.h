@@ -327,8 +327,8 @@ struct RopeArgs {
 // about 1.3e7 rad, i.e. shifts up to 2^23 positions); then the Taylor series
 // of sin and cos on |r| <= pi/4, through r^19 and r^20 (truncation below
 // 1e-22), and the quadrant k mod 4.  Within about one unit of 2^-53 of the
-// exact values.
-__device__ __forceinline__ void rope_sincos(double x, double* sp, double* cp) {
+// exact values.  Host-callable too, so a CPU test can check it against libm.
+__host__ __device__ __forceinline__ void rope_sincos(double x, double* sp, double* cp) {
   constexpr double kTwoOverPi = 0x1.45f306dc9c883p-1;
   constexpr double kP1 = 0x1.921fb54000000p+0;     // pi/2, first 30 bits
   constexpr double kP2 = 0x1.10b4611800000p-30;    // next 30 bits
@@ -364,8 +364,8 @@ __device__ __forceinline__ void rope_sincos(double x, double* sp, double* cp) {
 // reduction in fp64 (so a large x loses nothing), then the Taylor series of
 // sin and cos on |r| <= pi/4 in fp32 through r^11 and r^12 (truncation below
 // 2e-12), and the quadrant.  Within about two units of 2^-24 of the exact
-// values, at a fraction of the fp64 series' cost.
-__device__ __forceinline__ void rope_sincos_f32(double x, float* sp, float* cp) {
+// values, at a fraction of the fp64 series' cost.  Host-callable too.
+__host__ __device__ __forceinline__ void rope_sincos_f32(double x, float* sp, float* cp) {
   constexpr double kTwoOverPi = 0x1.45f306dc9c883p-1;
   constexpr double kP1 = 0x1.921fb54000000p+0;
   constexpr double kP2 = 0x1.10b4611800000p-30;

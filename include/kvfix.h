@@ -48,9 +48,11 @@
  *     per-segment page table.
  *   - Alignment: data pointers and every row must be 16-byte aligned (the
  *     kernels move 128-bit vectors); otherwise KVFIX_ERR_ALIGN.
- *   - Arithmetic: fp32 storage is computed in fp64; bf16 storage is computed
- *     in fp32 (apply, fit_mean) or fp64 (rotation-only, scores, diff paths);
- *     each output element is rounded once (round to nearest even).
+ *   - Arithmetic: fp32 storage is computed in fp64.  For bf16 storage:
+ *     kvfix_apply, kvfix_diff_decode and the anchor calls compute in fp32;
+ *     kvfix_rope_shift, kvfix_score, kvfix_fit_mean and kvfix_diff_encode's
+ *     compare compute in fp64.  Each output element is rounded once (round
+ *     to nearest even).
  */
 #ifndef KVFIX_H
 #define KVFIX_H
@@ -104,9 +106,13 @@ typedef struct {
 } kvfix_plane;
 
 /* Rotary shift: segment s is rotated forward by delta[s] positions, i.e. pair
- * i turns by delta[s] * theta^(-2i/hd) radians.  Angles are formed and their
- * sine/cosine taken in fp64 on the device.  [KVCMAS §2.2, App. A.3 "Correction
- * Weighting and Positional Alignment"; TD Algorithm 1, RoPERecover] */
+ * i turns by delta[s] * theta^(-2i/hd) radians.  Angles are formed in fp64
+ * and their sine/cosine taken by the library's own routines (within about one
+ * unit of 2^-53 of the exact values; the fp32 tables of bf16 applies within
+ * about one unit of 2^-24).  Limit: |delta[s]| < 2^23 positions, below which
+ * the reduction of the angle by pi/2 is exact; larger shifts are not
+ * detected (delta is device data) and lose accuracy.  [KVCMAS §2.2, App. A.3
+ * "Correction Weighting and Positional Alignment"; TD Algorithm 1, RoPERecover] */
 typedef struct {
   double         theta;
   int32_t        style;          /* kvfix_rope_style */
@@ -262,7 +268,14 @@ kvfix_status kvfix_select_grow(const float* scores, int32_t n_rows, int32_t n, i
  * mu: device fp32 [n_layers][n_segs][n_heads][head_dim], contiguous.
  * idx: device int32 [n_segs][b]; b >= 0 is the list width and may exceed
  * n_tokens (device data is not checked on the host).
- * out may alias reuse (in-place correction).
+ * out may alias reuse (in-place correction).  When it does, the members of
+ * each list must be distinct (a repeated index could read the fresh row
+ * that an earlier member already scattered over the reused one, which
+ * changes mu); kvfix_select_topb and kvfix_select_grow lists are distinct,
+ * and so is a kvfix_expand_chunks list whose chunk ids are.  Out of place,
+ * a repeated index is a repeated member and counts once per occurrence
+ * (with fresh_by_slot, which occurrence's fresh row lands in out is
+ * unspecified).
  * ws: device workspace of kvfix_fit_mean_workspace(...) bytes, 16-byte
  * aligned (fp64 partial sums of 256-probe slices); KVFIX_ERR_ARG when it is
  * missing, short or misaligned.
@@ -303,9 +316,10 @@ kvfix_status kvfix_apply(const kvfix_plane* reuse, const kvfix_plane* out,
  * closest to the group's shared structure, usually the one with the lowest
  * total deviation from the shared blocks]
  * totals[a] = sum over j of scores[a][j] in fp64, added in a fixed order:
- * each 64-token block in token order, then the block sums in block order;
- * *master = the a with the lowest total, ties to the lower index (a NaN
- * total ranks last).  The scores are per-token deviation scores, e.g.
+ * each 64-token block in token order, then the block sums in block order
+ * (deterministic; within (63 + ceil(n/64)) 2^-53 sum_j |scores[a][j]| of the
+ * exact sum); *master = the a with the lowest total, ties to the lower index
+ * (a NaN total ranks last).  The scores are per-token deviation scores, e.g.
  * kvfix_score of each request's cache against the shared blocks at the
  * check layer.  scores: device fp32 [n_agents][n]; totals: device fp64
  * [n_agents]; master: device int32 [1].  n_agents >= 1.
@@ -395,7 +409,8 @@ kvfix_status kvfix_diff_encode(const kvfix_plane* master_k, const kvfix_plane* m
 
 /* Decode: for every agent a, out(l, a) = master(l) with the listed blocks of
  * (a, l) overwritten by their packed values, keys then rotated forward by
- * from_master->delta[a] positions (fp64, one rounding); values copied.  No
+ * from_master->delta[a] positions (fp32 for bf16 planes, fp64 for fp32
+ * planes; sine and cosine from fp64; one rounding); values copied.  No
  * dense mirror is materialised: each master block is read once from HBM and
  * written to every agent.  out_k/out_v: planes with n_segs = n_agents.
  * A listed block whose slot lies at or past capacity_blocks (an encode that

@@ -870,11 +870,10 @@ def select_master(scores: np.ndarray):
     closest to the group's shared structure, usually the one with the lowest
     total deviation from the shared blocks.  Reading: the total of request a
     is the sum of its per-token deviation scores (the check-layer divergence
-    of a2) in float64, added in this order: the tokens of each 64-token block
-    in token order, then the block sums in block order (the pages fix no
-    order; this one is fixed so that both sides add the same numbers the same
-    way).  The master has the lowest total, ties to the lower request index.
-    scores: float32 [A][n] (no NaN).  Returns (master, totals float64 [A]).
+    of a2).  The pages fix no order of addition, so the oracle takes the sum
+    itself: the exact sum of the float32 scores, rounded once to float64
+    (math.fsum).  The master has the lowest total, ties to the lower request
+    index.  scores: float32 [A][n] (no NaN).  Returns (master, totals float64 [A]).
     """
     scores = np.asarray(scores, dtype=np.float32)
     if np.isnan(scores).any():
@@ -882,15 +881,8 @@ def select_master(scores: np.ndarray):
     A, n = scores.shape
     if A == 0:
         raise ValueError("empty group")
-    totals = np.zeros(A, dtype=np.float64)
-    for a in range(A):
-        total = 0.0
-        for j0 in range(0, n, 64):
-            block = 0.0
-            for j in range(j0, min(j0 + 64, n)):
-                block += float(scores[a, j])
-            total += block
-        totals[a] = total
+    totals = np.array([math.fsum(float(x) for x in scores[a]) for a in range(A)],
+                      dtype=np.float64)
     master = min(range(A), key=lambda a: (totals[a], a))
     return master, totals
 

@@ -153,6 +153,100 @@ def test_c2_shape_small_with_rank_state_and_clip(style):
     check_chain(cfg, case, g, style=name)
 
 
+def test_chain_with_weights_between_the_clip_limits():
+    """AKS weights each non-probe row by its own check-layer divergence,
+    clipped.  The residual is scaled down (mean offset N(0, 0.05), rank-4
+    component W ~ N(0, 0.05)) so that d falls below, between and above the
+    clip [1.3, 2] on both planes: the weight is neither constant nor
+    saturated, and the whole chain must still match the oracle."""
+    cfg = small_c2(mu_std=0.05, w_std=0.05, w_lo=1.3, w_hi=2.0)
+    case = correction_case(cfg)
+    g = gpu_chain(cfg, case)
+    check_chain(cfg, case, g)
+    for pi in range(2):
+        keep = ~K.mask_to_bool(g["mask"][pi, 0], cfg.n_tokens)
+        d = g["scores"][pi, 0][keep].astype(np.float64)
+        below, inside, above = np.mean(d < 1.3), np.mean((d > 1.3) & (d < 2.0)), np.mean(d > 2.0)
+        log("plane", pi, "non-probe weights below / inside / above the clip:", below, inside,
+            above)
+        assert below >= 0.03 and inside >= 1 / 3 and above >= 0.03, (below, inside, above)
+
+
+@pytest.mark.parametrize("dtype,rank,style", [("bf16", 4, "half"), ("bf16", 0, "half"),
+                                              ("bf16", 2, "interleaved"), ("f32", 4, "half")])
+def test_apply_weight_below_between_and_above_the_clip(dtype, rank, style):
+    """kvfix_apply with scores drawn uniformly in [-1, 3] against the clip
+    [0, 2] (and a few exactly at the limits), both planes, against the
+    oracle's apply given the same scores.  A kernel that ignored the scores
+    (w = 1) or always used w_hi would miss the bar by far (checked on the
+    oracle's side, so the test cannot pass that way)."""
+    cfg = small_c2(dtype=dtype, rank=rank, n_tokens=333, n_segs=2, b=40, per_segment_delta=True)
+    L, S, H, n, hd = cfg.n_layers, cfg.n_segs, cfg.n_kv_heads, cfg.n_tokens, cfg.head_dim
+    case = correction_case(cfg, style=style)
+    rng = np.random.default_rng(71 + rank)
+    scores = rng.uniform(-1.0, 3.0, (S, n)).astype(np.float32)
+    scores[0, :4] = [0.0, 2.0, 1.0, -0.0]
+    mu = rng.standard_normal((L, S, H, hd)).astype(np.float32)
+    idx = np.sort(np.stack([rng.choice(n, cfg.b, replace=False) for _ in range(S)]), axis=1)
+    mask = mask_from_idx(idx.astype(np.int32), n)
+    st = kv.ROPE_HALF if style == "half" else kv.ROPE_INTERLEAVED
+    delta = torch.tensor(case["deltas"], dtype=torch.int64, device=DEV)
+    for p in ("k", "v"):
+        reuse = from_np(case["reuse_" + p], DEV)
+        out = reuse.clone()
+        A = None if case["A_" + p] is None else torch.from_numpy(case["A_" + p]).to(DEV)
+        B = None if case["B_" + p] is None else torch.from_numpy(case["B_" + p]).to(DEV)
+        rope = (delta, cfg.theta) if p == "k" else (None, 0.0)
+        log("apply with clipped weights", dtype, rank, style, p)
+        kv.kvfix_apply(Plane.dense(reuse), Plane.dense(out), torch.from_numpy(mask.view(np.int32)).to(DEV),
+                       torch.from_numpy(mu).to(DEV), torch.from_numpy(scores).to(DEV), 0.0, 2.0,
+                       rope[0], rope[1], st, A, B)
+        torch.cuda.synchronize()
+        o_rope = (case["deltas"], cfg.theta) if p == "k" else (None, 0.0)
+        args = (case["A_" + p], case["B_" + p], o_rope[0], o_rope[1], style)
+        o = K.apply(case["reuse_" + p], dtype, mask, mu, scores, 0.0, 2.0, *args)
+        e = assert_values(to_np(out), o, dtype, f"clipped apply {p}")
+        log("max rel err", e)
+        for wrong in (None, np.full_like(scores, 2.0)):
+            o_wrong = K.apply(case["reuse_" + p], dtype, mask, mu, wrong, 0.0, 2.0, *args)
+            assert rel_err(o_wrong, o, dtype) > 10 * TOL[dtype]
+
+
+@pytest.mark.parametrize("style", ["half", None])
+def test_fit_mean_with_repeated_indices_out_of_place(style):
+    """A probe list that repeats rows (chunk ids listed twice, expanded to
+    tokens; the header allows repeats out of place): every occurrence is a
+    member of the mean, and the fresh rows land at their positions.  The
+    list is long enough to span several 256-probe slices of the fit, and its
+    repeats fall in different slices."""
+    cfg = small_c2(n_tokens=1000, n_segs=2, rank=4, per_segment_delta=True)
+    L, S, H, n, hd = cfg.n_layers, cfg.n_segs, cfg.n_kv_heads, cfg.n_tokens, cfg.head_dim
+    case = correction_case(cfg)
+    B = 64
+    ids = np.array([[7, 3, 7, 15, 3, 0, 7, 9, 15, 15], [2, 2, 2, 2, 11, 11, 14, 1, 2, 11]], np.int32)
+    idx, _, _ = K.expand_chunks(ids, n, B)            # 640 entries, -1 padding after chunk 15
+    b = idx.shape[1]
+    p = "k" if style else "v"
+    fresh, reuse = from_np(case["fresh_" + p], DEV), from_np(case["reuse_" + p], DEV)
+    out = torch.full_like(reuse, float("nan"))
+    mu = torch.full((L, S, H, hd), float("nan"), dtype=torch.float32, device=DEV)
+    A, Bm = torch.from_numpy(case["A_" + p]).to(DEV), torch.from_numpy(case["B_" + p]).to(DEV)
+    delta = torch.tensor(case["deltas"], dtype=torch.int64, device=DEV)
+    log("fit_mean with repeated indices", p, b)
+    kv.kvfix_fit_mean(Plane.dense(fresh), Plane.dense(reuse), Plane.dense(out),
+                      torch.from_numpy(idx).to(DEV), b, mu, delta if style else None, cfg.theta,
+                      kv.ROPE_HALF, A, Bm)
+    torch.cuda.synchronize()
+    rope = (case["deltas"], cfg.theta, "half") if style else (None, 0.0, "half")
+    o_mu = K.fit_mean(case["fresh_" + p], case["reuse_" + p], cfg.dtype, idx, rope[0], rope[1],
+                      rope[2], case["A_" + p], case["B_" + p])
+    assert rel_err(mu.cpu().numpy(), o_mu, "f32") <= 1e-5
+    g_out = to_np(out)
+    for s in range(S):
+        rows = np.unique(idx[s][idx[s] >= 0])
+        assert np.array_equal(g_out[:, s][:, :, rows], case["fresh_" + p][:, s][:, :, rows])
+
+
 @pytest.mark.parametrize("hd,dtype", [(64, "bf16"), (256, "bf16"), (128, "f32"), (256, "f32")])
 def test_head_dims_and_dtypes(hd, dtype):
     cfg = small_c2(head_dim=hd, dtype=dtype, n_tokens=77, n_segs=2, b=9, rank=3,

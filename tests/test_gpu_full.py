@@ -53,7 +53,7 @@ def test_c5_llama3_70b_paged_in_place_full_size():
     L, S, H, n, hd, ps, NP, b, c = (cfg.n_layers, cfg.n_segs, cfg.n_kv_heads, cfg.n_tokens,
                                     cfg.head_dim, cfg.page_size, cfg.n_pages, cfg.b,
                                     cfg.check_layer)
-    sample = [c, 40, L - 1]
+    sample = [0, c, 11, 25, 40, 53, 66, L - 1]          # eight layers, every segment and head
     deltas = [int(d) for d in draw_deltas(cfg).tolist()]
     neg = [-d for d in deltas]
     dev = "cuda"
@@ -158,7 +158,7 @@ def test_c4_qwen25_14b_draft_full_size():
                                 cfg.n_draft, cfg.n_tokens, cfg.head_dim, cfg.b)
     dev = "cuda"
     deltas = [int(d) for d in draw_deltas(cfg).tolist()]
-    sample = [0, 23, L - 1]
+    sample = [0, cfg.first_layer, 12, 23, 35, L - 1]          # six layers, every head
     reuse = {p: torch.empty(L, S, H, n, hd, dtype=torch.bfloat16, device=dev) for p in "kv"}
     fresh = {p: torch.empty(L, S, H, n, hd, dtype=torch.bfloat16, device=dev) for p in "kv"}
     log("c4 full: drawing 48 layers")
@@ -204,8 +204,7 @@ def test_c4_qwen25_14b_draft_full_size():
     assert e <= 1e-5
     i1, m1 = K.select_topb(g_scores, b)
     assert np.array_equal(g_idx, i1) and np.array_equal(g_mask, m1)
-    flips = check_selection(g_scores, o_scores, b, 1e-5)
-    log("c4 full: selection swaps within the error bound:", flips)
+    check_selection(g_scores, o_scores, b)
     del k_host
     for l in sample:
         for pi, p in enumerate("kv"):

@@ -2,9 +2,14 @@
 paged pool (TD §4.2 reuse plan output; TD Algorithm 1, the paged write
 through the slot mapping).
 
-Totals of the master selection are compared bit for bit (both sides add in
-fp64 in token order) and the master index exactly; the paged restore must
-equal the dense restore bit for bit."""
+The oracle's total is the exact sum of a request's scores (rounded once to
+fp64); the kernel adds in fp64 in a fixed order (64-token blocks in token
+order, then the block sums), so its totals must lie within that order's
+error bound of the exact sum, and the master index must be the oracle's
+unless the two totals are closer than their bounds (a near-tie).  The paged
+restore must equal the dense restore bit for bit."""
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -30,15 +35,49 @@ def gpu_master(sc: np.ndarray):
     return int(master.item()), totals.cpu().numpy()
 
 
+def total_bound(sc: np.ndarray) -> np.ndarray:
+    """Per request: how far a fixed-order fp64 sum of 64-token blocks, then
+    the block sums, may lie from the exact sum rounded once.  Recursive
+    summation of m terms errs by at most (m - 1) u sum|x| (u = 2^-53, to first
+    order); the two levels chain at most 63 + ceil(n/64) - 1 additions, and
+    the rounded exact sum adds one more u |s|; 1 % covers the second order."""
+    A, n = sc.shape
+    chain = 63 + max(-(-n // 64), 1)
+    u = 2.0 ** -53
+    return np.array([1.01 * (chain + 1) * u * math.fsum(abs(float(x)) for x in sc[a])
+                     for a in range(A)])
+
+
+def check_master(sc: np.ndarray, m: int, tot: np.ndarray):
+    om, otot = K.select_master(sc)
+    bound = total_bound(sc)
+    err = np.abs(tot - otot)
+    assert np.all(err <= bound), (err.max(), bound[np.argmax(err - bound)])
+    if m != om:
+        # a near-tie: the two exact totals are closer than the kernel's error
+        gap = otot[m] - otot[om]
+        log("master near-tie", m, om, gap, bound[m] + bound[om])
+        assert gap <= bound[m] + bound[om], (m, om, gap)
+    return om, otot
+
+
 @pytest.mark.parametrize("A,n", [(1, 100), (3, 1), (16, 8192), (40, 8193), (5, 0), (17, 333)])
 def test_select_master_matches_oracle(A, n):
     rng = np.random.default_rng(A * 1000 + n)
     sc = (np.exp(rng.standard_normal((A, n))) * 10.0 ** rng.integers(-3, 3, (A, 1))).astype(np.float32)
     log("select master", A, n)
     m, tot = gpu_master(sc)
-    om, otot = K.select_master(sc)
-    assert np.array_equal(tot.view(np.uint64), otot.view(np.uint64))
-    assert m == om
+    check_master(sc, m, tot)
+
+
+def test_select_master_totals_spanning_many_binades():
+    # scores over ~40 binades, so the order of addition changes the fp64 sum:
+    # the kernel's totals stay within the bound of the exact sums
+    rng = np.random.default_rng(77)
+    sc = np.exp(rng.standard_normal((24, 5000)) * 9.0).astype(np.float32)
+    log("select master, wide range")
+    m, tot = gpu_master(sc)
+    check_master(sc, m, tot)
 
 
 def test_select_master_ties_go_to_the_lower_index():
@@ -63,8 +102,7 @@ def test_select_master_on_collective_deviation_scores():
     torch.cuda.synchronize()
     g_sc = scores.cpu().numpy()
     m, tot = gpu_master(g_sc)
-    om, otot = K.select_master(g_sc)
-    assert m == om and np.array_equal(tot.view(np.uint64), otot.view(np.uint64))
+    check_master(g_sc, m, tot)
     planted = raw["planted"].numpy().sum(axis=1)
     assert planted[m] == planted.min(), (m, planted.tolist(), tot.tolist())
 

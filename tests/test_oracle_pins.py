@@ -9,6 +9,7 @@ import cmath
 import itertools
 import json
 import math
+from fractions import Fraction
 import os
 
 import numpy as np
@@ -926,11 +927,11 @@ def test_select_master_prefers_the_request_without_deviation():
     assert K.select_master(sc)[0] == 4
 
 
-def test_select_master_total_is_the_token_order_sum_of_the_l2_scores():
+def test_select_master_total_is_the_exact_sum_of_the_l2_scores():
     # the deviation of a request against the shared blocks: per-token L2
     # divergence of its keys from the shared keys re-aligned to its frame
     rng = np.random.default_rng(51)
-    A, H, n, hd = 4, 2, 64, 8
+    A, H, n, hd = 4, 2, 300, 8
     shared = K.store(rng.standard_normal((1, 1, H, n, hd)), "f32")
     agents = np.repeat(shared, A, axis=1).copy()
     planted = [5, 1, 3, 0]
@@ -941,9 +942,28 @@ def test_select_master_total_is_the_token_order_sum_of_the_l2_scores():
     m, tot = K.select_master(sc)
     assert m == 3 and tot[3] == 0.0
     assert np.argsort(tot, kind="stable").tolist() == np.argsort(planted, kind="stable").tolist()
-    # the total: 64-token block sums in token order, then the blocks in order
-    assert tot[0] == sum(sum(float(x) for x in sc[0][j:j + 64]) for j in range(0, n, 64))
-    assert abs(tot[0] - math.fsum(float(x) for x in sc[0])) <= 1e-12 * tot[0]
+    # the total is the sum itself: the exact rational sum of the float32
+    # scores, rounded once to float64 (Python's Fraction -> float rounds
+    # correctly), whatever order a machine adds them in
+    for a in range(A):
+        exact = float(sum((Fraction(float(x)) for x in sc[a]), Fraction(0)))
+        assert tot[a] == exact, a
+
+
+def test_select_master_total_does_not_depend_on_the_order_of_the_tokens():
+    # scores spanning 40 binades: a left-to-right float64 sum loses the small
+    # terms, the total does not; reversing or shuffling the tokens of a
+    # request leaves its total bit for bit unchanged
+    rng = np.random.default_rng(52)
+    sc = (np.exp(rng.standard_normal((3, 1000)) * 9.0)).astype(np.float32)
+    sc[0, 0] = np.float32(1e30)
+    _, tot = K.select_master(sc)
+    _, rev = K.select_master(sc[:, ::-1].copy())
+    _, shuf = K.select_master(sc[:, rng.permutation(1000)].copy())
+    assert np.array_equal(tot.view(np.uint64), rev.view(np.uint64))
+    assert np.array_equal(tot.view(np.uint64), shuf.view(np.uint64))
+    exact = float(sum((Fraction(float(x)) for x in sc[0]), Fraction(0)))
+    assert tot[0] == exact
 
 
 # ----------------------------------------------------------------------------
