@@ -11,6 +11,9 @@
 // constants live in LDS and registers for the whole chunk.  fit_mean gives
 // each block one whole unit and reduces in a fixed order (deterministic).
 #include <stdlib.h>
+
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -999,4 +1002,61 @@ extern "C" kvfix_status kvfix_apply(const kvfix_plane* reuse, const kvfix_plane*
                                     float w_hi, const float* mu, const kvfix_lowrank* lowrank,
                                     const kvfix_rope* rope, void* stream) {
   return kvfix_apply_ex(reuse, out, mask, scores, w_lo, w_hi, mu, lowrank, rope, nullptr, stream);
+}
+
+// ---------------------------------------------------------------------------
+// kvfix_fit_mean_noalloc: the fit with its slice partials in a file-scope
+// device array instead of a caller workspace, for callers that cannot
+// allocate.  Every GPU the library runs on holds its own copy of the array
+// (KVFIX_NOALLOC_SCRATCH_BYTES) until the process ends.  In host code the
+// array's name is only a stand-in: its device address is looked up once per
+// device (hipGetSymbolAddress, with that device current) and that address is
+// what the kernels receive.  Every call on a device shares its array, so
+// calls that overlap on one device race; nothing in it needs to start at
+// zero (each slice writes its own partial before the finisher reads it).
+// ---------------------------------------------------------------------------
+
+namespace kvfix {
+
+static __device__ __align__(256) unsigned char scratch[KVFIX_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+
+// Device address of this device's `scratch`, or nullptr on a HIP error.
+static void* scratch_address() {
+  static std::atomic<void*> addr[kMaxScratchDevices];
+  static std::mutex lock;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  std::lock_guard<std::mutex> guard(lock);
+  p = addr[dev].load(std::memory_order_relaxed);
+  if (p == nullptr) {
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr) return nullptr;
+    addr[dev].store(q, std::memory_order_release);
+    p = q;
+  }
+  return p;
+}
+
+}  // namespace kvfix
+
+extern "C" kvfix_status kvfix_fit_mean_noalloc(const kvfix_plane* fresh, int32_t fresh_by_slot,
+                                               const kvfix_plane* reuse, const kvfix_plane* out,
+                                               const int32_t* idx, int32_t b,
+                                               const kvfix_rope* rope,
+                                               const kvfix_lowrank* lowrank, float* mu,
+                                               void* stream) {
+  if (reuse == nullptr || b < 0) return KVFIX_ERR_ARG;
+  if (reuse->n_layers < 0 || reuse->n_segs < 0 || reuse->n_heads < 0 || reuse->head_dim < 0)
+    return KVFIX_ERR_ARG;
+  const size_t need = kvfix_fit_mean_workspace(reuse->n_layers, reuse->n_segs, reuse->n_heads,
+                                               reuse->head_dim, b);
+  if (need > (size_t)KVFIX_NOALLOC_SCRATCH_BYTES) return KVFIX_ERR_CAPACITY;
+  void* ws = scratch_address();
+  if (ws == nullptr) return KVFIX_ERR_HIP;
+  return kvfix_fit_mean_ex(fresh, fresh_by_slot, reuse, out, idx, b, rope, lowrank, nullptr, mu,
+                           ws, (size_t)KVFIX_NOALLOC_SCRATCH_BYTES, stream);
 }

@@ -25,7 +25,8 @@ EXPORTS = ("kvfix_rope_shift", "kvfix_score", "kvfix_score_draft_workspace", "kv
            "kvfix_select_grow", "kvfix_score_ex", "kvfix_fit_mean_ex", "kvfix_apply_ex",
            "kvfix_select_master", "kvfix_anchor_match_workspace", "kvfix_anchor_match",
            "kvfix_anchor_apply",
-           "kvfix_fit_mean_workspace", "kvfix_fit_mean", "kvfix_apply", "kvfix_diff_encode_workspace",
+           "kvfix_fit_mean_workspace", "kvfix_fit_mean", "kvfix_fit_mean_noalloc", "kvfix_apply",
+           "kvfix_diff_encode_workspace",
            "kvfix_diff_encode", "kvfix_diff_decode_workspace", "kvfix_diff_decode",
            "kvfix_status_string", "kvfix_version")
 
@@ -116,6 +117,7 @@ def lib() -> ctypes.CDLL:
             "kvfix_anchor_apply": [P, P, I32, P, P, I64, I64, ctypes.c_double, I32, P, P, P],
             "kvfix_fit_mean_workspace": [I32, I32, I32, I32, I32],
             "kvfix_fit_mean": [P, I32, P, P, P, I32, P, P, P, P, ctypes.c_size_t, P],
+            "kvfix_fit_mean_noalloc": [P, I32, P, P, P, I32, P, P, P, P],
             "kvfix_apply": [P, P, P, P, F, F, P, P, P, P],
             "kvfix_diff_encode_workspace": [I32, I32, I32, I32],
             "kvfix_diff_encode": [P, P, P, P, P, F, P, P, P, ctypes.c_size_t, P],
@@ -330,6 +332,26 @@ def kvfix_fit_mean(fresh: Plane, reuse: Plane, out: Optional[Plane], idx: torch.
             fresh.ref(), int(fresh_by_slot), reuse.ref(), out.ref() if out else None, _ptr(idx),
             b, rr, lrp, ctypes.byref(g), _ptr(mu), _ptr(ws), ws.numel() * ws.element_size(),
             _stream()))
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def kvfix_fit_mean_noalloc(fresh: Plane, reuse: Plane, out: Optional[Plane], idx: torch.Tensor,
+                           b: int, mu: torch.Tensor, delta: Optional[torch.Tensor] = None,
+                           theta: float = 0.0, style: int = ROPE_HALF, A=None, B=None,
+                           fresh_by_slot: bool = False) -> None:
+    """kvfix_fit_mean with the library's own per-device buffer instead of a
+    workspace (no allocation by the library or here)."""
+    rr = None
+    if delta is not None:
+        r, _ = make_rope(delta, theta, style)
+        rr = ctypes.byref(r)
+    lr = make_lowrank(A, B)
+    lrp = ctypes.byref(lr[0]) if lr else None
+    _check("kvfix_fit_mean_noalloc", lib().kvfix_fit_mean_noalloc(
+        fresh.ref(), int(fresh_by_slot), reuse.ref(), out.ref() if out else None, _ptr(idx), b,
+        rr, lrp, _ptr(mu), _stream()))
 
 
 def kvfix_apply(reuse: Plane, out: Plane, mask: Optional[torch.Tensor], mu: torch.Tensor,

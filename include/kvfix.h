@@ -68,7 +68,8 @@ typedef enum {
   KVFIX_OK = 0,
   KVFIX_ERR_ARG = 1,          /* null pointer, size or index out of range, shape mismatch */
   KVFIX_ERR_ALIGN = 2,        /* pointer or row stride not 16-byte aligned */
-  KVFIX_ERR_CAPACITY = 3,     /* diff encode listed more blocks than the diff can hold */
+  KVFIX_ERR_CAPACITY = 3,     /* diff encode listed more blocks than the diff can hold, or a
+                                 call needs more than a fixed library buffer holds */
   KVFIX_ERR_HIP = 4,          /* a HIP runtime or launch error */
   KVFIX_ERR_UNSUPPORTED = 5   /* dtype / head_dim / rank outside the compiled set */
 } kvfix_status;
@@ -288,6 +289,25 @@ kvfix_status kvfix_fit_mean(const kvfix_plane* fresh, int32_t fresh_by_slot,
                             const int32_t* idx, int32_t b, const kvfix_rope* rope,
                             const kvfix_lowrank* lowrank, float* mu, void* ws, size_t ws_bytes,
                             void* stream);
+
+/* kvfix_fit_mean without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The slice partials live in a fixed
+ * library array of KVFIX_NOALLOC_SCRATCH_BYTES per device, held by every GPU
+ * the library runs on until the process ends; the call allocates nothing
+ * (no hipMalloc / hipFree).  Same arguments, results and checks as
+ * kvfix_fit_mean; KVFIX_ERR_CAPACITY when kvfix_fit_mean_workspace(...)
+ * exceeds the array (64 MiB: at head_dim 128, b <= 512 for 80 layers x 32
+ * segments x 8 heads, b <= 61 184 for 32 layers x 8 heads).  Calls
+ * share their device's array: two calls that overlap on one device (other
+ * streams, other threads) race and give undefined means.  The array's
+ * address is looked up on a device's first call (KVFIX_ERR_HIP if that
+ * fails). */
+#define KVFIX_NOALLOC_SCRATCH_BYTES (64u << 20)
+kvfix_status kvfix_fit_mean_noalloc(const kvfix_plane* fresh, int32_t fresh_by_slot,
+                                    const kvfix_plane* reuse, const kvfix_plane* out,
+                                    const int32_t* idx, int32_t b, const kvfix_rope* rope,
+                                    const kvfix_lowrank* lowrank, float* mu, void* stream);
 
 /* ---------------------------------------------------------------------------
  * a6. Fused apply.  For every token j whose mask bit is clear:
