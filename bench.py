@@ -134,6 +134,45 @@ def timed_oracle(fn, repeats):
     return sorted(times)[len(times) // 2]
 
 
+def host_info():
+    """The host the oracle ran on: CPU model, logical CPUs, CPUs this process may use."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        aff = None
+    return {"cpu_model": model, "nproc": os.cpu_count(), "affinity_cpus": aff}
+
+
+def widen(np, a, dtype):
+    """Plane values as float64 (bf16 bit patterns widened exactly)."""
+    if dtype == "bf16":
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def max_rel_err(np, g, o, dtype="f32"):
+    """max |g - o| / (|o| + 1e-3): the parity metric of the tests."""
+    gv, ov = widen(np, g, dtype), widen(np, o, dtype)
+    return float(np.max(np.abs(gv - ov) / (np.abs(ov) + 1e-3))) if gv.size else 0.0
+
+
+def index_mismatches(np, g, o):
+    """Indices in one selection and not the other, summed over rows."""
+    return int(sum(len(set(a.tolist()) ^ set(b.tolist())) for a, b in zip(g, o)))
+
+
+PARITY_BAR = {"bf16 values": 8e-3, "fp32 values and means": 1e-5, "indices and masks": "exact"}
+
+
 class Workload:
     ALL = {}
     kernel_tag = "apply"
@@ -147,7 +186,10 @@ class Workload:
 
     def __init__(self, cfg, torch, kv):
         self.cfg, self.torch, self.kv = cfg, torch, kv
-        self.timed = Timed(torch)
+        self.timed = Timed(torch)              # the roofline kernel's launches
+        self.timed_v = Timed(torch)            # the value-plane apply, where there is one
+        self.extra_timed = {}
+        self.parity = None
 
 
 # ----------------------------------------------------------------------------
@@ -206,7 +248,7 @@ class Correction(Workload):
                 main.wait_event(self.ev_join)
             d = t["delta"] if p == "k" else None
             sc = t["scores"][i] if c.weight == "clip" else None
-            with self.timed:
+            with (self.timed if p == "k" else self.timed_v):
                 kv.kvfix_apply(self.reuse_planes[p], self.out_planes[p], t["mask"][i], t["mu"][i],
                                sc, c.w_lo, c.w_hi, d, c.theta, A=t["A_" + p], B=t["B_" + p])
 
@@ -261,12 +303,14 @@ class C2(Correction):
 
     def cpu_baseline(self, np):
         """The oracle (as it stands, one thread) on the same input bytes: the
-        whole step over all 32 layers, median of 3 runs."""
+        whole step over all 32 layers, median of 3 runs.  Its results are
+        compared with the GPU's last step (parity)."""
         torch, c, t = self.torch, self.cfg, self.t
         from oracle import kvref as K
         data = {k: host(t[k], torch, np) for k in ("reuse_k", "reuse_v", "fresh_k", "fresh_v",
                                                    "A_k", "B_k", "A_v", "B_v")}
         deltas = [int(v) for v in t["delta"].tolist()]
+        box = {}
 
         def run():
             ck = c.check_layer
@@ -274,11 +318,25 @@ class C2(Correction):
             sv = K.score_l2(data["fresh_v"], data["reuse_v"], "bf16", ck)
             for p, s in (("k", sk), ("v", sv)):
                 idx, mask = K.select_topb(s, c.b)
-                K.correct(data["fresh_" + p], data["reuse_" + p], "bf16", idx, mask, s, c.w_lo,
-                          c.w_hi, data["A_" + p], data["B_" + p],
-                          deltas if p == "k" else None, c.theta)
+                out, mu = K.correct(data["fresh_" + p], data["reuse_" + p], "bf16", idx, mask, s,
+                                    c.w_lo, c.w_hi, data["A_" + p], data["B_" + p],
+                                    deltas if p == "k" else None, c.theta)
+                box[p] = (s, idx, mask, out, mu)
 
         dt = timed_oracle(run, 3)
+        par = {"scope": f"the whole step, all {c.n_layers} layers, both planes, against the "
+                        "GPU's last timed step", "bar": PARITY_BAR, "max_rel_err": {},
+               "index_mismatches": {}, "mask_word_mismatches": {}}
+        for i, p in enumerate("kv"):
+            s, idx, mask, out, mu = box[p]
+            par["max_rel_err"]["scores_" + p] = max_rel_err(np, host(t["scores"][i], torch, np), s)
+            par["max_rel_err"]["mu_" + p] = max_rel_err(np, host(t["mu"][i], torch, np), mu)
+            par["max_rel_err"]["out_" + p] = max_rel_err(np, host(t["out_" + p], torch, np), out,
+                                                         "bf16")
+            par["index_mismatches"][p] = index_mismatches(np, host(t["idx"][i], torch, np), idx)
+            par["mask_word_mismatches"][p] = int(np.sum(
+                host(t["mask"][i], torch, np).view(np.uint32) != mask))
+        self.parity = par
         nbytes = self.alg_bytes()["total"]
         return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
                 "sample": f"the whole step on all {c.n_layers} layers of the same input bytes "
@@ -346,7 +404,10 @@ class C5(Correction):
 
     def cpu_baseline(self, np):
         """The oracle on a bounded sample: scores at the check layer for all 32
-        segments, selection, and fit + apply of K and V on layers 0 and 1."""
+        segments, selection, and fit + apply of K and V on layers 0 and 1.
+        The step corrects the pool in place, so parity takes layers 0-1 of
+        the pool before and after one more GPU step and runs the oracle on
+        the former."""
         torch, c, t = self.torch, self.cfg, self.t
         from oracle import kvref as K
         L2 = 2
@@ -364,8 +425,14 @@ class C5(Correction):
             data["fcheck_" + p] = host(t["fcheck_" + p], torch, np)
             data["A_" + p] = host(t["A_" + p][:L2], torch, np)
             data["B_" + p] = host(t["B_" + p][:L2], torch, np)
+        self.step()                                   # one more step: the pool after it
+        torch.cuda.synchronize()
+        after = {p: host(logical(t["pool_" + p]), torch, np) for p in "kv"}
+        g_idx = host(t["idx"], torch, np)
+        g_mask = host(t["mask"], torch, np).view(np.uint32)
         deltas = [int(v) for v in t["delta"].tolist()]
         ck = c.check_layer
+        box = {}
 
         def run():
             for p in "kv":
@@ -373,10 +440,22 @@ class C5(Correction):
                 s = K.score_l2(data["fcheck_" + p], data["reuse_" + p][ck:ck + 1], "bf16", 0, d,
                                c.theta)
                 idx, mask = K.select_topb(s, c.b)
-                K.correct(data["fslot_" + p], data["reuse_" + p], "bf16", idx, mask, None, 0.0,
-                          1.0, data["A_" + p], data["B_" + p], d, c.theta, "half", True)
+                out, _ = K.correct(data["fslot_" + p], data["reuse_" + p], "bf16", idx, mask,
+                                   None, 0.0, 1.0, data["A_" + p], data["B_" + p], d, c.theta,
+                                   "half", True)
+                box[p] = (idx, mask, out)
 
         dt = timed_oracle(run, 1)
+        par = {"scope": f"selection of all {S} segments and corrected layers 0-1 (2 of "
+                        f"{c.n_layers}) of the in-place pool, one GPU step against the oracle on "
+                        "the same pool bytes", "bar": PARITY_BAR, "max_rel_err": {},
+               "index_mismatches": {}, "mask_word_mismatches": {}}
+        for i, p in enumerate("kv"):
+            idx, mask, out = box[p]
+            par["max_rel_err"]["out_" + p + " layers 0-1"] = max_rel_err(np, after[p], out, "bf16")
+            par["index_mismatches"][p] = index_mismatches(np, g_idx[i], idx)
+            par["mask_word_mismatches"][p] = int(np.sum(g_mask[i] != mask))
+        self.parity = par
         sub = c.replace(n_layers=L2)
         ab = Correction.alg_bytes(type("X", (), {"cfg": sub})())
         nbytes = ab["total"]
@@ -415,8 +494,9 @@ class C4(Workload):
         return -(-self.cfg.n_tokens // self.CHUNK)
 
     def chunk_budget(self):
-        from oracle import kvref as K
-        return K.chunk_budget(self.cfg.n_tokens, self.CHUNK, *self.RHO, "alg1")
+        """Chunks repaired (BCR App. B Algorithm 1), from the library's own rule."""
+        return self.kv.kvfix_chunk_budget(self.cfg.n_tokens, self.CHUNK, *self.RHO,
+                                          self.kv.BUDGET_SKIP)
 
     def probe_rows(self):
         """Probe rows per segment of the layout (whole chunks: c * 64 here,
@@ -533,7 +613,7 @@ class C4(Workload):
             if p == "v":
                 main.wait_event(self.ev_join)
             d = t["delta"] if p == "k" else None
-            with self.timed:
+            with (self.timed if p == "k" else self.timed_v):
                 kv.kvfix_apply(P["reuse_" + p], P["out_" + p], t["mask"], t["mu"][i], None, 0.0,
                                1.0, d, c.theta)
 
@@ -558,15 +638,37 @@ class C4(Workload):
                 idx, mask = K.select_grow(s, c.b, self.TAU)
             else:
                 ks = K.chunk_means(s, self.CHUNK) if self.layout == "chunk" else keys
-                idx, _, mask = K.expand_chunks(K.select_topb(ks, self.chunk_budget())[0],
-                                               c.n_tokens, self.CHUNK)
+                nch = K.chunk_budget(c.n_tokens, self.CHUNK, *self.RHO, "alg1")
+                idx, _, mask = K.expand_chunks(K.select_topb(ks, nch)[0], c.n_tokens, self.CHUNK)
             for p in "kv":
                 K.correct(data["fresh_" + p], data["reuse_" + p], "bf16", idx, mask, None, 0.0,
                           1.0, None, None, deltas if p == "k" else None, c.theta)
 
         dt = timed_oracle(run, 1)
+        # parity: the GPU's selection of its own scores (the sample's draft
+        # mass covers layers 1-3 only, so its selection is not the step's),
+        # and layers 0-3 of the step's corrected planes against the oracle
+        # run on the GPU's probe set
+        g_idx = host(t["idx"], torch, np)
+        g_mask = host(t["mask"], torch, np).view(np.uint32)
+        par = {"scope": "the GPU's probe selection on its own draft scores, and corrected "
+                        f"layers 0-3 (4 of {c.n_layers}) of both planes with that selection",
+               "bar": PARITY_BAR, "max_rel_err": {}, "index_mismatches": {}}
+        if self.layout in ("rows", "grow"):
+            g_sc = host(t["scores"], torch, np)
+            o_idx, _ = (K.select_topb(g_sc, c.b) if self.layout == "rows"
+                        else K.select_grow(g_sc, c.b, self.TAU))
+            par["index_mismatches"]["selection on the GPU scores"] = index_mismatches(
+                np, g_idx, o_idx)
+        for i, p in enumerate("kv"):
+            out, mu = K.correct(data["fresh_" + p], data["reuse_" + p], "bf16", g_idx, g_mask,
+                                None, 0.0, 1.0, None, None, deltas if p == "k" else None, c.theta)
+            par["max_rel_err"]["mu_" + p] = max_rel_err(np, host(t["mu"][i][:L4], torch, np), mu)
+            par["max_rel_err"]["out_" + p] = max_rel_err(np, host(t["out_" + p][:L4], torch, np),
+                                                         out, "bf16")
+        self.parity = par
         sub = C4.__new__(C4)
-        sub.cfg, sub.layout = c.replace(n_layers=L4), self.layout
+        sub.cfg, sub.layout, sub.kv = c.replace(n_layers=L4), self.layout, self.kv
         nbytes = sub.alg_bytes()["total"]
         draft = "no draft; " if self.layout == "coin" else "draft mass over layers 1-3; "
         return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
@@ -682,6 +784,24 @@ class C3(Workload):
             kv.kvfix_diff_decode(P["m_k"], P["m_v"], self.diff, t["from_m"], c.theta, P["o_k"],
                                  P["o_v"], t["ws_d"])
 
+    def storage_report(self):
+        """The group's storage under the master-mirror layout, from the blocks
+        the encode listed (TD §6.4): every mirror's compression R = full
+        cache / its diff, and the round's full caches over master + diffs."""
+        np_ = __import__("numpy")
+        c = self.cfg
+        A, L = c.n_segs, c.n_layers
+        nb = -(-c.n_tokens // c.block_tokens)
+        off = host(self.diff.offsets, self.torch, np_)
+        per_agent = np_.array([off[(a + 1) * L] - off[a * L] for a in range(A)], dtype=np_.float64)
+        full_blocks = L * nb                     # one cache, in blocks (K and V alike)
+        return {"diff_blocks_listed": int(off[-1]),
+                "mirror_compression_mean": round(float(np_.mean(full_blocks / per_agent)), 2),
+                "mirror_compression_min_max": [round(float(full_blocks / per_agent.max()), 2),
+                                               round(float(full_blocks / per_agent.min()), 2)],
+                "group_full_over_master_plus_diffs": round(
+                    float(A * full_blocks / (full_blocks + per_agent.sum())), 2)}
+
     def cpu_baseline(self, np):
         """The oracle on a bounded sample: encode and restore of layer 0 for all
         16 agents."""
@@ -702,10 +822,36 @@ class C3(Workload):
                 K.select_master(dev)
             o = K.diff_encode(d["m_k"], d["m_v"], d["s_k"], d["s_v"], [-x for x in offs],
                               c.theta, c.eps, c.block_tokens)
-            K.diff_decode(d["m_k"], d["m_v"], o, offs, c.theta, c.n_segs, c.block_tokens)
+            ok, ov = K.diff_decode(d["m_k"], d["m_v"], o, offs, c.theta, c.n_segs, c.block_tokens)
             box["total"] = o["total"]
+            box["o"], box["ok"], box["ov"] = o, ok, ov
 
         dt = timed_oracle(run, 1)
+        # parity on layer 0: the listed blocks (bit-exact), their packed values
+        # and the restored caches against the oracle's encode and decode
+        A, L = c.n_segs, c.n_layers
+        o = box["o"]
+        g_mask = host(self.diff.mask, torch, np).view(np.uint32)
+        g_off = host(self.diff.offsets, torch, np)
+        slots = np.concatenate([np.arange(g_off[a * L], g_off[a * L + 1]) for a in range(A)])
+        par = {"scope": f"layer 0 (1 of {L}) of all {A} agents: the listed blocks, the packed "
+                        "values and the restored caches", "bar": PARITY_BAR, "max_rel_err": {},
+               "mismatches": {}}
+        par["mismatches"]["block mask words"] = int(np.sum(g_mask[:, 0:1] != o["mask"]))
+        g_bi = host(self.diff.block_idx, torch, np)[slots]
+        par["mismatches"]["block indices"] = (int(np.sum(g_bi != o["block_idx"]))
+                                              if len(g_bi) == len(o["block_idx"]) else -1)
+        if len(g_bi) == len(o["block_idx"]):
+            par["max_rel_err"]["packed K"] = max_rel_err(
+                np, host(self.diff.vals_k, torch, np)[slots], o["vals_k"], "bf16")
+            par["mismatches"]["packed V elements"] = int(np.sum(
+                host(self.diff.vals_v, torch, np)[slots] != o["vals_v"]))
+        if self.layout != "paged":
+            par["max_rel_err"]["restored K"] = max_rel_err(np, host(t["o_k"][:1], torch, np),
+                                                           box["ok"], "bf16")
+            par["mismatches"]["restored V elements"] = int(np.sum(
+                host(t["o_v"][:1], torch, np) != box["ov"]))
+        self.parity = par
         sub = C3.__new__(C3)
         sub.cfg, sub.total, sub.layout = c.replace(n_layers=1), box["total"], self.layout
         nbytes = sub.alg_bytes()["total"]
@@ -898,6 +1044,7 @@ def main():
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
     w.timed.on = True
+    w.timed_v.on = True
     for tm in w.extra_timed.values():
         tm.on = True
     torch.cuda.synchronize()
@@ -932,6 +1079,7 @@ def main():
             "alg_bytes_per_step": ab["total"],
             "copy_ceiling_GBs": round(copy_gbs, 1),
             "pct_copy_ceiling": round(100 * gbs / copy_gbs, 2),
+            "seed": c.seed,
         },
         "roofline": {
             "bound": bound,
@@ -949,10 +1097,21 @@ def main():
     }
     for label, tm in w.extra_timed.items():
         line["config"][f"avg_ms {label}"] = round(tm.avg_ms(), 5)
+    if w.timed_v.pairs:
+        # the value-plane apply, timed apart from the roofline (key-plane) kernel
+        v_ms = w.timed_v.avg_ms()
+        line["config"]["avg_ms apply_kernel value plane"] = round(v_ms, 5)
+        line["config"]["value plane apply GB/s"] = round(
+            ab["roofline_per_launch"] / (v_ms * 1e-3) / 1e9, 2)
     if hasattr(w, "mfma_flops"):
         line["config"]["mfma_TFLOPs"] = round(w.mfma_flops() / (ms * 1e-3) / 1e12, 1)
+    if hasattr(w, "storage_report"):
+        line["config"].update(w.storage_report())
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = w.cpu_baseline(np)
+        cb = w.cpu_baseline(np)
+        cb.update(host_info())
+        line["cpu_baseline"] = cb
+        line["parity"] = w.parity
     print(json.dumps(line), flush=True)
 
 
