@@ -159,6 +159,46 @@ __device__ __forceinline__ void rotate_lane(float* x, const float* tc, const flo
   }
 }
 
+// The same rotation, negated: -(rotated x), bit for bit (the sign goes on the
+// table operands, and round-to-nearest-even is symmetric).
+template <int STYLE>
+__device__ __forceinline__ void rotate_lane_neg(float* x, const float* tc, const float* ts,
+                                                int g) {
+  if (STYLE == kStyleHalf) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int q = 16 * g + e;
+      const float a = x[e], b = x[16 + e], c = tc[q], s = ts[q];
+      x[e] = fmaf(a, -c, b * s);
+      x[16 + e] = fmaf(b, -c, -(a * s));
+    }
+  } else {
+#pragma unroll
+    for (int part = 0; part < 2; ++part) {
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        const int q = 32 * part + 8 * g + e / 2;
+        const float a = x[16 * part + e], b = x[16 * part + e + 1], c = tc[q], s = ts[q];
+        x[16 * part + e] = fmaf(a, -c, b * s);
+        x[16 * part + e + 1] = fmaf(b, -c, -(a * s));
+      }
+    }
+  }
+}
+
+// x + (x of lane ^ 16), then + (that of lane ^ 32): the sum over a token
+// column's four lane groups, in the same order in every lane.  The swaps run
+// on the vector ALU (no LDS round trip); each lane adds its own value and its
+// partner's, and addition commutes, so both lanes of a pair get the same bits.
+__device__ __forceinline__ float sum_lane_groups(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
 // ----------------------------------------------------------------------------
 // match: token weights and gate partial sums
 // ----------------------------------------------------------------------------
@@ -175,7 +215,7 @@ struct MatchParams {
   int32_t n_list[2];               // anchors computed per plane, in order,
   uint64_t list[2];                // 4 bits per anchor id
   float* part1;      // [L][2][V][H][n] per-head sums of |source - A_v B_v|
-  float* part2;      // [L][V][H][n] per-head sums of squares (value plane)
+  double* gpart;     // [L][n_tiles][H][V] the gate prefix's squared sums per block
 };
 
 // One block = 128 tokens (4 waves x 2 bands of 16) of one (layer, plane,
@@ -190,9 +230,24 @@ struct MatchParams {
 // the end so every load is unconditional); absolute values (and squares on
 // the value plane) are summed per lane, added across the four lane groups of
 // a token column in a fixed order, and written as the head's sums.
+// Sum over the 16 lanes of a lane group, by DPP within rows of 16: lanes
+// i ^ 1, i ^ 2, then the row rotated by 4 and by 8.  Lane 16 g holds its
+// group's total (the order is fixed).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float sum_row16(float x) {
+  x += dpp_f32<0xb1>(x);       // quad_perm [1, 0, 3, 2]
+  x += dpp_f32<0x4e>(x);       // quad_perm [2, 3, 0, 1]
+  x += dpp_f32<0x124>(x);      // row_ror 4
+  x += dpp_f32<0x128>(x);      // row_ror 8
+  return x;
+}
+
 template <int STYLE, bool GATE>
 __device__ __forceinline__ void match_body(const MatchParams& P, int l, int h, int tile,
-                                           bf16_t* sbt, float* tc, float* ts) {
+                                           bf16_t* sbt, float* tc, float* ts, float* gw) {
   constexpr int p = GATE ? 1 : 0;
   if (STYLE != kStyleNone) rope_table<kHD, float>(P.rope, -P.src_off, tc, ts);
   __syncthreads();
@@ -201,19 +256,29 @@ __device__ __forceinline__ void match_body(const MatchParams& P, int l, int h, i
   const int j0 = tile * kMatchTokens, jw = j0 + wave * kMatchBands * 16;
   const int lim = GATE ? max(P.cover, P.k_gate) : P.cover;
   const int nl = P.n_list[p];
-  if (j0 >= lim || nl == 0) return;          // block-uniform: no barrier follows
   const uint64_t list = P.list[p];
   const int V = P.V, H = P.H, n = P.n;
+  double* gpart = P.gpart + (((int64_t)l * P.n_tiles + tile) * H + h) * V;
+  if (j0 >= lim || nl == 0) {                 // block-uniform: no barrier follows
+    if (GATE && tid < V) gpart[tid] = 0.0;    // no prefix rows here
+    return;
+  }
 
   float nx[kMatchBands][32];
 #pragma unroll
   for (int b = 0; b < kMatchBands; ++b) {
     vu4 xr[4];
     load_lane_raw(P.src[p], l, P.seg, h, jw + 16 * b + t, n, g, xr);
-    unpack_lane(xr, nx[b]);
-    if (STYLE != kStyleNone) rotate_lane<STYLE>(nx[b], tc, ts, g);
+    if (STYLE != kStyleNone) {
+      unpack_lane(xr, nx[b]);
+      rotate_lane_neg<STYLE>(nx[b], tc, ts, g);
+    } else {
 #pragma unroll
-    for (int e = 0; e < 32; ++e) nx[b][e] = -nx[b][e];
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) xr[q][w] ^= 0x80008000u;     // both halves negated
+      unpack_lane(xr, nx[b]);
+    }
   }
 
   auto anchor = [&](int i) { return (int)((list >> (4 * min(i, nl - 1))) & 15u); };
@@ -230,46 +295,62 @@ __device__ __forceinline__ void match_body(const MatchParams& P, int l, int h, i
       *reinterpret_cast<vu4*>(buf + slice_chunk(c, q, m)) = r[k2];
     }
   };
+  // Rows are clamped to the slab's last row, so every load stays inside the
+  // pool; a row an anchor does not store only feeds a sum that no later step
+  // reads (tokens past its length never use that anchor).
+  const int last = (int)P.G.n_max - 1;        // a listed anchor stores >= 1 row
   auto load_a = [&](int v, bf16x8* a) {
-    const int last = P.G.len[v] - 1;          // a listed anchor stores >= 1 row
 #pragma unroll
     for (int b = 0; b < kMatchBands; ++b)
       a[b] = ld_op(a_row(P.G, v, l, p, min(jw + 16 * b + t, last)) + 8 * g);
   };
-  auto compute = [&](const bf16_t* buf, const bf16x8* a, int v) {
+  auto compute = [&](const bf16_t* buf, const bf16x8* a, int i) {
+    const int v = anchor(i);
     bf16x8 bop[kTiles];
 #pragma unroll
     for (int c = 0; c < kTiles; ++c)
       bop[c] = *reinterpret_cast<const bf16x8*>(buf + slice_chunk(c, g, t));
     float* o1 = P.part1 + ((((int64_t)l * 2 + p) * V + v) * H + h) * n;
-    float* o2 = P.part2 + (((int64_t)l * V + v) * H + h) * n;
+    // Both bands' products of a tile are issued before either is summed, so
+    // one band's sums cover the other band's MFMA latency.  Per band the
+    // sums still run over the tiles in order.
+    float s1[kMatchBands][4], s2[kMatchBands][4];
 #pragma unroll
-    for (int b = 0; b < kMatchBands; ++b) {
-      float s1[4] = {0, 0, 0, 0}, s2[4] = {0, 0, 0, 0};
+    for (int b = 0; b < kMatchBands; ++b)
 #pragma unroll
-      for (int c = 0; c < kTiles; ++c) {
+      for (int e = 0; e < 4; ++e) s1[b][e] = s2[b][e] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < kTiles; ++c) {
+      f32x4 d[kMatchBands];
+#pragma unroll
+      for (int b = 0; b < kMatchBands; ++b) {
         const f32x4 cx = {nx[b][4 * c], nx[b][4 * c + 1], nx[b][4 * c + 2], nx[b][4 * c + 3]};
-        const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bop[c], a[b], cx, 0, 0, 0);
+        d[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bop[c], a[b], cx, 0, 0, 0);
+      }
+#pragma unroll
+      for (int b = 0; b < kMatchBands; ++b)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          s1[e] += fabsf(d[e]);
-          if (GATE) s2[e] = fmaf(d[e], d[e], s2[e]);
+          s1[b][e] += fabsf(d[b][e]);
+          if (GATE) s2[b][e] = fmaf(d[b][e], d[b][e], s2[b][e]);
         }
-      }
-      float c1 = (s1[0] + s1[1]) + (s1[2] + s1[3]);
-      c1 += __shfl_xor(c1, 16);
-      c1 += __shfl_xor(c1, 32);
-      float c2 = 0.0f;
-      if (GATE) {
-        c2 = (s2[0] + s2[1]) + (s2[2] + s2[3]);
-        c2 += __shfl_xor(c2, 16);
-        c2 += __shfl_xor(c2, 32);
-      }
+    }
+    // the wave's squared sums over its prefix rows (bands in order, then
+    // the 16 token columns), kept in LDS until the block adds its waves
+    float q = 0.0f;
+#pragma unroll
+    for (int b = 0; b < kMatchBands; ++b) {
+      const float c1 = sum_lane_groups((s1[b][0] + s1[b][1]) + (s1[b][2] + s1[b][3]));
       const int j = jw + 16 * b + t;
-      if (g == 0 && j < n) {
-        o1[j] = c1;
-        if (GATE) o2[j] = c2;
+      if (GATE) {
+        const float c2 = sum_lane_groups((s2[b][0] + s2[b][1]) + (s2[b][2] + s2[b][3]));
+        q += j < P.k_gate ? c2 : 0.0f;
       }
+      if (g == 0 && j < n) o1[j] = c1;
+    }
+    if (GATE) {
+      q = sum_row16(q);
+      if (lane == 0) gw[i * kMatchWaves + wave] = q;
     }
   };
 
@@ -282,14 +363,23 @@ __device__ __forceinline__ void match_body(const MatchParams& P, int l, int h, i
   for (int i = 0; i < nl; i += 2) {
     stage_load(anchor(i + 1), sr);
     load_a(anchor(i + 1), a1);
-    compute(sbt, a0, anchor(i));
+    compute(sbt, a0, i);
     stage_store(sr, sbt + kSlice);
     __syncthreads();
     stage_load(anchor(i + 2), sr);
     load_a(anchor(i + 2), a0);
-    if (i + 1 < nl) compute(sbt + kSlice, a1, anchor(i + 1));
+    if (i + 1 < nl) compute(sbt + kSlice, a1, i + 1);
     stage_store(sr, sbt);
     __syncthreads();
+  }
+  // (the loop's last barrier orders the waves' partials before this)
+  if (GATE && tid < V) {
+    double d = 0.0;                   // 0 for anchors outside the gate set
+    if ((P.gate_set >> tid) & 1u)     // (all listed: the prefix is not empty)
+      for (int i = 0; i < nl; ++i)
+        if (anchor(i) == tid)
+          for (int w = 0; w < kMatchWaves; ++w) d += (double)gw[i * kMatchWaves + w];
+    gpart[tid] = d;
   }
 }
 
@@ -298,6 +388,7 @@ __global__ __launch_bounds__(kMatchWaves * 64) __attribute__((amdgpu_waves_per_e
 void anchor_match_kernel(MatchParams P) {
   __shared__ __attribute__((aligned(16))) bf16_t sbt[2 * kSlice];
   __shared__ float tc[kHD / 2], ts[kHD / 2];
+  __shared__ float gw[kAnchorMax * kMatchWaves];
   const int id = blockIdx.x, xcd = id % kXcds, k = id / kXcds;
   const int h = k % P.H, k2 = k / P.H;
   const int tile = k2 % P.n_tiles;
@@ -305,90 +396,73 @@ void anchor_match_kernel(MatchParams P) {
   if (pair >= P.n_pairs) return;
   const int l = pair >> 1;
   if ((pair & 1) == 0)
-    match_body<STYLE, false>(P, l, h, tile, sbt, tc, ts);
+    match_body<STYLE, false>(P, l, h, tile, sbt, tc, ts, gw);
   else
-    match_body<kStyleNone, true>(P, l, h, tile, sbt, tc, ts);
+    match_body<kStyleNone, true>(P, l, h, tile, sbt, tc, ts, gw);
 }
 
 // Per token: the head sums added in head order give the distance sums;
-// weights = softmax over E of minus the mean absolute distance (T = 1); on
-// the value plane the squared sums of the gate prefix are added per block in
-// fp64 in a fixed order (token tree inside a wave, then waves).
+// weights = softmax over E of minus the mean absolute distance (T = 1).
 constexpr int kFinishTokens = 256;
+
+static_assert(kFinishTokens == 2 * kMatchTokens, "a finish block covers two match tiles");
 
 struct FinishParams {
   const float* part1;
-  const float* part2;
   int32_t n, H, V;
-  uint32_t elig, gate_set;
-  int32_t cover, k_gate;
-  int32_t n_tiles;                 // token tiles of kFinishTokens
+  uint32_t elig;
+  int32_t cover;
   float D;                         // features per token row (all heads)
   float* w;                        // [L][2][V][n]
-  double* gpart;                   // [L][n_tiles][V]
+  const double* gpart;             // [L][n_match_tiles][H][V] from the match
+  int32_t n_match_tiles, n_tiles;
+  double* gsum;                    // [L][n_tiles][V]
 };
 
+// On the value plane a block also adds the gate partials of its two match
+// tiles, tile by tile and head by head, into one partial per anchor.
 __global__ __launch_bounds__(kFinishTokens) void anchor_finish_kernel(FinishParams P) {
-  __shared__ double gsum[kFinishTokens / 64][kAnchorMax];
   const int tile = blockIdx.x, p = blockIdx.y & 1, l = blockIdx.y >> 1;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int j = tile * kFinishTokens + tid;
+  const int j = tile * kFinishTokens + threadIdx.x;
   const int V = P.V, H = P.H, n = P.n;
+  if (p == 1 && (int)threadIdx.x < V) {
+    double d = 0.0;
+    for (int tt = 2 * tile; tt < min(2 * tile + 2, P.n_match_tiles); ++tt)
+      for (int hh = 0; hh < H; ++hh)
+        d += P.gpart[(((int64_t)l * P.n_match_tiles + tt) * H + hh) * V + threadIdx.x];
+    P.gsum[((int64_t)l * P.n_tiles + tile) * V + threadIdx.x] = d;
+  }
+  if (j >= n) return;
+  float* wr = P.w + ((int64_t)l * 2 + p) * V * n + j;
+  if (j >= P.cover) {
+    for (int v = 0; v < V; ++v) wr[(int64_t)v * n] = 0.0f;
+    return;
+  }
   // Sums over heads, head by head (fixed order); the anchors' loads of one
   // head are independent and issued together.
-  auto head_sums = [&](const float* base, uint32_t set, bool rows, float* s) {
+  const float* base = P.part1 + ((int64_t)l * 2 + p) * V * H * n;
+  float s[kAnchorMax];
 #pragma unroll
-    for (int v = 0; v < kAnchorMax; ++v) s[v] = 0.0f;
-    if (!rows) return;
-    for (int hh = 0; hh < H; ++hh) {
-      float x[kAnchorMax];
+  for (int v = 0; v < kAnchorMax; ++v) s[v] = 0.0f;
+  for (int hh = 0; hh < H; ++hh) {
+    float x[kAnchorMax];
 #pragma unroll
-      for (int v = 0; v < kAnchorMax; ++v)
-        x[v] = (v < V && ((set >> v) & 1u)) ? base[((int64_t)v * H + hh) * n + j] : 0.0f;
+    for (int v = 0; v < kAnchorMax; ++v)
+      x[v] = (v < V && ((P.elig >> v) & 1u)) ? base[((int64_t)v * H + hh) * n + j] : 0.0f;
 #pragma unroll
-      for (int v = 0; v < kAnchorMax; ++v) s[v] += x[v];
-    }
-  };
-  {
-    float s[kAnchorMax];
-    head_sums(P.part1 + ((int64_t)l * 2 + p) * V * H * n, P.elig, j < P.cover, s);
-    if (j < n) {
-      float* wr = P.w + ((int64_t)l * 2 + p) * V * n + j;
-      if (j < P.cover) {
-        float m = INFINITY;
-#pragma unroll
-        for (int v = 0; v < kAnchorMax; ++v)
-          if (v < V && ((P.elig >> v) & 1u)) m = fminf(m, s[v] / P.D);
-        float sum = 0.0f;
-#pragma unroll
-        for (int v = 0; v < kAnchorMax; ++v)
-          if (v < V && ((P.elig >> v) & 1u)) sum += expf(m - s[v] / P.D);
-#pragma unroll
-        for (int v = 0; v < kAnchorMax; ++v)
-          if (v < V) wr[(int64_t)v * n] = ((P.elig >> v) & 1u) ? expf(m - s[v] / P.D) / sum : 0.0f;
-      } else {
-        for (int v = 0; v < V; ++v) wr[(int64_t)v * n] = 0.0f;
-      }
-    }
+    for (int v = 0; v < kAnchorMax; ++v) s[v] += x[v];
   }
-  if (p == 0) return;                        // block-uniform
-  float s2[kAnchorMax];
-  head_sums(P.part2 + (int64_t)l * V * H * n, P.gate_set, j < P.k_gate, s2);
+  float m = INFINITY;
 #pragma unroll
-  for (int v = 0; v < kAnchorMax; ++v) {
-    if (v >= V || !((P.gate_set >> v) & 1u)) continue;
-    double d = (double)s2[v];
+  for (int v = 0; v < kAnchorMax; ++v)
+    if (v < V && ((P.elig >> v) & 1u)) m = fminf(m, s[v] / P.D);
+  float sum = 0.0f;
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) d += __shfl_xor(d, off);
-    if (lane == 0) gsum[wave][v] = d;
-  }
-  __syncthreads();
-  if (tid < V) {
-    double d = 0.0;
-    if ((P.gate_set >> tid) & 1u)
-      for (int w = 0; w < kFinishTokens / 64; ++w) d += gsum[w][tid];
-    P.gpart[((int64_t)l * P.n_tiles + tile) * V + tid] = d;
-  }
+  for (int v = 0; v < kAnchorMax; ++v)
+    if (v < V && ((P.elig >> v) & 1u)) sum += expf(m - s[v] / P.D);
+#pragma unroll
+  for (int v = 0; v < kAnchorMax; ++v)
+    if (v < V) wr[(int64_t)v * n] = ((P.elig >> v) & 1u) ? expf(m - s[v] / P.D) / sum : 0.0f;
 }
 
 // Gate finish: d_v = sqrt of the summed partials (fp64, fixed order), then
@@ -668,19 +742,20 @@ RopeArgs rope_freqs(double theta, int32_t style) {
   return make_rope_args(&r, kHD);
 }
 
-// Workspace: the per-head distance sums of both planes, the per-head squared
-// sums of the value plane, and the gate's per-block partial sums.
+// Workspace: the per-head distance sums of both planes, the gate's partial
+// sums per match block (layer, 128-token tile, head, anchor) and per finish
+// block (layer, 256-token tile, anchor).
 struct MatchWs {
-  size_t part1, part2, gpart, total;
+  size_t part1, gpart, gsum, total;
 };
 
 MatchWs match_ws(int64_t L, int64_t H, int64_t n, int64_t V) {
   MatchWs w;
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
   w.part1 = up((size_t)(L * 2 * V * H * n) * sizeof(float));
-  w.part2 = up((size_t)(L * V * H * n) * sizeof(float));
-  w.gpart = up((size_t)(L * ((n + kFinishTokens - 1) / kFinishTokens) * V) * sizeof(double));
-  w.total = w.part1 + w.part2 + w.gpart + 256;
+  w.gpart = up((size_t)(L * ((n + kMatchTokens - 1) / kMatchTokens) * H * V) * sizeof(double));
+  w.gsum = up((size_t)(L * ((n + kFinishTokens - 1) / kFinishTokens) * V) * sizeof(double));
+  w.total = w.part1 + w.gpart + w.gsum + 256;
   return w;
 }
 
@@ -715,7 +790,9 @@ extern "C" kvfix_status kvfix_anchor_match(const kvfix_plane* src_k, const kvfix
   const hipStream_t st = (hipStream_t)stream;
   const Eligible e = eligible(base, n, k_gate);
   char* wsb = static_cast<char*>(ws);
-  double* gpart = reinterpret_cast<double*>(wsb + W.part1 + W.part2);
+  double* gpart = reinterpret_cast<double*>(wsb + W.part1);
+  double* gsum = reinterpret_cast<double*>(wsb + W.part1 + W.gpart);
+  const int32_t n_tiles = (n + kMatchTokens - 1) / kMatchTokens;
   const int32_t n_fin = (n + kFinishTokens - 1) / kFinishTokens;
 
   if (V > 0 && n > 0 && L > 0 && H > 0) {
@@ -735,7 +812,7 @@ extern "C" kvfix_status kvfix_anchor_match(const kvfix_plane* src_k, const kvfix
     P.cover = e.cover;
     P.k_gate = e.k_gate;
     P.n_pairs = 2 * L;
-    P.n_tiles = (n + kMatchTokens - 1) / kMatchTokens;
+    P.n_tiles = n_tiles;
     for (int v = 0; v < V; ++v) {
       const bool in_e = (e.elig >> v) & 1u;
       const bool in_gate = e.k_gate > 0 && ((e.gate_set >> v) & 1u);
@@ -743,7 +820,7 @@ extern "C" kvfix_status kvfix_anchor_match(const kvfix_plane* src_k, const kvfix
       if (in_e || in_gate) P.list[1] |= (uint64_t)v << (4 * P.n_list[1]++);
     }
     P.part1 = reinterpret_cast<float*>(wsb);
-    P.part2 = reinterpret_cast<float*>(wsb + W.part1);
+    P.gpart = gpart;
     const int64_t grid =
         (int64_t)H * P.n_tiles * ((P.n_pairs + kXcds - 1) / kXcds) * kXcds;
     if (rope_style == KVFIX_ROPE_HALF)
@@ -754,24 +831,23 @@ extern "C" kvfix_status kvfix_anchor_match(const kvfix_plane* src_k, const kvfix
 
     FinishParams F;
     F.part1 = P.part1;
-    F.part2 = P.part2;
     F.n = n;
     F.H = H;
     F.V = V;
     F.elig = e.elig;
-    F.gate_set = e.gate_set;
     F.cover = e.cover;
-    F.k_gate = e.k_gate;
-    F.n_tiles = n_fin;
     F.D = (float)(H * kHD);
     F.w = weights;
     F.gpart = gpart;
+    F.n_match_tiles = n_tiles;
+    F.n_tiles = n_fin;
+    F.gsum = gsum;
     anchor_finish_kernel<<<dim3((unsigned)n_fin, (unsigned)(2 * L)), dim3(kFinishTokens), 0,
                            st>>>(F);
     KVFIX_TRY(launch_status());
   }
   const int n_parts = (V > 0 && n > 0 && H > 0) ? L * n_fin : 0;
-  anchor_gate_kernel<<<dim3(1), dim3(1024), 0, st>>>(gpart, n_parts, V, e.gate_set, tau, gate,
+  anchor_gate_kernel<<<dim3(1), dim3(1024), 0, st>>>(gsum, n_parts, V, e.gate_set, tau, gate,
                                                       accept);
   return launch_status();
 }
