@@ -1,7 +1,7 @@
 // L2 divergence score (a2) and top-b selection (a4).
 //
-// score: one 256-thread block per (segment, RPW tokens).  The four waves
-// split the KV heads; each lane accumulates (fresh - align(reuse))^2 of its
+// score: one 256-thread block per (segment, RPW tokens), up to 8 such groups
+// per block on rotated planes.  The four waves split the KV heads; each lane accumulates (fresh - align(reuse))^2 of its
 // pairs in fp64, lanes of a row reduce by a fixed butterfly, the waves add in
 // index order, and sqrt is rounded once to fp32.
 //
@@ -12,6 +12,7 @@
 // compaction keeps every key > T and the lowest-index keys == T, placing
 // each by wave ballots and a scanned table of per-wave counts, and writes
 // indices in ascending order and the bitmask word by word.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -21,6 +22,8 @@
 namespace kvfix {
 
 constexpr int kScoreBlock = 256;
+constexpr int kScoreGroupsMax = 8;      // 8-token groups (RPW rows) per block, at most
+constexpr int kScoreMinBlocks = 2048;   // fewer groups per block below this many blocks
 
 struct ScoreParams {
   DPlane fresh, reuse;
@@ -28,12 +31,112 @@ struct ScoreParams {
   RopeArgs rope;
   float* scores;                  // [S][n], or [S][H][n] per head
   int32_t S, H, n, tok_blocks;
+  int32_t groups;                 // row groups per block (1..kScoreGroupsMax)
   int32_t per_head;
 };
 
+// Rotated planes: a block takes `groups` consecutive groups of RPW tokens of
+// one segment, so the segment's rotary table is built once per block, after
+// the loads of the block's first rows have been issued.
 template <typename T, int HD, int STYLE>
 __global__ __launch_bounds__(kScoreBlock) void score_l2_kernel(ScoreParams P) {
-  constexpr int MS = STYLE == kStyleNone ? kStyleHalf : STYLE;
+  static_assert(STYLE != kStyleNone, "unrotated planes take score_l2_plain_kernel");
+  constexpr int MS = STYLE;
+  using M = RowMap<T, HD, MS>;
+  using Cd = Codec<T, double>;
+  constexpr int V = M::V, G = M::G, RPW = M::RPW;
+  constexpr int W = kScoreBlock / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // (uniform)
+  const int g = lane % G, rw = lane / G;
+  const int grp0 = (blockIdx.x % P.tok_blocks) * P.groups;
+  const int s = blockIdx.x / P.tok_blocks;
+
+  __shared__ double tc[HD / 2], ts[HD / 2];
+  __shared__ double part[kScoreGroupsMax][W][RPW];
+  // the row pair (fresh, reuse) of token j, head h: four 16-byte pieces
+  const DPlane pf = P.fresh, pr = P.reuse;
+  const int fl = P.fl, rl = P.rl, n = P.n;
+  auto load = [&](int j, int h, vu4* r) {
+    const int64_t fo = j < n ? row_offset(pf, fl, s, h, j) : -1;
+    const int64_t ro = j < n ? row_offset(pr, rl, s, h, j) : -1;
+    if (fo < 0 || ro < 0) return false;
+    const T* fr = reinterpret_cast<const T*>(pf.data) + fo;
+    const T* rr = reinterpret_cast<const T*>(pr.data) + ro;
+    r[0] = ld16(fr + M::off0(g));
+    r[1] = ld16(fr + M::off1(g));
+    r[2] = ld16(rr + M::off0(g));
+    r[3] = ld16(rr + M::off1(g));
+    return true;
+  };
+  // the block's first rows are requested before the table is built
+  vu4 r[4];
+  bool ok = wave < P.H && load(grp0 * RPW + rw, wave, r);
+  rope_table<HD, double>(P.rope, P.rope.delta[s], tc, ts);
+  __syncthreads();
+  double cs[V], sn[V];
+#pragma unroll
+  for (int m = 0; m < V; ++m) { cs[m] = tc[g * V + m]; sn[m] = ts[g * V + m]; }
+
+#pragma unroll 1
+  for (int gi = 0; gi < P.groups; ++gi) {
+    const int j = (grp0 + gi) * RPW + rw;
+    // Every lane runs the head loop (the per-head sums reduce across lanes
+    // inside it); a lane past n or on a bad page id adds nothing.
+    double acc = 0.0;
+#pragma unroll 1
+    for (int h = wave; h < P.H; h += W) {
+      if (gi > 0 || h != wave) ok = load(j, h, r);     // (else already in)
+      double hacc = 0.0;
+      if (ok) {
+        double p0[V], p1[V], fa[V], fb[V], ra[V], rb[V];
+        Cd::unpack(r[0], p0);
+        Cd::unpack(r[1], p1);
+        parts_to_pairs<MS, V>(p0, p1, fa, fb);
+        Cd::unpack(r[2], p0);
+        Cd::unpack(r[3], p1);
+        parts_to_pairs<MS, V>(p0, p1, ra, rb);
+        rotate_pairs<V>(ra, rb, cs, sn);
+#pragma unroll
+        for (int m = 0; m < V; ++m) {
+          const double da = fa[m] - ra[m], db = fb[m] - rb[m];
+          hacc = fma(da, da, hacc);
+          hacc = fma(db, db, hacc);
+        }
+      }
+      if (P.per_head) {                            // uniform: this head's score of row j
+#pragma unroll
+        for (int off = 1; off < G; off <<= 1) hacc += __shfl_xor(hacc, off);
+        if (g == 0 && j < P.n) P.scores[((int64_t)s * P.H + h) * P.n + j] = (float)sqrt(hacc);
+      } else {
+        acc += hacc;
+      }
+    }
+    if (!P.per_head) {
+#pragma unroll
+      for (int off = 1; off < G; off <<= 1) acc += __shfl_xor(acc, off);
+      if (g == 0) part[gi][wave][rw] = acc;
+    }
+  }
+  if (P.per_head) return;                          // (uniform over the block)
+  __syncthreads();
+  // the waves' head sums of each row, added in wave order
+  if ((int)threadIdx.x < P.groups * RPW) {
+    const int gi = threadIdx.x / RPW, r = threadIdx.x % RPW;
+    const int jj = (grp0 + gi) * RPW + r;
+    if (jj < P.n) {
+      double t = 0.0;
+#pragma unroll
+      for (int w = 0; w < W; ++w) t += part[gi][w][r];
+      P.scores[(int64_t)s * P.n + jj] = (float)sqrt(t);
+    }
+  }
+}
+
+// Unrotated planes (no table to share): one group of RPW tokens per block.
+template <typename T, int HD>
+__global__ __launch_bounds__(kScoreBlock) void score_l2_plain_kernel(ScoreParams P) {
+  constexpr int MS = kStyleHalf;          // (any pairing: nothing is rotated)
   using M = RowMap<T, HD, MS>;
   using Cd = Codec<T, double>;
   constexpr int V = M::V, G = M::G, RPW = M::RPW;
@@ -44,15 +147,7 @@ __global__ __launch_bounds__(kScoreBlock) void score_l2_kernel(ScoreParams P) {
   const int s = blockIdx.x / P.tok_blocks;
   const int j = tb * RPW + rw;
 
-  __shared__ double tc[HD / 2], ts[HD / 2];
   __shared__ double part[W][RPW];
-  if constexpr (STYLE != kStyleNone) rope_table<HD, double>(P.rope, P.rope.delta[s], tc, ts);
-  __syncthreads();
-  double cs[V], sn[V];
-  if constexpr (STYLE != kStyleNone) {
-#pragma unroll
-    for (int m = 0; m < V; ++m) { cs[m] = tc[g * V + m]; sn[m] = ts[g * V + m]; }
-  }
 
   // Every lane runs the head loop (the per-head sums reduce across lanes
   // inside it); a lane past n or on a bad page id adds nothing.
@@ -73,7 +168,6 @@ __global__ __launch_bounds__(kScoreBlock) void score_l2_kernel(ScoreParams P) {
       Cd::unpack(q0, p0);
       Cd::unpack(q1, p1);
       parts_to_pairs<MS, V>(p0, p1, ra, rb);
-      if constexpr (STYLE != kStyleNone) rotate_pairs<V>(ra, rb, cs, sn);
 #pragma unroll
       for (int m = 0; m < V; ++m) {
         const double da = fa[m] - ra[m], db = fb[m] - rb[m];
@@ -111,10 +205,19 @@ struct ScoreLaunch {
     constexpr int MS = STYLE == kStyleNone ? kStyleHalf : STYLE;
     constexpr int RPW = RowMap<T, HD, MS>::RPW;
     ScoreParams Q = P;
-    Q.tok_blocks = (P.n + RPW - 1) / RPW;
+    // Several row groups per block only where they share a rotary table.
+    const int64_t groups_total = (int64_t)((P.n + RPW - 1) / RPW) * P.S;
+    Q.groups = STYLE == kStyleNone
+                   ? 1
+                   : (int)std::max<int64_t>(
+                         1, std::min<int64_t>(kScoreGroupsMax, groups_total / kScoreMinBlocks));
+    Q.tok_blocks = ((P.n + RPW - 1) / RPW + Q.groups - 1) / Q.groups;
     const int64_t grid = (int64_t)Q.tok_blocks * P.S;
     if (grid > kMaxGrid) return KVFIX_ERR_ARG;
-    score_l2_kernel<T, HD, STYLE><<<dim3((unsigned)grid), dim3(kScoreBlock), 0, st>>>(Q);
+    if constexpr (STYLE == kStyleNone)
+      score_l2_plain_kernel<T, HD><<<dim3((unsigned)grid), dim3(kScoreBlock), 0, st>>>(Q);
+    else
+      score_l2_kernel<T, HD, STYLE><<<dim3((unsigned)grid), dim3(kScoreBlock), 0, st>>>(Q);
     return launch_status();
   }
 };
