@@ -17,8 +17,8 @@
 // mass   : one 256-thread block per (s, split of the query rows, 1024 keys).
 //          The block first forms each of its rows' maximum M and 1/Z from
 //          the chunk statistics (fp64, fixed order), then every thread adds
-//          exp(x - M) / Z over the split's rows for four keys (16-byte loads,
-//          eight rows in flight), in fp64, in row order.  The exponentials
+//          exp(x - M) / Z over the split's rows for four keys (16-byte
+//          non-temporal loads, sixteen rows in flight), in fp64, in row order.  The exponentials
 //          are the hardware's base-2 exponential (within about one unit of
 //          2^-24 relative for these arguments, which are <= 0).
 // total  : per key, the splits added in split order, rounded once to fp32.
@@ -38,7 +38,7 @@ constexpr int kTilesPerWave = 16;
 constexpr int kDraftChunk = (kDraftBlock / kWave) * kTilesPerWave * 16;   // 1024 keys
 constexpr int kMassKeys = 1024;          // keys per mass block (4 per thread)
 constexpr int kMassRowsMax = 64;         // query rows per mass block (one split)
-constexpr int kMassUnroll = 8;           // rows in flight per thread
+constexpr int kMassUnroll = 16;          // rows in flight per thread
 
 struct DraftParams {
   const bf16_t* q;          // [S][L][Hq][T][hd]
@@ -316,7 +316,7 @@ __global__ __launch_bounds__(256) void draft_mass_kernel(MassParams P) {
 #pragma unroll
       for (int e = 0; e < kMassUnroll; ++e) {
         const float* p = lg + (int64_t)(r + e) * P.ldl + j0;
-        if (full) x[e] = *reinterpret_cast<const float4*>(p);
+        if (full) x[e] = __builtin_bit_cast(float4, ld16(p));     // read once: non-temporal
         else {
           x[e].x = p[0];
           x[e].y = j0 + 1 < P.n ? p[1] : 0.f;
