@@ -388,6 +388,41 @@ def paged_case(L=3, S=4, H=2, n=70, hd=128, ps=16, n_pages=29, seed=41):
     return pt, pps
 
 
+@pytest.mark.parametrize("S,n,groups", [(16, 2050, 2), (64, 1030, 4)])
+@pytest.mark.parametrize("style", ["half", "interleaved"])
+def test_score_blocks_of_several_token_groups(S, n, groups, style):
+    """Rotated planes give a block several 8-token groups once the grid would
+    exceed 2 x 2,048 blocks (here 2 and 4 groups), the last block ragged;
+    scores against the oracle to 2^-23, dense and through a paged pool."""
+    L, H, hd, ps, c = 2, 3, 128, 16, 1
+    assert max(1, min(8, (-(-n // 8) * S) // 2048)) == groups
+    rng = np.random.default_rng(7 + S)
+    bits = lambda a: (a.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)   # noqa: E731
+    reuse = bits(rng.standard_normal((L, S, H, n, hd)))
+    fresh = bits(rng.standard_normal((L, S, H, n, hd)))
+    deltas = [int(d) for d in rng.integers(1, 1 << 20, S)]
+    kst = kv.ROPE_HALF if style == "half" else kv.ROPE_INTERLEAVED
+    log("score groups", S, n, groups, style)
+    o = K.score_l2(fresh, reuse, "bf16", c, deltas, 5e5, style)
+    f_t, r_t = from_np(fresh, DEV), from_np(reuse, DEV)
+    delta = torch.tensor(deltas, dtype=torch.int64, device=DEV)
+    sc = torch.full((S, n), float("nan"), dtype=torch.float32, device=DEV)
+    kv.kvfix_score(Plane.dense(f_t), c, Plane.dense(r_t), c, sc, delta, 5e5, kst)
+    g = sc.cpu().numpy()
+    err = np.abs(g.astype(np.float64) - o) / np.maximum(np.abs(o), 1e-30)
+    assert err.max() <= 2.0 ** -23, f"dense: rel err {err.max():.3g}"
+    if S == 16:
+        n_pages = S * -(-n // ps) + 5
+        pt, _ = paged_case(L, S, H, n, hd, ps, n_pages)
+        pool = np.zeros(L * n_pages * ps * H * hd, dtype=np.uint16)
+        K.paged_scatter(pool, reuse, pt, ps)
+        plane = Plane.paged(from_np(pool.reshape(L, n_pages, ps, H, hd), DEV),
+                            torch.from_numpy(pt).to(DEV), ps, n)
+        sc2 = torch.full((S, n), float("nan"), dtype=torch.float32, device=DEV)
+        kv.kvfix_score(Plane.dense(f_t), c, plane, c, sc2, delta, 5e5, kst)
+        assert np.array_equal(sc2.cpu().numpy(), g)
+
+
 def test_paged_tagging_maps_every_row_exactly():
     L, S, H, n, hd, ps, n_pages = 3, 4, 2, 70, 128, 16, 29
     pt, pps = paged_case(L, S, H, n, hd, ps, n_pages)
