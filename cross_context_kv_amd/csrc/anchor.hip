@@ -214,8 +214,9 @@ struct MatchParams {
   int32_t n_pairs, n_tiles;
   int32_t n_list[2];               // anchors computed per plane, in order,
   uint64_t list[2];                // 4 bits per anchor id
-  float* part1;      // [L][2][V][H][n] per-head sums of |source - A_v B_v|
-  double* gpart;     // [L][n_tiles][H][V] the gate prefix's squared sums per block
+  int32_t hpb, HG;   // heads per block (1 or 2), head groups H / hpb
+  float* part1;      // [L][2][V][HG][n] sums of |source - A_v B_v| over a block's heads
+  double* gpart;     // [L][n_tiles][HG][V] the gate prefix's squared sums per block
 };
 
 // One block = 128 tokens (4 waves x 2 bands of 16) of one (layer, plane,
@@ -245,9 +246,10 @@ __device__ __forceinline__ float sum_row16(float x) {
   return x;
 }
 
-template <int STYLE, bool GATE>
-__device__ __forceinline__ void match_body(const MatchParams& P, int l, int h, int tile,
-                                           bf16_t* sbt, float* tc, float* ts, float* gw) {
+template <int STYLE, bool GATE, int HPB>
+__device__ __forceinline__ void match_body(const MatchParams& P, int l, int hg, int tile,
+                                           bf16_t* sbt, float* tc, float* ts, float* gw,
+                                           float* hsum) {
   constexpr int p = GATE ? 1 : 0;
   if (STYLE != kStyleNone) rope_table<kHD, float>(P.rope, -P.src_off, tc, ts);
   __syncthreads();
@@ -257,12 +259,20 @@ __device__ __forceinline__ void match_body(const MatchParams& P, int l, int h, i
   const int lim = GATE ? max(P.cover, P.k_gate) : P.cover;
   const int nl = P.n_list[p];
   const uint64_t list = P.list[p];
-  const int V = P.V, H = P.H, n = P.n;
-  double* gpart = P.gpart + (((int64_t)l * P.n_tiles + tile) * H + h) * V;
+  const int V = P.V, n = P.n;
+  double* gpart = P.gpart + (((int64_t)l * P.n_tiles + tile) * P.HG + hg) * V;
   if (j0 >= lim || nl == 0) {                 // block-uniform: no barrier follows
     if (GATE && tid < V) gpart[tid] = 0.0;    // no prefix rows here
     return;
   }
+  auto anchor = [&](int i) { return (int)((list >> (4 * min(i, nl - 1))) & 15u); };
+  // The block's heads one after the other; a token's sums over them are
+  // added in head order (a non-final head parks them in LDS, written and
+  // read back by the same lane) and written once per anchor.
+#pragma unroll
+  for (int hh = 0; hh < HPB; ++hh) {
+  const int h = hg * HPB + hh;
+  const bool last_head = hh == HPB - 1;
 
   float nx[kMatchBands][32];
 #pragma unroll
@@ -281,7 +291,6 @@ __device__ __forceinline__ void match_body(const MatchParams& P, int l, int h, i
     }
   }
 
-  auto anchor = [&](int i) { return (int)((list >> (4 * min(i, nl - 1))) & 15u); };
   auto stage_load = [&](int v, vu4* r) {
     const bf16_t* src = bt_row(P.G, v, l, p, h * kHD);
     r[0] = ld16_cached(src + 8 * tid);
@@ -310,7 +319,7 @@ __device__ __forceinline__ void match_body(const MatchParams& P, int l, int h, i
 #pragma unroll
     for (int c = 0; c < kTiles; ++c)
       bop[c] = *reinterpret_cast<const bf16x8*>(buf + slice_chunk(c, g, t));
-    float* o1 = P.part1 + ((((int64_t)l * 2 + p) * V + v) * H + h) * n;
+    float* o1 = P.part1 + ((((int64_t)l * 2 + p) * V + v) * P.HG + hg) * n;
     // Both bands' products of a tile are issued before either is summed, so
     // one band's sums cover the other band's MFMA latency.  Per band the
     // sums still run over the tiles in order.
@@ -340,17 +349,22 @@ __device__ __forceinline__ void match_body(const MatchParams& P, int l, int h, i
     float q = 0.0f;
 #pragma unroll
     for (int b = 0; b < kMatchBands; ++b) {
-      const float c1 = sum_lane_groups((s1[b][0] + s1[b][1]) + (s1[b][2] + s1[b][3]));
+      float c1 = sum_lane_groups((s1[b][0] + s1[b][1]) + (s1[b][2] + s1[b][3]));
       const int j = jw + 16 * b + t;
       if (GATE) {
         const float c2 = sum_lane_groups((s2[b][0] + s2[b][1]) + (s2[b][2] + s2[b][3]));
         q += j < P.k_gate ? c2 : 0.0f;
       }
-      if (g == 0 && j < n) o1[j] = c1;
+      float* hs = hsum + i * kMatchTokens + wave * kMatchBands * 16 + 16 * b + t;
+      if (hh > 0) c1 = *hs + c1;                    // the block's earlier heads first
+      if (g == 0) {
+        if (!last_head) *hs = c1;
+        else if (j < n) o1[j] = c1;
+      }
     }
     if (GATE) {
       q = sum_row16(q);
-      if (lane == 0) gw[i * kMatchWaves + wave] = q;
+      if (lane == 0) gw[i * kMatchWaves + wave] = hh > 0 ? gw[i * kMatchWaves + wave] + q : q;
     }
   };
 
@@ -372,6 +386,7 @@ __device__ __forceinline__ void match_body(const MatchParams& P, int l, int h, i
     stage_store(sr, sbt);
     __syncthreads();
   }
+  }                                            // heads
   // (the loop's last barrier orders the waves' partials before this)
   if (GATE && tid < V) {
     double d = 0.0;                   // 0 for anchors outside the gate set
@@ -383,22 +398,23 @@ __device__ __forceinline__ void match_body(const MatchParams& P, int l, int h, i
   }
 }
 
-template <int STYLE>
+template <int STYLE, int HPB>
 __global__ __launch_bounds__(kMatchWaves * 64) __attribute__((amdgpu_waves_per_eu(3)))
 void anchor_match_kernel(MatchParams P) {
   __shared__ __attribute__((aligned(16))) bf16_t sbt[2 * kSlice];
   __shared__ float tc[kHD / 2], ts[kHD / 2];
   __shared__ float gw[kAnchorMax * kMatchWaves];
+  __shared__ float hsum[kAnchorMax * kMatchTokens];
   const int id = blockIdx.x, xcd = id % kXcds, k = id / kXcds;
-  const int h = k % P.H, k2 = k / P.H;
+  const int hg = k % P.HG, k2 = k / P.HG;
   const int tile = k2 % P.n_tiles;
   const int pair = (k2 / P.n_tiles) * kXcds + xcd;
   if (pair >= P.n_pairs) return;
   const int l = pair >> 1;
   if ((pair & 1) == 0)
-    match_body<STYLE, false>(P, l, h, tile, sbt, tc, ts, gw);
+    match_body<STYLE, false, HPB>(P, l, hg, tile, sbt, tc, ts, gw, hsum);
   else
-    match_body<kStyleNone, true>(P, l, h, tile, sbt, tc, ts, gw);
+    match_body<kStyleNone, true, HPB>(P, l, hg, tile, sbt, tc, ts, gw, hsum);
 }
 
 // Per token: the head sums added in head order give the distance sums;
@@ -742,18 +758,22 @@ RopeArgs rope_freqs(double theta, int32_t style) {
   return make_rope_args(&r, kHD);
 }
 
-// Workspace: the per-head distance sums of both planes, the gate's partial
-// sums per match block (layer, 128-token tile, head, anchor) and per finish
-// block (layer, 256-token tile, anchor).
+// Workspace: the distance sums of both planes per block's heads, the gate's
+// partial sums per match block (layer, 128-token tile, head group, anchor)
+// and per finish block (layer, 256-token tile, anchor).
 struct MatchWs {
   size_t part1, gpart, gsum, total;
 };
 
+// Heads per match block: two when the head count is even.
+int match_hpb(int64_t H) { return H % 2 == 0 ? 2 : 1; }
+
 MatchWs match_ws(int64_t L, int64_t H, int64_t n, int64_t V) {
   MatchWs w;
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
-  w.part1 = up((size_t)(L * 2 * V * H * n) * sizeof(float));
-  w.gpart = up((size_t)(L * ((n + kMatchTokens - 1) / kMatchTokens) * H * V) * sizeof(double));
+  const int64_t HG = H > 0 ? H / match_hpb(H) : 0;
+  w.part1 = up((size_t)(L * 2 * V * HG * n) * sizeof(float));
+  w.gpart = up((size_t)(L * ((n + kMatchTokens - 1) / kMatchTokens) * HG * V) * sizeof(double));
   w.gsum = up((size_t)(L * ((n + kFinishTokens - 1) / kFinishTokens) * V) * sizeof(double));
   w.total = w.part1 + w.gpart + w.gsum + 256;
   return w;
@@ -806,6 +826,8 @@ extern "C" kvfix_status kvfix_anchor_match(const kvfix_plane* src_k, const kvfix
     P.seg = seg;
     P.n = n;
     P.H = H;
+    P.hpb = match_hpb(H);
+    P.HG = H / P.hpb;
     P.V = V;
     P.elig = e.elig;
     P.gate_set = e.gate_set;
@@ -822,17 +844,22 @@ extern "C" kvfix_status kvfix_anchor_match(const kvfix_plane* src_k, const kvfix
     P.part1 = reinterpret_cast<float*>(wsb);
     P.gpart = gpart;
     const int64_t grid =
-        (int64_t)H * P.n_tiles * ((P.n_pairs + kXcds - 1) / kXcds) * kXcds;
-    if (rope_style == KVFIX_ROPE_HALF)
-      anchor_match_kernel<kStyleHalf><<<dim3((unsigned)grid), dim3(kMatchWaves * 64), 0, st>>>(P);
-    else
-      anchor_match_kernel<kStyleInter><<<dim3((unsigned)grid), dim3(kMatchWaves * 64), 0, st>>>(P);
+        (int64_t)P.HG * P.n_tiles * ((P.n_pairs + kXcds - 1) / kXcds) * kXcds;
+    if (grid > kMaxGrid) return KVFIX_ERR_ARG;
+    const dim3 gd((unsigned)grid), bd(kMatchWaves * 64);
+    if (rope_style == KVFIX_ROPE_HALF) {
+      if (P.hpb == 2) anchor_match_kernel<kStyleHalf, 2><<<gd, bd, 0, st>>>(P);
+      else anchor_match_kernel<kStyleHalf, 1><<<gd, bd, 0, st>>>(P);
+    } else {
+      if (P.hpb == 2) anchor_match_kernel<kStyleInter, 2><<<gd, bd, 0, st>>>(P);
+      else anchor_match_kernel<kStyleInter, 1><<<gd, bd, 0, st>>>(P);
+    }
     KVFIX_TRY(launch_status());
 
     FinishParams F;
     F.part1 = P.part1;
     F.n = n;
-    F.H = H;
+    F.H = P.HG;                     // the head sums come per head group
     F.V = V;
     F.elig = e.elig;
     F.cover = e.cover;

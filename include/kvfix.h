@@ -496,11 +496,12 @@ typedef struct {
  * accept: device int32, 1 iff |A_k| >= 2 and gate[V] <= tau (else dense
  *   prefill is due).
  * ws: device workspace of kvfix_anchor_match_workspace(...) bytes, 256-byte
- *   aligned: per-head distance sums of both planes (fp32 [L][2][V][H][n]) and
- *   the gate's fp64 partial sums (per layer, 128-token block, head and
- *   anchor, then per layer, 256-token block and anchor).
- * Arithmetic: bf16 MFMA products; fp32 distance sums (per head, then the
- * heads added in order); gate squares summed in fp32 per head over 32-token
+ *   aligned: distance sums of both planes per group of heads (fp32
+ *   [L][2][V][G][n], G = n_heads / 2 for an even head count, else n_heads)
+ *   and the gate's fp64 partial sums (per layer, 128-token block, head group
+ *   and anchor, then per layer, 256-token block and anchor).
+ * Arithmetic: bf16 MFMA products; fp32 distance sums (per head; a group's
+ * heads added in order, then the groups in order); gate squares summed in fp32 per head over 32-token
  * groups, those groups and all further totals in fp64. */
 size_t kvfix_anchor_match_workspace(int32_t n_layers, int32_t n_heads, int32_t n_tokens,
                                     int32_t n_anchors);

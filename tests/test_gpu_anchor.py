@@ -127,6 +127,19 @@ def check_apply(case, lengths, w, tgt_off):
     return errs
 
 
+@pytest.mark.parametrize("H", [3, 4])
+def test_odd_and_even_head_counts(H):
+    """A match block takes two heads when the head count is even and one
+    when it is odd: both against the oracle (weights, gate, apply)."""
+    case = anchor_case(L=2, H=H, n=200, V=4, n_max=210, seed=67)
+    lengths = [200, 210, 205, 200]
+    log("anchor heads", H)
+    w, gate, acc = gpu_match(case, lengths, 150, 0.5)
+    check_weights(case, lengths, w)
+    check_gate(case, lengths, 150, 0.5, gate, acc)
+    check_apply(case, lengths, w, tgt_off=500)
+
+
 @pytest.mark.parametrize("style", ["half", "interleaved"])
 def test_match_gate_and_apply_match_oracle(style):
     case = anchor_case(style=style, n_max=320)

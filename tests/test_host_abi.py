@@ -151,12 +151,15 @@ def test_anchor_call_validation():
     p = plane()
     w, gate, acc = ctypes.c_void_p(512), ctypes.c_void_p(1024), ctypes.c_void_p(2048)
     up = lambda x: (x + 255) // 256 * 256                       # noqa: E731
-    # per-head distance sums [L][2][V][H][n] and the gate's fp64 partials,
-    # [L][128-token blocks][H][V] then [L][256-token blocks][V]
+    # distance sums per head group [L][2][V][G][n] (G = H / 2 for even H, else
+    # H) and the gate's fp64 partials, [L][128-token blocks][G][V] then
+    # [L][256-token blocks][V]
     need = L.kvfix_anchor_match_workspace(2, 2, 64, 3)
-    assert need == up(2 * 2 * 3 * 2 * 64 * 4) + up(2 * 1 * 2 * 3 * 8) + up(2 * 1 * 3 * 8) + 256
+    assert need == up(2 * 2 * 3 * 1 * 64 * 4) + up(2 * 1 * 1 * 3 * 8) + up(2 * 1 * 3 * 8) + 256
     assert L.kvfix_anchor_match_workspace(2, 2, 300, 3) == \
-        up(2 * 2 * 3 * 2 * 300 * 4) + up(2 * 3 * 2 * 3 * 8) + up(2 * 2 * 3 * 8) + 256
+        up(2 * 2 * 3 * 1 * 300 * 4) + up(2 * 3 * 1 * 3 * 8) + up(2 * 2 * 3 * 8) + 256
+    assert L.kvfix_anchor_match_workspace(2, 3, 64, 3) == \
+        up(2 * 2 * 3 * 3 * 64 * 4) + up(2 * 1 * 3 * 3 * 8) + up(2 * 1 * 3 * 8) + 256
     ws = ctypes.c_void_p(4096)
 
     def match(pk=p, pv=p, seg=0, pool=None, src_off=100, theta=1e4, style=kv.ROPE_HALF, k=64,
