@@ -491,35 +491,58 @@ __global__ __launch_bounds__(1024) void anchor_gate_kernel(const double* part, i
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (wave < V) {
     double s = 0.0;
-    for (int i = lane; i < n_parts; i += 64) s += part[(int64_t)i * V + wave];
+    int i = lane;
+    for (; i + 7 * 64 < n_parts; i += 8 * 64) {   // eight loads in flight, added in order
+      double x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = part[(int64_t)(i + 64 * e) * V + wave];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += x[e];
+    }
+    for (; i < n_parts; i += 64) s += part[(int64_t)i * V + wave];
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
     if (lane == 0) sd[wave] = ((gate_set >> wave) & 1u) ? sqrt(s) : __builtin_nan("");
   }
   __syncthreads();
-  if (threadIdx.x != 0) return;
+  if (wave != 0) return;
+  // the exponentials and logarithms one anchor per lane; the sums in anchor
+  // order by lane 0
+  __shared__ double se[kAnchorMax], sl[kAnchorMax];
   int na = 0;
   double dmin = INFINITY;
   for (int v = 0; v < V; ++v) {
-    gate[v] = sd[v];
     if ((gate_set >> v) & 1u) {
       ++na;
       dmin = fmin(dmin, sd[v]);
     }
   }
+  if (lane < V) gate[lane] = sd[lane];
   if (na < 2) {
-    gate[V] = __builtin_nan("");
-    *accept = 0;
+    if (lane == 0) {
+      gate[V] = __builtin_nan("");
+      *accept = 0;
+    }
     return;
   }
+  const bool in = lane < V && ((gate_set >> lane) & 1u);
+  const double ev = in ? exp(dmin - sd[lane]) : 0.0;
+  if (lane < V) se[lane] = ev;
+  __builtin_amdgcn_wave_barrier();
   double sum = 0.0;
   for (int v = 0; v < V; ++v)
-    if ((gate_set >> v) & 1u) sum += exp(dmin - sd[v]);
+    if ((gate_set >> v) & 1u) sum += se[v];
+  if (lane < V) {
+    const double gv = ev / sum;
+    sl[lane] = in && gv > 0.0 ? gv * log2(gv) : 0.0;
+  }
+  __builtin_amdgcn_wave_barrier();
+  if (lane != 0) return;
   double hsum = 0.0;
   for (int v = 0; v < V; ++v) {
     if (!((gate_set >> v) & 1u)) continue;
-    const double gv = exp(dmin - sd[v]) / sum;
-    if (gv > 0.0) hsum += gv * log2(gv);
+    const double gv = se[v] / sum;
+    if (gv > 0.0) hsum += sl[v];
   }
   double hbar = -hsum / log2((double)na);
   hbar = fmin(1.0, fmax(0.0, hbar));
