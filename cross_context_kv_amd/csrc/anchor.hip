@@ -47,6 +47,7 @@ constexpr int kTiles = 8;                       // 16-dim MFMA tiles per head
 constexpr int kMatchWaves = 4, kMatchBands = 2;
 constexpr int kMatchTokens = kMatchWaves * kMatchBands * 16;    // 128
 constexpr int kApplyWaves = 4, kApplyBands = 4;
+constexpr int kApplyThreads = kApplyWaves * 64;
 constexpr int kApplyTokens = kApplyWaves * kApplyBands * 16;    // 256
 constexpr int kSlice = kTiles * 16 * kRank;   // one head's right factor, bf16 elements (8 KiB)
 constexpr int kXcds = 8;
@@ -114,10 +115,8 @@ __device__ __forceinline__ void unpack_lane(const vu4* r, float* x) {
     }
 }
 
-__device__ __forceinline__ void store_lane_row(const DPlane& O, int l, int seg, int h, int j,
-                                               int g, const float* y) {
-  const int64_t off = row_offset(O, l, seg, h, j);
-  if (off < 0) return;
+// The lane's 32 dims of the row at element offset off, rounded to bf16.
+__device__ __forceinline__ void store_lane_at(const DPlane& O, int64_t off, int g, const float* y) {
   bf16_t* row = reinterpret_cast<bf16_t*>(O.data) + off;
 #pragma unroll
   for (int part = 0; part < 2; ++part) {
@@ -568,17 +567,47 @@ struct AnchorApplyParams {
   const float* w;    // [L][2][V][n]
 };
 
-template <int STYLE>
-__device__ __forceinline__ void apply_body(const AnchorApplyParams& P, int l, int p, int h,
-                                           int tile, bf16_t* sbt, float* tab) {
-  float *tc1 = tab, *ts1 = tab + 64, *tc2 = tab + 128, *ts2 = tab + 192;
-  if (STYLE != kStyleNone) {
-    rope_table<kHD, float>(P.rope, P.tgt_off - P.src_off, tc1, ts1);
-    rope_table<kHD, float>(P.rope, P.tgt_off, tc2, ts2);
-  }
-  __syncthreads();
+// One anchor's operands for an apply block, staged in LDS: the head's
+// right-factor slice in MFMA operand order, the left rows of the block's
+// tokens and their weights.
+constexpr int kStageBt = kSlice * 2;                    // 8 KiB
+constexpr int kStageA = kApplyTokens * kRank * 2;       // 16 KiB
+constexpr int kStageW = kApplyThreads * 4;              // 1 KiB
+constexpr int kStageBytes = kStageBt + kStageA + kStageW;
+constexpr int kApplyStages = 3;
+constexpr int kApplyPages = kApplyTokens + 1;           // page ids a tile can span
+// Direct global-to-LDS loads per thread and anchor (slice chunks, row
+// chunks, one weight): the in-order count that the pipeline waits on.
+constexpr int kBtLoads = kStageBt / (16 * kApplyThreads), kALoads = kStageA / (16 * kApplyThreads);
+constexpr int kStageLoads = kBtLoads + kALoads + 1;
+static_assert(kBtLoads * 16 * kApplyThreads == kStageBt && kALoads * 16 * kApplyThreads == kStageA,
+              "stage loads");
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, t = lane & 15;
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+__device__ __forceinline__ lds_ptr to_lds(void* p) {
+  return (lds_ptr)(__builtin_amdgcn_readfirstlane((int)(uintptr_t)p));
+}
+
+// Wait until at most N of this thread's vector memory operations are
+// outstanding and its LDS operations are done, then meet the block.  The
+// compiler may not move memory accesses across it; unlike __syncthreads it
+// does not wait for every direct-to-LDS load in flight.
+template <int N>
+__device__ __forceinline__ void stage_barrier() {
+  static_assert(N >= 0 && N < 16, "vmcnt");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(N | (7 << 4));      // vmcnt(N), lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int STYLE, bool PAGED>
+__device__ __forceinline__ void apply_body(const AnchorApplyParams& P, int l, int p, int h,
+                                           int tile, char* stages, float* tab, int32_t* pages) {
+  float *tc1 = tab, *ts1 = tab + 64, *tc2 = tab + 128, *ts2 = tab + 192;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, t = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j0 = tile * kApplyTokens, jw = j0 + wave * kApplyBands * 16;
   f32x4 acc[kApplyBands][kTiles];
 #pragma unroll
@@ -586,86 +615,150 @@ __device__ __forceinline__ void apply_body(const AnchorApplyParams& P, int l, in
 #pragma unroll
     for (int c = 0; c < kTiles; ++c) acc[b][c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // The eligible anchors in order.  The head's right-factor slice of anchor
-  // i + 1 is staged in LDS (two buffers, in MFMA operand order) and its left
-  // rows and weights loaded while anchor i computes; one barrier per anchor.
-  // Indices are clamped at the end, so every load is unconditional; rows past
-  // the covered prefix read the last covered row and get weight 0.
+  // The eligible anchors in order, three stages deep: anchor i + 2's
+  // operands are loaded into LDS while anchor i computes, one barrier per
+  // anchor.  Token indices are clamped to the covered prefix, so every load
+  // is in bounds; rows past the prefix get weight 0.
   const int nl = P.n_list;
-  if (j0 < P.cover && nl > 0) {
-    const float* wl = P.w + ((int64_t)l * 2 + p) * P.V * P.n;
-    const int last = P.cover - 1;
-    auto anchor = [&](int i) { return (int)((P.list >> (4 * min(i, nl - 1))) & 15u); };
-    auto stage_load = [&](int v, vu4* r) {
-      const bf16_t* src = bt_row(P.G, v, l, p, h * kHD);
-      r[0] = ld16_cached(src + 8 * tid);
-      r[1] = ld16_cached(src + 8 * (tid + 256));
-    };
-    auto stage_store = [&](const vu4* r, bf16_t* buf) {
+  const bool run = j0 < P.cover && nl > 0;
+  const int last = P.cover - 1;
+  const float* wl = P.w + ((int64_t)l * 2 + p) * P.V * P.n;
+  auto issue = [&](int i) {
+    const int v = (int)((P.list >> (4 * i)) & 15u);
+    char* st = stages + (i % kApplyStages) * kStageBytes;
+    // slice chunk k*256 + tid holds rank chunk q of feature row
+    // tile_dim(c, m) (the inverse of slice_chunk)
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        const int u = tid + 256 * k2, f = u >> 2, q = u & 3;
-        const int c = ((f >> 6) << 2) | ((f >> 2) & 3), m = (((f >> 4) & 3) << 2) | (f & 3);
-        *reinterpret_cast<vu4*>(buf + slice_chunk(c, q, m)) = r[k2];
+    for (int k = 0; k < kBtLoads; ++k) {
+      const int u = k * kApplyThreads + tid, c = u >> 6, q = (u >> 4) & 3, m = (u & 15) ^ (q << 2);
+      const bf16_t* src = bt_row(P.G, v, l, p, h * kHD + tile_dim(c, m)) + 8 * q;
+      __builtin_amdgcn_global_load_lds(src, to_lds(st + (k * kApplyThreads + wave * 64) * 16),
+                                       16, 0, 0);
+    }
+    // left rows: token-major, 4 chunks per token
+#pragma unroll
+    for (int k = 0; k < kALoads; ++k) {
+      const int u = k * kApplyThreads + tid;
+      const bf16_t* src = a_row(P.G, v, l, p, min(j0 + (u >> 2), last)) + 8 * (u & 3);
+      __builtin_amdgcn_global_load_lds(
+          src, to_lds(st + kStageBt + (k * kApplyThreads + wave * 64) * 16), 16, 0, 0);
+    }
+    // weights: every thread loads one, so that every wave counts the same
+    // loads (threads past the tile's tokens repeat the last ones)
+    __builtin_amdgcn_global_load_lds(
+        wl + (int64_t)v * P.n + min(j0 + tid % kApplyTokens, last),
+        to_lds(st + kStageBt + kStageA + wave * 64 * 4), 4, 0, 0);
+  };
+  // Row addresses.  A paged plane's page ids for the tile are staged in LDS
+  // before the first anchor (covered by its barrier), so no row address
+  // waits on a global load once stores are in flight.
+  const DPlane& S = P.src[p];
+  const DPlane& O = P.out[p];
+  int first_s = 0, first_o = 0;
+  if (PAGED) {
+    const int j1 = min(j0 + kApplyTokens, P.n);
+    first_s = stage_pages(S, P.seg, j0, j1, pages);
+    first_o = stage_pages(O, P.seg, j0, j1, pages + kApplyPages);
+  }
+  auto src_off = [&](int b) -> int64_t {
+    const int j = min(jw + 16 * b + t, P.n - 1);
+    if (PAGED) return row_offset_staged(S, l, P.seg, h, j, pages, first_s);
+    return (int64_t)l * S.s_layer + (int64_t)P.seg * S.s_seg + (int64_t)h * S.s_head +
+           (int64_t)j * S.s_token;
+  };
+  auto out_off = [&](int b) -> int64_t {
+    const int j = jw + 16 * b + t;
+    if (j >= P.n) return -1;
+    if (PAGED) return row_offset_staged(O, l, P.seg, h, j, pages + kApplyPages, first_o);
+    return (int64_t)l * O.s_layer + (int64_t)P.seg * O.s_seg + (int64_t)h * O.s_head +
+           (int64_t)j * O.s_token;
+  };
+  auto load_band = [&](int b, vu4* r) {
+    const bf16_t* row = reinterpret_cast<const bf16_t*>(S.data) + max(src_off(b), int64_t(0));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r[q] = ld16(row + (q >> 1) * 64 + 16 * g + 8 * (q & 1));
+  };
+  // Source rows of two bands in flight; the first two bands are loaded at
+  // the top of the last anchor, behind its products.
+  vu4 xr[2][4];
+  if (run) {
+    issue(0);
+    if (nl > 1) issue(1);
+  }
+  if (STYLE != kStyleNone) {
+    rope_table<kHD, float>(P.rope, P.tgt_off - P.src_off, tc1, ts1);
+    rope_table<kHD, float>(P.rope, P.tgt_off, tc2, ts2);
+  }
+  if (run) {
+    for (int i = 0; i < nl; ++i) {
+      if (i + 1 < nl)
+        stage_barrier<kStageLoads>();
+      else
+        stage_barrier<0>();
+      if (i + 2 < nl) issue(i + 2);
+      if (i + 1 == nl) {
+        load_band(0, xr[0]);
+        load_band(1, xr[1]);
       }
-    };
-    struct AOps {
-      bf16x8 a[kApplyBands];
-      float w[kApplyBands];
-    };
-    auto load_a = [&](int v, AOps& o) {
+      const char* st = stages + (i % kApplyStages) * kStageBytes;
+      const bf16_t* sb = reinterpret_cast<const bf16_t*>(st);
+      const bf16_t* sa = reinterpret_cast<const bf16_t*>(st + kStageBt);
+      const float* sw = reinterpret_cast<const float*>(st + kStageBt + kStageA);
+      bf16x8 aop[kApplyBands];
+      float wv[kApplyBands];
 #pragma unroll
       for (int b = 0; b < kApplyBands; ++b) {
-        const int j = jw + 16 * b + t;
-        const int jr = min(j, last);
-        o.a[b] = ld_op(a_row(P.G, v, l, p, jr) + 8 * g);
-        const float wv = wl[(int64_t)v * P.n + jr];
-        o.w[b] = j < P.cover ? wv : 0.0f;
+        const int r = wave * kApplyBands * 16 + 16 * b + t;
+        aop[b] = *reinterpret_cast<const bf16x8*>(sa + r * kRank + 8 * g);
+        wv[b] = jw + 16 * b + t < P.cover ? sw[r] : 0.0f;
       }
-    };
-    auto compute = [&](const bf16_t* buf, const AOps& o) {
-      bf16x8 bop[kTiles];
+      // Tile-major: each right-factor tile is read once and serves the four
+      // bands.  Product k + 1 is issued before product k is weighted into
+      // its accumulator (two temporaries), so the matrix unit and the vector
+      // unit overlap instead of each vector step waiting out a product.
+      bf16x8 bop = *reinterpret_cast<const bf16x8*>(sb + slice_chunk(0, g, t));
+      f32x4 d[2];
+      d[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bop, aop[0], f32x4{0.0f, 0.0f, 0.0f, 0.0f},
+                                                     0, 0, 0);
 #pragma unroll
-      for (int c = 0; c < kTiles; ++c)
-        bop[c] = *reinterpret_cast<const bf16x8*>(buf + slice_chunk(c, g, t));
-#pragma unroll
-      for (int b = 0; b < kApplyBands; ++b)
-#pragma unroll
-        for (int c = 0; c < kTiles; ++c) {
-          const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              bop[c], o.a[b], f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[b][c][e] = fmaf(o.w[b], d[e], acc[b][c][e]);
+      for (int k = 0; k < kTiles * kApplyBands; ++k) {
+        const int c = k / kApplyBands, b = k % kApplyBands;
+        if (k + 1 < kTiles * kApplyBands) {
+          const int c1 = (k + 1) / kApplyBands, b1 = (k + 1) % kApplyBands;
+          if (b1 == 0) bop = *reinterpret_cast<const bf16x8*>(sb + slice_chunk(c1, g, t));
+          d[(k + 1) & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              bop, aop[b1], f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
         }
-    };
-    vu4 sr[2];
-    AOps A0, A1;
-    stage_load(anchor(0), sr);
-    load_a(anchor(0), A0);
-    stage_store(sr, sbt);
-    __syncthreads();
-    for (int i = 0; i < nl; i += 2) {
-      stage_load(anchor(i + 1), sr);
-      load_a(anchor(i + 1), A1);
-      compute(sbt, A0);
-      stage_store(sr, sbt + kSlice);
-      __syncthreads();
-      stage_load(anchor(i + 2), sr);
-      load_a(anchor(i + 2), A0);
-      if (i + 1 < nl) compute(sbt + kSlice, A1);
-      stage_store(sr, sbt);
-      __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[b][c][e] = fmaf(wv[b], d[k & 1][e], acc[b][c][e]);
+      }
     }
+    // Nothing is in flight here (the last anchor waited for everything);
+    // saying so lets the epilogue's waits count its own loads exactly.
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));   // vmcnt(0)
+  } else {
+    __syncthreads();
   }
 
+  // Epilogue.  The source loads are unconditional (a row past the end reads
+  // the last row; in a paged plane a row on a bad page reads element 0 and is
+  // zeroed) and one band ahead, and only the store depends on the row, so no
+  // band's loads wait for an earlier band's stores (loads and stores share
+  // one in-order counter).
+  if (!run) load_band(0, xr[0]);
 #pragma unroll
   for (int b = 0; b < kApplyBands; ++b) {
-    const int j = jw + 16 * b + t;
-    if (j >= P.n) continue;
-    vu4 xr[4];
+    if (b + 1 < kApplyBands && !(run && b == 0)) load_band(b + 1, xr[(b + 1) & 1]);
+    const bool valid = !PAGED || src_off(b) >= 0;
     float x[32], dl[32];
-    load_lane_raw(P.src[p], l, P.seg, h, j, P.n, g, xr);
-    unpack_lane(xr, x);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t u = valid ? xr[b & 1][q][w] : 0u;
+        x[8 * q + 2 * w] = bf16_lo(u);
+        x[8 * q + 2 * w + 1] = bf16_hi(u);
+      }
 #pragma unroll
     for (int c = 0; c < kTiles; ++c)
 #pragma unroll
@@ -676,18 +769,20 @@ __device__ __forceinline__ void apply_body(const AnchorApplyParams& P, int l, in
     }
 #pragma unroll
     for (int e = 0; e < 32; ++e) x[e] += dl[e];
-    store_lane_row(P.out[p], l, P.seg, h, j, g, x);
+    const int64_t oq = out_off(b);
+    if (oq >= 0) store_lane_at(O, oq, g, x);
   }
 }
 
 // Blocks of one (layer, plane) run on one XCD and walk its heads fastest, so
 // the delta left factors and weights of a token tile are read from HBM once
 // and reused from L2 by every head.
-template <int STYLE>
+template <int STYLE, bool PAGED>
 __global__ __launch_bounds__(kApplyWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void anchor_apply_kernel(AnchorApplyParams P) {
-  __shared__ __attribute__((aligned(16))) bf16_t sbt[2 * kSlice];
+  __shared__ __attribute__((aligned(16))) char stages[kApplyStages * kStageBytes];
   __shared__ float tab[4 * (kHD / 2)];
+  __shared__ int32_t pages[PAGED ? 2 * kApplyPages : 1];
   const int id = blockIdx.x, xcd = id % kXcds, k = id / kXcds;
   const int h = k % P.H, k2 = k / P.H;
   const int tile = k2 % P.n_tiles;
@@ -695,9 +790,9 @@ void anchor_apply_kernel(AnchorApplyParams P) {
   if (pair >= P.n_pairs) return;
   const int l = pair >> 1;
   if ((pair & 1) == 0)
-    apply_body<STYLE>(P, l, 0, h, tile, sbt, tab);
+    apply_body<STYLE, PAGED>(P, l, 0, h, tile, stages, tab, pages);
   else
-    apply_body<kStyleNone>(P, l, 1, h, tile, sbt, tab);
+    apply_body<kStyleNone, PAGED>(P, l, 1, h, tile, stages, tab, pages);
 }
 
 // ----------------------------------------------------------------------------
@@ -943,9 +1038,19 @@ extern "C" kvfix_status kvfix_anchor_apply(const kvfix_plane* src_k, const kvfix
   const int64_t grid =
       (int64_t)P.H * P.n_tiles * ((P.n_pairs + kXcds - 1) / kXcds) * kXcds;
   const hipStream_t st = (hipStream_t)stream;
-  if (rope_style == KVFIX_ROPE_HALF)
-    anchor_apply_kernel<kStyleHalf><<<dim3((unsigned)grid), dim3(kApplyWaves * 64), 0, st>>>(P);
-  else
-    anchor_apply_kernel<kStyleInter><<<dim3((unsigned)grid), dim3(kApplyWaves * 64), 0, st>>>(P);
+  const dim3 gd((unsigned)grid), bd(kApplyWaves * 64);
+  const bool paged = P.src[0].page_table || P.src[1].page_table || P.out[0].page_table ||
+                     P.out[1].page_table;
+  if (rope_style == KVFIX_ROPE_HALF) {
+    if (paged)
+      anchor_apply_kernel<kStyleHalf, true><<<gd, bd, 0, st>>>(P);
+    else
+      anchor_apply_kernel<kStyleHalf, false><<<gd, bd, 0, st>>>(P);
+  } else {
+    if (paged)
+      anchor_apply_kernel<kStyleInter, true><<<gd, bd, 0, st>>>(P);
+    else
+      anchor_apply_kernel<kStyleInter, false><<<gd, bd, 0, st>>>(P);
+  }
   return launch_status();
 }
