@@ -87,6 +87,45 @@ __device__ __forceinline__ bf16x8 ld_op(const bf16_t* p) {
   return __builtin_bit_cast(bf16x8, ld16_cached(p));
 }
 
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+__device__ __forceinline__ lds_ptr to_lds(void* p) {
+  return (lds_ptr)(__builtin_amdgcn_readfirstlane((int)(uintptr_t)p));
+}
+
+// Wait until at most N of this thread's vector memory operations are
+// outstanding and its LDS operations are done, then meet the block.  The
+// compiler may not move memory accesses across it; unlike __syncthreads it
+// does not wait for every direct-to-LDS load in flight.
+template <int N>
+__device__ __forceinline__ void stage_barrier() {
+  static_assert(N >= 0 && N < 16, "vmcnt");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(N | (7 << 4));      // vmcnt(N), lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Direct global-to-LDS loads of one head's right-factor slice (anchor v,
+// layer l, plane p, head h) into an LDS stage in MFMA operand order: slice
+// chunk k * 256 + tid holds rank chunk q of feature row tile_dim(c, m), the
+// inverse of slice_chunk.  Two loads per thread of a 256-thread block.
+constexpr int kSliceLoads = kSlice * 2 / (16 * 256);
+__device__ __forceinline__ void stage_slice(const Pool& G, int v, int l, int p, int h, char* st,
+                                            int tid, int wave) {
+#pragma unroll
+  for (int k = 0; k < kSliceLoads; ++k) {
+    const int u = k * 256 + tid, c = u >> 6, q = (u >> 4) & 3, m = (u & 15) ^ (q << 2);
+    const bf16_t* src = bt_row(G, v, l, p, h * kHD + tile_dim(c, m)) + 8 * q;
+    __builtin_amdgcn_global_load_lds(src, to_lds(st + (k * 256 + wave * 64) * 16), 16, 0, 0);
+  }
+}
+
+// Keeps the compiler from moving memory accesses across this point, so that
+// loads are issued in the order the stage barriers count them.
+__device__ __forceinline__ void issue_order() { asm volatile("" ::: "memory"); }
+
+
 // The lane's 32 dims of row (l, seg, h, j) as four raw 16-byte pieces:
 // dims [16g, 16g+8), [16g+8, 16g+16), [64+16g, ..+8), [64+16g+8, ..+16).
 // Zeros for a row outside the segment or on a bad page.
@@ -578,29 +617,9 @@ constexpr int kApplyStages = 3;
 constexpr int kApplyPages = kApplyTokens + 1;           // page ids a tile can span
 // Direct global-to-LDS loads per thread and anchor (slice chunks, row
 // chunks, one weight): the in-order count that the pipeline waits on.
-constexpr int kBtLoads = kStageBt / (16 * kApplyThreads), kALoads = kStageA / (16 * kApplyThreads);
-constexpr int kStageLoads = kBtLoads + kALoads + 1;
-static_assert(kBtLoads * 16 * kApplyThreads == kStageBt && kALoads * 16 * kApplyThreads == kStageA,
-              "stage loads");
-
-typedef __attribute__((address_space(3))) void* lds_ptr;
-
-__device__ __forceinline__ lds_ptr to_lds(void* p) {
-  return (lds_ptr)(__builtin_amdgcn_readfirstlane((int)(uintptr_t)p));
-}
-
-// Wait until at most N of this thread's vector memory operations are
-// outstanding and its LDS operations are done, then meet the block.  The
-// compiler may not move memory accesses across it; unlike __syncthreads it
-// does not wait for every direct-to-LDS load in flight.
-template <int N>
-__device__ __forceinline__ void stage_barrier() {
-  static_assert(N >= 0 && N < 16, "vmcnt");
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(N | (7 << 4));      // vmcnt(N), lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
+constexpr int kALoads = kStageA / (16 * kApplyThreads);
+constexpr int kStageLoads = kSliceLoads + kALoads + 1;
+static_assert(kApplyThreads == 256 && kALoads * 16 * kApplyThreads == kStageA, "stage loads");
 
 template <int STYLE, bool PAGED>
 __device__ __forceinline__ void apply_body(const AnchorApplyParams& P, int l, int p, int h,
@@ -626,15 +645,7 @@ __device__ __forceinline__ void apply_body(const AnchorApplyParams& P, int l, in
   auto issue = [&](int i) {
     const int v = (int)((P.list >> (4 * i)) & 15u);
     char* st = stages + (i % kApplyStages) * kStageBytes;
-    // slice chunk k*256 + tid holds rank chunk q of feature row
-    // tile_dim(c, m) (the inverse of slice_chunk)
-#pragma unroll
-    for (int k = 0; k < kBtLoads; ++k) {
-      const int u = k * kApplyThreads + tid, c = u >> 6, q = (u >> 4) & 3, m = (u & 15) ^ (q << 2);
-      const bf16_t* src = bt_row(P.G, v, l, p, h * kHD + tile_dim(c, m)) + 8 * q;
-      __builtin_amdgcn_global_load_lds(src, to_lds(st + (k * kApplyThreads + wave * 64) * 16),
-                                       16, 0, 0);
-    }
+    stage_slice(P.G, v, l, p, h, st, tid, wave);
     // left rows: token-major, 4 chunks per token
 #pragma unroll
     for (int k = 0; k < kALoads; ++k) {
