@@ -83,6 +83,16 @@ __device__ __forceinline__ int slice_chunk(int c, int q, int m) {
   return ((c * 4 + q) * 16 + (m ^ (q << 2))) * 8;
 }
 
+// Layer-plane pairs on XCDs: XCD x takes layers x, x + 8, ..., each with its
+// key plane then its value plane, so every XCD holds both planes' work (the
+// key plane's rotations and the value plane's squares cost differently) and
+// one pair's blocks share that XCD's L2.  Local slot q of XCD x is layer
+// (q / 2) * 8 + x, plane q % 2.
+__host__ __device__ __forceinline__ int xcd_pair(int q, int xcd) {
+  return 2 * ((q >> 1) * kXcds + xcd) + (q & 1);
+}
+inline int64_t pair_slots(int64_t L) { return 2 * ((L + kXcds - 1) / kXcds) * kXcds; }
+
 __device__ __forceinline__ bf16x8 ld_op(const bf16_t* p) {
   return __builtin_bit_cast(bf16x8, ld16_cached(p));
 }
@@ -446,7 +456,7 @@ void anchor_match_kernel(MatchParams P) {
   const int id = blockIdx.x, xcd = id % kXcds, k = id / kXcds;
   const int hg = k % P.HG, k2 = k / P.HG;
   const int tile = k2 % P.n_tiles;
-  const int pair = (k2 / P.n_tiles) * kXcds + xcd;
+  const int pair = xcd_pair(k2 / P.n_tiles, xcd);
   if (pair >= P.n_pairs) return;
   const int l = pair >> 1;
   if ((pair & 1) == 0)
@@ -797,7 +807,7 @@ void anchor_apply_kernel(AnchorApplyParams P) {
   const int id = blockIdx.x, xcd = id % kXcds, k = id / kXcds;
   const int h = k % P.H, k2 = k / P.H;
   const int tile = k2 % P.n_tiles;
-  const int pair = (k2 / P.n_tiles) * kXcds + xcd;
+  const int pair = xcd_pair(k2 / P.n_tiles, xcd);
   if (pair >= P.n_pairs) return;
   const int l = pair >> 1;
   if ((pair & 1) == 0)
@@ -972,8 +982,7 @@ extern "C" kvfix_status kvfix_anchor_match(const kvfix_plane* src_k, const kvfix
     }
     P.part1 = reinterpret_cast<float*>(wsb);
     P.gpart = gpart;
-    const int64_t grid =
-        (int64_t)P.HG * P.n_tiles * ((P.n_pairs + kXcds - 1) / kXcds) * kXcds;
+    const int64_t grid = (int64_t)P.HG * P.n_tiles * pair_slots(L);
     if (grid > kMaxGrid) return KVFIX_ERR_ARG;
     const dim3 gd((unsigned)grid), bd(kMatchWaves * 64);
     if (rope_style == KVFIX_ROPE_HALF) {
@@ -1046,8 +1055,8 @@ extern "C" kvfix_status kvfix_anchor_apply(const kvfix_plane* src_k, const kvfix
   for (int v = 0; v < V; ++v)
     if ((e.elig >> v) & 1u) P.list |= (uint64_t)v << (4 * P.n_list++);
   P.w = weights;
-  const int64_t grid =
-      (int64_t)P.H * P.n_tiles * ((P.n_pairs + kXcds - 1) / kXcds) * kXcds;
+  const int64_t grid = (int64_t)P.H * P.n_tiles * pair_slots(L);
+  if (grid > kMaxGrid) return KVFIX_ERR_ARG;
   const hipStream_t st = (hipStream_t)stream;
   const dim3 gd((unsigned)grid), bd(kApplyWaves * 64);
   const bool paged = P.src[0].page_table || P.src[1].page_table || P.out[0].page_table ||
