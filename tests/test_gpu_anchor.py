@@ -227,6 +227,53 @@ def test_paged_source_and_in_place_apply():
         assert np.array_equal(pv_np[:, page, j % ps], gv[:, 0, :, j])
 
 
+@pytest.mark.parametrize("V", [1, 3, 16])
+def test_list_lengths_and_ragged_tiles(V):
+    """One, three and sixteen eligible anchors (the apply keeps three
+    anchors' operands in a ring of LDS stages, so these reuse no stage, each
+    once, and five times) over three token tiles of the apply, the last one
+    ragged."""
+    n = 600
+    case = anchor_case(L=2, H=2, n=n, V=V, n_max=n, seed=70 + V)
+    lengths = [n] * V
+    log("anchor list length", V)
+    w, gate, acc = gpu_match(case, lengths, n // 2, 0.5)
+    check_weights(case, lengths, w)
+    check_gate(case, lengths, n // 2, 0.5, gate, acc)
+    check_apply(case, lengths, w, tgt_off=321)
+
+
+def test_paged_one_token_pages_partial_cover():
+    """A paged plane with one token per page (a tile spans 256 page ids) and
+    a covered prefix that ends inside the first tile, so the second tile has
+    no anchor work: in place on the pool against the dense apply."""
+    case = anchor_case(L=2, H=2, n=300, V=3, n_max=300, seed=69)
+    L, H, n, hd = 2, 2, 300, 128
+    lengths = [150, 150, 90]                 # E = {0, 1}, covered prefix 150
+    n_pages = n + 7
+    rng = np.random.default_rng(9)
+    pt_np = rng.permutation(n_pages)[:n].astype(np.int32)[None]
+    pools = []
+    for key in ("src_k", "src_v"):
+        src = case[key][:, 0]                                   # [L, H, n, hd]
+        pool = np.zeros((L, n_pages, 1, H, hd), dtype=np.uint16)
+        pool[:, pt_np[0], 0] = src.transpose(0, 2, 1, 3)
+        pools.append(from_np(pool, DEV))
+    pt = torch.from_numpy(pt_np).to(DEV)
+    pk, pv = Plane.paged(pools[0], pt, 1, n), Plane.paged(pools[1], pt, 1, n)
+    log("anchor apply in place, one-token pages")
+    w, gate, acc = gpu_match(case, lengths, 100, 0.5)
+    check_weights(case, lengths, w)
+    delta = AnchorPool(from_np(case["a_delta"], DEV), from_np(case["bt_delta"], DEV), lengths)
+    kv.kvfix_anchor_apply(pk, pv, 0, delta, w, case["src_off"], 77, case["theta"], pk, pv)
+    torch.cuda.synchronize()
+    gk, gv = gpu_apply(case, lengths, w, 77)
+    pk_np, pv_np = to_np(pools[0]), to_np(pools[1])
+    assert np.array_equal(pk_np[:, pt_np[0], 0], gk[:, 0].transpose(0, 2, 1, 3))
+    assert np.array_equal(pv_np[:, pt_np[0], 0], gv[:, 0].transpose(0, 2, 1, 3))
+    check_apply(case, lengths, w, tgt_off=77)
+
+
 def test_runs_are_bitwise_repeatable():
     case = anchor_case(L=2, H=2, n=257, V=4, seed=66)
     lengths = [257] * 4
