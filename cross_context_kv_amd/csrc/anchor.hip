@@ -12,11 +12,13 @@
 //          distance to the source row over all heads (keys first turned to
 //          canonical positions) and the softmax over anchors (T = 1): the
 //          token-wise weights.  On the value plane the same pass accumulates
-//          the squared distances over the gate prefix; a one-block finish
-//          turns them into the gate distances, the normalized entropy and
-//          the decision.
-//   apply  reconstructs the delta rows A_v B_v with MFMA, blends them with
-//          the token weights in fp32 and adds them to the re-aligned source:
+//          the squared distances over the gate prefix.  A finish kernel forms
+//          the weights from the head sums and pre-adds the gate partials; a
+//          one-block gate kernel turns those into the gate distances, the
+//          normalized entropy and the decision.
+//   apply  reconstructs the delta rows A_v B_v with MFMA (each anchor's
+//          operands staged in LDS three anchors ahead), blends them with the
+//          token weights in fp32 and adds them to the re-aligned source:
 //          keys R(p_t - p_s) x + R(p_t) delta, values x + delta; rows past
 //          the covered prefix are only re-aligned.
 //
