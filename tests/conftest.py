@@ -15,7 +15,7 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # GPU tests are skipped (not failed) when no GPU is visible, so the CPU
-    # suite stays green; on a GPU machine they run and must pass.
+    # suite stays green; where a GPU is visible they run and must pass.
     try:
         import torch
         has_gpu = torch.cuda.is_available()
