@@ -953,8 +953,8 @@ extern "C" kvfix_status kvfix_anchor_match(const kvfix_plane* src_k, const kvfix
   char* wsb = static_cast<char*>(ws);
   double* gpart = reinterpret_cast<double*>(wsb + W.part1);
   double* gsum = reinterpret_cast<double*>(wsb + W.part1 + W.gpart);
-  const int32_t n_tiles = (n + kMatchTokens - 1) / kMatchTokens;
-  const int32_t n_fin = (n + kFinishTokens - 1) / kFinishTokens;
+  const int32_t n_tiles = (int32_t)ceil_div(n, kMatchTokens);
+  const int32_t n_fin = (int32_t)ceil_div(n, kFinishTokens);
 
   if (V > 0 && n > 0 && L > 0 && H > 0) {
     MatchParams P;
@@ -1053,7 +1053,7 @@ extern "C" kvfix_status kvfix_anchor_apply(const kvfix_plane* src_k, const kvfix
   P.elig = e.elig;
   P.cover = e.cover;
   P.n_pairs = 2 * L;
-  P.n_tiles = (n + kApplyTokens - 1) / kApplyTokens;
+  P.n_tiles = (int32_t)ceil_div(n, kApplyTokens);
   for (int v = 0; v < V; ++v)
     if ((e.elig >> v) & 1u) P.list |= (uint64_t)v << (4 * P.n_list++);
   P.w = weights;

@@ -70,7 +70,7 @@ __global__ __launch_bounds__(kSelBlock) void expand_chunks_kernel(
   __shared__ uint32_t scan[160];
   __shared__ int32_t s_first[kSelBlock], s_off[kSelBlock];
   const int row = blockIdx.x, t = threadIdx.x;
-  const int nc = (n + B - 1) / B;
+  const int nc = (int)(((int64_t)n + B - 1) / B);
   const int32_t* ci = chunk_idx + (int64_t)row * c;
   int32_t* out = idx + (int64_t)row * c * B;
   uint32_t* m = mask + (int64_t)row * words;
@@ -459,7 +459,7 @@ extern "C" kvfix_status kvfix_expand_chunks(const int32_t* chunk_idx, int32_t n_
       (c > 0 && (chunk_idx == nullptr || idx == nullptr)))
     return KVFIX_ERR_ARG;
   if (n_rows > kMaxGrid) return KVFIX_ERR_ARG;
-  const int words = (n + 31) / 32;
+  const int words = (int)ceil_div(n, 32);
   expand_chunks_kernel<<<dim3((unsigned)n_rows), dim3(kSelBlock), 0, (hipStream_t)stream>>>(
       chunk_idx, c, n, chunk, words, idx, counts, mask);
   return launch_status();
@@ -479,7 +479,7 @@ extern "C" kvfix_status kvfix_select_grow(const float* scores, int32_t n_rows, i
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(&select_grow_kernel),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)G.bytes) != hipSuccess)
     return KVFIX_ERR_HIP;
-  const int words = (n + 31) / 32;
+  const int words = (int)ceil_div(n, 32);
   select_grow_kernel<<<dim3((unsigned)n_rows), dim3(kSelBlock), G.bytes, (hipStream_t)stream>>>(
       scores, n, b, tau, idx, mask, words, G);
   return launch_status();

@@ -865,7 +865,7 @@ extern "C" kvfix_status kvfix_rope_shift(const kvfix_plane* src, const kvfix_pla
   P.rope = make_rope_args(rope, src->head_dim);
   P.S = src->n_segs; P.H = src->n_heads; P.n = src->n_tokens;
   P.rows_per_block = kRowsPerBlock;
-  P.chunks = (src->n_tokens + kRowsPerBlock - 1) / kRowsPerBlock;
+  P.chunks = (int32_t)ceil_div(src->n_tokens, kRowsPerBlock);
   const int64_t grid = units * P.chunks;
   if (grid > kMaxGrid) return KVFIX_ERR_ARG;
   return dispatch_t_hd_style<RopeShiftLaunch>(src->dtype, src->head_dim, rope->style, P, grid,
@@ -981,7 +981,7 @@ extern "C" kvfix_status kvfix_apply_ex(const kvfix_plane* reuse, const kvfix_pla
             (P.lr.sB_seg * 4) % 16 == 0 && (P.lr.sB_head * 4) % 16 == 0;
   P.rope = make_rope_args(rope, reuse->head_dim);
   P.S = reuse->n_segs; P.L = reuse->n_layers; P.H = reuse->n_heads; P.n = reuse->n_tokens;
-  P.mask_words = (reuse->n_tokens + 31) / 32;
+  P.mask_words = (int32_t)ceil_div(reuse->n_tokens, 32);
   P.per_head = opt ? opt->per_head : 0;
   P.cover = opt ? opt->cover : nullptr;
   const int ch = apply_chunk_rows(reuse->dtype == KVFIX_F32 ? 4 : 8, reuse->head_dim);

@@ -552,7 +552,7 @@ extern "C" kvfix_status kvfix_diff_encode(const kvfix_plane* master_k, const kvf
   KVFIX_TRY(check_rope(to_master, master_k->head_dim));
   const int32_t A = sib_k->n_segs, L = sib_k->n_layers, n = sib_k->n_tokens;
   const int32_t bt = out->block_tokens;
-  const int32_t nb = (n + bt - 1) / bt, words = (nb + 31) / 32;
+  const int32_t nb = (int32_t)ceil_div(n, bt), words = (int32_t)ceil_div(nb, 32);
   if ((int64_t)A * L > 0x7fffffff / 2) return KVFIX_ERR_ARG;
   if ((int64_t)A * L * words > 0 && out->mask == nullptr) return KVFIX_ERR_ARG;
   const size_t need = kvfix_diff_encode_workspace(A, L, n, bt);
@@ -609,7 +609,7 @@ extern "C" kvfix_status kvfix_diff_decode(const kvfix_plane* master_k, const kvf
   KVFIX_TRY(check_rope(from_master, master_k->head_dim));
   const int32_t A = out_k->n_segs, L = out_k->n_layers, n = out_k->n_tokens;
   const int32_t bt = diff->block_tokens;
-  const int32_t nb = (n + bt - 1) / bt, words = (nb + 31) / 32;
+  const int32_t nb = (int32_t)ceil_div(n, bt), words = (int32_t)ceil_div(nb, 32);
   if (A == 0 || L == 0 || n == 0 || out_k->n_heads == 0) return KVFIX_OK;
   if (diff->mask == nullptr) return KVFIX_ERR_ARG;
   const size_t need = kvfix_diff_decode_workspace(A, master_k->head_dim);

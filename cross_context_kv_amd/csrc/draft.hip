@@ -418,9 +418,9 @@ extern "C" kvfix_status kvfix_score_draft(const void* q, int32_t n_q_heads, int3
   const int32_t Lf = L - first_layer;
   const int64_t qps = (int64_t)Lf * n_q_heads * n_draft;
   const int64_t rows = (int64_t)S * qps;
-  const int32_t n_chunks = (n + kDraftChunk - 1) / kDraftChunk;
+  const int32_t n_chunks = (int32_t)ceil_div(n, kDraftChunk);
   const int splits = qps > 0 ? mass_splits(qps) : 1;
-  const int key_blocks = (n + kMassKeys - 1) / kMassKeys;
+  const int key_blocks = (int)ceil_div(n, kMassKeys);
   // every grid size is checked before the first launch
   const int64_t lgrid = (int64_t)S * Lf * k->n_heads * n_chunks;
   const int64_t mgrid = (int64_t)S * splits * key_blocks;

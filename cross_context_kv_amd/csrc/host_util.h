@@ -114,6 +114,10 @@ inline int rank_variant(int r) { return r == 0 ? 0 : r <= 2 ? 2 : r <= 4 ? 4 : 8
 
 constexpr int64_t kMaxGrid = 0x7fffffffLL;
 
+// ceil(a / b) for a >= 0 and b > 0, in 64 bits: token counts near 2^31 do
+// not wrap (a + b - 1 would overflow int32).
+constexpr int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
 // Compute units of the current device, cached per device id.
 inline int device_cus() {
   static std::atomic<int> cache[64];

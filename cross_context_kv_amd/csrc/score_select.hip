@@ -211,7 +211,7 @@ struct ScoreLaunch {
                    ? 1
                    : (int)std::max<int64_t>(
                          1, std::min<int64_t>(kScoreGroupsMax, groups_total / kScoreMinBlocks));
-    Q.tok_blocks = ((P.n + RPW - 1) / RPW + Q.groups - 1) / Q.groups;
+    Q.tok_blocks = (int32_t)ceil_div(ceil_div(P.n, RPW), Q.groups);
     const int64_t grid = (int64_t)Q.tok_blocks * P.S;
     if (grid > kMaxGrid) return KVFIX_ERR_ARG;
     if constexpr (STYLE == kStyleNone)
@@ -320,10 +320,10 @@ extern "C" kvfix_status kvfix_select_topb(const float* scores, int32_t n_rows, i
   if (n_rows == 0 || n == 0) return KVFIX_OK;
   if (scores == nullptr || mask == nullptr || (b > 0 && idx == nullptr)) return KVFIX_ERR_ARG;
   if (n_rows > kMaxGrid) return KVFIX_ERR_ARG;
-  const int words = (n + 31) / 32;
+  const int words = (int)ceil_div(n, 32);
   // register keys per thread: the fewest columns (a power of two) that hold
   // the row; longer rows stream from memory through the 32-column path
-  const int cols = (n + kSelBlock - 1) / kSelBlock;
+  const int cols = (int)ceil_div(n, kSelBlock);
   const dim3 grid((unsigned)n_rows), block(kSelBlock);
   hipStream_t st = (hipStream_t)stream;
   if (cols <= 1) select_topb_kernel<1><<<grid, block, 0, st>>>(scores, n, b, idx, mask, words);

@@ -199,6 +199,12 @@ def test_anchor_call_validation():
     assert apply(tgt_off=-(1 << 23) - 50) == 1                      # tgt - src out of range too
     assert apply(wts=None) == 1                                     # eligible anchors need weights
     assert apply(ok=plane(n_heads=3)) == 1
+    # more blocks than one launch takes (heads x 256-token tiles x layer-plane
+    # slots past 2^31 - 1): refused before any launch
+    n_big, h_big = (1 << 31) - 1, 64
+    big = plane(n_layers=2, n_heads=h_big, n_tokens=n_big, s_token=128, s_head=n_big * 128,
+                s_seg=h_big * n_big * 128, s_layer=h_big * n_big * 128)
+    assert apply(pk=big, pv=big, ok=big, ov=big, pool=anchor_pool(n_max=n_big)) == 1
     # no eligible anchor and no rows: nothing to launch
     assert apply(wts=None, pool=anchor_pool(lengths=[0, 0, 0]), pk=plane(n_layers=0),
                  pv=plane(n_layers=0), ok=plane(n_layers=0), ov=plane(n_layers=0)) == 0
