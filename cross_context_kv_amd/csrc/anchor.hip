@@ -654,23 +654,41 @@ __device__ __forceinline__ void apply_body(const AnchorApplyParams& P, int l, in
   const bool run = j0 < P.cover && nl > 0;
   const int last = P.cover - 1;
   const float* wl = P.w + ((int64_t)l * 2 + p) * P.V * P.n;
+  // Each lane's byte offsets from an anchor's slice, the tile's first left
+  // row and first weight, the same for every anchor (and small: inside one
+  // head's slice or one tile): a staging load is then the anchor's uniform
+  // base plus a 32-bit lane offset.  Slice chunk k * 256 + tid holds rank
+  // chunk q of feature row tile_dim(c, m) (the inverse of slice_chunk); left
+  // rows go token-major, 4 chunks per token; every thread loads one weight,
+  // so that every wave counts the same loads (threads past the tile's tokens
+  // repeat the last ones).
+  uint32_t ob[kSliceLoads], oa[kALoads];
+#pragma unroll
+  for (int k = 0; k < kSliceLoads; ++k) {
+    const int u = k * 256 + tid, c = u >> 6, q = (u >> 4) & 3, m = (u & 15) ^ (q << 2);
+    ob[k] = (uint32_t)(((h * kHD + tile_dim(c, m)) * kRank + 8 * q) * 2);
+  }
+#pragma unroll
+  for (int k = 0; k < kALoads; ++k) {
+    const int u = k * kApplyThreads + tid;
+    oa[k] = (uint32_t)(((min(j0 + (u >> 2), last) - j0) * kRank + 8 * (u & 3)) * 2);
+  }
+  const uint32_t ow = (uint32_t)((min(j0 + tid % kApplyTokens, last) - j0) * 4);
   auto issue = [&](int i) {
     const int v = (int)((P.list >> (4 * i)) & 15u);
     char* st = stages + (i % kApplyStages) * kStageBytes;
-    stage_slice(P.G, v, l, p, h, st, tid, wave);
-    // left rows: token-major, 4 chunks per token
+    const char* bt = reinterpret_cast<const char*>(bt_row(P.G, v, l, p, 0));
+    const char* ar = reinterpret_cast<const char*>(a_row(P.G, v, l, p, j0));
+    const char* wr = reinterpret_cast<const char*>(wl + (int64_t)v * P.n + j0);
 #pragma unroll
-    for (int k = 0; k < kALoads; ++k) {
-      const int u = k * kApplyThreads + tid;
-      const bf16_t* src = a_row(P.G, v, l, p, min(j0 + (u >> 2), last)) + 8 * (u & 3);
+    for (int k = 0; k < kSliceLoads; ++k)
+      __builtin_amdgcn_global_load_lds(bt + ob[k], to_lds(st + (k * 256 + wave * 64) * 16), 16, 0, 0);
+#pragma unroll
+    for (int k = 0; k < kALoads; ++k)
       __builtin_amdgcn_global_load_lds(
-          src, to_lds(st + kStageBt + (k * kApplyThreads + wave * 64) * 16), 16, 0, 0);
-    }
-    // weights: every thread loads one, so that every wave counts the same
-    // loads (threads past the tile's tokens repeat the last ones)
-    __builtin_amdgcn_global_load_lds(
-        wl + (int64_t)v * P.n + min(j0 + tid % kApplyTokens, last),
-        to_lds(st + kStageBt + kStageA + wave * 64 * 4), 4, 0, 0);
+          ar + oa[k], to_lds(st + kStageBt + (k * kApplyThreads + wave * 64) * 16), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(wr + ow, to_lds(st + kStageBt + kStageA + wave * 64 * 4), 4,
+                                     0, 0);
   };
   // Row addresses.  A paged plane's page ids for the tile are staged in LDS
   // before the first anchor (covered by its barrier), so no row address
