@@ -341,27 +341,38 @@ __device__ __forceinline__ void match_body(const MatchParams& P, int l, int hg, 
     }
   }
 
+  // Every per-anchor load is a uniform base (the anchor's slice, its left
+  // row of the tile's first token) plus a lane offset computed here once.
+  // The staged slice's LDS positions are per lane and fixed as well.
+  int spos[2];
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2) {
+    const int u = tid + 256 * k2, f = u >> 2, q = u & 3;
+    const int c = ((f >> 6) << 2) | ((f >> 2) & 3), m = (((f >> 4) & 3) << 2) | (f & 3);
+    spos[k2] = slice_chunk(c, q, m);
+  }
   auto stage_load = [&](int v, vu4* r) {
-    const bf16_t* src = bt_row(P.G, v, l, p, h * kHD);
-    r[0] = ld16_cached(src + 8 * tid);
-    r[1] = ld16_cached(src + 8 * (tid + 256));
+    const char* src = reinterpret_cast<const char*>(bt_row(P.G, v, l, p, h * kHD));
+    r[0] = ld16_cached(src + 16 * tid);
+    r[1] = ld16_cached(src + 16 * (tid + 256));
   };
   auto stage_store = [&](const vu4* r, bf16_t* buf) {
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-      const int u = tid + 256 * k2, f = u >> 2, q = u & 3;
-      const int c = ((f >> 6) << 2) | ((f >> 2) & 3), m = (((f >> 4) & 3) << 2) | (f & 3);
-      *reinterpret_cast<vu4*>(buf + slice_chunk(c, q, m)) = r[k2];
-    }
+    for (int k2 = 0; k2 < 2; ++k2) *reinterpret_cast<vu4*>(buf + spos[k2]) = r[k2];
   };
   // Rows are clamped to the slab's last row, so every load stays inside the
   // pool; a row an anchor does not store only feeds a sum that no later step
   // reads (tokens past its length never use that anchor).
   const int last = (int)P.G.n_max - 1;        // a listed anchor stores >= 1 row
-  auto load_a = [&](int v, bf16x8* a) {
+  const int jb = min(j0, last);
+  uint32_t oa[kMatchBands];
 #pragma unroll
-    for (int b = 0; b < kMatchBands; ++b)
-      a[b] = ld_op(a_row(P.G, v, l, p, min(jw + 16 * b + t, last)) + 8 * g);
+  for (int b = 0; b < kMatchBands; ++b)
+    oa[b] = (uint32_t)((min(jw + 16 * b + t, last) - jb) * kRank * 2 + 16 * g);
+  auto load_a = [&](int v, bf16x8* a) {
+    const char* base = reinterpret_cast<const char*>(a_row(P.G, v, l, p, jb));
+#pragma unroll
+    for (int b = 0; b < kMatchBands; ++b) a[b] = __builtin_bit_cast(bf16x8, ld16_cached(base + oa[b]));
   };
   auto compute = [&](const bf16_t* buf, const bf16x8* a, int i) {
     const int v = anchor(i);
