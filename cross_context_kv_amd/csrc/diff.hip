@@ -290,7 +290,68 @@ struct DecodeParams {
   int32_t A, L, H, n, bt, nb, words;
 };
 
-template <typename T, int HD, int STYLE>
+// Wait until at most N of this wave's vector memory operations are in
+// flight (LDS operations not waited on); memory accesses stay on their side.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// Element offset of row (l, s, h, j) of a plane known to be dense.
+__device__ __forceinline__ int64_t dense_offset(const DPlane& p, int l, int s, int h, int j) {
+  return (int64_t)l * p.s_layer + (int64_t)s * p.s_seg + (int64_t)h * p.s_head +
+         (int64_t)j * p.s_token;
+}
+
+// An LDS address as a wave-uniform 32-bit offset.
+__device__ __forceinline__ lds_ptr to_lds(void* p) {
+  return (lds_ptr)(__builtin_amdgcn_readfirstlane((int)(uintptr_t)p));
+}
+
+// Direct-to-LDS loads of this wave's master rows (K and V, two 16-byte
+// pieces each per lane) for head h, token j of a dense master: piece q of
+// lane L lands at ring[q * 64 + L].
+template <typename T, typename M>
+__device__ __forceinline__ void master_dma(const DecodeParams& P, int l, int h, int j, int g,
+                                           vu4* ring) {
+  const T* mkp = reinterpret_cast<const T*>(P.mk.data) + dense_offset(P.mk, l, 0, h, j);
+  const T* mvp = reinterpret_cast<const T*>(P.mv.data) + dense_offset(P.mv, l, 0, h, j);
+  const void* src[4] = {mkp + M::off0(g), mkp + M::off1(g), mvp + M::off0(g), mvp + M::off1(g)};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) __builtin_amdgcn_global_load_lds(src[q], to_lds(ring + 64 * q), 16, 0, 0);
+}
+
+// The same for an agent's packed rows (diff slot `slot`, head h, token t of
+// the block).
+template <typename T, typename M, int HD>
+__device__ __forceinline__ void vals_dma(const DecodeParams& P, int64_t slot, int h, int t, int g,
+                                         vu4* ring) {
+  const int64_t e = ((slot * P.H + h) * (int64_t)P.bt + t) * HD;
+  const T* pk = reinterpret_cast<const T*>(P.vals_k) + e;
+  const T* pv = reinterpret_cast<const T*>(P.vals_v) + e;
+  const void* src[4] = {pk + M::off0(g), pk + M::off1(g), pv + M::off0(g), pv + M::off1(g)};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) __builtin_amdgcn_global_load_lds(src[q], to_lds(ring + 64 * q), 16, 0, 0);
+}
+
+// Wait until every vector memory operation of this wave issued before its
+// last `younger` ones is complete (the wait allows 2^k - 1 operations in
+// flight for the largest such count not above `younger`, at most 63).
+__device__ __forceinline__ void wait_vm_behind(int younger) {
+  if (younger >= 63) wait_vm<63>();
+  else if (younger >= 31) wait_vm<31>();
+  else if (younger >= 15) wait_vm<15>();
+  else if (younger >= 7) wait_vm<7>();
+  else if (younger >= 3) wait_vm<3>();
+  else wait_vm<0>();
+}
+
+template <typename T, int HD, int STYLE, bool DENSE>
 __global__ __launch_bounds__(kDiffBlock) void diff_decode_kernel(DecodeParams P,
                                                                  const double2* tab) {
   // Values are rotated in fp32 for bf16 storage (one rounding to bf16, as in
@@ -303,7 +364,16 @@ __global__ __launch_bounds__(kDiffBlock) void diff_decode_kernel(DecodeParams P,
   __shared__ int64_t sslot[kAgentGroup];       // packed slot of the agent's block, or -1
   // page ids of the group's output rows (paged output planes: the slot
   // mapping), staged once per group so that no store waits on a table read
-  __shared__ int32_t spk[kAgentGroup * kMaxBlockTokens], spv[kAgentGroup * kMaxBlockTokens];
+  __shared__ int32_t spk[DENSE ? 1 : kAgentGroup * kMaxBlockTokens];
+  __shared__ int32_t spv[DENSE ? 1 : kAgentGroup * kMaxBlockTokens];
+  // dense planes: each wave's master rows of the next pass and the packed
+  // rows of the pass's first agent with a diff block, loaded straight into
+  // LDS (four 16-byte pieces per lane each); the group's agents in the order
+  // the passes take them, agents without a diff block first
+  __shared__ vu4 mring[DENSE ? kDiffBlock / 64 : 1][4][64];
+  __shared__ vu4 dring[DENSE ? kDiffBlock / 64 : 1][4][64];
+  __shared__ int32_t sorder[kAgentGroup];
+  __shared__ int32_t sndiff;
   const int g = threadIdx.x % G, rr = threadIdx.x / G;
   const int beta = blockIdx.x % P.nb;
   const int l = blockIdx.x / P.nb;
@@ -327,24 +397,69 @@ __global__ __launch_bounds__(kDiffBlock) void diff_decode_kernel(DecodeParams P,
       }
       sslot[threadIdx.x] = slot;
     }
-    for (int i = threadIdx.x; i < na * tb; i += kDiffBlock) {
-      const int a = i / tb, t = i % tb;
-      spk[a * kMaxBlockTokens + t] = page_of(P.ok, a0 + a, t0 + t);
-      spv[a * kMaxBlockTokens + t] = page_of(P.ov, a0 + a, t0 + t);
+    if (!DENSE) {
+      for (int i = threadIdx.x; i < na * tb; i += kDiffBlock) {
+        const int a = i / tb, t = i % tb;
+        spk[a * kMaxBlockTokens + t] = page_of(P.ok, a0 + a, t0 + t);
+        spv[a * kMaxBlockTokens + t] = page_of(P.ov, a0 + a, t0 + t);
+      }
     }
     __syncthreads();
-    for (int r = rr; r < rows; r += RPB) {
+    if (DENSE) {
+      if (threadIdx.x == 0) {
+        int k = 0, nd = 0;
+        for (int a = 0; a < na; ++a)
+          if (sslot[a] < 0) sorder[k++] = a;
+        for (int a = 0; a < na; ++a)
+          if (sslot[a] >= 0) { sorder[k++] = a; ++nd; }
+        sndiff = nd;
+      }
+      __syncthreads();
+    }
+    // Dense planes: loads and stores share one in-order counter, so a load
+    // issued behind stores cannot be waited for without waiting for them.
+    // A pass's master rows are therefore loaded into the wave's LDS ring at
+    // the start of the previous pass, before its stores (at least 4 * na:
+    // K and V, two pieces each, per agent), and the packed rows of the
+    // pass's first agent with a diff block at the start of the pass, before
+    // the stores of the agents without one, which go first.  Paged planes
+    // load every row in place.
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int nd = DENSE ? sndiff : 0;
+    if (DENSE && rr < rows) master_dma<T, M>(P, l, rr / tb, t0 + rr % tb, g, &mring[wave][0][0]);
+    for (int r = rr, pass = 0; r < rows; r += RPB, ++pass) {
       const int h = r / tb, t = r % tb;
       // the master row, once per group of agents
-      const T* mkp = reinterpret_cast<const T*>(P.mk.data) + row_offset(P.mk, l, 0, h, t0 + t);
-      const T* mvp = reinterpret_cast<const T*>(P.mv.data) + row_offset(P.mv, l, 0, h, t0 + t);
-      vu4 mk0 = ld16(mkp + M::off0(g)), mk1 = ld16(mkp + M::off1(g));
-      vu4 mv0 = ld16(mvp + M::off0(g)), mv1 = ld16(mvp + M::off1(g));
-      settle(mk0); settle(mk1); settle(mv0); settle(mv1);
-      for (int a = 0; a < na; ++a) {
-        const int64_t slot = sslot[a];          // uniform over the block
+      vu4 mk0, mk1, mv0, mv1;
+      if (DENSE) {
+        wait_vm_behind(pass == 0 ? 0 : 4 * na);
+        mk0 = mring[wave][0][lane]; mk1 = mring[wave][1][lane];
+        mv0 = mring[wave][2][lane]; mv1 = mring[wave][3][lane];
+        // the rings are this wave's and this lane's: once the reads are done
+        // (the packed rows' in the previous pass too) they take new rows
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (nd > 0) vals_dma<T, M, HD>(P, sslot[sorder[na - nd]], h, t, g, &dring[wave][0][0]);
+        if (r + RPB < rows)
+          master_dma<T, M>(P, l, (r + RPB) / tb, t0 + (r + RPB) % tb, g, &mring[wave][0][0]);
+      } else {
+        const T* mkp = reinterpret_cast<const T*>(P.mk.data) + row_offset(P.mk, l, 0, h, t0 + t);
+        const T* mvp = reinterpret_cast<const T*>(P.mv.data) + row_offset(P.mv, l, 0, h, t0 + t);
+        mk0 = ld16(mkp + M::off0(g)); mk1 = ld16(mkp + M::off1(g));
+        mv0 = ld16(mvp + M::off0(g)); mv1 = ld16(mvp + M::off1(g));
+        settle(mk0); settle(mk1); settle(mv0); settle(mv1);
+      }
+      for (int i = 0; i < na; ++i) {
+        const int a = DENSE ? sorder[i] : i;    // uniform over the block
+        const int64_t slot = sslot[a];
         vu4 k0 = mk0, k1 = mk1, v0 = mv0, v1 = mv1;
-        if (slot >= 0) {
+        if (DENSE && i == na - nd) {
+          // the first agent with a diff block: its rows are in the ring,
+          // with at least 4 stores per agent without one issued since
+          wait_vm_behind(4 * (na - nd));
+          k0 = dring[wave][0][lane]; k1 = dring[wave][1][lane];
+          v0 = dring[wave][2][lane]; v1 = dring[wave][3][lane];
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        } else if (slot >= 0) {
           const int64_t e = ((slot * P.H + h) * (int64_t)P.bt + t) * HD;
           const T* pk = reinterpret_cast<const T*>(P.vals_k) + e;
           const T* pv = reinterpret_cast<const T*>(P.vals_v) + e;
@@ -366,14 +481,18 @@ __global__ __launch_bounds__(kDiffBlock) void diff_decode_kernel(DecodeParams P,
         parts_to_pairs<STYLE, V>(p0, p1, xa, xb);
         rotate_pairs<V>(xa, xb, cs, sn);
         pairs_to_parts<STYLE, V>(xa, xb, p0, p1);
-        const int64_t ko = row_offset_page(P.ok, l, a0 + a, h, t0 + t, spk[a * kMaxBlockTokens + t]);
-        const int64_t vo = row_offset_page(P.ov, l, a0 + a, h, t0 + t, spv[a * kMaxBlockTokens + t]);
-        if (ko >= 0) {
+        const int64_t ko =
+            DENSE ? dense_offset(P.ok, l, a0 + a, h, t0 + t)
+                  : row_offset_page(P.ok, l, a0 + a, h, t0 + t, spk[a * kMaxBlockTokens + t]);
+        const int64_t vo =
+            DENSE ? dense_offset(P.ov, l, a0 + a, h, t0 + t)
+                  : row_offset_page(P.ov, l, a0 + a, h, t0 + t, spv[a * kMaxBlockTokens + t]);
+        if (DENSE || ko >= 0) {
           T* dk = reinterpret_cast<T*>(P.ok.data) + ko;
           st16(dk + M::off0(g), Cd::pack(p0));
           st16(dk + M::off1(g), Cd::pack(p1));
         }
-        if (vo >= 0) {
+        if (DENSE || vo >= 0) {
           T* dv = reinterpret_cast<T*>(P.ov.data) + vo;
           st16(dv + M::off0(g), v0);
           st16(dv + M::off1(g), v1);
@@ -487,8 +606,12 @@ struct PackLaunch {
 template <typename T, int HD, int STYLE>
 struct DecodeLaunch {
   static kvfix_status run(const DecodeParams& P, const double2* tab, hipStream_t st) {
-    diff_decode_kernel<T, HD, STYLE>
-        <<<dim3((unsigned)((int64_t)P.L * P.nb)), dim3(kDiffBlock), 0, st>>>(P, tab);
+    const dim3 grid((unsigned)((int64_t)P.L * P.nb)), block(kDiffBlock);
+    const bool dense = !P.mk.page_table && !P.mv.page_table && !P.ok.page_table && !P.ov.page_table;
+    if (dense)
+      diff_decode_kernel<T, HD, STYLE, true><<<grid, block, 0, st>>>(P, tab);
+    else
+      diff_decode_kernel<T, HD, STYLE, false><<<grid, block, 0, st>>>(P, tab);
     return launch_status();
   }
 };

@@ -222,6 +222,51 @@ def test_diff_encode_decode_small_collective(style, dtype, hd_note):
         assert np.abs(ok.astype(np.float64) - sk).max() <= 8 * 2.0 ** -24 * np.abs(sk).max()
 
 
+# listed agents per block of the decode's mixes below: every agent, none,
+# two, only the first, and three across the boundary of the first 16-agent
+# group (the last block is ragged: 11 of 16 tokens)
+LISTED_MIX = {0: list(range(19)), 1: [], 2: [3, 11], 3: [0], 4: [15, 16, 18]}
+
+
+@pytest.mark.parametrize("hd,dtype,style", [(128, "bf16", "half"), (64, "bf16", "interleaved"),
+                                            (256, "bf16", "half"), (128, "f32", "half")])
+def test_diff_decode_listed_block_mixes(hd, dtype, style):
+    rng = np.random.default_rng(83 + hd)
+    L, A, H, n, bt, theta, eps = 2, 19, 3, 75, 16, 1e4, 0.0625
+    offs = [int(o) for o in rng.integers(0, 16385, size=A)]
+    master_k = K.store(rng.standard_normal((L, 1, H, n, hd)), dtype)
+    master_v = K.store(rng.standard_normal((L, 1, H, n, hd)), dtype)
+    yk = np.repeat(K.to_f64(master_k, dtype), A, axis=1)
+    yv = np.repeat(K.to_f64(master_v, dtype), A, axis=1)
+    for beta, agents in LISTED_MIX.items():
+        tb = min(bt, n - beta * bt)
+        for a in agents:
+            for l in range(L):
+                h, t, d = rng.integers(H), beta * bt + rng.integers(tb), rng.integers(hd)
+                yk[l, a, h, t, d] += 1.0
+                yv[l, a, h, (t + 1 - beta * bt) % tb + beta * bt, d] -= 1.0
+    sk = K.rope_shift(K.store(yk, dtype), dtype, offs, theta, style)
+    sv = K.store(yv, dtype)
+    st = kv.ROPE_HALF if style == "half" else kv.ROPE_INTERLEAVED
+    o = K.diff_encode(master_k, master_v, sk, sv, [-x for x in offs], theta, eps, bt, style,
+                      dtype)
+    for a in range(A):
+        for l in range(L):
+            listed = [b for b in range(5) if K.mask_bit(o["mask"][a, l], b)]
+            assert listed == [b for b, ag in LISTED_MIX.items() if a in ag]
+    diff, status, t = gpu_encode(master_k, master_v, sk, sv, [-x for x in offs], theta, eps, bt,
+                                 o["total"] + 5, st)
+    assert status == 0
+    g = diff_np(diff)
+    assert np.array_equal(g["mask"], o["mask"])
+    assert np.array_equal(g["offsets"], o["offsets"])
+    ok, ov = gpu_decode(t, diff, offs, theta, A, st)
+    ook, oov = K.diff_decode(master_k, master_v, g, offs, theta, A, bt, style, dtype)
+    assert_values(ok, ook, dtype, "decode K")
+    assert np.array_equal(ov, oov)
+    assert np.array_equal(ov, sv)
+
+
 def test_diff_lossless_roundtrip_zero_shift_zero_eps():
     rng = np.random.default_rng(61)
     L, A, H, n, hd, bt = 2, 3, 2, 37, 128, 16
