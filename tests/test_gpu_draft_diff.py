@@ -265,6 +265,25 @@ def test_diff_decode_listed_block_mixes(hd, dtype, style):
     assert_values(ok, ook, dtype, "decode K")
     assert np.array_equal(ov, oov)
     assert np.array_equal(ov, sv)
+    # the same restore into a paged pool (its rows addressed through the
+    # slot mapping, the master's loaded in place): equal bit for bit
+    ps = 16
+    pps = -(-n // ps)
+    n_pages = A * pps + 3
+    pt_np = np.random.default_rng(hd).permutation(n_pages)[: A * pps].reshape(A, pps)
+    pt = torch.from_numpy(pt_np.astype(np.int32)).to(DEV)
+    pool_k = torch.full((L, n_pages, ps, H, hd), float("nan"), dtype=t["mk"].dtype, device=DEV)
+    pool_v = torch.full_like(pool_k, float("nan"))
+    ws = torch.empty(kv.kvfix_diff_decode_workspace(A, hd) + 256, dtype=torch.uint8, device=DEV)
+    d = torch.tensor(offs, dtype=torch.int64, device=DEV)
+    log("diff_decode paged", (L, A, H, n, hd))
+    kv.kvfix_diff_decode(Plane.dense(t["mk"]), Plane.dense(t["mv"]), diff, d, theta,
+                         Plane.paged(pool_k, pt, ps, n), Plane.paged(pool_v, pt, ps, n), ws, st)
+    torch.cuda.synchronize()
+    tok = np.arange(n)
+    for pool, dense in ((pool_k, ok), (pool_v, ov)):
+        rows = to_np(pool)[:, pt_np[:, tok // ps], tok % ps]         # [L][A][n][H][hd]
+        assert np.array_equal(rows.transpose(0, 1, 3, 2, 4), dense)
 
 
 def test_diff_lossless_roundtrip_zero_shift_zero_eps():
