@@ -99,12 +99,6 @@ __device__ __forceinline__ bf16x8 ld_op(const bf16_t* p) {
   return __builtin_bit_cast(bf16x8, ld16_cached(p));
 }
 
-typedef __attribute__((address_space(3))) void* lds_ptr;
-
-__device__ __forceinline__ lds_ptr to_lds(void* p) {
-  return (lds_ptr)(__builtin_amdgcn_readfirstlane((int)(uintptr_t)p));
-}
-
 // Wait until at most N of this thread's vector memory operations are
 // outstanding and its LDS operations are done, then meet the block.  The
 // compiler may not move memory accesses across it; unlike __syncthreads it
@@ -113,7 +107,7 @@ template <int N>
 __device__ __forceinline__ void stage_barrier() {
   static_assert(N >= 0 && N < 16, "vmcnt");
   asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(N | (7 << 4));      // vmcnt(N), lgkmcnt(0)
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(N, 0));
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }

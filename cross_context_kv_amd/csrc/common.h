@@ -28,6 +28,20 @@ constexpr int kMaxHeadDim = 256;
 typedef uint16_t bf16_t;          // bfloat16 storage (bit pattern)
 typedef uint32_t vu4 __attribute__((ext_vector_type(4)));   // one 16-byte vector
 
+// Immediate of s_waitcnt: at most vm vector memory operations (6 bits, split
+// over bits 3:0 and 15:14) and lgkm LDS / scalar operations (4 bits) left in
+// flight; export count not waited on.
+constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8);
+}
+
+// An LDS address as a wave-uniform 32-bit offset, the form a direct
+// global-to-LDS load takes.
+typedef __attribute__((address_space(3))) void* lds_ptr;
+__device__ __forceinline__ lds_ptr to_lds(void* p) {
+  return (lds_ptr)(__builtin_amdgcn_readfirstlane((int)(uintptr_t)p));
+}
+
 // Device view of a plane (element strides; byte base pointer).
 struct DPlane {
   char* data;

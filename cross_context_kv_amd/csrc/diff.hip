@@ -296,21 +296,14 @@ template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt");
   asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(N, 15));
   asm volatile("" ::: "memory");
 }
-
-typedef __attribute__((address_space(3))) void* lds_ptr;
 
 // Element offset of row (l, s, h, j) of a plane known to be dense.
 __device__ __forceinline__ int64_t dense_offset(const DPlane& p, int l, int s, int h, int j) {
   return (int64_t)l * p.s_layer + (int64_t)s * p.s_seg + (int64_t)h * p.s_head +
          (int64_t)j * p.s_token;
-}
-
-// An LDS address as a wave-uniform 32-bit offset.
-__device__ __forceinline__ lds_ptr to_lds(void* p) {
-  return (lds_ptr)(__builtin_amdgcn_readfirstlane((int)(uintptr_t)p));
 }
 
 // Direct-to-LDS loads of this wave's master rows (K and V, two 16-byte
