@@ -286,6 +286,44 @@ def test_diff_decode_listed_block_mixes(hd, dtype, style):
         assert np.array_equal(rows.transpose(0, 1, 3, 2, 4), dense)
 
 
+@pytest.mark.parametrize("bt,n", [(1, 9), (7, 50), (32, 97), (64, 130)])
+def test_diff_block_sizes(bt, n):
+    """Encode and restore with block sizes from one token to the largest,
+    ragged tails, about a third of the (agent, layer, block) triples listed."""
+    rng = np.random.default_rng(1000 + bt)
+    L, A, H, hd, theta, eps = 2, 5, 2, 128, 1e4, 0.0625
+    nb = -(-n // bt)
+    offs = [int(o) for o in rng.integers(0, 16385, size=A)]
+    master_k = K.store(rng.standard_normal((L, 1, H, n, hd)), "bf16")
+    master_v = K.store(rng.standard_normal((L, 1, H, n, hd)), "bf16")
+    yk = np.repeat(K.to_f64(master_k, "bf16"), A, axis=1)
+    yv = np.repeat(K.to_f64(master_v, "bf16"), A, axis=1)
+    planted = rng.random((A, L, nb)) < 0.35
+    for a, l, beta in zip(*np.nonzero(planted)):
+        t = beta * bt + rng.integers(min(bt, n - beta * bt))
+        if rng.random() < 0.5:
+            yk[l, a, rng.integers(H), t, rng.integers(hd)] += 1.0
+        else:
+            yv[l, a, rng.integers(H), t, rng.integers(hd)] -= 1.0
+    sk = K.rope_shift(K.store(yk, "bf16"), "bf16", offs, theta)
+    sv = K.store(yv, "bf16")
+    o = K.diff_encode(master_k, master_v, sk, sv, [-x for x in offs], theta, eps, bt)
+    for a in range(A):
+        for l in range(L):
+            assert [K.mask_bit(o["mask"][a, l], b) for b in range(nb)] == planted[a, l].tolist()
+    diff, status, t = gpu_encode(master_k, master_v, sk, sv, [-x for x in offs], theta, eps, bt,
+                                 o["total"] + 2)
+    assert status == 0
+    g = diff_np(diff)
+    assert np.array_equal(g["mask"], o["mask"])
+    assert np.array_equal(g["offsets"], o["offsets"])
+    assert np.array_equal(g["block_idx"][: o["total"]], o["block_idx"])
+    ok, ov = gpu_decode(t, diff, offs, theta, A)
+    ook, oov = K.diff_decode(master_k, master_v, g, offs, theta, A, bt)
+    assert_values(ok, ook, "bf16", "decode K")
+    assert np.array_equal(ov, oov) and np.array_equal(ov, sv)
+
+
 def test_diff_lossless_roundtrip_zero_shift_zero_eps():
     rng = np.random.default_rng(61)
     L, A, H, n, hd, bt = 2, 3, 2, 37, 128, 16
