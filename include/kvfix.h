@@ -431,8 +431,9 @@ kvfix_status kvfix_diff_encode(const kvfix_plane* master_k, const kvfix_plane* m
  * (a, l) overwritten by their packed values, keys then rotated forward by
  * from_master->delta[a] positions (fp32 for bf16 planes, fp64 for fp32
  * planes; sine and cosine from fp64; one rounding); values copied.  No
- * dense mirror is materialised: each master block is read once from HBM and
- * written to every agent.  out_k/out_v: planes with n_segs = n_agents.
+ * dense mirror is materialised: each master block is read from HBM once per
+ * group of 16 agents and written to each of them.  out_k/out_v: planes with
+ * n_segs = n_agents.
  * A listed block whose slot lies at or past capacity_blocks (an encode that
  * reported KVFIX_ERR_CAPACITY) is restored from the master instead.
  * ws: device workspace of kvfix_diff_decode_workspace(...) bytes (the
