@@ -344,7 +344,7 @@ __device__ __forceinline__ void wait_vm_behind(int younger) {
   else wait_vm<0>();
 }
 
-template <typename T, int HD, int STYLE, bool DENSE>
+template <typename T, int HD, int STYLE, bool RING, bool PAGED_OUT>
 __global__ __launch_bounds__(kDiffBlock) void diff_decode_kernel(DecodeParams P,
                                                                  const double2* tab) {
   // Values are rotated in fp32 for bf16 storage (one rounding to bf16, as in
@@ -357,14 +357,14 @@ __global__ __launch_bounds__(kDiffBlock) void diff_decode_kernel(DecodeParams P,
   __shared__ int64_t sslot[kAgentGroup];       // packed slot of the agent's block, or -1
   // page ids of the group's output rows (paged output planes: the slot
   // mapping), staged once per group so that no store waits on a table read
-  __shared__ int32_t spk[DENSE ? 1 : kAgentGroup * kMaxBlockTokens];
-  __shared__ int32_t spv[DENSE ? 1 : kAgentGroup * kMaxBlockTokens];
-  // dense planes: each wave's master rows of the next pass and the packed
+  __shared__ int32_t spk[PAGED_OUT ? kAgentGroup * kMaxBlockTokens : 1];
+  __shared__ int32_t spv[PAGED_OUT ? kAgentGroup * kMaxBlockTokens : 1];
+  // dense master planes: each wave's master rows of the next pass and the packed
   // rows of the pass's first agent with a diff block, loaded straight into
   // LDS (four 16-byte pieces per lane each); the group's agents in the order
   // the passes take them, agents without a diff block first
-  __shared__ vu4 mring[DENSE ? kDiffBlock / 64 : 1][4][64];
-  __shared__ vu4 dring[DENSE ? kDiffBlock / 64 : 1][4][64];
+  __shared__ vu4 mring[RING ? kDiffBlock / 64 : 1][4][64];
+  __shared__ vu4 dring[RING ? kDiffBlock / 64 : 1][4][64];
   __shared__ int32_t sorder[kAgentGroup];
   __shared__ int32_t sndiff;
   const int g = threadIdx.x % G, rr = threadIdx.x / G;
@@ -390,7 +390,7 @@ __global__ __launch_bounds__(kDiffBlock) void diff_decode_kernel(DecodeParams P,
       }
       sslot[threadIdx.x] = slot;
     }
-    if (!DENSE) {
+    if (PAGED_OUT) {
       for (int i = threadIdx.x; i < na * tb; i += kDiffBlock) {
         const int a = i / tb, t = i % tb;
         spk[a * kMaxBlockTokens + t] = page_of(P.ok, a0 + a, t0 + t);
@@ -398,7 +398,7 @@ __global__ __launch_bounds__(kDiffBlock) void diff_decode_kernel(DecodeParams P,
       }
     }
     __syncthreads();
-    if (DENSE) {
+    if (RING) {
       if (threadIdx.x == 0) {
         int k = 0, nd = 0;
         for (int a = 0; a < na; ++a)
@@ -409,31 +409,37 @@ __global__ __launch_bounds__(kDiffBlock) void diff_decode_kernel(DecodeParams P,
       }
       __syncthreads();
     }
-    // Dense planes: loads and stores share one in-order counter, so a load
+    // Dense master planes: loads and stores share one in-order counter, so a load
     // issued behind stores cannot be waited for without waiting for them.
     // A pass's master rows are therefore loaded into the wave's LDS ring at
     // the start of the previous pass, before its stores (at least 4 * na:
     // K and V, two pieces each, per agent), and the packed rows of the
     // pass's first agent with a diff block at the start of the pass, before
-    // the stores of the agents without one, which go first.  Paged planes
-    // load every row in place.
+    // the stores of the agents without one, which go first.  A dense output
+    // issues 4 stores per agent; a paged one skips a store where no lane has
+    // a valid row, so its waits count the stores the wave has issued since
+    // (loads are not counted, which only makes a wait stricter).  Paged
+    // master planes load every row in place.
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int nd = DENSE ? sndiff : 0;
-    if (DENSE && rr < rows) master_dma<T, M>(P, l, rr / tb, t0 + rr % tb, g, &mring[wave][0][0]);
+    const int nd = RING ? sndiff : 0;
+    if (RING && rr < rows) master_dma<T, M>(P, l, rr / tb, t0 + rr % tb, g, &mring[wave][0][0]);
+    int since_m = 0, since_d = 0;   // stores issued since the master / packed-row loads
     for (int r = rr, pass = 0; r < rows; r += RPB, ++pass) {
       const int h = r / tb, t = r % tb;
       // the master row, once per group of agents
       vu4 mk0, mk1, mv0, mv1;
-      if (DENSE) {
-        wait_vm_behind(pass == 0 ? 0 : 4 * na);
+      if (RING) {
+        wait_vm_behind(pass == 0 ? 0 : PAGED_OUT ? since_m : 4 * na);
         mk0 = mring[wave][0][lane]; mk1 = mring[wave][1][lane];
         mv0 = mring[wave][2][lane]; mv1 = mring[wave][3][lane];
         // the rings are this wave's and this lane's: once the reads are done
         // (the packed rows' in the previous pass too) they take new rows
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if (nd > 0) vals_dma<T, M, HD>(P, sslot[sorder[na - nd]], h, t, g, &dring[wave][0][0]);
+        since_d = 0;
         if (r + RPB < rows)
           master_dma<T, M>(P, l, (r + RPB) / tb, t0 + (r + RPB) % tb, g, &mring[wave][0][0]);
+        since_m = 0;
       } else {
         const T* mkp = reinterpret_cast<const T*>(P.mk.data) + row_offset(P.mk, l, 0, h, t0 + t);
         const T* mvp = reinterpret_cast<const T*>(P.mv.data) + row_offset(P.mv, l, 0, h, t0 + t);
@@ -442,13 +448,13 @@ __global__ __launch_bounds__(kDiffBlock) void diff_decode_kernel(DecodeParams P,
         settle(mk0); settle(mk1); settle(mv0); settle(mv1);
       }
       for (int i = 0; i < na; ++i) {
-        const int a = DENSE ? sorder[i] : i;    // uniform over the block
+        const int a = RING ? sorder[i] : i;     // uniform over the block
         const int64_t slot = sslot[a];
         vu4 k0 = mk0, k1 = mk1, v0 = mv0, v1 = mv1;
-        if (DENSE && i == na - nd) {
+        if (RING && i == na - nd) {
           // the first agent with a diff block: its rows are in the ring,
-          // with at least 4 stores per agent without one issued since
-          wait_vm_behind(4 * (na - nd));
+          // behind the stores of the agents without one
+          wait_vm_behind(PAGED_OUT ? since_d : 4 * (na - nd));
           k0 = dring[wave][0][lane]; k1 = dring[wave][1][lane];
           v0 = dring[wave][2][lane]; v1 = dring[wave][3][lane];
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -475,20 +481,25 @@ __global__ __launch_bounds__(kDiffBlock) void diff_decode_kernel(DecodeParams P,
         rotate_pairs<V>(xa, xb, cs, sn);
         pairs_to_parts<STYLE, V>(xa, xb, p0, p1);
         const int64_t ko =
-            DENSE ? dense_offset(P.ok, l, a0 + a, h, t0 + t)
-                  : row_offset_page(P.ok, l, a0 + a, h, t0 + t, spk[a * kMaxBlockTokens + t]);
+            PAGED_OUT ? row_offset_page(P.ok, l, a0 + a, h, t0 + t, spk[a * kMaxBlockTokens + t])
+                      : dense_offset(P.ok, l, a0 + a, h, t0 + t);
         const int64_t vo =
-            DENSE ? dense_offset(P.ov, l, a0 + a, h, t0 + t)
-                  : row_offset_page(P.ov, l, a0 + a, h, t0 + t, spv[a * kMaxBlockTokens + t]);
-        if (DENSE || ko >= 0) {
+            PAGED_OUT ? row_offset_page(P.ov, l, a0 + a, h, t0 + t, spv[a * kMaxBlockTokens + t])
+                      : dense_offset(P.ov, l, a0 + a, h, t0 + t);
+        if (!PAGED_OUT || ko >= 0) {
           T* dk = reinterpret_cast<T*>(P.ok.data) + ko;
           st16(dk + M::off0(g), Cd::pack(p0));
           st16(dk + M::off1(g), Cd::pack(p1));
         }
-        if (DENSE || vo >= 0) {
+        if (!PAGED_OUT || vo >= 0) {
           T* dv = reinterpret_cast<T*>(P.ov.data) + vo;
           st16(dv + M::off0(g), v0);
           st16(dv + M::off1(g), v1);
+        }
+        if (RING && PAGED_OUT) {
+          const int issued = 2 * (__ballot(ko >= 0) != 0) + 2 * (__ballot(vo >= 0) != 0);
+          since_m += issued;
+          since_d += issued;
         }
       }
     }
@@ -600,11 +611,15 @@ template <typename T, int HD, int STYLE>
 struct DecodeLaunch {
   static kvfix_status run(const DecodeParams& P, const double2* tab, hipStream_t st) {
     const dim3 grid((unsigned)((int64_t)P.L * P.nb)), block(kDiffBlock);
-    const bool dense = !P.mk.page_table && !P.mv.page_table && !P.ok.page_table && !P.ov.page_table;
-    if (dense)
-      diff_decode_kernel<T, HD, STYLE, true><<<grid, block, 0, st>>>(P, tab);
+    // the LDS rings need dense master planes; paged outputs take staged page ids
+    const bool ring = !P.mk.page_table && !P.mv.page_table;
+    const bool paged_out = P.ok.page_table || P.ov.page_table;
+    if (ring && !paged_out)
+      diff_decode_kernel<T, HD, STYLE, true, false><<<grid, block, 0, st>>>(P, tab);
+    else if (ring)
+      diff_decode_kernel<T, HD, STYLE, true, true><<<grid, block, 0, st>>>(P, tab);
     else
-      diff_decode_kernel<T, HD, STYLE, false><<<grid, block, 0, st>>>(P, tab);
+      diff_decode_kernel<T, HD, STYLE, false, true><<<grid, block, 0, st>>>(P, tab);
     return launch_status();
   }
 };
