@@ -229,7 +229,8 @@ LISTED_MIX = {0: list(range(19)), 1: [], 2: [3, 11], 3: [0], 4: [15, 16, 18]}
 
 
 @pytest.mark.parametrize("hd,dtype,style", [(128, "bf16", "half"), (64, "bf16", "interleaved"),
-                                            (256, "bf16", "half"), (128, "f32", "half")])
+                                            (256, "bf16", "half"), (128, "f32", "half"),
+                                            (64, "f32", "half"), (256, "f32", "interleaved")])
 def test_diff_decode_listed_block_mixes(hd, dtype, style):
     rng = np.random.default_rng(83 + hd)
     L, A, H, n, bt, theta, eps = 2, 19, 3, 75, 16, 1e4, 0.0625
