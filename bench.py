@@ -847,10 +847,16 @@ class C3(Workload):
             par["mismatches"]["packed V elements"] = int(np.sum(
                 host(self.diff.vals_v, torch, np)[slots] != o["vals_v"]))
         if self.layout != "paged":
-            par["max_rel_err"]["restored K"] = max_rel_err(np, host(t["o_k"][:1], torch, np),
-                                                           box["ok"], "bf16")
-            par["mismatches"]["restored V elements"] = int(np.sum(
-                host(t["o_v"][:1], torch, np) != box["ov"]))
+            g_ok, g_ov = host(t["o_k"][:1], torch, np), host(t["o_v"][:1], torch, np)
+        else:
+            # layer 0 gathered from the pool through the slot mapping:
+            # pool [L][page][16][H][hd] -> [1][A][H][n][hd]
+            tok = np.arange(c.n_tokens)
+            pt = host(t["pt"], torch, np)
+            g_ok, g_ov = ((host(t[k][:1], torch, np)[:, pt[:, tok // 16], tok % 16]
+                           .transpose(0, 1, 3, 2, 4)) for k in ("o_k", "o_v"))
+        par["max_rel_err"]["restored K"] = max_rel_err(np, g_ok, box["ok"], "bf16")
+        par["mismatches"]["restored V elements"] = int(np.sum(g_ov != box["ov"]))
         self.parity = par
         sub = C3.__new__(C3)
         sub.cfg, sub.total, sub.layout = c.replace(n_layers=1), box["total"], self.layout
