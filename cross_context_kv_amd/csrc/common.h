@@ -39,7 +39,7 @@ constexpr int waitcnt_imm(int vm, int lgkm) {
 // global-to-LDS load takes.
 typedef __attribute__((address_space(3))) void* lds_ptr;
 __device__ __forceinline__ lds_ptr to_lds(void* p) {
-  return (lds_ptr)(__builtin_amdgcn_readfirstlane((int)(uintptr_t)p));
+  return (lds_ptr)(uintptr_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uintptr_t)p);
 }
 
 // Device view of a plane (element strides; byte base pointer).
